@@ -1,0 +1,210 @@
+"""CPU oracle of the W4A16 group-wise quantization core -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py``
+may import this package.  The product path (``w4a16_group_wise_amd``) never touches it and
+shares no code with it.  The arithmetic lives in ``oracle.c`` (plain C, fp64), compiled with
+gcc into ``liboracle.so``; this module only marshals numpy arrays.
+
+Functions and the passages they follow (page titles and sections):
+  hessian, hessian_entries  -- "Opt.Gear-QAT: Preserving On-Device Performance with QAT",
+                               section 2 (second-order view, H = X^T X).
+  code, candidate           -- model card "Opt.Gear-1B-qat-int4-per-channel-unquantized",
+                               "Quantization Configuration" (symmetric, zero-point 0) and the
+                               blog's "Quantization parameters" (group 32).
+  scale_search(_groups)     -- model card "Quantization Configuration" objective, per group.
+  pack                      -- model card "QAT Highlights" / "Quickstart"; blog "Conclusion".
+  lsq_fwd, lsq_bwd          -- blog section 3 (LSQ forward, STE, normalised scale gradient).
+  gemm_cols                 -- model card intro (W4A16: INT4 weights, 16-bit activations).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile liboracle.so with gcc (OpenMP across independent units, no fp contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off",
+                               "-fno-fast-math", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _L():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int64
+        lib.orc_threads.restype = ctypes.c_int
+        lib.orc_f32_to_f16.restype = ctypes.c_uint16
+        lib.orc_f32_to_f16.argtypes = [ctypes.c_float]
+        lib.orc_f16_to_f64.restype = ctypes.c_double
+        lib.orc_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.orc_bf16_to_f64.restype = ctypes.c_double
+        lib.orc_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.orc_code.restype = ctypes.c_int
+        lib.orc_code.argtypes = [ctypes.c_double, ctypes.c_double]
+        lib.orc_candidate.restype = ctypes.c_float
+        lib.orc_candidate.argtypes = [ctypes.c_float, ctypes.c_float]
+        lib.orc_unpack.restype = ctypes.c_int
+        lib.orc_unpack.argtypes = [P, I]
+        lib.orc_hessian.argtypes = [P, I, I, P]
+        lib.orc_hessian_entries.argtypes = [P, I, I, P, I, P]
+        lib.orc_scale_search.argtypes = [P, I, I, P, I, P, ctypes.c_int, P, P, P, P]
+        lib.orc_scale_search_groups.argtypes = [P, I, P, I, P, ctypes.c_int, P, P, I, P, P, P, P]
+        lib.orc_pack.argtypes = [P, P, I, I, P, P]
+        lib.orc_lsq_fwd.argtypes = [P, P, I, I, P]
+        lib.orc_lsq_bwd.argtypes = [P, P, P, I, I, ctypes.c_double, P, P, P]
+        lib.orc_gemm_cols.argtypes = [P, I, P, P, I, P, I, P, P]
+        _lib = lib
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def threads() -> int:
+    return int(_L().orc_threads())
+
+
+# -------------------------------------------------------------- scalar helpers (for pins)
+def f32_to_f16(v: float) -> int:
+    return int(_L().orc_f32_to_f16(float(np.float32(v))))
+
+
+def f16_to_f64(bits: int) -> float:
+    return float(_L().orc_f16_to_f64(int(bits)))
+
+
+def bf16_to_f64(bits: int) -> float:
+    return float(_L().orc_bf16_to_f64(int(bits)))
+
+
+def code(w: float, d: float) -> int:
+    return int(_L().orc_code(float(w), float(d)))
+
+
+def candidate(amax: float, alpha: float) -> float:
+    return float(np.float32(_L().orc_candidate(float(np.float32(amax)), float(np.float32(alpha)))))
+
+
+def unpack(packed_row: np.ndarray, k: int) -> int:
+    row = _c(packed_row, np.uint8)
+    return int(_L().orc_unpack(_p(row), int(k)))
+
+
+# ----------------------------------------------------------------------- array calls
+def hessian(x_bf16: np.ndarray) -> np.ndarray:
+    x = _c(x_bf16, np.uint16)
+    n, d = x.shape
+    h = np.empty((d, d), dtype=np.float64)
+    _L().orc_hessian(_p(x), n, d, _p(h))
+    return h
+
+
+def hessian_entries(x_bf16: np.ndarray, ij: np.ndarray) -> np.ndarray:
+    x = _c(x_bf16, np.uint16)
+    n, d = x.shape
+    ij = _c(ij, np.int64).reshape(-1, 2)
+    out = np.empty(ij.shape[0], dtype=np.float64)
+    _L().orc_hessian_entries(_p(x), n, d, _p(ij), ij.shape[0], _p(out))
+    return out
+
+
+def scale_search(w: np.ndarray, h: np.ndarray, alpha: np.ndarray, with_all: bool = False):
+    """-> (scale f32 [d_out][G], idx u8, obj f64 [d_out][G], obj_all f64 [d_out][G][K] | None)."""
+    w = _c(w, np.float32)
+    h = _c(h, np.float32)
+    alpha = _c(alpha, np.float32)
+    d_out, d_in = w.shape
+    G, K = d_in // 32, alpha.shape[0]
+    scale = np.empty((d_out, G), np.float32)
+    idx = np.empty((d_out, G), np.uint8)
+    obj = np.empty((d_out, G), np.float64)
+    obj_all = np.empty((d_out, G, K), np.float64) if with_all else None
+    _L().orc_scale_search(_p(w), d_out, d_in, _p(h), h.shape[1], _p(alpha), K, _p(scale),
+                          _p(idx), _p(obj), _p(obj_all))
+    return scale, idx, obj, obj_all
+
+
+def scale_search_groups(w: np.ndarray, h: np.ndarray, alpha: np.ndarray, rows: np.ndarray,
+                        groups: np.ndarray, with_all: bool = False):
+    w = _c(w, np.float32)
+    h = _c(h, np.float32)
+    alpha = _c(alpha, np.float32)
+    rows = _c(rows, np.int64)
+    groups = _c(groups, np.int64)
+    cnt, K = rows.shape[0], alpha.shape[0]
+    scale = np.empty(cnt, np.float32)
+    idx = np.empty(cnt, np.uint8)
+    obj = np.empty(cnt, np.float64)
+    obj_all = np.empty((cnt, K), np.float64) if with_all else None
+    _L().orc_scale_search_groups(_p(w), w.shape[1], _p(h), h.shape[1], _p(alpha), K, _p(rows),
+                                 _p(groups), cnt, _p(scale), _p(idx), _p(obj), _p(obj_all))
+    return scale, idx, obj, obj_all
+
+
+def pack(w: np.ndarray, scale: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    w = _c(w, np.float32)
+    scale = _c(scale, np.float32)
+    d_out, d_in = w.shape
+    packed = np.empty((d_out, d_in // 2), np.uint8)
+    s16 = np.empty((d_out, d_in // 32), np.uint16)
+    _L().orc_pack(_p(w), _p(scale), d_out, d_in, _p(packed), _p(s16))
+    return packed, s16
+
+
+def lsq_fwd(w: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    w = _c(w, np.float32)
+    scale = _c(scale, np.float32)
+    out = np.empty_like(w)
+    _L().orc_lsq_fwd(_p(w), _p(scale), w.shape[0], w.shape[1], _p(out))
+    return out
+
+
+def lsq_bwd(w: np.ndarray, scale: np.ndarray, g: np.ndarray, gs: float):
+    """-> (grad_w f32, grad_scale f64 [d_out][G], w_hat f32)."""
+    w = _c(w, np.float32)
+    scale = _c(scale, np.float32)
+    g = _c(g, np.float32)
+    gw = np.empty_like(w)
+    gsc = np.empty((w.shape[0], w.shape[1] // 32), np.float64)
+    wh = np.empty_like(w)
+    _L().orc_lsq_bwd(_p(w), _p(scale), _p(g), w.shape[0], w.shape[1], float(gs), _p(gw),
+                     _p(gsc), _p(wh))
+    return gw, gsc, wh
+
+
+def gemm_cols(x_bf16: np.ndarray, packed: np.ndarray, s16: np.ndarray,
+              cols: Optional[np.ndarray] = None):
+    """-> (y f64 [m][len(cols)], yabs f64 [m][len(cols)]) with yabs = sum |x * w_hat|."""
+    x = _c(x_bf16, np.uint16)
+    packed = _c(packed, np.uint8)
+    s16 = _c(s16, np.uint16)
+    m, d_in = x.shape
+    if cols is None:
+        cols = np.arange(packed.shape[0])
+    cols = _c(cols, np.int64)
+    y = np.empty((m, cols.shape[0]), np.float64)
+    ya = np.empty_like(y)
+    _L().orc_gemm_cols(_p(x), m, _p(packed), _p(s16), d_in, _p(cols), cols.shape[0], _p(y), _p(ya))
+    return y, ya

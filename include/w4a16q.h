@@ -91,7 +91,7 @@ int quant_hessian(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int acc
  *
  *   w        fp32 [d_out][d_in], 16-B aligned.
  *   h        fp32 [d_in][ldh]; only the 32x32 diagonal blocks are read, and each block is
- *            taken to be symmetric (its lower triangle is read).  4-B aligned.
+ *            taken to be symmetric (its upper triangle, diagonal included, is read).
  *   alpha    fp32 [n_cand] DEVICE array of candidate multipliers (> 0, finite).
  *   scale    fp32 [d_out][G] out: Delta_idx (an fp16-representable value).
  *   idx      uint8 [d_out][G] out: chosen candidate index.

@@ -1,0 +1,273 @@
+"""GPU parity of every step against the CPU oracle (configs 1-2 in full, edge cases, ragged
+shapes).  Inputs are the seeded synthetic layers of w4a16_group_wise_amd.synth; each stage is
+fed identical inputs on both sides (e.g. the search gets the GPU's fp32 H on both sides)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w4a16_group_wise_amd as w4q
+from w4a16_group_wise_amd import synth
+from gpu_util import (GEMM_REL, LSQ_REL, bf16_bits_to_np, check_gemm, check_hessian,
+                      check_search, dev_bf16, dev_f32, host_bf16_bits, host_f16_bits)
+
+pytestmark = pytest.mark.gpu
+GS = 1.0 / np.sqrt(32 * 7)
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _search_both(w, h_gpu, alpha, dev, with_all=True):
+    wt, ht, at = dev_f32(w, dev), dev_f32(h_gpu, dev), dev_f32(alpha, dev)
+    sc, ix, ob, oa = w4q.quant_scale_search(wt, ht, at, with_obj=True, with_obj_all=with_all)
+    torch.cuda.synchronize()
+    so, io, oo, oao = oracle.scale_search(w, h_gpu, alpha, with_all=True)
+    return (sc.cpu().numpy(), ix.cpu().numpy(), ob.cpu().numpy(),
+            None if oa is None else oa.cpu().numpy(), so, io, oo, oao)
+
+
+def _cand_fn(w, alpha):
+    G = w.shape[1] // 32
+    amax = np.abs(w.reshape(w.shape[0], G, 32)).max(axis=2).reshape(-1)
+    return lambda i, k: oracle.candidate(float(amax[i]), float(alpha[k]))
+
+
+# ---------------------------------------------------------------------------------- Hessian
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_hessian_config(dev, cfg):
+    c = synth.CONFIGS[cfg]
+    x = c.x(0, "attn")
+    say("hessian cfg", cfg, x.shape)
+    h = w4q.quant_hessian(dev_bf16(x, dev)).cpu().numpy()
+    assert np.array_equal(h, h.T)
+    check_hessian(h, oracle.hessian(x))
+
+
+@pytest.mark.parametrize("n_tok,d", [(1, 8), (100, 136), (65, 256), (130, 520)])
+def test_hessian_ragged(dev, n_tok, d):
+    x = synth.calib_x(31, 0, n_tok, n_tok, d, 1.0)
+    say("hessian ragged", n_tok, d)
+    h = w4q.quant_hessian(dev_bf16(x, dev)).cpu().numpy()
+    assert np.array_equal(h, h.T)
+    check_hessian(h, oracle.hessian(x))
+
+
+def test_hessian_accumulate(dev):
+    x = synth.calib_x(31, 1, 0, 192, 264, 1.5)
+    say("hessian accumulate")
+    h = w4q.quant_hessian(dev_bf16(x[:100], dev))
+    w4q.quant_hessian(dev_bf16(x[100:], dev), h=h, accumulate=True)
+    hn = h.cpu().numpy()
+    assert np.array_equal(hn, hn.T)
+    check_hessian(hn, oracle.hessian(x))
+
+
+# ------------------------------------------------------------------------------ scale search
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_search_config(dev, cfg):
+    c = synth.CONFIGS[cfg]
+    lin = c.linears[0]
+    w = c.weight(0, lin)
+    x = c.x(0, lin.inp)
+    say("search cfg", cfg, w.shape)
+    h = w4q.quant_hessian(dev_bf16(x, dev)).cpu().numpy()
+    alpha = c.alpha()
+    sc, ix, ob, oa, so, io, oo, oao = _search_both(w, h, alpha, dev)
+    n_tie = check_search(ix, sc, ob, io, so, oo, oao, _cand_fn(w, alpha))
+    assert n_tie <= max(2, ix.size // 5000)
+    # every candidate's objective, not only the chosen one
+    err = np.abs(oa.astype(np.float64) - oao)
+    assert np.all(err <= 1e-5 * oao + 1e-30)
+
+
+def test_search_identity_hessian_and_edges(dev):
+    # all-zero groups, outlier-only groups, weights on midpoints, fp16-subnormal scales
+    d_out, d_in = 70, 32 * 7
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal((d_out, d_in)) * 0.02).astype(np.float32)
+    w[0, :] = 0.0                                          # all-zero row
+    w[1, 32:64] = 0.0
+    w[1, 40] = 0.7                                         # outlier-only group
+    w[2, :] = (rng.standard_normal(d_in) * 1e-6).astype(np.float32)  # subnormal fp16 scales
+    w[3, :32] = np.float32(0.25) * (np.arange(32) % 16 - 7.5).astype(np.float32)  # midpoints
+    w[4, :32] = np.float32(1e-7)
+    h = np.eye(d_in, dtype=np.float32) * np.float32(2.0)
+    alpha = synth.alpha_grid(17, 0.3, 1.0)
+    say("search edges")
+    sc, ix, ob, oa, so, io, oo, oao = _search_both(w, h, alpha, dev)
+    check_search(ix, sc, ob, io, so, oo, oao, _cand_fn(w, alpha))
+    assert np.all(sc[0] == 0) and np.all(ix[0] == 0)
+
+
+def test_search_ragged_and_single_candidate(dev):
+    x = synth.calib_x(31, 2, 0, 96, 96, 1.0)
+    h = w4q.quant_hessian(dev_bf16(x, dev)).cpu().numpy()
+    w = synth.weights(31, 2, 1, 300, 96, 0.01)
+    for K in (1, 3, 255):
+        alpha = synth.alpha_grid(K, 0.4, 1.0)
+        say("search ragged K", K)
+        sc, ix, ob, oa, so, io, oo, oao = _search_both(w, h, alpha, dev)
+        check_search(ix, sc, ob, io, so, oo, oao, _cand_fn(w, alpha))
+
+
+def test_search_deterministic(dev):
+    c = synth.CONFIGS[1]
+    w = c.weight(0, c.linears[0])
+    h = w4q.quant_hessian(dev_bf16(c.x(0, "attn"), dev))
+    wt, at = dev_f32(w, dev), dev_f32(c.alpha(), dev)
+    say("search determinism")
+    a = [t.cpu() for t in w4q.quant_scale_search(wt, h, at)[:3]]
+    b = [t.cpu() for t in w4q.quant_scale_search(wt, h, at)[:3]]
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+# ---------------------------------------------------------------------------------- pack
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_pack_config(dev, cfg):
+    c = synth.CONFIGS[cfg]
+    w = c.weight(0, c.linears[0])
+    G = w.shape[1] // 32
+    # scales: max-based candidates stretched per group (fp32, not yet on the fp16 grid)
+    rng = np.random.default_rng(cfg)
+    scale = (np.abs(w.reshape(-1, G, 32)).max(axis=2) / 7 * rng.uniform(0.4, 1.0, (w.shape[0], G))).astype(np.float32)
+    say("pack cfg", cfg)
+    p, s16 = w4q.quant_pack(dev_f32(w, dev), dev_f32(scale, dev))
+    po, so = oracle.pack(w, scale)
+    assert np.array_equal(p.cpu().numpy(), po)
+    assert np.array_equal(host_f16_bits(s16), so)
+
+
+def test_pack_edges(dev):
+    d = np.float32(0.25)
+    mids = ((np.arange(-9, 8) + 0.5) * d).astype(np.float32)
+    w = np.zeros((3, 64), np.float32)
+    w[0, :mids.size] = mids
+    w[0, 17:19] = [7 * d, -8 * d]
+    w[1, :] = 1e-3
+    scale = np.array([[d, d], [0.0, 1e-7], [6e-8, 65504.0]], np.float32)
+    say("pack edges")
+    p, s16 = w4q.quant_pack(dev_f32(w, dev), dev_f32(scale, dev))
+    po, so = oracle.pack(w, scale)
+    assert np.array_equal(p.cpu().numpy(), po)
+    assert np.array_equal(host_f16_bits(s16), so)
+
+
+# ------------------------------------------------------------------------------------ LSQ
+def _lsq_check(w, scale, g, dev, fused):
+    wt, st, gt = dev_f32(w, dev), dev_f32(scale, dev), dev_f32(g, dev)
+    wh = w4q.lsq_fwd(wt, st).cpu().numpy()
+    gw, gsc, wh2 = w4q.lsq_bwd(wt, st, gt, GS, with_w_hat=fused)
+    gw, gsc = gw.cpu().numpy(), gsc.cpu().numpy()
+    gwo, gsco, who = oracle.lsq_bwd(w, scale, g, GS)
+    assert np.array_equal(wh, who)
+    assert np.array_equal(oracle.lsq_fwd(w, scale), who)
+    if fused:
+        assert np.array_equal(wh2.cpu().numpy(), who)
+    assert np.array_equal(gw, gwo)
+    # tolerance: 1e-4 * gs * sum|G f| + gs * 2^-20 * sum|G|
+    d = np.repeat(scale.astype(np.float64), 32, axis=1)
+    q = who.astype(np.float64) / np.where(d == 0, 1, d)
+    m = (w >= -8 * d) & (w <= 7 * d)
+    f = np.where(m, q - w / d, q)
+    G = w.shape[1] // 32
+    gf = np.abs(g * f).reshape(w.shape[0], G, 32).sum(axis=2)
+    ga = np.abs(g).reshape(w.shape[0], G, 32).sum(axis=2)
+    tol = LSQ_REL * GS * gf + GS * 2.0 ** -20 * ga
+    assert np.all(np.abs(gsc - gsco) <= tol)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_lsq_config1(dev, fused):
+    c = synth.CONFIGS[1]
+    lin = c.linears[0]
+    w = c.weight(0, lin)
+    g = c.grad(0, lin)
+    G = w.shape[1] // 32
+    rng = np.random.default_rng(5)
+    scale = (np.abs(w.reshape(-1, G, 32)).max(axis=2) / 7 * rng.uniform(0.3, 1.1, (w.shape[0], G))).astype(np.float32)
+    say("lsq cfg1 fused", fused)
+    _lsq_check(w, scale, g, dev, fused)
+
+
+def test_lsq_edges(dev):
+    d = np.float32(0.25)
+    w = np.zeros((2, 64), np.float32)
+    w[0, :8] = [0.375, 1.875, 1.75, -2.125, -2.0, 0.1, 7 * 0.25, -8 * 0.25]
+    w[0, 8:32] = ((np.arange(24) - 12) * 0.125).astype(np.float32)
+    w[1, :] = np.linspace(-3, 3, 64, dtype=np.float32)
+    scale = np.array([[d, np.float32(0.013)], [np.float32(1e-30), np.float32(100.0)]], np.float32)
+    g = np.random.default_rng(9).standard_normal((2, 64)).astype(np.float32)
+    say("lsq edges")
+    _lsq_check(w, scale, g, dev, True)
+
+
+# ----------------------------------------------------------------------------------- GEMM
+def _packed_layer(cfg, layer=0):
+    c = synth.CONFIGS[cfg]
+    lin = c.linears[0]
+    w = c.weight(layer, lin)
+    G = w.shape[1] // 32
+    scale = (np.abs(w.reshape(-1, G, 32)).max(axis=2) / 7).astype(np.float32)
+    packed, s16 = oracle.pack(w, scale)
+    return c, lin, packed, s16
+
+
+@pytest.mark.parametrize("cfg,m", [(1, 1), (2, 1), (2, 4), (2, 16), (2, 3), (2, 17), (2, 256)])
+@pytest.mark.parametrize("bf16_out", [False, True])
+def test_gemm_config(dev, cfg, m, bf16_out):
+    c, lin, packed, s16 = _packed_layer(cfg)
+    x = c.x(0, lin.inp)[:m]
+    say("gemm cfg", cfg, "m", m, "bf16", bf16_out)
+    y = w4q.w4a16_gemm(dev_bf16(x, dev), torch.from_numpy(packed).to(dev),
+                       torch.from_numpy(s16.view(np.float16)).to(dev),
+                       out_dtype=torch.bfloat16 if bf16_out else torch.float32)
+    yg = bf16_bits_to_np(host_bf16_bits(y)) if bf16_out else y.cpu().numpy()
+    cols = np.arange(packed.shape[0]) if m <= 16 else np.arange(0, packed.shape[0], 7)
+    yr, ya = oracle.gemm_cols(x, packed, s16, cols)
+    check_gemm(yg[:, cols], yr, ya, bf16_out)
+
+
+@pytest.mark.parametrize("m,d_out,d_in", [(1, 1, 32), (1, 3, 96), (2, 130, 224), (5, 64, 1056),
+                                          (1, 77, 3072), (33, 200, 160), (130, 129, 96)])
+def test_gemm_ragged(dev, m, d_out, d_in):
+    w = synth.weights(32, 0, d_out, d_out, d_in, 0.01)
+    scale = (np.abs(w.reshape(d_out, -1, 32)).max(axis=2) / 6).astype(np.float32)
+    scale[0, 0] = 0.0                                        # an all-zero code group
+    packed, s16 = oracle.pack(w, scale)
+    x = synth.calib_x(32, 0, m, m, d_in, 1.0)
+    say("gemm ragged", m, d_out, d_in)
+    y = w4q.w4a16_gemm(dev_bf16(x, dev), torch.from_numpy(packed).to(dev),
+                       torch.from_numpy(s16.view(np.float16)).to(dev))
+    yr, ya = oracle.gemm_cols(x, packed, s16)
+    check_gemm(y.cpu().numpy(), yr, ya)
+
+
+def test_gemm_rows_agree_with_m1(dev):
+    c, lin, packed, s16 = _packed_layer(2)
+    x = c.x(0, lin.inp)[:40]
+    pt = torch.from_numpy(packed).to(dev)
+    st = torch.from_numpy(s16.view(np.float16)).to(dev)
+    say("gemm row consistency")
+    yb = w4q.w4a16_gemm(dev_bf16(x, dev), pt, st).cpu().numpy()
+    yr, ya = oracle.gemm_cols(x, packed, s16)
+    for r in (0, 17, 39):
+        y1 = w4q.w4a16_gemm(dev_bf16(x[r:r + 1], dev), pt, st).cpu().numpy()
+        assert np.all(np.abs(y1[0] - yb[r]) <= 2 * GEMM_REL * ya[r])
+
+
+def test_gemm_zero_codes_exact(dev):
+    packed = np.zeros((64, 1024), np.uint8)
+    s16 = np.full((64, 64), 0x3C00, np.uint16)
+    x = synth.calib_x(33, 0, 0, 4, 2048, 1.0)
+    say("gemm zero codes")
+    for m in (1, 4, 32):
+        y = w4q.w4a16_gemm(dev_bf16(x[:m] if m <= 4 else np.tile(x, (8, 1)), dev),
+                           torch.from_numpy(packed).to(dev),
+                           torch.from_numpy(s16.view(np.float16)).to(dev))
+        assert torch.count_nonzero(y).item() == 0

@@ -1,0 +1,20 @@
+"""W4A16 group-wise quantization core for AMD gfx950 (MI355X).
+
+Thin Python binding over libw4a16q.so (hand-written HIP kernels behind a C ABI, declared in
+include/w4a16q.h).  The functions here only check tensor metadata, allocate outputs with
+torch and pass raw device pointers plus the current HIP stream; every step of the
+computation runs in the library's kernels.  There is no CPU fallback: if the library is
+missing the calls raise.
+
+Entry points (same names as the C ABI):
+  quant_hessian, quant_scale_search, quant_pack, lsq_fwd, lsq_bwd, w4a16_gemm
+"""
+from ._lib import (LIB_PATH, W4Q_EALIGN, W4Q_EHIP, W4Q_EINVAL, W4Q_ESHAPE, W4Q_EUNSUPPORTED,
+                   W4Q_GROUP, W4Q_OK, W4QError, lib, status_string, version)
+from .ops import (lsq_bwd, lsq_fwd, quant_hessian, quant_pack, quant_scale_search, w4a16_gemm)
+
+__all__ = [
+    "quant_hessian", "quant_scale_search", "quant_pack", "lsq_fwd", "lsq_bwd", "w4a16_gemm",
+    "W4QError", "lib", "LIB_PATH", "status_string", "version", "W4Q_GROUP", "W4Q_OK",
+    "W4Q_EINVAL", "W4Q_ESHAPE", "W4Q_EALIGN", "W4Q_EUNSUPPORTED", "W4Q_EHIP",
+]

@@ -1,0 +1,71 @@
+"""ctypes loader for libw4a16q.so and the exported C symbols (see include/w4a16q.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libw4a16q.so")
+
+W4Q_GROUP = 32
+W4Q_OK = 0
+W4Q_EINVAL = -1
+W4Q_ESHAPE = -2
+W4Q_EALIGN = -3
+W4Q_EUNSUPPORTED = -4
+W4Q_EHIP = -5
+
+# every function the header declares, with its ctypes signature
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+_F = ctypes.c_float
+SIGNATURES = {
+    "w4q_status_string": (ctypes.c_char_p, [_INT]),
+    "w4q_version": (_INT, []),
+    "quant_hessian": (_INT, [_P, _I64, _I64, _P, _INT, _P]),
+    "quant_scale_search": (_INT, [_P, _I64, _I64, _P, _I64, _P, _INT, _P, _P, _P, _P, _P]),
+    "quant_pack": (_INT, [_P, _P, _I64, _I64, _P, _P, _P]),
+    "lsq_fwd": (_INT, [_P, _P, _I64, _I64, _P, _P]),
+    "lsq_bwd": (_INT, [_P, _P, _P, _I64, _I64, _F, _P, _P, _P, _P]),
+    "w4a16_gemm": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _INT, _P]),
+}
+
+
+class W4QError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libw4a16q.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m w4a16_group_wise_amd.build` "
+                "(hipcc, gfx950).  There is no fallback implementation.")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().w4q_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(lib().w4q_version())
+
+
+def check(fn: str, status: int) -> None:
+    if status != W4Q_OK:
+        raise W4QError(fn, status)

@@ -1,0 +1,153 @@
+// hessian.hip -- H = X^T X for bf16 calibration activations on the bf16 matrix cores.
+//
+// Method: blog "Opt.Gear-QAT: Preserving On-Device Performance with QAT", section 2 (the
+// second-order output-reconstruction view from GPTQ; layer sensitivity from calibration
+// inputs): for the objective of the model card's "Quantization Configuration",
+// ||W X - Q(W) X||^2 is a quadratic form in the weight error with matrix X^T X.
+//
+// Only the tiles on and above the diagonal are computed (the algorithmic work is the unique
+// entries of the symmetric result); each value is written to both (i, j) and (j, i), so H is
+// bitwise symmetric.  X is row-major with the reduction (token) axis strided, while an MFMA
+// fragment wants 8 consecutive tokens of one feature per lane: each thread loads an 8x8
+// (tokens x features) bf16 block with 16-byte loads, transposes it in registers with byte
+// permutes, and writes 8 feature rows of 8 tokens into LDS, where fragments are single
+// 16-byte reads.  128x128 tiles, 4 wavefronts of 64x64 (2x2 v_mfma_f32_32x32x16_bf16
+// blocks), 64 tokens per double-buffered LDS stage.
+#include "common.hpp"
+
+namespace w4q {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int HT = 128;      // tile edge in features
+constexpr int HK = 64;       // tokens per stage
+constexpr int HLD = HK + 8;  // bf16 per LDS feature row (144 bytes)
+
+__global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __restrict__ x, int64_t n_tok,
+                                                              int64_t d, float* __restrict__ h,
+                                                              int accumulate, int nt) {
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][2 * HT * HLD];
+
+  // upper-triangle tile (ti <= tj) of this block
+  int rem = blockIdx.x, ti = 0;
+  while (rem >= nt - ti) {
+    rem -= nt - ti;
+    ++ti;
+  }
+  const int tj = ti + rem;
+  const bool diag = ti == tj;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+
+  // load role: 8 tokens (token block tb) x 8 features (feature block fb of the 256 staged)
+  const int tb = lane & 7;
+  const int fb = (lane >> 3) + 8 * wid;         // 0..31: 0..15 -> I rows, 16..31 -> J rows
+  const bool jrow = fb >= 16;
+  const int64_t feat = jrow ? (int64_t)tj * HT + 8 * (fb - 16) : (int64_t)ti * HT + 8 * fb;
+  const bool f_ok = feat < d && !(diag && jrow);  // diagonal tiles stage the I rows only
+  const uint16_t* xf = x + (f_ok ? feat : 0);
+
+  u32x4 rv[8];
+  auto gload = [&](int64_t k0) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int64_t tok = k0 + 8 * tb + t;
+      rv[t] = (f_ok && tok < n_tok) ? *reinterpret_cast<const u32x4*>(xf + tok * d) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto lstore = [&](int buf) {
+    if (diag && jrow) return;
+    // 8x8 transpose: out[f] holds tokens 0..7 of feature f as 4 bf16 pairs
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const int wsel = f >> 1;
+      const uint32_t sel = (f & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t o[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t lo = rv[2 * p][wsel], hi = rv[2 * p + 1][wsel];
+        o[p] = __builtin_amdgcn_perm(hi, lo, sel);
+      }
+      *reinterpret_cast<u32x4*>(&Xs[buf][(fb * 8 + f) * HLD + 8 * tb]) = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // on a diagonal tile the (wm = 1, wn = 0) quadrant is the mirror of (0, 1): skip it
+  const bool work = !(diag && wm == 1 && wn == 0);
+  const int jbase = diag ? 0 : HT;  // B fragments come from the I rows on diagonal tiles
+  const int fr = lane & 31;
+  const int fk = 8 * (lane >> 5);
+  const int64_t nstage = (n_tok + HK - 1) / HK;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int64_t st = 0; st < nstage; ++st) {
+    const int cur = static_cast<int>(st & 1);
+    const bool more = st + 1 < nstage;
+    if (more) gload((st + 1) * HK);
+    if (work) {
+#pragma unroll
+      for (int s = 0; s < HK / 16; ++s) {
+        bf16x8 a[2], b[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          a[i] = *reinterpret_cast<const bf16x8*>(&Xs[cur][(wm * 64 + 32 * i + fr) * HLD + 16 * s + fk]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          b[j] = *reinterpret_cast<const bf16x8*>(&Xs[cur][(jbase + wn * 64 + 32 * j + fr) * HLD + 16 * s + fk]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (more) lstore(cur ^ 1);
+    __syncthreads();
+  }
+  if (!work) return;
+
+  // 32x32 accumulator layout: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, column l%32
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = (int64_t)tj * HT + wn * 64 + 32 * j + fr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = (int64_t)ti * HT + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row >= d || col >= d || row > col) continue;
+        float v = acc[i][j][r];
+        if (accumulate) v += h[row * d + col];
+        h[row * d + col] = v;
+        if (row != col) h[col * d + row] = v;
+      }
+    }
+}
+
+}  // namespace
+}  // namespace w4q
+
+using namespace w4q;
+
+int w4q_launch_hessian(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accumulate,
+                       hipStream_t s) {
+  const int64_t nt = (d + HT - 1) / HT;
+  const int64_t tiles = nt * (nt + 1) / 2;
+  if (tiles > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
+  hipLaunchKernelGGL(hessian_kernel, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s, x,
+                     n_tok, d, h, accumulate, static_cast<int>(nt));
+  return w4q_launch_status();
+}

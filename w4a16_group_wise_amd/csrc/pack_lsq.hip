@@ -1,0 +1,139 @@
+// pack_lsq.hip -- the elementwise, HBM-bound steps: export onto the INT4 grid (quant_pack),
+// the LSQ fake-quant forward (lsq_fwd) and the straight-through / step-size backward (lsq_bwd).
+//
+// Each thread owns 8 consecutive weights of one row (a quarter of a 32-weight group), so a
+// wavefront reads and writes fully coalesced 32-byte pieces and 4 lanes share one group; the
+// per-group step-size gradient is reduced across those 4 lanes (after a 2-element local sum)
+// with a fixed butterfly, so results are run-to-run deterministic.
+#include "common.hpp"
+
+namespace w4q {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPer = 8;  // weights per thread
+
+// Export ([card] "QAT Highlights" / "Quickstart", [blog] "Conclusion"): fp16 scale, codes on
+// that scale, two's-complement nibbles with the even index in the low nibble.
+__global__ __launch_bounds__(kThreads) void pack_kernel(const float* __restrict__ w,
+                                                        const float* __restrict__ scale,
+                                                        int64_t n8, int64_t d_in,
+                                                        uint32_t* __restrict__ packed,
+                                                        uint16_t* __restrict__ s16) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t >= n8) return;
+  const int64_t e0 = t * kPer;                 // first weight (flat index)
+  const int64_t grp = e0 / kGroup;             // flat group index (= row * G + g)
+  const f32x4 a = *reinterpret_cast<const f32x4*>(w + e0);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(w + e0 + 4);
+  const uint16_t hs = f32_to_f16_bits(scale[grp]);
+  const float d = f16_bits_to_f32(hs);
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = static_cast<int>(code_div(v[i], d));
+    word |= (static_cast<uint32_t>(q) & 0xFu) << (4 * i);
+  }
+  packed[t] = word;
+  if ((e0 % kGroup) == 0) s16[grp] = hs;
+  (void)d_in;
+}
+
+// [blog] section 3 forward: w_hat = D * code(w, D) with the fp32 learnable step D.
+__global__ __launch_bounds__(kThreads) void lsq_fwd_kernel(const float* __restrict__ w,
+                                                           const float* __restrict__ scale,
+                                                           int64_t n8, float* __restrict__ w_hat) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t >= n8) return;
+  const int64_t e0 = t * kPer;
+  const float d = scale[e0 / kGroup];
+  f32x4 a = *reinterpret_cast<const f32x4*>(w + e0);
+  f32x4 b = *reinterpret_cast<const f32x4*>(w + e0 + 4);
+  a.x = d * code_div(a.x, d); a.y = d * code_div(a.y, d);
+  a.z = d * code_div(a.z, d); a.w = d * code_div(a.w, d);
+  b.x = d * code_div(b.x, d); b.y = d * code_div(b.y, d);
+  b.z = d * code_div(b.z, d); b.w = d * code_div(b.w, d);
+  *reinterpret_cast<f32x4*>(w_hat + e0) = a;
+  *reinterpret_cast<f32x4*>(w_hat + e0 + 4) = b;
+}
+
+// [blog] section 3 backward.  m = [-8 D <= w <= 7 D] (signs from fma, exact);
+// grad_w = G m;  f = q - (w / D) m;  grad_scale = gs * sum_group G f.
+template <bool kFwd>
+__global__ __launch_bounds__(kThreads) void lsq_bwd_kernel(const float* __restrict__ w,
+                                                           const float* __restrict__ scale,
+                                                           const float* __restrict__ g,
+                                                           int64_t n8, float gs,
+                                                           float* __restrict__ grad_w,
+                                                           float* __restrict__ grad_scale,
+                                                           float* __restrict__ w_hat) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const bool live = t < n8;
+  const int64_t e0 = (live ? t : 0) * kPer;
+  const float d = scale[e0 / kGroup];
+  const f32x4 wa = *reinterpret_cast<const f32x4*>(w + e0);
+  const f32x4 wb = *reinterpret_cast<const f32x4*>(w + e0 + 4);
+  const f32x4 ga = *reinterpret_cast<const f32x4*>(g + e0);
+  const f32x4 gb = *reinterpret_cast<const f32x4*>(g + e0 + 4);
+  const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+  const float gv[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+  float gw[8], wh[8];
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float q = code_div(wv[i], d);
+    const bool in = (__builtin_fmaf(8.0f, d, wv[i]) >= 0.0f) && (__builtin_fmaf(-7.0f, d, wv[i]) <= 0.0f);
+    gw[i] = in ? gv[i] : 0.0f;
+    const float f = in ? q - wv[i] / d : q;
+    acc = __builtin_fmaf(gv[i], f, acc);
+    wh[i] = d * q;
+  }
+  // 4 lanes (32 weights) per group: butterfly over lane bits 0 and 1
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  if (!live) return;
+  *reinterpret_cast<f32x4*>(grad_w + e0) = f32x4{gw[0], gw[1], gw[2], gw[3]};
+  *reinterpret_cast<f32x4*>(grad_w + e0 + 4) = f32x4{gw[4], gw[5], gw[6], gw[7]};
+  if (kFwd) {
+    *reinterpret_cast<f32x4*>(w_hat + e0) = f32x4{wh[0], wh[1], wh[2], wh[3]};
+    *reinterpret_cast<f32x4*>(w_hat + e0 + 4) = f32x4{wh[4], wh[5], wh[6], wh[7]};
+  }
+  if ((t & 3) == 0) grad_scale[e0 / kGroup] = gs * acc;
+}
+
+inline unsigned blocks_for(int64_t n8) { return static_cast<unsigned>((n8 + kThreads - 1) / kThreads); }
+
+}  // namespace
+}  // namespace w4q
+
+using namespace w4q;
+
+int w4q_launch_pack(const float* w, const float* scale, int64_t d_out, int64_t d_in,
+                    uint8_t* packed, uint16_t* scale_f16, hipStream_t s) {
+  const int64_t n8 = d_out * d_in / kPer;
+  hipLaunchKernelGGL(pack_kernel, dim3(blocks_for(n8)), dim3(kThreads), 0, s, w, scale, n8, d_in,
+                     reinterpret_cast<uint32_t*>(packed), scale_f16);
+  return w4q_launch_status();
+}
+
+int w4q_launch_lsq_fwd(const float* w, const float* scale, int64_t d_out, int64_t d_in,
+                       float* w_hat, hipStream_t s) {
+  const int64_t n8 = d_out * d_in / kPer;
+  hipLaunchKernelGGL(lsq_fwd_kernel, dim3(blocks_for(n8)), dim3(kThreads), 0, s, w, scale, n8,
+                     w_hat);
+  return w4q_launch_status();
+}
+
+int w4q_launch_lsq_bwd(const float* w, const float* scale, const float* g, int64_t d_out,
+                       int64_t d_in, float gs, float* grad_w, float* grad_scale, float* w_hat,
+                       hipStream_t s) {
+  const int64_t n8 = d_out * d_in / kPer;
+  if (w_hat)
+    hipLaunchKernelGGL(lsq_bwd_kernel<true>, dim3(blocks_for(n8)), dim3(kThreads), 0, s, w, scale,
+                       g, n8, gs, grad_w, grad_scale, w_hat);
+  else
+    hipLaunchKernelGGL(lsq_bwd_kernel<false>, dim3(blocks_for(n8)), dim3(kThreads), 0, s, w,
+                       scale, g, n8, gs, grad_w, grad_scale, w_hat);
+  return w4q_launch_status();
+}

@@ -1,0 +1,142 @@
+"""Torch-tensor front end of the C ABI: metadata checks, output allocation, pointer marshalling.
+
+All tensors must be contiguous CUDA (HIP) tensors on one device; work is enqueued on the
+current stream of that device and nothing is synchronised here.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import W4Q_GROUP, check, lib
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _out(t: Optional[torch.Tensor], name, shape, dtype, device) -> torch.Tensor:
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _need(t, name, dtype, shape, device)
+    return t
+
+
+def quant_hessian(x: torch.Tensor, h: Optional[torch.Tensor] = None,
+                  accumulate: bool = False) -> torch.Tensor:
+    """H = X^T X (or H += X^T X) for bf16 X [n_tok][d]; returns fp32 H [d][d]."""
+    _need(x, "x", torch.bfloat16)
+    n_tok, d = x.shape
+    if accumulate and h is None:
+        raise ValueError("accumulate=True needs h")
+    h = _out(h, "h", (d, d), torch.float32, x.device)
+    check("quant_hessian", lib().quant_hessian(x.data_ptr(), n_tok, d, h.data_ptr(),
+                                               1 if accumulate else 0, _stream(x)))
+    return h
+
+
+def quant_scale_search(w: torch.Tensor, h: torch.Tensor, alpha: torch.Tensor,
+                       with_obj: bool = True, with_obj_all: bool = False,
+                       out: Optional[Tuple[torch.Tensor, ...]] = None):
+    """-> (scale f32 [d_out][G], idx u8 [d_out][G], obj f32 | None, obj_all f32 | None)."""
+    _need(w, "w", torch.float32)
+    d_out, d_in = w.shape
+    if h.dim() != 2 or h.shape[0] != d_in:
+        raise ValueError(f"h must be [{d_in}][ldh], got {tuple(h.shape)}")
+    _need(h, "h", torch.float32, device=w.device)
+    _need(alpha, "alpha", torch.float32, device=w.device)
+    G, K = d_in // W4Q_GROUP, alpha.numel()
+    dev = w.device
+    if out is None:
+        scale = torch.empty((d_out, G), dtype=torch.float32, device=dev)
+        idx = torch.empty((d_out, G), dtype=torch.uint8, device=dev)
+        obj = torch.empty((d_out, G), dtype=torch.float32, device=dev) if with_obj else None
+        obj_all = (torch.empty((d_out, G, K), dtype=torch.float32, device=dev)
+                   if with_obj_all else None)
+    else:
+        scale, idx, obj, obj_all = out
+    check("quant_scale_search", lib().quant_scale_search(
+        w.data_ptr(), d_out, d_in, h.data_ptr(), h.shape[1], alpha.data_ptr(), K,
+        scale.data_ptr(), idx.data_ptr(), obj.data_ptr() if obj is not None else None,
+        obj_all.data_ptr() if obj_all is not None else None, _stream(w)))
+    return scale, idx, obj, obj_all
+
+
+def quant_pack(w: torch.Tensor, scale: torch.Tensor,
+               out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """-> (packed u8 [d_out][d_in/2], scale_f16 fp16 [d_out][G])."""
+    _need(w, "w", torch.float32)
+    d_out, d_in = w.shape
+    _need(scale, "scale", torch.float32, (d_out, d_in // W4Q_GROUP), w.device)
+    if out is None:
+        packed = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=w.device)
+        s16 = torch.empty((d_out, d_in // W4Q_GROUP), dtype=torch.float16, device=w.device)
+    else:
+        packed, s16 = out
+    check("quant_pack", lib().quant_pack(w.data_ptr(), scale.data_ptr(), d_out, d_in,
+                                         packed.data_ptr(), s16.data_ptr(), _stream(w)))
+    return packed, s16
+
+
+def lsq_fwd(w: torch.Tensor, scale: torch.Tensor, out: Optional[torch.Tensor] = None):
+    _need(w, "w", torch.float32)
+    d_out, d_in = w.shape
+    _need(scale, "scale", torch.float32, (d_out, d_in // W4Q_GROUP), w.device)
+    w_hat = _out(out, "w_hat", (d_out, d_in), torch.float32, w.device)
+    check("lsq_fwd", lib().lsq_fwd(w.data_ptr(), scale.data_ptr(), d_out, d_in,
+                                   w_hat.data_ptr(), _stream(w)))
+    return w_hat
+
+
+def lsq_bwd(w: torch.Tensor, scale: torch.Tensor, grad_w_hat: torch.Tensor, grad_scale: float,
+            with_w_hat: bool = False, out: Optional[Tuple] = None):
+    """-> (grad_w f32, grad_scale_out f32 [d_out][G], w_hat f32 | None)."""
+    _need(w, "w", torch.float32)
+    d_out, d_in = w.shape
+    _need(scale, "scale", torch.float32, (d_out, d_in // W4Q_GROUP), w.device)
+    _need(grad_w_hat, "grad_w_hat", torch.float32, (d_out, d_in), w.device)
+    if out is None:
+        gw = torch.empty_like(w)
+        gsc = torch.empty((d_out, d_in // W4Q_GROUP), dtype=torch.float32, device=w.device)
+        wh = torch.empty_like(w) if with_w_hat else None
+    else:
+        gw, gsc, wh = out
+    check("lsq_bwd", lib().lsq_bwd(w.data_ptr(), scale.data_ptr(), grad_w_hat.data_ptr(), d_out,
+                                   d_in, float(grad_scale), gw.data_ptr(), gsc.data_ptr(),
+                                   wh.data_ptr() if wh is not None else None, _stream(w)))
+    return gw, gsc, wh
+
+
+def w4a16_gemm(x: torch.Tensor, packed: torch.Tensor, scale_f16: torch.Tensor,
+               out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None):
+    """y [m][d_out] = x [m][d_in] (bf16) times the dequantised packed weights, transposed."""
+    _need(x, "x", torch.bfloat16)
+    m, d_in = x.shape
+    _need(packed, "packed", torch.uint8, device=x.device)
+    d_out = packed.shape[0]
+    if packed.dim() != 2 or packed.shape[1] * 2 != d_in:
+        raise ValueError(f"packed must be [d_out][{d_in // 2}], got {tuple(packed.shape)}")
+    _need(scale_f16, "scale_f16", torch.float16, (d_out, d_in // W4Q_GROUP), x.device)
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    y = _out(out, "y", (m, d_out), out_dtype, x.device)
+    check("w4a16_gemm", lib().w4a16_gemm(x.data_ptr(), m, packed.data_ptr(), scale_f16.data_ptr(),
+                                         d_out, d_in, y.data_ptr(),
+                                         0 if out_dtype == torch.float32 else 1, _stream(x)))
+    return y

@@ -1,0 +1,363 @@
+"""Benchmark of the W4A16 group-wise hot path on one MI355X.
+
+One step = one pass of the whole path over one synthetic layer, inputs resident in HBM:
+  quant_hessian (X^T X) -> quant_scale_search (K candidates/group) -> quant_pack ->
+  lsq_fwd -> lsq_bwd (fused forward) -> w4a16_gemm at M = 1, 4, 16 (decode GEMV) and at
+  M = n_tok (prefill GEMM on the matrix cores).
+
+Default workload: the 2048x2048 attention-projection layer (X 2048 tokens x 2048 bf16,
+K = 40 candidates over alpha in [0.4, 1.0]).  Every kernel is timed with HIP events on the
+stream it runs on; the JSON line reports the M=1 GEMV bandwidth as `value`, each kernel's
+rate against its roofline, and the CPU oracle timed on a bounded sample of the same work.
+
+    python bench.py [--steps K] [--warmup W] [--workload cfg2|cfg3|cfg5] [--no-cpu]
+    python bench.py --pmc-summary FETCH_DIR WRITE_DIR   (writes profiles/traffic_<workload>.json)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 GEMV GB/s (% HBM peak); scale-search groups/s; Hessian+GEMM MFMA util"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
+PEAK_FP32_VALU_TFLOPS = 157.3  # fp32 vector (published; counts packed FP32)
+GS = 1.0 / np.sqrt(32 * 7)
+CSRC = os.path.join(ROOT, "w4a16_group_wise_amd", "csrc")
+
+# kernel family -> (source file, symbol substrings as they appear in a kernel trace)
+KERNELS = {
+    "hessian": ("hessian.hip", ["hessian_kernel"]),
+    "scale_search": ("scale_search.hip", ["search_fp32_kernel", "search_fp64_kernel"]),
+    "pack": ("pack_lsq.hip", ["pack_kernel"]),
+    "lsq_fwd": ("pack_lsq.hip", ["lsq_fwd_kernel"]),
+    "lsq_bwd": ("pack_lsq.hip", ["lsq_bwd_kernel"]),
+    "gemv_m1": ("gemv.hip", ["gemv_kernel<1,"]),
+    "gemv_m4": ("gemv.hip", ["gemv_kernel<4,"]),
+    "gemv_m16": ("gemv.hip", ["gemv_kernel<4,"]),
+    "gemm": ("gemm.hip", ["gemm_kernel"]),
+}
+
+
+def src_hash(fname: str) -> str:
+    h = hashlib.sha256()
+    for f in (fname, "common.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+WORKLOADS = {
+    "cfg2": dict(cfg=2, lin=0, desc="2048x2048 attention-projection layer; X 2048 tok x 2048 bf16 "
+                 "(lognormal(0,1) channel scales); K=40, alpha in [0.4,1.0]; GEMV M=1,4,16; "
+                 "GEMM M=2048", gemm_m=2048),
+    "cfg3": dict(cfg=3, lin=0, desc="MLP gate 8192x2048; X 4096 tok x 2048 bf16 (lognormal(0,1.5)); "
+                 "K=40; GEMV M=1,4,16; GEMM M=256", gemm_m=256),
+    "cfg5": dict(cfg=5, lin=4, desc="36-layer stack's gate projection 12288x4096; X 8192 tok x 4096 "
+                 "bf16; K=40; GEMV M=1,4,16; GEMM M=2048", gemm_m=2048),
+}
+
+
+class Step:
+    """Preallocated inputs/outputs and the ordered launches of one step."""
+
+    def __init__(self, wl, dev):
+        import torch
+        from w4a16_group_wise_amd import synth
+
+        c = synth.CONFIGS[wl["cfg"]]
+        lin = c.linears[wl["lin"]]
+        self.c, self.lin = c, lin
+        w = c.weight(0, lin)
+        x = c.x(0, lin.inp)
+        g = c.grad(0, lin)
+        self.host = dict(w=w, x=x, g=g, alpha=c.alpha())
+        self.dev = dev
+        self.w = torch.from_numpy(w).to(dev)
+        self.x = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.g = torch.from_numpy(g).to(dev)
+        self.alpha = torch.from_numpy(self.host["alpha"]).to(dev)
+        d_out, d_in = w.shape
+        G, K = d_in // 32, c.n_cand
+        self.d_out, self.d_in, self.G, self.K, self.n_tok = d_out, d_in, G, K, x.shape[0]
+        f32 = torch.float32
+        self.h = torch.empty((d_in, d_in), dtype=f32, device=dev)
+        self.scale = torch.empty((d_out, G), dtype=f32, device=dev)
+        self.idx = torch.empty((d_out, G), dtype=torch.uint8, device=dev)
+        self.obj = torch.empty((d_out, G), dtype=f32, device=dev)
+        self.packed = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=dev)
+        self.s16 = torch.empty((d_out, G), dtype=torch.float16, device=dev)
+        self.w_hat = torch.empty_like(self.w)
+        self.gw = torch.empty_like(self.w)
+        self.gsc = torch.empty((d_out, G), dtype=f32, device=dev)
+        self.w_hat2 = torch.empty_like(self.w)
+        self.gemm_m = min(wl["gemm_m"], self.n_tok)
+        self.y = {m: torch.empty((m, d_out), dtype=f32, device=dev) for m in (1, 4, 16, self.gemm_m)}
+        self.names = ["hessian", "scale_search", "pack", "lsq_fwd", "lsq_bwd", "gemv_m1", "gemv_m4",
+                      "gemv_m16", "gemm"]
+
+    def launches(self):
+        import w4a16_group_wise_amd as w4q
+
+        yield "hessian", lambda: w4q.quant_hessian(self.x, h=self.h)
+        yield "scale_search", lambda: w4q.quant_scale_search(
+            self.w, self.h, self.alpha, out=(self.scale, self.idx, self.obj, None))
+        yield "pack", lambda: w4q.quant_pack(self.w, self.scale, out=(self.packed, self.s16))
+        yield "lsq_fwd", lambda: w4q.lsq_fwd(self.w, self.scale, out=self.w_hat)
+        yield "lsq_bwd", lambda: w4q.lsq_bwd(self.w, self.scale, self.g, GS,
+                                             out=(self.gw, self.gsc, self.w_hat2))
+        for m, name in ((1, "gemv_m1"), (4, "gemv_m4"), (16, "gemv_m16"), (self.gemm_m, "gemm")):
+            yield name, (lambda m=m: w4q.w4a16_gemm(self.x[:m], self.packed, self.s16, out=self.y[m]))
+
+    def work(self):
+        """Algorithmic work per launch: (amount, unit, bound, peak)."""
+        d_out, d_in, G, K, N = self.d_out, self.d_in, self.G, self.K, self.n_tok
+        nw = d_out * d_in
+        ng = d_out * G
+
+        def gemv_bytes(m):
+            return nw * 9 / 16 + 2 * m * d_in + 4 * m * d_out
+
+        return {
+            "hessian": (N * d_in * (d_in + 1), "flop", "mfma", PEAK_BF16_TFLOPS * 1e12),
+            "scale_search": (ng * K * 1056, "flop", "alu", PEAK_FP32_VALU_TFLOPS * 1e12),
+            "pack": (nw * 4.5 + ng * 6, "byte", "hbm", PEAK_HBM_GBS * 1e9),
+            "lsq_fwd": (nw * 8 + ng * 4, "byte", "hbm", PEAK_HBM_GBS * 1e9),
+            "lsq_bwd": (nw * 16 + ng * 8, "byte", "hbm", PEAK_HBM_GBS * 1e9),
+            "gemv_m1": (gemv_bytes(1), "byte", "hbm", PEAK_HBM_GBS * 1e9),
+            "gemv_m4": (gemv_bytes(4), "byte", "hbm", PEAK_HBM_GBS * 1e9),
+            "gemv_m16": (gemv_bytes(16), "byte", "hbm", PEAK_HBM_GBS * 1e9),
+            "gemm": (2 * self.gemm_m * d_out * d_in, "flop", "mfma", PEAK_BF16_TFLOPS * 1e12),
+        }
+
+
+def cpu_baseline(step, budget_s=15.0):
+    """The oracle (as it is) on a bounded sample of the same workload, on the host cores."""
+    import oracle
+
+    h = step.host
+    w, x, alpha = h["w"], h["x"], h["alpha"]
+    d_out, d_in, G = step.d_out, step.d_in, step.G
+    hh = step.h.cpu().numpy()
+    sc = step.scale.cpu().numpy()
+    packed = step.packed.cpu().numpy()
+    s16 = step.s16.cpu().view(__import__("torch").int16).numpy().view(np.uint16)
+    rates = {}
+    t_total = 0.0
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    # GEMV M=1 over every output row (bytes as on the GPU)
+    reps = 0
+    t = 0.0
+    while t < budget_s * 0.25 or reps < 1:
+        t += timed(lambda: oracle.gemm_cols(x[:1], packed, s16))
+        reps += 1
+    gemv_bytes = d_out * d_in * 9 / 16 + 2 * d_in + 4 * d_out
+    rates["gemv_m1_GBps"] = gemv_bytes * reps / t / 1e9
+    t_total += t / reps
+    # scale search on the first rows (groups/s)
+    rows = max(1, min(d_out, int(4096 / G)))
+    ts = timed(lambda: oracle.scale_search(w[:rows], hh, alpha))
+    rates["search_groups_per_s"] = rows * G / ts
+    t_total += ts * d_out / rows
+    # Hessian: a 256-column slab of X^T X (entries/s -> flop/s)
+    cols = min(256, d_in)
+    ij = np.stack(np.meshgrid(np.arange(cols), np.arange(cols), indexing="ij"), -1).reshape(-1, 2)
+    ij = ij[ij[:, 0] <= ij[:, 1]]
+    th = timed(lambda: oracle.hessian_entries(x, ij))
+    rates["hessian_GFLOPs"] = ij.shape[0] * 2 * x.shape[0] / th / 1e9
+    t_total += th * (d_in * (d_in + 1) / 2) / ij.shape[0]
+    # pack + LSQ on the first 1M weights
+    r1 = max(1, min(d_out, (1 << 20) // d_in))
+    tp = timed(lambda: oracle.pack(w[:r1], sc[:r1]))
+    tl = timed(lambda: oracle.lsq_bwd(w[:r1], sc[:r1], h["g"][:r1], GS))
+    rates["pack_GBps"] = r1 * d_in * 4.5 / tp / 1e9
+    rates["lsq_bwd_GBps"] = r1 * d_in * 16 / tl / 1e9
+    t_total += (tp + 2 * tl) * d_out / r1
+    # prefill GEMM on 16 output columns
+    cols_g = np.arange(min(16, d_out))
+    tg = timed(lambda: oracle.gemm_cols(x[:step.gemm_m], packed, s16, cols_g))
+    rates["gemm_GFLOPs"] = 2 * step.gemm_m * cols_g.shape[0] * d_in / tg / 1e9
+    t_total += tg * d_out / cols_g.shape[0] + t / reps * (4 + 16)  # GEMV M=4, M=16 ~ linear in M
+    return dict(
+        value=rates["gemv_m1_GBps"], unit="GB/s", cores=oracle.threads(), kind="oracle",
+        sample=(f"GEMV M=1 over all {d_out} rows x{reps}; search on {rows * G} groups; Hessian "
+                f"{ij.shape[0]} entries of a {cols}-col slab; pack/LSQ on {r1 * d_in} weights; "
+                f"GEMM M={step.gemm_m} on {cols_g.shape[0]} cols"),
+        rates=rates, step_ms_extrapolated=t_total * 1e3)
+
+
+def traffic_for(workload, kernel):
+    """HBM bytes/launch from committed PMC counters, if the kernel source is unchanged."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    k = t.get("kernels", {}).get(kernel)
+    if not k or k.get("src_hash") != src_hash(KERNELS[kernel][0]):
+        return None
+    return k.get("bytes_per_launch")
+
+
+def run(args):
+    import torch
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                          "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    wl = WORKLOADS[args.workload]
+    step = Step(wl, dev)
+    torch.cuda.synchronize()
+    work = step.work()
+    launches = list(step.launches())
+    for _ in range(args.warmup):
+        for _, fn in launches:
+            fn()
+    torch.cuda.synchronize()
+    ev = {n: [] for n, _ in launches}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for name, fn in launches:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ev[name].append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    comps = {}
+    for name, pairs in ev.items():
+        us = float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e3
+        amt, unit, bound, peak = work[name]
+        rate = amt / (us * 1e-6)
+        comps[name] = dict(us=round(us, 3), work=amt, work_unit=unit, bound=bound,
+                           achieved=round(rate / (1e9 if unit == "byte" else 1e12), 3),
+                           rate_unit="GB/s" if unit == "byte" else "TFLOP/s",
+                           frac=round(rate / peak, 4))
+    dom = max(comps, key=lambda n: comps[n]["us"])
+    d = comps[dom]
+    roof = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"],
+            "peak": PEAK_HBM_GBS if d["bound"] == "hbm" else (
+                PEAK_BF16_TFLOPS if d["bound"] == "mfma" else PEAK_FP32_VALU_TFLOPS),
+            "unit": d["rate_unit"], "frac": d["frac"], "traffic": traffic_for(args.workload, dom)}
+    gv = comps["gemv_m1"]
+    out = {
+        "metric": METRIC, "value": gv["achieved"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16+fp32",
+        "data": "synthetic (seeded; see w4a16_group_wise_amd/synth.py)",
+        "config": {"workload": f"{args.workload}: {wl['desc']}", "d_out": step.d_out,
+                   "d_in": step.d_in, "n_tok": step.n_tok, "n_cand": step.K,
+                   "gemm_m": step.gemm_m, "parallelism": "single GPU"},
+        "roofline": roof,
+        "components": {
+            "gemv_m1_frac_hbm": gv["frac"],
+            "search_groups_per_s": round(step.d_out * step.G / (comps["scale_search"]["us"] * 1e-6), 1),
+            "hessian_mfma_frac": comps["hessian"]["frac"],
+            "gemm_mfma_frac": comps["gemm"]["frac"],
+        },
+        "kernels": comps,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(step)
+    print(json.dumps(out))
+
+
+def pmc_summary(args):
+    """Per-kernel FETCH_SIZE / WRITE_SIZE (KiB per dispatch) -> bytes per launch, scaled by the
+    counter reading of torch's plain copy of a known size that bench.py --pmc-copy runs."""
+    import csv
+    import glob
+
+    def read(dirn, counter):
+        rows = {}
+        for f in glob.glob(os.path.join(dirn, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r.get("Counter_Name") != counter:
+                        continue
+                    rows.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return rows
+
+    fetch = read(args.pmc_summary[0], "FETCH_SIZE")
+    write = read(args.pmc_summary[1], "WRITE_SIZE")
+    copy_bytes = float(args.copy_bytes)
+
+    def mean_of(rows, keys):
+        vals = [v for k, vs in rows.items() if any(s in k for s in keys) for v in vs]
+        return float(np.mean(vals)) if vals else None
+
+    cf = mean_of(fetch, ["elementwise_kernel", "copy"])
+    cw = mean_of(write, ["elementwise_kernel", "copy"])
+    f_scale = copy_bytes / (cf * 1024) if cf else 1.0
+    w_scale = copy_bytes / (cw * 1024) if cw else 1.0
+    res = {"workload": args.workload, "copy_bytes": copy_bytes, "fetch_scale": f_scale,
+           "write_scale": w_scale, "kernels": {}}
+    for name, (src, keys) in KERNELS.items():
+        fk = mean_of(fetch, keys)
+        wk = mean_of(write, keys)
+        if fk is None or wk is None:
+            continue
+        res["kernels"][name] = {"fetch_kib": fk, "write_kib": wk,
+                                "bytes_per_launch": fk * 1024 * f_scale + wk * 1024 * w_scale,
+                                "src_hash": src_hash(src)}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    p = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    with open(p, "w") as f:
+        json.dump(res, f, indent=1)
+    print(p)
+
+
+def pmc_copy(args):
+    """A plain device-to-device copy of known size, to calibrate the byte counters."""
+    import torch
+
+    n = int(args.copy_bytes) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print("copy done", n * 4)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="cfg2", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--pmc-copy", action="store_true")
+    ap.add_argument("--copy-bytes", type=float, default=float(1 << 30))
+    args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args)
+    elif args.pmc_copy:
+        pmc_copy(args)
+    else:
+        run(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -46,14 +46,16 @@ __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __builtin_bit_c
 
 // One correction step around an estimate c0 of the code (|c0 - code| <= 1 after clamping).
 // The signs of w - (c +- 1/2) D come from single fused multiply-adds, whose rounding never
-// changes a sign, so the decision is exact for any finite D > 0.
+// changes a sign, so the decision is exact for any finite D > 0.  Branch-free (bitwise
+// combinations of lane masks and selects).
 __device__ __forceinline__ float code_correct(float w, float d, float c) {
   c = __builtin_fminf(__builtin_fmaxf(c, -8.0f), 7.0f);
   const float rh = __builtin_fmaf(-(c + 0.5f), d, w);
   const float rl = __builtin_fmaf(-(c - 0.5f), d, w);
-  const bool odd = (static_cast<int>(c) & 1) != 0;
-  const bool up = (c < 7.0f) && (rh > 0.0f || (rh == 0.0f && odd));
-  const bool dn = (c > -8.0f) && (rl < 0.0f || (rl == 0.0f && odd));
+  const float half = c * 0.5f;
+  const bool odd = half != __builtin_rintf(half);
+  const bool up = ((rh > 0.0f) | ((rh == 0.0f) & odd)) & (c < 7.0f);
+  const bool dn = ((rl < 0.0f) | ((rl == 0.0f) & odd)) & (c > -8.0f);
   return c + (up ? 1.0f : 0.0f) - (dn ? 1.0f : 0.0f);
 }
 

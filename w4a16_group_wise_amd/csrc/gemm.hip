@@ -11,8 +11,10 @@
 // products unrounded.
 //
 // Tiling: 128x128 block tile, 4 wavefronts of 64x64 (2x2 MFMA blocks each), double-buffered
-// LDS with one barrier per group.  LDS rows are padded to 80 bytes so the 16-byte fragment
-// reads of 8 consecutive lanes fall in distinct banks.
+// LDS with one barrier per group, and a register ring that keeps the global loads of the next
+// PD - 1 groups in flight (one group of compute is far shorter than a memory round trip).
+// LDS rows are padded to 80 bytes so the 16-byte fragment reads of 8 consecutive lanes fall
+// in distinct banks.
 #include "common.hpp"
 
 namespace w4q {
@@ -22,6 +24,7 @@ constexpr int kThreads = 256;
 constexpr int BM = 128;
 constexpr int BN = 128;
 constexpr int LDA = 40;  // bf16 per LDS row (32 + 8 pad)
+constexpr int PD = 4;    // groups in flight between global memory and registers
 
 // 16 two's-complement nibbles (k ascending) -> 16 exact bf16 codes as 8 dwords.
 __device__ __forceinline__ void expand16(u32x2 v, u32x4& lo, u32x4& hi) {
@@ -63,30 +66,37 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint16_t* __res
   // load roles: A row ar (two 16-byte halves by ah), B column bc (8 bytes = 16 codes by bh)
   const int ar = tid >> 1, ah = tid & 1;
   const int bc = tid >> 1, bh = tid & 1;
-  const bool a_ok = m0 + ar < M;
-  const bool b_ok = n0 + bc < N;
-  const uint16_t* xa = x + (a_ok ? m0 + ar : 0) * K + 16 * ah;
-  const uint8_t* pb = packed + (b_ok ? n0 + bc : 0) * prow + 8 * bh;
-  const uint16_t* sb = s16 + (b_ok ? n0 + bc : 0) * G;
+  // rows / columns past the edge read row / column 0 instead: they only feed outputs that
+  // are never stored, and unconditional loads keep the prefetch free of branches and waits
+  const int64_t arow = m0 + ar < M ? m0 + ar : 0;
+  const int64_t bcol = n0 + bc < N ? n0 + bc : 0;
+  const uint16_t* xa = x + arow * K + 16 * ah;
+  const uint8_t* pb = packed + bcol * prow + 8 * bh;
+  const uint16_t* sb = s16 + bcol * G;
 
-  u32x4 ra0, ra1;
-  u32x2 rb;
-  uint16_t rsc = 0;
-  auto gload = [&](int64_t g) {
-    const u32x4 z4 = u32x4{0u, 0u, 0u, 0u};
-    ra0 = a_ok ? *reinterpret_cast<const u32x4*>(xa + g * kGroup) : z4;
-    ra1 = a_ok ? *reinterpret_cast<const u32x4*>(xa + g * kGroup + 8) : z4;
-    rb = b_ok ? *reinterpret_cast<const u32x2*>(pb + g * 16) : u32x2{0u, 0u};
-    if (bh == 0) rsc = b_ok ? sb[g] : static_cast<uint16_t>(0);
+  // global -> register ring, PD groups deep: the loads of group g + PD - 1 are issued while
+  // group g is multiplied, and reach LDS one iteration before they are used
+  struct Stage {
+    u32x4 a0, a1;
+    u32x2 b;
+    uint32_t sc;
   };
-  auto lstore = [&](int buf) {
-    *reinterpret_cast<u32x4*>(&As[buf][ar * LDA + 16 * ah]) = ra0;
-    *reinterpret_cast<u32x4*>(&As[buf][ar * LDA + 16 * ah + 8]) = ra1;
+  Stage st[PD];
+  auto gload = [&](int64_t g, Stage& t) {
+    const int64_t gg = g < G ? g : G - 1;  // clamped: the tail re-reads the last group
+    t.a0 = *reinterpret_cast<const u32x4*>(xa + gg * kGroup);
+    t.a1 = *reinterpret_cast<const u32x4*>(xa + gg * kGroup + 8);
+    t.b = *reinterpret_cast<const u32x2*>(pb + gg * 16);
+    t.sc = sb[gg];
+  };
+  auto lstore = [&](int buf, const Stage& t) {
+    *reinterpret_cast<u32x4*>(&As[buf][ar * LDA + 16 * ah]) = t.a0;
+    *reinterpret_cast<u32x4*>(&As[buf][ar * LDA + 16 * ah + 8]) = t.a1;
     u32x4 blo, bhi;
-    expand16(rb, blo, bhi);
+    expand16(t.b, blo, bhi);
     *reinterpret_cast<u32x4*>(&Bs[buf][bc * LDA + 16 * bh]) = blo;
     *reinterpret_cast<u32x4*>(&Bs[buf][bc * LDA + 16 * bh + 8]) = bhi;
-    if (bh == 0) Ss[buf][bc] = f16_bits_to_f32(rsc);
+    if (bh == 0) Ss[buf][bc] = f16_bits_to_f32(static_cast<uint16_t>(t.sc));
   };
 
   f32x16 acc[2][2];
@@ -97,17 +107,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint16_t* __res
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
   const f32x16 zero16 = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f,
                          0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   const int fr = lane & 31;
   const int fk = 8 * (lane >> 5);
-  for (int64_t g = 0; g < G; ++g) {
-    const int cur = static_cast<int>(g & 1);
-    const bool more = g + 1 < G;
-    if (more) gload(g + 1);
+  auto mma_group = [&](int cur) {
     f32x16 tmp[2][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -132,8 +136,23 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint16_t* __res
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(sc, tmp[i][j][r], acc[i][j][r]);
     }
-    if (more) lstore(cur ^ 1);
-    __syncthreads();
+  };
+
+#pragma unroll
+  for (int p = 0; p < PD - 1; ++p) gload(p, st[p]);
+  lstore(0, st[0]);
+  __syncthreads();
+  for (int64_t g0 = 0; g0 < G; g0 += PD) {
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+      const int64_t g = g0 + u;
+      if (g >= G) break;  // uniform
+      gload(g + PD - 1, st[(u + PD - 1) % PD]);
+      asm volatile("" ::: "memory");  // keep the prefetch issued here
+      mma_group(static_cast<int>(g & 1));
+      if (g + 1 < G) lstore(static_cast<int>((g + 1) & 1), st[(u + 1) % PD]);
+      __syncthreads();
+    }
   }
 
   // 32x32 accumulator layout: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, column l%32

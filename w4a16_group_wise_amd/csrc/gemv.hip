@@ -16,17 +16,18 @@
 // bf16 with exponent 2^7, giving the exact value 8 * (24 + q); v_dot2 multiplies two such codes
 // with two activations into an fp32 sum.  The constant part is removed per group by the same
 // dot2 chain run on the code q = 0 (bitwise the same sum when every code of the group is 0),
-// and the factor 8 is folded into the scale.  The bias is 24/|q| times the signal, so the
-// fp32 sum error stays near 2^-24 * 31 * sum|x| per group.
+// and the factor 8 is removed (exactly) after the row reduction.  The bias is 24/|q| times the
+// signal, so the fp32 sum error stays near 2^-24 * 31 * sum|x| per group.  The next chunk's
+// codes, scales and activations are loaded while the current chunk is being reduced.
 #include "common.hpp"
 
 namespace w4q {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr uint32_t kMagic = 0x43004300u;  // bf16 pair with exponent 2^7, zero mantissa
-constexpr uint32_t kMask = 0x00780078u;   // mantissa bits 3..6 of each half
-constexpr uint32_t kZero = 0x43404340u;   // code q = 0 (n = 8) in both halves
+constexpr uint32_t kMask = 0x00780078u;  // mantissa bits 3..6 of each bf16 half
+constexpr uint32_t kC0 = 0x43404340u;    // bf16 pair 2^7 with the nibble bias folded in
+constexpr uint32_t kZero = 0x43404340u;  // code q = 0 (n = 8) in both halves
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
@@ -35,28 +36,38 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 
 // 8 activations x[8b .. 8b+7] as 4 dwords (x0,x1)(x2,x3)(x4,x5)(x6,x7) -> the pairs
 // (x0,x4)(x1,x5)(x2,x6)(x3,x7) that match the nibble pairs extracted below.
-__device__ __forceinline__ void pair_x(const u32x4 d, uint32_t (&p)[4]) {
+__device__ __forceinline__ void pair_x(const u32x4 d, uint32_t* p) {
   p[0] = __builtin_amdgcn_perm(d.z, d.x, 0x05040100u);
   p[1] = __builtin_amdgcn_perm(d.z, d.x, 0x07060302u);
   p[2] = __builtin_amdgcn_perm(d.w, d.y, 0x05040100u);
   p[3] = __builtin_amdgcn_perm(d.w, d.y, 0x07060302u);
 }
 
-// 8 two's-complement nibbles -> biased bf16 code pairs (nibble i and i+4 share a dword).
-__device__ __forceinline__ void codes_bf16(uint32_t v, uint32_t (&c)[4]) {
-  v ^= 0x88888888u;  // two's complement -> offset binary n = q + 8
-  c[0] = ((v << 3) & kMask) | kMagic;
-  c[1] = ((v >> 1) & kMask) | kMagic;
-  c[2] = ((v >> 5) & kMask) | kMagic;
-  c[3] = ((v >> 9) & kMask) | kMagic;
+// 8 two's-complement nibbles (one dword) -> 4 bf16 pairs (nibble i with i+4) holding
+// 8 * (24 + q).  ((v >> s) & mask) ^ c0 moves a nibble to mantissa bits 3..6 and flips its top
+// bit (two's complement -> offset binary n = q + 8) while inserting the exponent; the
+// compiler emits one v_bitop3 per pair with mask in an SGPR and c0 in a VGPR.
+__device__ __forceinline__ void codes_bf16(uint32_t v, uint32_t mask, uint32_t c0, uint32_t* c) {
+  c[0] = ((v << 3) & mask) ^ c0;
+  c[1] = ((v >> 1) & mask) ^ c0;
+  c[2] = ((v >> 5) & mask) ^ c0;
+  c[3] = ((v >> 9) & mask) ^ c0;
 }
 
+template <int MT, int RS>
+struct Chunk {
+  u32x4 code[RS];
+  uint32_t sc[RS];
+  u32x4 xv[MT][4];
+};
+
 template <int MT, int LPR, int RS>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(const uint16_t* __restrict__ x, int64_t m_rows,
+__global__ __launch_bounds__(kThreads) void gemv_kernel(const uint16_t* __restrict__ x, int m_rows,
                                                         const uint8_t* __restrict__ packed,
                                                         const uint16_t* __restrict__ s16,
                                                         int64_t d_out, int64_t d_in,
-                                                        void* __restrict__ y, int y_dtype) {
+                                                        void* __restrict__ y, int y_dtype,
+                                                        uint32_t mask) {
   constexpr int RPS = 64 / LPR;  // rows per row-step
   const int lane = threadIdx.x & 63;
   const int sub = lane / LPR;
@@ -64,9 +75,38 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint16_t* __restri
   const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + threadIdx.x / 64;
   const int64_t row0 = wave * (RPS * RS);
   if (row0 >= d_out) return;  // uniform per wavefront
-  const int64_t G = d_in / kGroup;
-  const int64_t nchunk = G / LPR;
-  const int64_t prow = d_in / 2;
+  const int G = static_cast<int>(d_in / kGroup);
+  const int nchunk = G / LPR;
+  uint32_t c0 = kC0;
+  asm volatile("" : "+v"(c0));  // keep the constant in a VGPR so v_bitop3 can take it
+
+  // per row-step base pointers (64-bit once), then 32-bit offsets per chunk
+  const uint8_t* prow[RS];
+  const uint16_t* srow[RS];
+  bool rok[RS];
+#pragma unroll
+  for (int rs = 0; rs < RS; ++rs) {
+    const int64_t n = row0 + rs * RPS + sub;
+    rok[rs] = n < d_out;
+    const int64_t nn = rok[rs] ? n : 0;
+    prow[rs] = packed + nn * (d_in / 2) + j * 16;
+    srow[rs] = s16 + nn * G + j;
+  }
+  const uint16_t* xrow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) xrow[m] = x + (m < m_rows ? m : 0) * d_in + j * kGroup;
+
+  auto load = [&](int c, Chunk<MT, RS>& k) {
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs) {
+      k.code[rs] = *reinterpret_cast<const u32x4*>(prow[rs] + c * (LPR * 16));
+      k.sc[rs] = srow[rs][c * LPR];
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) k.xv[m][b] = *reinterpret_cast<const u32x4*>(xrow[m] + c * (LPR * kGroup) + 8 * b);
+  };
 
   float acc[RS][MT];
 #pragma unroll
@@ -74,35 +114,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint16_t* __restri
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[rs][m] = 0.0f;
 
-  for (int64_t c = 0; c < nchunk; ++c) {
-    const int64_t g = c * LPR + j;
-    // codes + scales of this chunk for all row-steps (issued first, HBM stream)
-    u32x4 cw[RS];
-    float sc[RS];
-#pragma unroll
-    for (int rs = 0; rs < RS; ++rs) {
-      const int64_t n = row0 + rs * RPS + sub;
-      const bool ok = n < d_out;
-      const int64_t nn = ok ? n : 0;
-      cw[rs] = *reinterpret_cast<const u32x4*>(packed + nn * prow + g * 16);
-      sc[rs] = ok ? f16_bits_to_f32(s16[nn * G + g]) * 0.125f : 0.0f;
-    }
-    // activations of this group, paired, plus the zero-code sum
+  auto compute = [&](const Chunk<MT, RS>& cur) {
+    // activations of this group, paired, plus the zero-code sum (same dot2 order as below)
     uint32_t xp[MT][16];
     float corr[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const bool okm = m < m_rows;
-      const uint16_t* xr = x + (okm ? m : 0) * d_in + g * kGroup;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        u32x4 d = *reinterpret_cast<const u32x4*>(xr + 8 * b);
-        if (!okm) d = u32x4{0u, 0u, 0u, 0u};
-        uint32_t p[4];
-        pair_x(d, p);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xp[m][4 * b + i] = p[i];
-      }
+      for (int b = 0; b < 4; ++b) pair_x(m < m_rows ? cur.xv[m][b] : u32x4{0u, 0u, 0u, 0u}, &xp[m][4 * b]);
       float a = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) a = dot2(xp[m][i], kZero, a);
@@ -111,24 +130,35 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint16_t* __restri
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs) {
       uint32_t cb[16];
-      const uint32_t words[4] = {cw[rs].x, cw[rs].y, cw[rs].z, cw[rs].w};
+      const uint32_t words[4] = {cur.code[rs].x, cur.code[rs].y, cur.code[rs].z, cur.code[rs].w};
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        uint32_t cc[4];
-        codes_bf16(words[b], cc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cb[4 * b + i] = cc[i];
-      }
+      for (int b = 0; b < 4; ++b) codes_bf16(words[b], mask, c0, &cb[4 * b]);
+      const float sc = f16_bits_to_f32(static_cast<uint16_t>(cur.sc[rs]));
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         float a = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) a = dot2(xp[m][i], cb[i], a);
-        acc[rs][m] = __builtin_fmaf(sc[rs], a - corr[m], acc[rs][m]);
+        acc[rs][m] = __builtin_fmaf(sc, a - corr[m], acc[rs][m]);
       }
     }
+  };
+
+  // two register sets: the loads of one chunk are in flight while the other is reduced
+  // (the empty asm with a memory clobber keeps each batch of loads where it is issued)
+  Chunk<MT, RS> ca, cb;
+  load(0, ca);
+  int c = 0;
+  for (; c + 1 < nchunk; c += 2) {
+    load(c + 1, cb);
+    asm volatile("" ::: "memory");
+    compute(ca);
+    if (c + 2 < nchunk) load(c + 2, ca);
+    asm volatile("" ::: "memory");
+    compute(cb);
   }
-  // reduce the LPR lane partials of each row (fixed butterfly order)
+  if (c < nchunk) compute(ca);
+  // reduce the LPR lane partials of each row (fixed butterfly order); undo the factor 8
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs) {
     const int64_t n = row0 + rs * RPS + sub;
@@ -137,7 +167,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint16_t* __restri
       float v = acc[rs][m];
 #pragma unroll
       for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-      if (j == 0 && n < d_out && m < m_rows) {
+      v *= 0.125f;
+      if (j == 0 && rok[rs] && m < m_rows) {
         if (y_dtype == 0)
           reinterpret_cast<float*>(y)[m * d_out + n] = v;
         else
@@ -156,14 +187,14 @@ int launch_lpr(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16
   if (waves1 >= 4 * 1024) {
     const int64_t waves = (d_out + 4 * RPS - 1) / (4 * RPS);
     hipLaunchKernelGGL((gemv_kernel<MT, LPR, 4>), dim3(static_cast<unsigned>((waves + 3) / 4)),
-                       dim3(kThreads), 0, s, x, m, packed, s16, d_out, d_in, y, ydt);
+                       dim3(kThreads), 0, s, x, static_cast<int>(m), packed, s16, d_out, d_in, y, ydt, kMask);
   } else if (waves1 >= 2 * 1024) {
     const int64_t waves = (d_out + 2 * RPS - 1) / (2 * RPS);
     hipLaunchKernelGGL((gemv_kernel<MT, LPR, 2>), dim3(static_cast<unsigned>((waves + 3) / 4)),
-                       dim3(kThreads), 0, s, x, m, packed, s16, d_out, d_in, y, ydt);
+                       dim3(kThreads), 0, s, x, static_cast<int>(m), packed, s16, d_out, d_in, y, ydt, kMask);
   } else {
     hipLaunchKernelGGL((gemv_kernel<MT, LPR, 1>), dim3(static_cast<unsigned>((waves1 + 3) / 4)),
-                       dim3(kThreads), 0, s, x, m, packed, s16, d_out, d_in, y, ydt);
+                       dim3(kThreads), 0, s, x, static_cast<int>(m), packed, s16, d_out, d_in, y, ydt, kMask);
   }
   return w4q_launch_status();
 }

@@ -22,6 +22,7 @@ constexpr int kThreads = 256;
 constexpr int HT = 128;      // tile edge in features
 constexpr int HK = 64;       // tokens per stage
 constexpr int HLD = HK + 8;  // bf16 per LDS feature row (144 bytes)
+constexpr int PD = 3;        // stages in flight between global memory and registers
 
 __global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __restrict__ x, int64_t n_tok,
                                                               int64_t d, float* __restrict__ h,
@@ -47,19 +48,29 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __
   const int fb = (lane >> 3) + 8 * wid;         // 0..31: 0..15 -> I rows, 16..31 -> J rows
   const bool jrow = fb >= 16;
   const int64_t feat = jrow ? (int64_t)tj * HT + 8 * (fb - 16) : (int64_t)ti * HT + 8 * fb;
-  const bool f_ok = feat < d && !(diag && jrow);  // diagonal tiles stage the I rows only
-  const uint16_t* xf = x + (f_ok ? feat : 0);
+  // (on a diagonal tile the J rows repeat the I rows; they are staged anyway, which keeps the
+  // loads free of branches, but never read)
+  // features past d read feature 0 instead (they only feed entries that are never stored);
+  // tokens past n_tok read the last token and are zeroed when staged into LDS.  Unconditional
+  // loads keep the prefetch ring free of branches and early waits.
+  const uint16_t* xf = x + (feat < d ? feat : 0);
 
-  u32x4 rv[8];
-  auto gload = [&](int64_t k0) {
+  struct Stage {
+    u32x4 v[8];
+  };
+  Stage st[PD];
+  auto gload = [&](int64_t k0, Stage& t) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int64_t tok = k0 + 8 * tb + t;
-      rv[t] = (f_ok && tok < n_tok) ? *reinterpret_cast<const u32x4*>(xf + tok * d) : u32x4{0u, 0u, 0u, 0u};
+    for (int r = 0; r < 8; ++r) {
+      int64_t tok = k0 + 8 * tb + r;
+      tok = tok < n_tok ? tok : n_tok - 1;
+      t.v[r] = *reinterpret_cast<const u32x4*>(xf + tok * d);
     }
   };
-  auto lstore = [&](int buf) {
-    if (diag && jrow) return;
+  auto lstore = [&](int buf, int64_t k0, const Stage& t) {
+    u32x4 rv[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) rv[r] = (k0 + 8 * tb + r < n_tok) ? t.v[r] : u32x4{0u, 0u, 0u, 0u};
     // 8x8 transpose: out[f] holds tokens 0..7 of feature f as 4 bf16 pairs
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
@@ -90,32 +101,42 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __
   const int fk = 8 * (lane >> 5);
   const int64_t nstage = (n_tok + HK - 1) / HK;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int64_t st = 0; st < nstage; ++st) {
-    const int cur = static_cast<int>(st & 1);
-    const bool more = st + 1 < nstage;
-    if (more) gload((st + 1) * HK);
-    if (work) {
+  auto mma_stage = [&](int cur) {
+    if (!work) return;
 #pragma unroll
-      for (int s = 0; s < HK / 16; ++s) {
-        bf16x8 a[2], b[2];
+    for (int s = 0; s < HK / 16; ++s) {
+      bf16x8 a[2], b[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          a[i] = *reinterpret_cast<const bf16x8*>(&Xs[cur][(wm * 64 + 32 * i + fr) * HLD + 16 * s + fk]);
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(&Xs[cur][(wm * 64 + 32 * i + fr) * HLD + 16 * s + fk]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const bf16x8*>(&Xs[cur][(jbase + wn * 64 + 32 * j + fr) * HLD + 16 * s + fk]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          b[j] = *reinterpret_cast<const bf16x8*>(&Xs[cur][(jbase + wn * 64 + 32 * j + fr) * HLD + 16 * s + fk]);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (more) lstore(cur ^ 1);
-    __syncthreads();
+  };
+
+  // register ring PD stages deep: loads of stage st + PD - 1 are issued while stage st is
+  // multiplied, and reach LDS one iteration before they are used
+#pragma unroll
+  for (int p = 0; p < PD - 1; ++p) gload(p * HK, st[p]);
+  lstore(0, 0, st[0]);
+  __syncthreads();
+  for (int64_t s0 = 0; s0 < nstage; s0 += PD) {
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+      const int64_t sg = s0 + u;
+      if (sg >= nstage) break;  // uniform
+      gload((sg + PD - 1) * HK, st[(u + PD - 1) % PD]);
+      asm volatile("" ::: "memory");  // keep the prefetch issued here
+      mma_stage(static_cast<int>(sg & 1));
+      if (sg + 1 < nstage) lstore(static_cast<int>((sg + 1) & 1), (sg + 1) * HK, st[(u + 1) % PD]);
+      __syncthreads();
+    }
   }
   if (!work) return;
 

@@ -10,93 +10,104 @@
 // scale of column n is applied once per group (acc += s * P_g), so the weights enter the
 // products unrounded.
 //
-// Tiling: 128x128 block tile, 4 wavefronts of 64x64 (2x2 MFMA blocks each), double-buffered
-// LDS with one barrier per group, and a register ring that keeps the global loads of the next
-// PD - 1 groups in flight (one group of compute is far shorter than a memory round trip).
-// LDS rows are padded to 80 bytes so the 16-byte fragment reads of 8 consecutive lanes fall
-// in distinct banks.
+// Tiling: 256x128 (or 128x128 for short M) block tile, wavefronts of 64x64 (2x2 MFMA blocks
+// each) that all share one expansion of the codes per group, double-buffered LDS with one
+// barrier per group, and a register ring that keeps the global loads of the next PD - 1
+// groups in flight (one group of compute is far shorter than a memory round trip).  LDS rows
+// are XOR-swizzled in 16-byte chunks so fragment reads and tile writes are bank-conflict free.
 #include "common.hpp"
 
 namespace w4q {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int BM = 128;
-constexpr int BN = 128;
-constexpr int LDA = 40;  // bf16 per LDS row (32 + 8 pad)
-constexpr int PD = 4;    // groups in flight between global memory and registers
+constexpr int WN = 2;   // wavefronts along N (64 columns each)
+constexpr int BN = 64 * WN;
+constexpr int PD = 4;   // groups in flight between global memory and registers
 
-// 16 two's-complement nibbles (k ascending) -> 16 exact bf16 codes as 8 dwords.
-__device__ __forceinline__ void expand16(u32x2 v, u32x4& lo, u32x4& hi) {
-  uint32_t o[8];
+// LDS tiles are rows of 32 bf16 (4 chunks of 16 bytes, no padding); chunk c of row r is stored
+// at chunk c ^ ((r >> 1) & 3).  Eight lanes reading one chunk of eight consecutive rows, and
+// eight lanes writing the four chunks of two consecutive rows, then hit distinct banks.
+__device__ __forceinline__ int swz(int r, int c) { return r * 32 + 8 * (c ^ ((r >> 1) & 3)); }
+
+// 8 two's-complement nibbles (k ascending) -> 8 exact bf16 codes as 4 dwords.
+__device__ __forceinline__ u32x4 expand8(uint32_t word) {
+  uint32_t o[4];
 #pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    const uint32_t word = w == 0 ? v.x : v.y;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int q0 = static_cast<int>(word << (28 - 8 * p)) >> 28;
-      const int q1 = static_cast<int>(word << (24 - 8 * p)) >> 28;
-      const uint32_t f0 = __builtin_bit_cast(uint32_t, static_cast<float>(q0));
-      const uint32_t f1 = __builtin_bit_cast(uint32_t, static_cast<float>(q1));
-      o[4 * w + p] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);  // small integers: exact
-    }
+  for (int p = 0; p < 4; ++p) {
+    const int q0 = static_cast<int>(word << (28 - 8 * p)) >> 28;
+    const int q1 = static_cast<int>(word << (24 - 8 * p)) >> 28;
+    const uint32_t f0 = __builtin_bit_cast(uint32_t, static_cast<float>(q0));
+    const uint32_t f1 = __builtin_bit_cast(uint32_t, static_cast<float>(q1));
+    o[p] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);  // small integers: exact in bf16
   }
-  lo = u32x4{o[0], o[1], o[2], o[3]};
-  hi = u32x4{o[4], o[5], o[6], o[7]};
+  return u32x4{o[0], o[1], o[2], o[3]};
 }
 
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint16_t* __restrict__ x, int64_t M,
-                                                           const uint8_t* __restrict__ packed,
-                                                           const uint16_t* __restrict__ s16,
-                                                           int64_t N, int64_t K,
-                                                           void* __restrict__ y, int y_dtype) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDA];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDA];
+// WM wavefronts along M (64 rows each) x WN along N; block tile (64 WM) x 128.
+template <int WM>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                          const uint8_t* __restrict__ packed,
+                                                          const uint16_t* __restrict__ s16,
+                                                          int64_t N, int64_t K,
+                                                          void* __restrict__ y, int y_dtype,
+                                                          int64_t gn, int64_t tiles, int64_t per_xcd) {
+  constexpr int NT = 64 * WM * WN;  // threads
+  constexpr int BM = 64 * WM;
+  constexpr int BJ = BN * 4 / NT;   // B dwords (8 codes) per thread per group
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * 32];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * 32];
   __shared__ float Ss[2][BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int64_t n0 = (int64_t)blockIdx.x * BN;
-  const int64_t G = K / kGroup;
+  const int wm = wid % WM, wn = wid / WM;
+  // workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous run of tiles in
+  // N-fastest order, so the tiles resident on one XCD share their activation panel in its L2
+  const int64_t t = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (t >= tiles) return;
+  const int64_t m0 = (t / gn) * BM;
+  const int64_t n0 = (t % gn) * BN;
+  const int G = static_cast<int>(K / kGroup);
   const int64_t prow = K / 2;
 
-  // load roles: A row ar (two 16-byte halves by ah), B column bc (8 bytes = 16 codes by bh)
-  const int ar = tid >> 1, ah = tid & 1;
-  const int bc = tid >> 1, bh = tid & 1;
-  // rows / columns past the edge read row / column 0 instead: they only feed outputs that
-  // are never stored, and unconditional loads keep the prefetch free of branches and waits
-  const int64_t arow = m0 + ar < M ? m0 + ar : 0;
-  const int64_t bcol = n0 + bc < N ? n0 + bc : 0;
-  const uint16_t* xa = x + arow * K + 16 * ah;
-  const uint8_t* pb = packed + bcol * prow + 8 * bh;
-  const uint16_t* sb = s16 + bcol * G;
+  // load roles.  A: row tid/2, 16-byte chunks 2*(tid%2) and +1.  B: column (tid + NT*j)/4,
+  // dword (tid % 4) = codes 8*(tid%4) .. +7.  Rows / columns past the edge read row / column 0
+  // (they only feed outputs that are never stored), so every load is unconditional.
+  const int ar = tid >> 1, ac = 2 * (tid & 1);
+  const uint16_t* xa = x + (m0 + ar < M ? m0 + ar : 0) * K + 8 * ac;
+  const uint32_t* pb[BJ];
+  int bcol[BJ];
+#pragma unroll
+  for (int j = 0; j < BJ; ++j) {
+    bcol[j] = (tid + NT * j) >> 2;
+    const int64_t n = n0 + bcol[j] < N ? n0 + bcol[j] : 0;
+    pb[j] = reinterpret_cast<const uint32_t*>(packed + n * prow) + (tid & 3);
+  }
+  const bool s_role = tid < BN;
+  const uint16_t* sb = s16 + (s_role && n0 + tid < N ? n0 + tid : 0) * G;
 
-  // global -> register ring, PD groups deep: the loads of group g + PD - 1 are issued while
-  // group g is multiplied, and reach LDS one iteration before they are used
   struct Stage {
     u32x4 a0, a1;
-    u32x2 b;
+    uint32_t b[BJ];
     uint32_t sc;
   };
   Stage st[PD];
-  auto gload = [&](int64_t g, Stage& t) {
-    const int64_t gg = g < G ? g : G - 1;  // clamped: the tail re-reads the last group
+  auto gload = [&](int g, Stage& t) {
+    const int gg = g < G ? g : G - 1;  // clamped: the tail re-reads the last group
     t.a0 = *reinterpret_cast<const u32x4*>(xa + gg * kGroup);
     t.a1 = *reinterpret_cast<const u32x4*>(xa + gg * kGroup + 8);
-    t.b = *reinterpret_cast<const u32x2*>(pb + gg * 16);
+#pragma unroll
+    for (int j = 0; j < BJ; ++j) t.b[j] = pb[j][gg * 4];
     t.sc = sb[gg];
   };
   auto lstore = [&](int buf, const Stage& t) {
-    *reinterpret_cast<u32x4*>(&As[buf][ar * LDA + 16 * ah]) = t.a0;
-    *reinterpret_cast<u32x4*>(&As[buf][ar * LDA + 16 * ah + 8]) = t.a1;
-    u32x4 blo, bhi;
-    expand16(t.b, blo, bhi);
-    *reinterpret_cast<u32x4*>(&Bs[buf][bc * LDA + 16 * bh]) = blo;
-    *reinterpret_cast<u32x4*>(&Bs[buf][bc * LDA + 16 * bh + 8]) = bhi;
-    if (bh == 0) Ss[buf][bc] = f16_bits_to_f32(static_cast<uint16_t>(t.sc));
+    *reinterpret_cast<u32x4*>(&As[buf][swz(ar, ac)]) = t.a0;
+    *reinterpret_cast<u32x4*>(&As[buf][swz(ar, ac + 1)]) = t.a1;
+#pragma unroll
+    for (int j = 0; j < BJ; ++j)
+      *reinterpret_cast<u32x4*>(&Bs[buf][swz(bcol[j], tid & 3)]) = expand8(t.b[j]);
+    if (s_role) Ss[buf][tid] = f16_bits_to_f32(static_cast<uint16_t>(t.sc));
   };
 
   f32x16 acc[2][2];
@@ -110,7 +121,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint16_t* __res
   const f32x16 zero16 = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f,
                          0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   const int fr = lane & 31;
-  const int fk = 8 * (lane >> 5);
+  const int fh = lane >> 5;
   auto mma_group = [&](int cur) {
     f32x16 tmp[2][2];
 #pragma unroll
@@ -118,10 +129,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint16_t* __res
       bf16x8 a[2], b[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(&As[cur][(wm * 64 + 32 * i + fr) * LDA + 16 * s + fk]);
+        a[i] = *reinterpret_cast<const bf16x8*>(&As[cur][swz(wm * 64 + 32 * i + fr, 2 * s + fh)]);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(&Bs[cur][(wn * 64 + 32 * j + fr) * LDA + 16 * s + fk]);
+        b[j] = *reinterpret_cast<const bf16x8*>(&Bs[cur][swz(wn * 64 + 32 * j + fr, 2 * s + fh)]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -142,15 +153,15 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint16_t* __res
   for (int p = 0; p < PD - 1; ++p) gload(p, st[p]);
   lstore(0, st[0]);
   __syncthreads();
-  for (int64_t g0 = 0; g0 < G; g0 += PD) {
+  for (int g0 = 0; g0 < G; g0 += PD) {
 #pragma unroll
     for (int u = 0; u < PD; ++u) {
-      const int64_t g = g0 + u;
+      const int g = g0 + u;
       if (g >= G) break;  // uniform
       gload(g + PD - 1, st[(u + PD - 1) % PD]);
       asm volatile("" ::: "memory");  // keep the prefetch issued here
-      mma_group(static_cast<int>(g & 1));
-      if (g + 1 < G) lstore(static_cast<int>((g + 1) & 1), st[(u + 1) % PD]);
+      mma_group(g & 1);
+      if (g + 1 < G) lstore((g + 1) & 1, st[(u + 1) % PD]);
       __syncthreads();
     }
   }
@@ -164,7 +175,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint16_t* __res
       if (col >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t row = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * fh + (r & 3);
         if (row < M) {
           if (y_dtype == 0)
             reinterpret_cast<float*>(y)[row * N + col] = acc[i][j][r];
@@ -182,9 +193,21 @@ using namespace w4q;
 
 int w4q_launch_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
                     int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t s) {
-  const int64_t gm = (m + BM - 1) / BM, gn = (d_out + BN - 1) / BN;
-  if (gm > 65535 || gn > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
-  hipLaunchKernelGGL(gemm_kernel, dim3(static_cast<unsigned>(gn), static_cast<unsigned>(gm)),
-                     dim3(kThreads), 0, s, x, m, packed, s16, d_out, d_in, y, y_dtype);
+  if (d_in / kGroup > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
+  const int64_t gn = (d_out + BN - 1) / BN;
+  // 256-row tiles (8 wavefronts share one expansion of the codes) when they still give at
+  // least one tile per compute unit, 128-row tiles otherwise
+  const int64_t gm4 = (m + 255) / 256, gm2 = (m + 127) / 128;
+  const bool big = gm4 * gn >= 256;
+  const int64_t tiles = (big ? gm4 : gm2) * gn;
+  const int64_t per_xcd = (tiles + 7) / 8;
+  if (8 * per_xcd > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
+  const dim3 grid(static_cast<unsigned>(8 * per_xcd));
+  if (big)
+    hipLaunchKernelGGL(gemm_kernel<4>, grid, dim3(64 * 4 * WN), 0, s, x, m, packed, s16, d_out, d_in, y,
+                       y_dtype, gn, tiles, per_xcd);
+  else
+    hipLaunchKernelGGL(gemm_kernel<2>, grid, dim3(64 * 2 * WN), 0, s, x, m, packed, s16, d_out, d_in, y,
+                       y_dtype, gn, tiles, per_xcd);
   return w4q_launch_status();
 }

@@ -26,11 +26,16 @@ constexpr int PD = 3;        // stages in flight between global memory and regis
 
 __global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __restrict__ x, int64_t n_tok,
                                                               int64_t d, float* __restrict__ h,
-                                                              int accumulate, int nt) {
+                                                              int accumulate, int nt,
+                                                              int64_t tiles, int64_t per_xcd) {
   __shared__ __attribute__((aligned(16))) uint16_t Xs[2][2 * HT * HLD];
 
+  // workgroups are dealt to the 8 XCDs round-robin; each XCD takes a contiguous run of the
+  // row-major upper-triangle tiles, so its resident tiles share I panels in its L2
+  const int64_t t = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (t >= tiles) return;
   // upper-triangle tile (ti <= tj) of this block
-  int rem = blockIdx.x, ti = 0;
+  int rem = static_cast<int>(t), ti = 0;
   while (rem >= nt - ti) {
     rem -= nt - ti;
     ++ti;
@@ -167,8 +172,9 @@ int w4q_launch_hessian(const uint16_t* x, int64_t n_tok, int64_t d, float* h, in
                        hipStream_t s) {
   const int64_t nt = (d + HT - 1) / HT;
   const int64_t tiles = nt * (nt + 1) / 2;
-  if (tiles > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
-  hipLaunchKernelGGL(hessian_kernel, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s, x,
-                     n_tok, d, h, accumulate, static_cast<int>(nt));
+  const int64_t per_xcd = (tiles + 7) / 8;
+  if (8 * per_xcd > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
+  hipLaunchKernelGGL(hessian_kernel, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(kThreads), 0, s, x,
+                     n_tok, d, h, accumulate, static_cast<int>(nt), tiles, per_xcd);
   return w4q_launch_status();
 }

@@ -112,9 +112,12 @@ __global__ __launch_bounds__(kThreads) void search_fp32_kernel(
 
   float best = __builtin_inff(), second = __builtin_inff(), dbest = 0.0f;
   int kbest = 0;
+  float a_next = alpha[0];
 #pragma unroll 1
   for (int k = 0; k < n_cand; ++k) {
-    const float d = candidate(amax, alpha[k]);
+    const float a = a_next;
+    a_next = alpha[k + 1 < n_cand ? k + 1 : k];  // scalar prefetch for the next candidate
+    const float d = candidate(amax, a);
     float e[16];
     codes<16>(wv, d, e);
 #pragma unroll
@@ -127,16 +130,16 @@ __global__ __launch_bounds__(kThreads) void search_fp32_kernel(
     float part = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) part = __builtin_fmaf(e[i], acc[i], part);
+    // both lanes of a row get the sum of the two halves (fp32 addition is commutative, so
+    // both see the same bits)
     const float o = part + __shfl_xor(part, 32);
     if (obj_all != nullptr && live && hh == 0) obj_all[(r * G + g) * n_cand + k] = o;
-    if (o < best) {
-      second = best;
-      best = o;
-      kbest = k;
-      dbest = d;
-    } else if (o < second) {
-      second = o;
-    }
+    // running first minimum and second-smallest score (branch-free)
+    const bool better = o < best;
+    second = better ? best : __builtin_fminf(second, o);
+    kbest = better ? k : kbest;
+    dbest = better ? d : dbest;
+    best = better ? o : best;
   }
   if (!live || hh != 0) return;
   const int64_t o_ = r * G + g;

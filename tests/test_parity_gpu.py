@@ -48,7 +48,8 @@ def test_hessian_config(dev, cfg):
     check_hessian(h, oracle.hessian(x))
 
 
-@pytest.mark.parametrize("n_tok,d", [(1, 8), (100, 136), (65, 256), (130, 520)])
+# (45, 5640): wide enough for the 256-wide tiles, ragged in features (22 * 256 + 8) and tokens
+@pytest.mark.parametrize("n_tok,d", [(1, 8), (100, 136), (65, 256), (130, 520), (45, 5640)])
 def test_hessian_ragged(dev, n_tok, d):
     x = synth.calib_x(31, 0, n_tok, n_tok, d, 1.0)
     say("hessian ragged", n_tok, d)
@@ -57,9 +58,10 @@ def test_hessian_ragged(dev, n_tok, d):
     check_hessian(h, oracle.hessian(x))
 
 
-def test_hessian_accumulate(dev):
-    x = synth.calib_x(31, 1, 0, 192, 264, 1.5)
-    say("hessian accumulate")
+@pytest.mark.parametrize("d", [264, 5888])
+def test_hessian_accumulate(dev, d):
+    x = synth.calib_x(31, 1, 0, 192, d, 1.5)
+    say("hessian accumulate", d)
     h = w4q.quant_hessian(dev_bf16(x[:100], dev))
     w4q.quant_hessian(dev_bf16(x[100:], dev), h=h, accumulate=True)
     hn = h.cpu().numpy()

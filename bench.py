@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -37,14 +38,14 @@ CSRC = os.path.join(ROOT, "w4a16_group_wise_amd", "csrc")
 
 # kernel family -> (source file, symbol substrings as they appear in a kernel trace)
 KERNELS = {
-    "hessian": ("hessian.hip", ["hessian_kernel"]),
+    "hessian": ("hessian.hip", ["hessian_kernel", "hessian256_kernel"]),
     "scale_search": ("scale_search.hip", ["search_fp32_kernel", "search_fp64_kernel"]),
     "pack": ("pack_lsq.hip", ["pack_kernel"]),
     "lsq_fwd": ("pack_lsq.hip", ["lsq_fwd_kernel"]),
     "lsq_bwd": ("pack_lsq.hip", ["lsq_bwd_kernel"]),
     "gemv_m1": ("gemv.hip", ["gemv_kernel<1,"]),
-    "gemv_m4": ("gemv.hip", ["gemv_kernel<4,"]),
-    "gemv_m16": ("gemv.hip", ["gemv_kernel<4,"]),
+    "gemv_m4": ("gemv.hip", []),   # same kernel as the M=16 passes: not separable by name
+    "gemv_m16": ("gemv.hip", []),
     "gemm": ("gemm.hip", ["gemm_kernel"]),
 }
 
@@ -303,11 +304,18 @@ def pmc_summary(args):
     copy_bytes = float(args.copy_bytes)
 
     def mean_of(rows, keys):
-        vals = [v for k, vs in rows.items() if any(s in k for s in keys) for v in vs]
-        return float(np.mean(vals)) if vals else None
+        """Sum over the launch's kernels of each kernel's mean per dispatch."""
+        tot, found = 0.0, False
+        for key in keys:
+            pat = re.compile(r"\b" + re.escape(key) + (r"" if key.endswith(",") else r"\b"))
+            vals = [v for k, vs in rows.items() if pat.search(k) for v in vs]
+            if vals:
+                tot += float(np.mean(vals))
+                found = True
+        return tot if found else None
 
-    cf = mean_of(fetch, ["elementwise_kernel", "copy"])
-    cw = mean_of(write, ["elementwise_kernel", "copy"])
+    cf = mean_of(fetch, ["neg_kernel_cuda"])
+    cw = mean_of(write, ["neg_kernel_cuda"])
     f_scale = copy_bytes / (cf * 1024) if cf else 1.0
     w_scale = copy_bytes / (cw * 1024) if cw else 1.0
     res = {"workload": args.workload, "copy_bytes": copy_bytes, "fetch_scale": f_scale,
@@ -328,14 +336,15 @@ def pmc_summary(args):
 
 
 def pmc_copy(args):
-    """A plain device-to-device copy of known size, to calibrate the byte counters."""
+    """A plain streaming kernel of known size (b = -a: reads and writes copy_bytes each), to
+    calibrate the byte counters."""
     import torch
 
     n = int(args.copy_bytes) // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda:0")
     b = torch.empty_like(a)
     for _ in range(3):
-        b.copy_(a)
+        torch.neg(a, out=b)
     torch.cuda.synchronize()
     print("copy done", n * 4)
 

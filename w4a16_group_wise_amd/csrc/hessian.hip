@@ -5,302 +5,368 @@
 // inputs): for the objective of the model card's "Quantization Configuration",
 // ||W X - Q(W) X||^2 is a quadratic form in the weight error with matrix X^T X.
 //
-// Only the tiles on and above the diagonal are computed (the algorithmic work is the unique
-// entries of the symmetric result); each value is written to both (i, j) and (j, i), so H is
-// bitwise symmetric.  X is row-major with the reduction (token) axis strided, while an MFMA
-// fragment wants 8 consecutive tokens of one feature per lane: each thread loads an 8x8
-// (tokens x features) bf16 block with 16-byte loads, transposes it in registers with byte
-// permutes, and writes 8 feature rows of 8 tokens into LDS, where fragments are single
-// 16-byte reads.  128x128 tiles, 4 wavefronts of 64x64 (2x2 v_mfma_f32_32x32x16_bf16
-// blocks), 64 tokens per double-buffered LDS stage.
+// Only the 256x256 tiles on and above the diagonal are computed (the algorithmic work is the
+// unique entries of the symmetric result); each value is written to both (i, j) and (j, i), so
+// H is bitwise symmetric.
+//
+// Work split (stream-K): the (tile, 32-token stage) iterations of the whole triangle, tile-major,
+// are cut into one contiguous range per workgroup, so every compute unit gets the same number of
+// matrix-core steps whatever the tile count.  A tile whose stages are spread over several
+// workgroups is finished by a second kernel that adds the partial tiles in the fixed order of
+// their token ranges: the result does not depend on scheduling.
+//
+// Per workgroup: 4 wavefronts of 128x128 (4x4 v_mfma_f32_32x32x16_bf16 blocks, accumulators in
+// AGPRs), 64 tokens per stage, two LDS stage buffers.  X is row-major [token][feature], the
+// layout in which it is copied straight from memory into LDS by buffer loads to LDS (16 bytes
+// per lane, no registers); the MFMA fragments, which want 8 consecutive tokens of one feature per
+// lane, are then read with the transposing LDS read ds_read_b64_tr_b16.  Buffer loads past the
+// end of X return zeros, which pads the token tail without any test in the loop.
 #include "common.hpp"
+
+#include <mutex>
+#include <type_traits>
 
 namespace w4q {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int HT = 128;      // tile edge in features
-constexpr int HK = 64;       // tokens per stage
-constexpr int HLD = HK + 8;  // bf16 per LDS feature row (144 bytes)
-constexpr int PD = 3;        // stages in flight between global memory and registers
+constexpr int BT = 256;                // tile edge in features
+constexpr int BK = 64;                 // tokens per stage
+constexpr int kTileElems = BT * BT;    // floats per partial tile
+constexpr int kMinChunk = 8;           // stages per workgroup before more workgroups are used
+constexpr int kMaxBlocks = 256;        // one workgroup per compute unit (256 AGPR accumulators)
+constexpr uint32_t kBufferFlags = 0x00020000u;  // raw 32-bit buffer resource (gfx9 family)
+constexpr int kStageBytes = 2 * BK * BT * 2;    // I and J panels, bf16: 64 KB
 
-__global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __restrict__ x, int64_t n_tok,
-                                                              int64_t d, float* __restrict__ h,
-                                                              int accumulate, int nt,
-                                                              int64_t tiles, int64_t per_xcd) {
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][2 * HT * HLD];
+// LDS stage layout: panel p (I = 0, J = 1), token t, 16-byte chunk position cp (32 per token row
+// of 256 features).  Chunk c (features 8c .. 8c + 7) of token t sits at position c ^ swz(t % 4).
+// A transposing read of 16 lanes covers 4 consecutive tokens x 2 chunks (and a pair of 16-lane
+// groups 4 tokens x 4 chunks); with these four masks the 16 lanes hit 8 distinct 16-byte bank
+// slots modulo 128 bytes, and the 32 lanes 16 distinct slots modulo 256 bytes.
+__device__ __forceinline__ int swz(int t) { return (0xCA60 >> (4 * (t & 3))) & 15; }  // 0, 6, 10, 12
 
-  // workgroups are dealt to the 8 XCDs round-robin; each XCD takes a contiguous run of the
-  // row-major upper-triangle tiles, so its resident tiles share I panels in its L2
-  const int64_t t = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (t >= tiles) return;
-  // upper-triangle tile (ti <= tj) of this block
-  int rem = static_cast<int>(t), ti = 0;
-  while (rem >= nt - ti) {
-    rem -= nt - ti;
-    ++ti;
+// upper-triangle tile t, numbered row-major over ti <= tj
+__device__ __forceinline__ void tile_coords(int t, int nt, int& ti, int& tj) {
+  int rem = t, i = 0;
+  while (rem >= nt - i) {
+    rem -= nt - i;
+    ++i;
   }
-  const int tj = ti + rem;
-  const bool diag = ti == tj;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
-
-  // load role: 8 tokens (token block tb) x 8 features (feature block fb of the 256 staged)
-  const int tb = lane & 7;
-  const int fb = (lane >> 3) + 8 * wid;         // 0..31: 0..15 -> I rows, 16..31 -> J rows
-  const bool jrow = fb >= 16;
-  const int64_t feat = jrow ? (int64_t)tj * HT + 8 * (fb - 16) : (int64_t)ti * HT + 8 * fb;
-  // (on a diagonal tile the J rows repeat the I rows; they are staged anyway, which keeps the
-  // loads free of branches, but never read)
-  // features past d read feature 0 instead (they only feed entries that are never stored);
-  // tokens past n_tok read the last token and are zeroed when staged into LDS.  Unconditional
-  // loads keep the prefetch ring free of branches and early waits.
-  const uint16_t* xf = x + (feat < d ? feat : 0);
-
-  struct Stage {
-    u32x4 v[8];
-  };
-  Stage st[PD];
-  auto gload = [&](int64_t k0, Stage& t) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      int64_t tok = k0 + 8 * tb + r;
-      tok = tok < n_tok ? tok : n_tok - 1;
-      t.v[r] = *reinterpret_cast<const u32x4*>(xf + tok * d);
-    }
-  };
-  auto lstore = [&](int buf, int64_t k0, const Stage& t) {
-    u32x4 rv[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) rv[r] = (k0 + 8 * tb + r < n_tok) ? t.v[r] : u32x4{0u, 0u, 0u, 0u};
-    // 8x8 transpose: out[f] holds tokens 0..7 of feature f as 4 bf16 pairs
-#pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      const int wsel = f >> 1;
-      const uint32_t sel = (f & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t o[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t lo = rv[2 * p][wsel], hi = rv[2 * p + 1][wsel];
-        o[p] = __builtin_amdgcn_perm(hi, lo, sel);
-      }
-      *reinterpret_cast<u32x4*>(&Xs[buf][(fb * 8 + f) * HLD + 8 * tb]) = u32x4{o[0], o[1], o[2], o[3]};
-    }
-  };
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  // on a diagonal tile the (wm = 1, wn = 0) quadrant is the mirror of (0, 1): skip it
-  const bool work = !(diag && wm == 1 && wn == 0);
-  const int jbase = diag ? 0 : HT;  // B fragments come from the I rows on diagonal tiles
-  const int fr = lane & 31;
-  const int fk = 8 * (lane >> 5);
-  const int64_t nstage = (n_tok + HK - 1) / HK;
-
-  auto mma_stage = [&](int cur) {
-    if (!work) return;
-#pragma unroll
-    for (int s = 0; s < HK / 16; ++s) {
-      bf16x8 a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(&Xs[cur][(wm * 64 + 32 * i + fr) * HLD + 16 * s + fk]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(&Xs[cur][(jbase + wn * 64 + 32 * j + fr) * HLD + 16 * s + fk]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  // register ring PD stages deep: loads of stage st + PD - 1 are issued while stage st is
-  // multiplied, and reach LDS one iteration before they are used
-#pragma unroll
-  for (int p = 0; p < PD - 1; ++p) gload(p * HK, st[p]);
-  lstore(0, 0, st[0]);
-  __syncthreads();
-  for (int64_t s0 = 0; s0 < nstage; s0 += PD) {
-#pragma unroll
-    for (int u = 0; u < PD; ++u) {
-      const int64_t sg = s0 + u;
-      if (sg >= nstage) break;  // uniform
-      gload((sg + PD - 1) * HK, st[(u + PD - 1) % PD]);
-      asm volatile("" ::: "memory");  // keep the prefetch issued here
-      mma_stage(static_cast<int>(sg & 1));
-      if (sg + 1 < nstage) lstore(static_cast<int>((sg + 1) & 1), (sg + 1) * HK, st[(u + 1) % PD]);
-      __syncthreads();
-    }
-  }
-  if (!work) return;
-
-  // 32x32 accumulator layout: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, column l%32
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = (int64_t)tj * HT + wn * 64 + 32 * j + fr;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = (int64_t)ti * HT + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= d || col >= d || row > col) continue;
-        float v = acc[i][j][r];
-        if (accumulate) v += h[row * d + col];
-        h[row * d + col] = v;
-        if (row != col) h[col * d + row] = v;
-      }
-    }
+  ti = i;
+  tj = i + rem;
 }
 
-// ---------------------------------------------------------------------------------------
-// 256x256 tiles for wide H (many tiles): 4 wavefronts of 128x128 (4x4 MFMA blocks, the
-// accumulators live in AGPRs), 32 tokens per LDS stage, a 2-stage register prefetch ring.
-// Per 16-token step a wavefront issues 16 MFMAs for 8 fragment reads (half the LDS traffic
-// per MFMA of the 64x64 layout).  LDS rows are 32 tokens (64 bytes) with the 16-byte chunk c
-// of row r stored at chunk c ^ ((r >> 1) & 3), so both the staging writes (4 lanes per row)
-// and the fragment reads (8 consecutive rows per chunk) are bank-conflict free.
-constexpr int BT = 256;    // tile edge in features
-constexpr int BK = 32;     // tokens per stage
-constexpr int BPD = 2;     // stages in flight between global memory and registers
-
-__device__ __forceinline__ int swz32(int r, int c) { return r * 32 + 8 * (c ^ ((r >> 1) & 3)); }
-
-__global__ __launch_bounds__(kThreads, 1) void hessian256_kernel(const uint16_t* __restrict__ x, int64_t n_tok,
-                                                                 int64_t d, float* __restrict__ h,
-                                                                 int accumulate, int nt,
-                                                                 int64_t tiles, int64_t per_xcd) {
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][2 * BT * BK];
-
-  const int64_t t = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (t >= tiles) return;
-  int rem = static_cast<int>(t), ti = 0;
-  while (rem >= nt - ti) {
-    rem -= nt - ti;
-    ++ti;
+// Store one 32x32 accumulator block whose top-left entry is (row0, col0), row0 <= col0 (both
+// wave-uniform), into both triangles.  Accumulator layout: lane l, register r -> row
+// 8(r/4) + 4(l/32) + r%4, column l%32; registers 4a..4a+3 are four consecutive rows, i.e. four
+// consecutive entries of one row of the mirrored block, written with one 16-byte store.
+__device__ __forceinline__ void store_block(float* __restrict__ h, int d, int row0, int col0, const f32x16& v,
+                                            int accumulate, int lane) {
+  const int c = lane & 31;
+  if (col0 + c >= d) return;
+  float* __restrict__ hd = h + (int64_t)row0 * d + col0;  // direct block, row-major
+  float* __restrict__ hm = h + (int64_t)col0 * d + row0;  // mirrored block
+  const bool straddle = row0 == col0;                     // the block holds diagonal entries
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int r = 8 * a + 4 * (lane >> 5);
+    if (row0 + r >= d) continue;  // d % 8 == 0: rows r .. r + 3 are all inside or all outside
+    float o[4] = {v[4 * a], v[4 * a + 1], v[4 * a + 2], v[4 * a + 3]};
+    if (!straddle) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (accumulate) o[q] += hd[(r + q) * d + c];
+        hd[(r + q) * d + c] = o[q];
+      }
+      *reinterpret_cast<f32x4*>(hm + c * d + r) = f32x4{o[0], o[1], o[2], o[3]};
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (r + q > c) continue;
+        float val = o[q];
+        if (accumulate) val += hd[(r + q) * d + c];
+        hd[(r + q) * d + c] = val;
+        if (r + q != c) hm[c * d + r + q] = val;
+      }
+    }
   }
-  const int tj = ti + rem;
-  const bool diag = ti == tj;
+}
+
+// partial-tile layout (per workgroup slot): wave w, block (i, j), register quad a, lane l ->
+// float4 at ((w * 16 + i * 4 + j) * 4 + a) * 256 + 4 l; each store instruction writes 1 KB.
+__device__ __forceinline__ int64_t part_off(int w, int i, int j, int a, int lane) {
+  return (int64_t)(((w * 16 + i * 4 + j) * 4 + a) * 256 + 4 * lane);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define W4Q_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define W4Q_LDS4(p) ((__attribute__((address_space(3))) v4i16*)(p))
+
+__global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __restrict__ x, int n_tok, int d,
+                                                              float* __restrict__ h, int accumulate, int nt,
+                                                              int ns, int total, int chunk, int nblk,
+                                                              int per_xcd, float* __restrict__ ws) {
+  // the two stage buffers are separate arrays, so the compiler can tell that reads of one need
+  // not wait for the loads in flight into the other
+  __shared__ __attribute__((aligned(16))) uint16_t L0[kStageBytes / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t L1[kStageBytes / 2];
+
+  // workgroups are dealt to the 8 XCDs round-robin; consecutive ranges (which share tiles and
+  // hence I panels and partial tiles) go to the same XCD
+  const int lb = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (lb >= nblk) return;
+  const int it_begin = lb * chunk;
+  const int it_end = it_begin + chunk < total ? it_begin + chunk : total;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid >> 1, wn = wid & 1;
 
-  // load role: 8 tokens (token block tb of 4) x 8 features (feature block fb of 64 across the
-  // 512 staged rows: 0..31 -> I rows, 32..63 -> J rows)
-  const int tb = tid & 3;
-  const int fb = tid >> 2;
-  const bool jrow = fb >= 32;
-  const int64_t feat = jrow ? (int64_t)tj * BT + 8 * (fb - 32) : (int64_t)ti * BT + 8 * fb;
-  // features past d read feature 0 (they only feed entries that are never stored); tokens past
-  // n_tok read the last token and are zeroed when staged
-  const uint16_t* xf = x + (feat < d ? feat : 0);
-
-  struct Stage {
-    u32x4 v[8];
-  };
-  Stage st[BPD];
-  auto gload = [&](int64_t k0, Stage& u) {
+  // load role: load instruction q (0..15) of wave w fills the 1 KB of LDS at slot
+  // (16 w + q) * 64: panel w / 2, tokens 32 (w % 2) + 2 q + lane / 32, chunk position lane % 32
+  const int ld_panel = wid >> 1;
+  int ld_tok[16], ld_chunk[16];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      int64_t tok = k0 + 8 * tb + r;
-      tok = tok < n_tok ? tok : n_tok - 1;
-      u.v[r] = *reinterpret_cast<const u32x4*>(xf + tok * d);
-    }
-  };
-  auto lstore = [&](int buf, int64_t k0, const Stage& u) {
-    u32x4 rv[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) rv[r] = (k0 + 8 * tb + r < n_tok) ? u.v[r] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      const int wsel = f >> 1;
-      const uint32_t sel = (f & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t o[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) o[p] = __builtin_amdgcn_perm(rv[2 * p + 1][wsel], rv[2 * p][wsel], sel);
-      *reinterpret_cast<u32x4*>(&Xs[buf][swz32(fb * 8 + f, tb)]) = u32x4{o[0], o[1], o[2], o[3]};
-    }
-  };
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  const bool work = !(diag && wm == 1 && wn == 0);  // mirror quadrant of a diagonal tile
-  const int jbase = diag ? 0 : BT;
-  const int fr = lane & 31;
-  const int fh = lane >> 5;
-  const int64_t nstage = (n_tok + BK - 1) / BK;
-
-  auto mma_stage = [&](int cur) {
-    if (!work) return;
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(&Xs[cur][swz32(wm * 128 + 32 * i + fr, 2 * s + fh)]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(&Xs[cur][swz32(jbase + wn * 128 + 32 * j + fr, 2 * s + fh)]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-#pragma unroll
-  for (int p = 0; p < BPD - 1; ++p) gload(p * BK, st[p]);
-  lstore(0, 0, st[0]);
-  __syncthreads();
-  for (int64_t s0 = 0; s0 < nstage; s0 += BPD) {
-#pragma unroll
-    for (int u = 0; u < BPD; ++u) {
-      const int64_t sg = s0 + u;
-      if (sg >= nstage) break;  // uniform
-      gload((sg + BPD - 1) * BK, st[(u + BPD - 1) % BPD]);
-      asm volatile("" ::: "memory");  // keep the prefetch issued here
-      mma_stage(static_cast<int>(sg & 1));
-      if (sg + 1 < nstage) lstore(static_cast<int>((sg + 1) & 1), (sg + 1) * BK, st[(u + 1) % BPD]);
-      __syncthreads();
-    }
+  for (int q = 0; q < 16; ++q) {
+    ld_tok[q] = 32 * (wid & 1) + 2 * q + (lane >> 5);
+    ld_chunk[q] = (lane & 31) ^ swz(ld_tok[q]);
   }
-  if (!work) return;
 
-  // 32x32 accumulator layout: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, column l%32
+  // read role (transposing reads): 16-lane group g = lane / 16, lane j = lane % 16 in it points
+  // at token 8 (g / 2) + j / 4 (+ 4 for the second read) and at features 16 (g % 2) + 4 (j % 4)
+  // of a 32-feature block; it receives feature 16 (g % 2) + j of four consecutive tokens
+  const int rg = lane >> 4, rj = lane & 15;
+  const int rtok = 8 * (rg >> 1) + (rj >> 2);
+  const int rsw = swz(rj >> 2);
+  const int rlo = 2 * (rg & 1) + ((rj >> 1) & 1);  // chunk within a 32-feature block
+  const int rhalf = 8 * (rj & 1);                  // byte within the chunk
+  // byte offset in a stage of the read for 32-feature block `blk` (0..7 of a panel)
+  auto rd_off = [&](int panel, int blk) { return panel * (kStageBytes / 2) + rtok * 512 + 16 * ((4 * blk + rlo) ^ rsw) + rhalf; };
+
+  const f32x16 zero16 = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f,
+                         0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+
+  int it = it_begin;
+  while (it < it_end) {
+    const int t = it / ns;
+    const int s0 = it - t * ns;
+    const int s1 = s0 + (it_end - it) < ns ? s0 + (it_end - it) : ns;
+    int ti, tj;
+    tile_coords(t, nt, ti, tj);
+    const bool diag = ti == tj;
+
+    // byte offsets of this lane's 16 loads within a stage; features past d read into the next
+    // token or past the end (zeros): they only feed entries that are never stored
+    const int fbase = (ld_panel ? tj : ti) * BT;
+    int voff[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int q = 0; q < 16; ++q) voff[q] = (ld_tok[q] * d + fbase + 8 * ld_chunk[q]) * 2;
+    // on a diagonal tile the J panel is the I panel: its loads are switched off
+    const bool ld_on = !(diag && ld_panel == 1);
+
+    auto issue = [&](int s, uint16_t* L) {
+      const int64_t tok0 = (int64_t)s * BK;
+      // bytes from the stage start to the end of X; 0 (every load returns zeros without touching
+      // memory) for stages outside this range.  All wave-uniform (readfirstlane keeps the buffer
+      // resource in SGPRs; it returns int, so each half is taken back as unsigned).
+      const int bytes =
+          __builtin_amdgcn_readfirstlane((s < s1 && ld_on) ? (n_tok - static_cast<int>(tok0)) * d * 2 : 0);
+      const uint64_t base = reinterpret_cast<uint64_t>(x + tok0 * d);
+      const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(base)));
+      const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(base >> 32)));
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), 0, bytes, kBufferFlags);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = (int64_t)tj * BT + wn * 128 + 32 * j + fr;
+      for (int q = 0; q < 16; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, W4Q_LDS(L + (16 * wid + q) * 512), 16, voff[q], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);  // issue the loads here, ahead of the stage's products
+    };
+
+    f32x16 acc[4][4];
+    const int bpanel = diag ? 0 : 1;  // B fragments come from the I panel on diagonal tiles
+    // one stage: 4 steps of 16 tokens; `first` starts the sums from a zero accumulator.  (On a
+    // diagonal tile the (wm = 1, wn = 0) quadrant, the mirror of (0, 1), is computed as well,
+    // which keeps the loop free of branches around the accumulators, but never stored.)
+    auto compute = [&](const uint16_t* L, auto first) {
+      const char* Lb = reinterpret_cast<const char*>(L);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = (int64_t)ti * BT + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * fh + (r & 3);
-        if (row >= d || col >= d || row > col) continue;
-        float v = acc[i][j][r];
-        if (accumulate) v += h[row * d + col];
-        h[row * d + col] = v;
-        if (row != col) h[col * d + row] = v;
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        bf16x8 a[4], b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const char* p = Lb + rd_off(0, 4 * wm + i) + kk * 16 * 512;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(W4Q_LDS4(p));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(W4Q_LDS4(p + 4 * 512));
+          a[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const char* p = Lb + rd_off(bpanel, 4 * wn + j) + kk * 16 * 512;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(W4Q_LDS4(p));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(W4Q_LDS4(p + 4 * 512));
+          b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if constexpr (decltype(first)::value) {
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], kk == 0 ? zero16 : acc[i][j], 0, 0, 0);
+            } else {
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            }
+          }
+      }
+    };
+
+    // stage s lives in L0 for s - s0 even and in L1 for s - s0 odd.  Each barrier (which waits
+    // for this wave's loads to LDS) makes the next stage visible to all wavefronts and frees the
+    // other buffer; the loads of stage s + 1 then run under the products of stage s.
+    issue(s0, L0);
+    __syncthreads();
+    issue(s0 + 1, L1);
+    compute(L0, std::true_type{});
+    for (int s = s0 + 1; s < s1; s += 2) {
+      __syncthreads();
+      issue(s + 1, L0);
+      compute(L1, std::false_type{});
+      if (s + 1 >= s1) break;  // uniform
+      __syncthreads();
+      issue(s + 2, L1);
+      compute(L0, std::false_type{});
+    }
+    __syncthreads();  // both buffers free for the next range
+
+    const bool work = !(diag && wm == 1 && wn == 0);
+    if (work) {
+      if (s0 == 0 && s1 == ns) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row0 = ti * BT + wm * 128 + 32 * i;
+            const int col0 = tj * BT + wn * 128 + 32 * j;
+            if (row0 <= col0 && row0 < d) store_block(h, d, row0, col0, acc[i][j], accumulate, lane);
+            asm volatile("" ::: "memory");  // one block at a time (bounds the live registers)
+          }
+      } else {
+        // slot 0: the first tile of this range, slot 1: its last
+        float* slot = ws + (int64_t)(2 * lb + (it == it_begin ? 0 : 1)) * kTileElems;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              *reinterpret_cast<f32x4*>(slot + part_off(wid, i, j, a, lane)) =
+                  f32x4{acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2], acc[i][j][4 * a + 3]};
+              asm volatile("" ::: "memory");
+            }
       }
     }
+    it += s1 - s0;
+  }
+}
+
+// Tiles whose stages were spread over several workgroups: sum the partial tiles in the order of
+// their token ranges (workgroup index), then store as the main kernel does.  One workgroup per
+// (tile, 32x32 block row i, block column j) of every wavefront's quadrant.
+__global__ __launch_bounds__(kThreads) void hessian_fixup_kernel(float* __restrict__ h, int d, int accumulate, int nt,
+                                                                 int ns, int chunk, const float* __restrict__ ws) {
+  const int t = blockIdx.x >> 4;
+  const int i = (blockIdx.x >> 2) & 3, j = blockIdx.x & 3;
+  const int first = static_cast<int>((int64_t)t * ns / chunk);
+  const int last = static_cast<int>(((int64_t)t * ns + ns - 1) / chunk);
+  if (first == last) return;  // written whole by the main kernel
+  int ti, tj;
+  tile_coords(t, nt, ti, tj);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid >> 1, wn = wid & 1;
+  if (ti == tj && wm == 1 && wn == 0) return;
+  const int row0 = ti * BT + wm * 128 + 32 * i;
+  const int col0 = tj * BT + wn * 128 + 32 * j;
+  if (row0 > col0 || row0 >= d || col0 >= d) return;
+  f32x16 v;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = 0.0f;
+  for (int b = first; b <= last; ++b) {
+    // tile t is the first tile of workgroup b's range unless b started before it
+    const int slot = 2 * b + ((int64_t)b * chunk >= (int64_t)t * ns ? 0 : 1);
+    const float* p = ws + (int64_t)slot * kTileElems;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(p + part_off(wid, i, j, a, lane));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * a + e] += q[e];
+    }
+  }
+  store_block(h, d, row0, col0, v, accumulate, lane);
+}
+
+// Library-owned stream-ordered pool per device for the partial tiles (kept, not released to
+// the system between calls).
+constexpr int kMaxDevices = 64;
+std::mutex g_pool_mu;
+hipMemPool_t g_pool[kMaxDevices];
+
+hipMemPool_t device_pool(int dev) {
+  std::lock_guard<std::mutex> lk(g_pool_mu);
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (!g_pool[dev]) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t p = nullptr;
+    if (hipMemPoolCreate(&p, &props) != hipSuccess) return nullptr;
+    uint64_t keep = UINT64_MAX;
+    hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
+    g_pool[dev] = p;
+  }
+  return g_pool[dev];
+}
+
+// One pass over at most 2^31 - 1 bytes of X (32-bit buffer offsets).
+int launch_pass(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accumulate, hipStream_t s) {
+  const int64_t nt = (d + BT - 1) / BT;
+  const int64_t tiles = nt * (nt + 1) / 2;
+  const int64_t ns = (n_tok + BK - 1) / BK;
+  const int64_t total = tiles * ns;
+  if (total > 0x3FFFFFFF) return W4Q_EUNSUPPORTED;
+  int64_t nblk = (total + kMinChunk - 1) / kMinChunk;
+  if (nblk > kMaxBlocks) nblk = kMaxBlocks;
+  const int64_t chunk = (total + nblk - 1) / nblk;
+  nblk = (total + chunk - 1) / chunk;
+  const bool split = nblk > 1 && chunk % ns != 0;
+  const int64_t per_xcd = (nblk + 7) / 8;
+
+  float* ws = nullptr;
+  if (split) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return W4Q_EHIP;
+    hipMemPool_t pool = device_pool(dev);
+    if (!pool) return W4Q_EHIP;
+    const size_t bytes = (size_t)nblk * 2 * kTileElems * sizeof(float);
+    if (hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), bytes, pool, s) != hipSuccess) return W4Q_EHIP;
+  }
+  hipLaunchKernelGGL(hessian_kernel, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(kThreads), 0, s, x,
+                     static_cast<int>(n_tok), static_cast<int>(d), h, accumulate, static_cast<int>(nt),
+                     static_cast<int>(ns), static_cast<int>(total), static_cast<int>(chunk),
+                     static_cast<int>(nblk), static_cast<int>(per_xcd), ws);
+  int rc = w4q_launch_status();
+  if (split) {
+    if (rc == W4Q_OK) {
+      hipLaunchKernelGGL(hessian_fixup_kernel, dim3(static_cast<unsigned>(16 * tiles)), dim3(kThreads), 0, s, h,
+                         static_cast<int>(d), accumulate, static_cast<int>(nt), static_cast<int>(ns),
+                         static_cast<int>(chunk), ws);
+      rc = w4q_launch_status();
+    }
+    if (hipFreeAsync(ws, s) != hipSuccess && rc == W4Q_OK) rc = W4Q_EHIP;
+  }
+  return rc;
 }
 
 }  // namespace
@@ -310,21 +376,12 @@ using namespace w4q;
 
 int w4q_launch_hessian(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accumulate,
                        hipStream_t s) {
-  // 256-wide tiles when they still give at least one tile per compute unit
-  const int64_t nt2 = (d + BT - 1) / BT;
-  const int64_t tiles2 = nt2 * (nt2 + 1) / 2;
-  if (tiles2 >= 256) {
-    const int64_t per2 = (tiles2 + 7) / 8;
-    if (8 * per2 > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
-    hipLaunchKernelGGL(hessian256_kernel, dim3(static_cast<unsigned>(8 * per2)), dim3(kThreads), 0, s, x,
-                       n_tok, d, h, accumulate, static_cast<int>(nt2), tiles2, per2);
-    return w4q_launch_status();
+  // X is taken in passes of whole tokens that fit 32-bit buffer offsets; later passes add on
+  const int64_t max_tok = 0x7FFFFFFF / (2 * d);
+  for (int64_t t0 = 0; t0 < n_tok; t0 += max_tok) {
+    const int64_t n = n_tok - t0 < max_tok ? n_tok - t0 : max_tok;
+    const int rc = launch_pass(x + t0 * d, n, d, h, t0 == 0 ? accumulate : 1, s);
+    if (rc != W4Q_OK) return rc;
   }
-  const int64_t nt = (d + HT - 1) / HT;
-  const int64_t tiles = nt * (nt + 1) / 2;
-  const int64_t per_xcd = (tiles + 7) / 8;
-  if (8 * per_xcd > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
-  hipLaunchKernelGGL(hessian_kernel, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(kThreads), 0, s, x,
-                     n_tok, d, h, accumulate, static_cast<int>(nt), tiles, per_xcd);
-  return w4q_launch_status();
+  return W4Q_OK;
 }

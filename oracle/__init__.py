@@ -70,6 +70,9 @@ def _L():
         lib.orc_lsq_fwd.argtypes = [P, P, I, I, P]
         lib.orc_lsq_bwd.argtypes = [P, P, P, I, I, ctypes.c_double, P, P, P]
         lib.orc_gemm_cols.argtypes = [P, I, P, P, I, P, I, P, P]
+        lib.orc_gemm_cols_mode.argtypes = [P, I, P, P, I, P, I, ctypes.c_int, P, P]
+        lib.orc_round_bf16.restype = ctypes.c_double
+        lib.orc_round_bf16.argtypes = [ctypes.c_double]
         _lib = lib
     return _lib
 
@@ -105,6 +108,10 @@ def code(w: float, d: float) -> int:
 
 def candidate(amax: float, alpha: float) -> float:
     return float(np.float32(_L().orc_candidate(float(np.float32(amax)), float(np.float32(alpha)))))
+
+
+def round_bf16(v: float) -> float:
+    return float(_L().orc_round_bf16(float(v)))
 
 
 def unpack(packed_row: np.ndarray, k: int) -> int:
@@ -195,8 +202,9 @@ def lsq_bwd(w: np.ndarray, scale: np.ndarray, g: np.ndarray, gs: float):
 
 
 def gemm_cols(x_bf16: np.ndarray, packed: np.ndarray, s16: np.ndarray,
-              cols: Optional[np.ndarray] = None):
-    """-> (y f64 [m][len(cols)], yabs f64 [m][len(cols)]) with yabs = sum |x * w_hat|."""
+              cols: Optional[np.ndarray] = None, dequant_bf16: bool = False):
+    """-> (y f64 [m][len(cols)], yabs f64 [m][len(cols)]) with yabs = sum |x * w_hat|.
+    w_hat = s16 * q exactly, or bf16_RNE(s16 * q) with dequant_bf16."""
     x = _c(x_bf16, np.uint16)
     packed = _c(packed, np.uint8)
     s16 = _c(s16, np.uint16)
@@ -206,5 +214,6 @@ def gemm_cols(x_bf16: np.ndarray, packed: np.ndarray, s16: np.ndarray,
     cols = _c(cols, np.int64)
     y = np.empty((m, cols.shape[0]), np.float64)
     ya = np.empty_like(y)
-    _L().orc_gemm_cols(_p(x), m, _p(packed), _p(s16), d_in, _p(cols), cols.shape[0], _p(y), _p(ya))
+    _L().orc_gemm_cols_mode(_p(x), m, _p(packed), _p(s16), d_in, _p(cols), cols.shape[0],
+                            1 if dequant_bf16 else 0, _p(y), _p(ya))
     return y, ya

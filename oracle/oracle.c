@@ -296,6 +296,48 @@ void orc_lsq_bwd(const float* w, const float* scale, const float* gup, int64_t d
  * y[m][c] = sum_k x[m][k] * s16[n][k/32] * q[n][k] for n = cols[c], in fp64; yabs receives
  * sum_k |x[m][k] * w_hat[n][k]| (the scale of the rounding-error bound).
  */
+/* The nearest bfloat16 value (8 significant bits) to a finite v, ties to the even
+ * significand.  v is a product s16 * q here: exact in fp64, far inside the bf16 range. */
+double orc_round_bf16(double v) {
+  if (v == 0.0) return v;
+  double a = fabs(v);
+  int e;
+  frexp(a, &e);
+  double quantum = ldexp(1.0, e - 1 - 7); /* a in [2^(e-1), 2^e): 7 fraction bits */
+  double r = a / quantum;                 /* exact */
+  double n = floor(r);
+  double frac = r - n;
+  if (frac > 0.5 || (frac == 0.5 && fmod(n, 2.0) != 0.0)) n += 1.0;
+  double out = n * quantum;
+  return v < 0 ? -out : out;
+}
+
+/* y = x W_hat^T on the chosen output columns.  Two readings of the dequantized weight:
+ *   dq = 0: w_hat = s16 * q exactly ([card] W4A16 deployment with the [blog] group grid);
+ *   dq = 1: w_hat = bf16_RNE(s16 * q), the weight as a bf16 operand of the matrix product
+ *           (dequantization to the 16-bit activation format before the product). */
+void orc_gemm_cols_mode(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
+                        int64_t d_in, const int64_t* cols, int64_t ncols, int dq, double* y, double* yabs) {
+  int64_t G = d_in / GROUP;
+#pragma omp parallel for schedule(static)
+  for (int64_t c = 0; c < ncols; ++c) {
+    int64_t n = cols[c];
+    const uint8_t* prow = packed + n * (d_in / 2);
+    for (int64_t mi = 0; mi < m; ++mi) {
+      double s = 0.0, sa = 0.0;
+      for (int64_t k = 0; k < d_in; ++k) {
+        double wh = orc_f16_to_f64(s16[n * G + k / GROUP]) * (double)orc_unpack(prow, k);
+        if (dq) wh = orc_round_bf16(wh);
+        double p = orc_bf16_to_f64(x[mi * d_in + k]) * wh;
+        s += p;
+        sa += fabs(p);
+      }
+      y[mi * ncols + c] = s;
+      if (yabs) yabs[mi * ncols + c] = sa;
+    }
+  }
+}
+
 void orc_gemm_cols(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
                    int64_t d_in, const int64_t* cols, int64_t ncols, double* y, double* yabs) {
   int64_t G = d_in / GROUP;

@@ -370,3 +370,69 @@ def test_gemm_matches_numpy_matmul():
     cols = np.array([39, 0, 7])
     y2, _ = oracle.gemm_cols(x, packed, s16, cols)
     assert np.array_equal(y2, y[:, cols])
+
+
+# ------------------------------------------------- GEMM with weights dequantized to bf16
+def _bf16_nearest_bruteforce(v):
+    """Nearest bf16 value by enumeration of the bf16 patterns around v (ties: even pattern)."""
+    from fractions import Fraction
+    f = np.float32(v)
+    base = int(np.array([f], np.float32).view(np.uint32)[0] >> 16)
+    best = None
+    for b in range(max(base - 2, 0), base + 3):
+        cand = np.array([b << 16], np.uint32).view(np.float32)[0]
+        dist = abs(Fraction(float(cand)) - Fraction(float(v)))
+        key = (dist, b & 1)
+        if best is None or key < best[0]:
+            best = (key, float(cand))
+    return best[1]
+
+
+def test_round_bf16_worked_ties():
+    # s = 1 + 2^-8 (fp16 0x3C04): s*1 and s*2 sit exactly halfway between bf16 neighbours
+    s = oracle.f16_to_f64(0x3C04)
+    assert s == 1.00390625
+    assert oracle.round_bf16(s * 1) == 1.0            # tie -> even significand
+    assert oracle.round_bf16(s * 2) == 2.0            # tie -> even
+    assert oracle.round_bf16(s * 3) == 3.015625       # 0.75 ulp above 3 -> up
+    assert oracle.round_bf16(-s * 3) == -3.015625
+    assert oracle.round_bf16(s * -8) == -8.0          # 1/2 ulp at 8 (2^-4): tie -> even
+
+
+def test_round_bf16_bruteforce():
+    rng = np.random.default_rng(11)
+    s16 = rng.integers(0x0001, 0x7BFF, 300)            # positive finite fp16 patterns
+    for sb in s16:
+        s = oracle.f16_to_f64(int(sb))
+        for q in (-8, -7, -3, 1, 5, 7):
+            v = s * q
+            assert oracle.round_bf16(v) == _bf16_nearest_bruteforce(v)
+
+
+def test_gemm_dequant_bf16_matches_torch_rounding():
+    torch = pytest.importorskip("torch")
+    w = synth.weights(9, 0, 6, 24, 128, 0.01)
+    sc = np.abs(w.reshape(24, 4, 32)).max(axis=2) / np.float32(7)
+    packed, s16 = oracle.pack(w, sc)
+    x = synth.calib_x(9, 0, 6, 3, 128, 1.0)
+    y, ya = oracle.gemm_cols(x, packed, s16, dequant_bf16=True)
+    wh = _numpy_dequant(packed, s16).astype(np.float32)         # s * q, exact in fp32
+    wb = torch.from_numpy(wh).to(torch.bfloat16).to(torch.float64).numpy()  # library RNE
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+    assert np.allclose(y, xf @ wb.T, rtol=1e-12, atol=1e-12)
+    assert np.allclose(ya, np.abs(xf) @ np.abs(wb).T, rtol=1e-12)
+    # and it differs from the exact reading somewhere (the rounding is really applied)
+    ye, _ = oracle.gemm_cols(x, packed, s16)
+    assert not np.array_equal(y, ye)
+
+
+def test_gemm_dequant_bf16_power_of_two_scales_is_exact():
+    # scales that are powers of two make s * q exact in bf16: both readings agree bit for bit
+    codes = np.random.default_rng(3).integers(-8, 8, (16, 64)).astype(np.float32)
+    sc = np.float32(2.0) ** np.random.default_rng(4).integers(-6, 3, (16, 2)).astype(np.float32)
+    w = codes * np.repeat(sc, 32, axis=1)
+    packed, s16 = oracle.pack(w, sc)
+    x = synth.calib_x(9, 0, 7, 4, 64, 1.0)
+    y1, _ = oracle.gemm_cols(x, packed, s16, dequant_bf16=True)
+    y0, _ = oracle.gemm_cols(x, packed, s16)
+    assert np.array_equal(y0, y1)

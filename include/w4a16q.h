@@ -13,10 +13,13 @@
  *           and role table survive intact.
  *
  * Common conventions for every entry point:
- *   - Tensors are caller-owned DEVICE memory, row-major, contiguous.  The library never
- *     allocates, frees or synchronises; every call only enqueues kernels on `stream`
- *     (0 = the legacy default stream) and returns.  Results are valid once the caller has
- *     synchronised that stream.
+ *   - Tensors are caller-owned DEVICE memory, row-major, contiguous.  Every call only
+ *     enqueues work on `stream` (0 = the legacy default stream) and returns; the library never
+ *     synchronises.  Results are valid once the caller has synchronised that stream.  The
+ *     library allocates nothing except, for quant_hessian and for w4a16_gemm / w4a16_gemm_dq
+ *     with m > 16, partial-tile scratch taken from and returned to a library-owned
+ *     stream-ordered memory pool on the same stream (at most 128 MB per call; the pool keeps
+ *     its memory for later calls).
  *   - Weights W are fp32 [d_out][d_in]; a group is 32 consecutive weights of one row along
  *     d_in, so d_in must be a positive multiple of 32 (W4Q_GROUP).  G = d_in / 32 groups/row.
  *   - Codes are integers in [-8, 7] (W4Q_QMIN..W4Q_QMAX).  code(w, D) is the code c that
@@ -157,11 +160,26 @@ int lsq_bwd(const float* w, const float* scale, const float* grad_w_hat, int64_t
  *   packed    uint8 [d_out][d_in/2] as written by quant_pack, 16-B aligned.
  *   scale_f16 fp16 bits [d_out][G].
  *   y         [m][d_out], fp32 (y_dtype 0) or bf16 RNE of the fp32 result (y_dtype 1).
- *   m >= 1.  Small m streams the packed weights (bandwidth bound); large m runs on the
- *   bf16 matrix cores with the codes expanded to bf16 in registers.
+ *   m >= 1.  Small m (<= 16) streams the packed weights (bandwidth bound); larger m runs on
+ *   the bf16 matrix cores: each weight s*q (at most 11 x 4 significant bits, exact in fp32) is
+ *   split exactly into two bf16 values hi + lo in registers and both are multiplied, so the
+ *   weights enter the products unrounded.
  */
 int w4a16_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
                int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t stream);
+
+/*
+ * w4a16_gemm_dq -- the same product with the weights dequantized to the 16-bit activation
+ * format before the product ([card] W4A16: INT4 weights, 16-bit activations; the matrix cores
+ * take bf16 operands):
+ *   w_hat[n][k] = bf16_RNE(fp32(scale_f16[n][k/32]) * q[n][k])
+ *   y[m][n]     = sum_k x[m][k] * w_hat[n][k]          (fp32 accumulation)
+ * Arguments, layouts and y_dtype as for w4a16_gemm.  One bf16 matrix-core product per weight
+ * (half the products of w4a16_gemm for m > 16); any m >= 1 runs on the matrix cores.
+ * d_in must be a multiple of 256 (else W4Q_EUNSUPPORTED).
+ */
+int w4a16_gemm_dq(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
+                  int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t stream);
 
 #ifdef __cplusplus
 }

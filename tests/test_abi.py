@@ -23,7 +23,8 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"w4q_status_string", "w4q_version", "quant_hessian",
-                          "quant_scale_search", "quant_pack", "lsq_fwd", "lsq_bwd", "w4a16_gemm"}
+                          "quant_scale_search", "quant_pack", "lsq_fwd", "lsq_bwd", "w4a16_gemm",
+                          "w4a16_gemm_dq"}
     l = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(l, n), n
@@ -86,6 +87,10 @@ def test_pack_lsq_gemm_argument_errors():
     assert L.w4a16_gemm(A, 1, A, A, 4, 65, A, 0, None) == w4q.W4Q_ESHAPE
     assert L.w4a16_gemm(A + 2, 1, A, A, 4, 64, A, 0, None) == w4q.W4Q_EALIGN
     assert L.w4a16_gemm(A, 1, A, A, 4, 64, A + 1, 1, None) == w4q.W4Q_EALIGN
+    assert L.w4a16_gemm_dq(A, 1, A, A, 4, 256, A, 2, None) == w4q.W4Q_EINVAL
+    assert L.w4a16_gemm_dq(A, 0, A, A, 4, 256, A, 0, None) == w4q.W4Q_ESHAPE
+    assert L.w4a16_gemm_dq(A + 2, 1, A, A, 4, 256, A, 0, None) == w4q.W4Q_EALIGN
+    assert L.w4a16_gemm_dq(A, 1, A, A, 4, 64, A, 0, None) == w4q.W4Q_EUNSUPPORTED
 
 
 def test_python_front_end_rejects_host_tensors():

@@ -273,3 +273,46 @@ def test_gemm_zero_codes_exact(dev):
                            torch.from_numpy(packed).to(dev),
                            torch.from_numpy(s16.view(np.float16)).to(dev))
         assert torch.count_nonzero(y).item() == 0
+
+
+# ------------------------------------------------ matrix-core product, both weight readings
+# shapes on the 256x256-tile kernel (d_in % 256 == 0): ragged rows / columns, K split over
+# workgroups (partial tiles) or not, and several tiles per workgroup
+@pytest.mark.parametrize("m,d_out,d_in", [(17, 40, 256), (300, 520, 512), (64, 256, 4096),
+                                          (513, 1000, 768), (256, 2304, 1024)])
+@pytest.mark.parametrize("dq", [False, True])
+def test_gemm_mma_shapes(dev, m, d_out, d_in, dq):
+    w = synth.weights(34, 0, d_out, d_out, d_in, 0.01)
+    scale = (np.abs(w.reshape(d_out, -1, 32)).max(axis=2) / 7).astype(np.float32)
+    scale[1 % d_out, 0] = 0.0                                  # an all-zero code group
+    packed, s16 = oracle.pack(w, scale)
+    x = synth.calib_x(34, 0, m, m, d_in, 1.0)
+    say("gemm mma", m, d_out, d_in, "dq" if dq else "exact")
+    fn = w4q.w4a16_gemm_dq if dq else w4q.w4a16_gemm
+    y = fn(dev_bf16(x, dev), torch.from_numpy(packed).to(dev), torch.from_numpy(s16.view(np.float16)).to(dev))
+    yg = y.cpu().numpy()
+    cols = np.arange(d_out) if d_out * m <= 200000 else np.arange(0, d_out, 5)
+    yr, ya = oracle.gemm_cols(x, packed, s16, cols, dequant_bf16=dq)
+    check_gemm(yg[:, cols], yr, ya)
+
+
+@pytest.mark.parametrize("cfg,m", [(1, 1), (2, 16), (2, 2048)])
+@pytest.mark.parametrize("bf16_out", [False, True])
+def test_gemm_dq_config(dev, cfg, m, bf16_out):
+    c, lin, packed, s16 = _packed_layer(cfg)
+    x = c.x(0, lin.inp)[:m]
+    say("gemm dq cfg", cfg, "m", m, "bf16", bf16_out)
+    y = w4q.w4a16_gemm_dq(dev_bf16(x, dev), torch.from_numpy(packed).to(dev),
+                          torch.from_numpy(s16.view(np.float16)).to(dev),
+                          out_dtype=torch.bfloat16 if bf16_out else torch.float32)
+    yg = bf16_bits_to_np(host_bf16_bits(y)) if bf16_out else y.cpu().numpy()
+    cols = np.arange(packed.shape[0]) if m <= 16 else np.arange(0, packed.shape[0], 7)
+    yr, ya = oracle.gemm_cols(x, packed, s16, cols, dequant_bf16=True)
+    check_gemm(yg[:, cols], yr, ya, bf16_out)
+    if not bf16_out:
+        # the kernel follows the bf16 reading, not the exact one: its distance to the bf16-weight
+        # reference (fp32 accumulation only) is far below its distance to the exact weights
+        ye, _ = oracle.gemm_cols(x, packed, s16, cols)
+        e_dq = np.max(np.abs(yg[:, cols] - yr) / ya)
+        e_ex = np.max(np.abs(yg[:, cols] - ye) / ya)
+        assert e_dq * 4 < e_ex, (e_dq, e_ex)

@@ -29,6 +29,7 @@ SIGNATURES = {
     "lsq_fwd": (_INT, [_P, _P, _I64, _I64, _P, _P]),
     "lsq_bwd": (_INT, [_P, _P, _P, _I64, _I64, _F, _P, _P, _P, _P]),
     "w4a16_gemm": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _INT, _P]),
+    "w4a16_gemm_dq": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _INT, _P]),
 }
 
 

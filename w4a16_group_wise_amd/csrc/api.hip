@@ -89,8 +89,8 @@ int lsq_bwd(const float* w, const float* scale, const float* grad_w_hat, int64_t
                             w_hat, stream);
 }
 
-int w4a16_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
-               int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t stream) {
+static int gemm_args(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
+                     int64_t d_out, int64_t d_in, void* y, int y_dtype) {
   if (!x || !packed || !scale_f16 || !y || (y_dtype != 0 && y_dtype != 1)) return W4Q_EINVAL;
   if (m <= 0) return W4Q_ESHAPE;
   int rc = check_wshape(d_out, d_in);
@@ -99,8 +99,23 @@ int w4a16_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16
   if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scale_f16, 2) ||
       !aligned(y, y_dtype == 0 ? 4 : 2))
     return W4Q_EALIGN;
+  return W4Q_OK;
+}
+
+int w4a16_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
+               int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t stream) {
+  const int rc = gemm_args(x, m, packed, scale_f16, d_out, d_in, y, y_dtype);
+  if (rc != W4Q_OK) return rc;
   if (m <= 16) return w4q_launch_gemv(x, m, packed, scale_f16, d_out, d_in, y, y_dtype, stream);
-  return w4q_launch_gemm(x, m, packed, scale_f16, d_out, d_in, y, y_dtype, stream);
+  return w4q_launch_gemm(x, m, packed, scale_f16, d_out, d_in, y, y_dtype, 0, stream);
+}
+
+int w4a16_gemm_dq(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
+                  int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t stream) {
+  const int rc = gemm_args(x, m, packed, scale_f16, d_out, d_in, y, y_dtype);
+  if (rc != W4Q_OK) return rc;
+  if (d_in % 256 != 0) return W4Q_EUNSUPPORTED;
+  return w4q_launch_gemm(x, m, packed, scale_f16, d_out, d_in, y, y_dtype, 1, stream);
 }
 
 }  // extern "C"

@@ -16,6 +16,7 @@ namespace w4q {
 
 constexpr int kGroup = W4Q_GROUP;
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -77,9 +78,84 @@ __device__ __forceinline__ float candidate(float amax, float alpha) {
   return f16_bits_to_f32(f32_to_f16_bits(u));
 }
 
+// ---------------------------------------------------------------- buffer loads to LDS
+typedef int v4i32 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kBufferFlags = 0x00020000u;  // raw 32-bit buffer resource (gfx9 family)
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding
+// (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their "no wait" maxima)
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// the same, also waiting for every LDS operation of this wavefront
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// LDS byte address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes return zeros without
+// touching memory.  base and bytes must be wave-uniform; readfirstlane keeps the resource in
+// SGPRs (it returns int, so each half of the address is taken back as unsigned).
+__device__ __forceinline__ v4i32 buffer_rsrc(const void* base, int bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  v4i32 rs;
+  rs[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b)));
+  rs[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32)));
+  rs[2] = __builtin_amdgcn_readfirstlane(bytes);
+  rs[3] = static_cast<int>(kBufferFlags);
+  return rs;
+}
+
+// Buffer loads of 16 bytes per lane straight to LDS: load i fills the 1 KB of LDS at
+// lds + 1024 i (lane l at + 16 l) from byte offsets vo[i].  Written as asm so that the loads may
+// stay in flight across barriers (the caller waits for them with an explicit s_waitcnt); the
+// blocks have no register outputs, M0 is restored, and they use only moves on scalar registers
+// (no instruction that writes SCC, which the compiler may keep live across the block).
+__device__ __forceinline__ void dma_x1(uint32_t lds, v4i32 rs, int v0) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[m0]\n\t"
+      "buffer_load_dwordx4 %[v0], %[rs], 0 offen lds\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [m0] "s"(__builtin_amdgcn_readfirstlane(lds)), [rs] "s"(rs), [v0] "v"(v0)
+      : "memory", "scc");
+}
+__device__ __forceinline__ void dma_x4(uint32_t lds, v4i32 rs, const int (&vo)[4]) {
+  const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[m0]\n\t"
+      "buffer_load_dwordx4 %[v0], %[rs], 0 offen lds\n\t"
+      "s_mov_b32 m0, %[m1]\n\t"
+      "buffer_load_dwordx4 %[v1], %[rs], 0 offen lds\n\t"
+      "s_mov_b32 m0, %[m2]\n\t"
+      "buffer_load_dwordx4 %[v2], %[rs], 0 offen lds\n\t"
+      "s_mov_b32 m0, %[m3]\n\t"
+      "buffer_load_dwordx4 %[v3], %[rs], 0 offen lds\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [m0] "s"(l0), [m1] "s"(l0 + 1024), [m2] "s"(l0 + 2048), [m3] "s"(l0 + 3072), [rs] "s"(rs),
+        [v0] "v"(vo[0]), [v1] "v"(vo[1]), [v2] "v"(vo[2]), [v3] "v"(vo[3])
+      : "memory", "scc");
+}
+__device__ __forceinline__ void dma_x8(uint32_t lds, v4i32 rs, const int (&vo)[8]) {
+  const int lo[4] = {vo[0], vo[1], vo[2], vo[3]};
+  const int hi[4] = {vo[4], vo[5], vo[6], vo[7]};
+  dma_x4(lds, rs, lo);
+  dma_x4(lds + 4096, rs, hi);
+}
+
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
 }  // namespace w4q
+
+// Stream-ordered device scratch (partial tiles); return a w4q_status.
+int w4q_workspace_alloc(void** ptr, size_t bytes, hipStream_t s);
+int w4q_workspace_free(void* ptr, hipStream_t s);
 
 // Launchers (one per source file); return a w4q_status.
 int w4q_launch_hessian(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accumulate,
@@ -96,8 +172,9 @@ int w4q_launch_lsq_bwd(const float* w, const float* scale, const float* g, int64
                        hipStream_t s);
 int w4q_launch_gemv(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
                     int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t s);
+// w_mode: 0 = exact weights (s16 * q), 1 = weights dequantized to bf16 (RNE of s16 * q)
 int w4q_launch_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
-                    int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t s);
+                    int64_t d_out, int64_t d_in, void* y, int y_dtype, int w_mode, hipStream_t s);
 
 static inline int w4q_launch_status() {
   return hipGetLastError() == hipSuccess ? W4Q_OK : W4Q_EHIP;

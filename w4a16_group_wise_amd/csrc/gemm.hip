@@ -45,7 +45,7 @@ __device__ __forceinline__ u32x4 expand8(uint32_t word) {
 
 // WM wavefronts along M (64 rows each) x WN along N; block tile (64 WM) x 128.
 template <int WM>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const uint16_t* __restrict__ x, int64_t M,
+__global__ __launch_bounds__(64 * WM * WN) void gemm_group_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                           const uint8_t* __restrict__ packed,
                                                           const uint16_t* __restrict__ s16,
                                                           int64_t N, int64_t K,
@@ -186,13 +186,325 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const uint16_t* __re
     }
 }
 
+
+// ---------------------------------------------------------------------------------------
+// Matrix-core kernel: 256x256 output tiles, 4 wavefronts of 128x128 (4x4 blocks of
+// v_mfma_f32_32x32x16_bf16, accumulators in AGPRs), one K-group (32 codes) per stage.
+//   x tile   : buffer loads straight to LDS, [row][16-byte chunk] with chunk c of row r at
+//              position c ^ ((r >> 1) & 3), 4 stage buffers (loads run 3 stages ahead).
+//   codes    : 16 bytes (the group's 32 nibbles) per column, loaded to LDS the same way and
+//              3 stages ahead; fp16 scales 16 bytes (8 groups) per column, every 8 groups.
+//   weights  : each thread owns one column: it reads its codes and scale from LDS, forms the
+//              bf16 weights in registers and writes them to a double-buffered [column][chunk]
+//              LDS tile (same swizzle), one stage ahead of the products.
+// kMode 1 (dequantized to bf16): w = bf16_RNE(s * q), one product per step.
+// kMode 0 (exact): s * q (exact in fp32: at most 11 x 4 significant bits) = hi + lo with
+//              hi = bf16_RNE(s * q) and lo = s * q - hi, also exact in bf16 (at most 7 bits);
+//              two products per step, no per-group scaling on the vector ALUs.
+// Work split as for the Hessian: stream-K over (tile, group), partial tiles summed in a fixed
+// order by a second kernel.  All loads are the asm loads to LDS, so the explicit vmcnt waits
+// count exactly 6 loads per stage and wavefront (4 x rows, 1 codes, 1 scales or an empty load).
+constexpr int GT = 256;                // tile edge (x rows and output columns)
+constexpr int GNB = 4;                 // x / codes stage buffers
+constexpr int kXStage = GT * 32 * 2;   // 16 KB
+constexpr int kCStage = GT * 16;       // 4 KB
+constexpr int kSBlock = GT * 16;       // 4 KB: scales of 8 groups
+constexpr int kGTileElems = GT * GT;
+constexpr int kGMinChunk = 16;
+constexpr int kGMaxBlocks = 256;
+constexpr int kOpsPerStage = 6;
+template <int kMode>
+constexpr int kWStage = GT * 32 * 2 * (kMode == 0 ? 2 : 1);  // bf16 weights (hi, lo planes)
+constexpr int kOffC = GNB * kXStage;                // 64 KB
+constexpr int kOffS = kOffC + GNB * kCStage;        // 80 KB
+constexpr int kOffJunk = kOffS + 2 * kSBlock;       // 88 KB (target of the empty loads)
+constexpr int kOffW = kOffJunk + 1024;              // 89 KB
+template <int kMode>
+constexpr int kGemmLds = kOffW + 2 * kWStage<kMode>;  // 121 KB (dequantized) or 153 KB (exact)
+
+__device__ __forceinline__ int gswz(int r, int c) { return 16 * (c ^ ((r >> 1) & 3)); }
+
+// partial-tile layout of the accumulators (as for the Hessian): 1 KB per store instruction
+__device__ __forceinline__ int64_t gpart_off(int w, int i, int j, int a, int lane) {
+  return (int64_t)(((w * 16 + i * 4 + j) * 4 + a) * 256 + 4 * lane);
+}
+
+// Store one 32x32 accumulator block (rows row0.., columns col0..) of y.
+__device__ __forceinline__ void gstore_block(void* __restrict__ y, int y_dtype, int M, int N, int row0, int col0,
+                                             const f32x16& v, int lane) {
+  const int col = col0 + (lane & 31);
+  if (col >= N) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = row0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    if (row >= M) continue;
+    const int64_t o = (int64_t)row * N + col;
+    if (y_dtype == 0)
+      reinterpret_cast<float*>(y)[o] = v[r];
+    else
+      reinterpret_cast<uint16_t*>(y)[o] = f32_to_bf16_bits(v[r]);
+  }
+}
+
+template <int kMode>
+__global__ __launch_bounds__(256, 1) void gemm_mma_kernel(const uint16_t* __restrict__ x, int M,
+                                                          const uint8_t* __restrict__ packed,
+                                                          const uint16_t* __restrict__ s16, int N, int K,
+                                                          void* __restrict__ y, int y_dtype, int tn_count,
+                                                          int total, int chunk, int nblk, int per_xcd,
+                                                          float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kGemmLds<kMode>];
+  const int G = K >> 5;
+  const int lb = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (lb >= nblk) return;
+  const int it_begin = lb * chunk;
+  const int it_end = it_begin + chunk < total ? it_begin + chunk : total;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid >> 1, wn = wid & 1;
+  const uint32_t lds0 = lds_addr(lds);
+
+  // x loads: load q (0..3) of wave w fills rows 16 (4 w + q) .. + 15, lane l -> row + l / 4,
+  // position l % 4, which holds chunk (l % 4) ^ ((row >> 1) & 3)
+  int xvo[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 16 * (4 * wid + q) + (lane >> 2);
+    xvo[q] = r * K * 2 + 16 * ((lane & 3) ^ ((r >> 1) & 3));
+  }
+  // codes and scales: column 64 w + l of the tile, i.e. this thread's own column
+  const int cvo = tid * (K >> 1);
+  const int svo = tid * G * 2;
+
+  // fragment reads: lane l reads row (col) base + l % 32, chunk 2 kk + l / 32
+  const int fr = lane & 31, fh = lane >> 5;
+
+  const f32x16 zero16 = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f,
+                         0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+
+  int it = it_begin;
+  while (it < it_end) {
+    const int t = it / G;
+    const int s0 = it - t * G;
+    const int s1 = s0 + (it_end - it) < G ? s0 + (it_end - it) : G;
+    const int tm = t / tn_count, tn = t - tm * tn_count;
+    const int m0 = tm * GT, n0 = tn * GT;
+    const uint16_t* xt = x + (int64_t)m0 * K;
+    const uint8_t* pt = packed + (int64_t)n0 * (K >> 1);
+    const uint16_t* st = s16 + (int64_t)n0 * G;
+    const int xbytes = (M - m0) * K * 2;
+    const int cbytes = (N - n0) * (K >> 1);
+    const int sbytes = (N - n0) * G * 2;
+
+    // loads of group g (x rows, codes; scales when g starts a block of 8 or the range)
+    auto issue = [&](int g) {
+      const bool live = g < s1;
+      dma_x4(lds0 + (g % GNB) * kXStage + wid * 4096, buffer_rsrc(xt + g * 32, live ? xbytes - g * 64 : 0), xvo);
+      dma_x1(lds0 + kOffC + (g % GNB) * kCStage + wid * 1024, buffer_rsrc(pt + g * 16, live ? cbytes - g * 16 : 0),
+             cvo);
+      const bool sl = live && ((g & 7) == 0 || g == s0);
+      dma_x1(sl ? lds0 + kOffS + ((g >> 3) & 1) * kSBlock + wid * 1024 : lds0 + kOffJunk,
+             buffer_rsrc(st + (g & ~7), sl ? sbytes - (g & ~7) * 2 : 0), svo);
+    };
+    // this thread's column of group g as bf16 weights (hi plane, and lo plane in exact mode)
+    auto dequant = [&](int g) {
+      const u32x4 c = *reinterpret_cast<const u32x4*>(lds + kOffC + (g % GNB) * kCStage + tid * 16);
+      const float sc =
+          f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(lds + kOffS + ((g >> 3) & 1) * kSBlock + tid * 16 + (g & 7) * 2));
+      uint8_t* wb = lds + kOffW + (g & 1) * kWStage<kMode>;
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) {  // 8 codes (k = 8 ch .. 8 ch + 7) per 16-byte chunk
+        const uint32_t word = c[ch];
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float w0 = static_cast<float>(static_cast<int>(word << (28 - 8 * p)) >> 28) * sc;
+          const float w1 = static_cast<float>(static_cast<int>(word << (24 - 8 * p)) >> 28) * sc;
+          const bf16x2 h = __builtin_convertvector(f32x2{w0, w1}, bf16x2);
+          hi[p] = __builtin_bit_cast(uint32_t, h);
+          if constexpr (kMode == 0) {
+            const float r0 = w0 - __builtin_bit_cast(float, hi[p] << 16);
+            const float r1 = w1 - __builtin_bit_cast(float, hi[p] & 0xFFFF0000u);
+            lo[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
+          }
+        }
+        *reinterpret_cast<u32x4*>(wb + tid * 64 + gswz(tid, ch)) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (kMode == 0)
+          *reinterpret_cast<u32x4*>(wb + GT * 64 + tid * 64 + gswz(tid, ch)) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      }
+    };
+
+    f32x16 acc[4][4];
+    auto compute = [&](int g, auto first) {
+      const uint8_t* xb = lds + (g % GNB) * kXStage;
+      const uint8_t* wb = lds + kOffW + (g & 1) * kWStage<kMode>;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 a[4], b[4], bl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = wm * 128 + 32 * i + fr;
+          a[i] = *reinterpret_cast<const bf16x8*>(xb + r * 64 + gswz(r, 2 * kk + fh));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = wn * 128 + 32 * j + fr;
+          b[j] = *reinterpret_cast<const bf16x8*>(wb + n * 64 + gswz(n, 2 * kk + fh));
+          if constexpr (kMode == 0) bl[j] = *reinterpret_cast<const bf16x8*>(wb + GT * 64 + n * 64 + gswz(n, 2 * kk + fh));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if constexpr (decltype(first)::value) {
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], kk == 0 ? zero16 : acc[i][j], 0, 0, 0);
+            } else {
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            }
+          }
+        if constexpr (kMode == 0) {
+          // the lo plane after all hi products: no back-to-back dependent products
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bl[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    };
+    // wait for this wave's loads of the x tile of group g and of the codes of group g + 1
+    // (the 6 loads of the stage after them stay in flight) and for its LDS writes, then a
+    // barrier: the x tile and the weights of group g are visible to all wavefronts, and the
+    // buffers the next loads and weights overwrite are free
+    auto stage_sync = [&]() {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kOpsPerStage));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+
+    // group g: x in buffer g % GNB, codes in g % GNB, weights in g & 1; loads issued 3 stages
+    // ahead, weights formed one stage ahead
+    issue(s0);
+    issue(s0 + 1);
+    issue(s0 + 2);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kOpsPerStage));  // own codes and scales of s0
+    asm volatile("" ::: "memory");
+    dequant(s0);
+    stage_sync();
+    issue(s0 + 3);
+    if (s0 + 1 < s1) dequant(s0 + 1);
+    compute(s0, std::true_type{});
+    for (int g = s0 + 1; g < s1; ++g) {
+      stage_sync();
+      issue(g + 3);
+      if (g + 1 < s1) dequant(g + 1);
+      compute(g, std::false_type{});
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    if (s0 == 0 && s1 == G) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          gstore_block(y, y_dtype, M, N, m0 + wm * 128 + 32 * i, n0 + wn * 128 + 32 * j, acc[i][j], lane);
+          asm volatile("" ::: "memory");
+        }
+    } else {
+      float* slot = ws + (int64_t)(2 * lb + (it == it_begin ? 0 : 1)) * kGTileElems;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            *reinterpret_cast<f32x4*>(slot + gpart_off(wid, i, j, a, lane)) =
+                f32x4{acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2], acc[i][j][4 * a + 3]};
+            asm volatile("" ::: "memory");
+          }
+    }
+    it += s1 - s0;
+  }
+}
+
+// Tiles whose groups were spread over several workgroups: sum the partial tiles in the order of
+// their K ranges, then store.  One workgroup per (tile, block row i, block column j).
+__global__ __launch_bounds__(256) void gemm_fixup_kernel(void* __restrict__ y, int y_dtype, int M, int N, int G,
+                                                         int tn_count, int chunk, const float* __restrict__ ws) {
+  const int t = blockIdx.x >> 4;
+  const int i = (blockIdx.x >> 2) & 3, j = blockIdx.x & 3;
+  const int first = static_cast<int>((int64_t)t * G / chunk);
+  const int last = static_cast<int>(((int64_t)t * G + G - 1) / chunk);
+  if (first == last) return;
+  const int tm = t / tn_count, tn = t - tm * tn_count;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wid >> 1, wn = wid & 1;
+  f32x16 v;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = 0.0f;
+  for (int b = first; b <= last; ++b) {
+    const int slot = 2 * b + ((int64_t)b * chunk >= (int64_t)t * G ? 0 : 1);
+    const float* p = ws + (int64_t)slot * kGTileElems;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(p + gpart_off(wid, i, j, a, lane));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * a + e] += q[e];
+    }
+  }
+  gstore_block(y, y_dtype, M, N, tm * GT + wm * 128 + 32 * i, tn * GT + wn * 128 + 32 * j, v, lane);
+}
+
+template <int kMode>
+int launch_mma_pass(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16, int64_t N,
+                    int64_t K, void* y, int y_dtype, hipStream_t s) {
+  const int64_t G = K / 32;
+  const int64_t tm_count = (m + GT - 1) / GT, tn_count = (N + GT - 1) / GT;
+  const int64_t tiles = tm_count * tn_count;
+  const int64_t total = tiles * G;
+  if (total > 0x3FFFFFFF) return W4Q_EUNSUPPORTED;
+  int64_t nblk = (total + kGMinChunk - 1) / kGMinChunk;
+  if (nblk > kGMaxBlocks) nblk = kGMaxBlocks;
+  const int64_t chunk = (total + nblk - 1) / nblk;
+  nblk = (total + chunk - 1) / chunk;
+  const bool split = nblk > 1 && chunk % G != 0;
+  const int64_t per_xcd = (nblk + 7) / 8;
+  float* ws = nullptr;
+  if (split && w4q_workspace_alloc(reinterpret_cast<void**>(&ws), (size_t)nblk * 2 * kGTileElems * sizeof(float), s) !=
+                   W4Q_OK)
+    return W4Q_EHIP;
+  hipLaunchKernelGGL(gemm_mma_kernel<kMode>, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(256), 0, s,
+                     x, static_cast<int>(m), packed, s16, static_cast<int>(N), static_cast<int>(K), y, y_dtype,
+                     static_cast<int>(tn_count), static_cast<int>(total), static_cast<int>(chunk),
+                     static_cast<int>(nblk), static_cast<int>(per_xcd), ws);
+  int rc = w4q_launch_status();
+  if (split) {
+    if (rc == W4Q_OK) {
+      hipLaunchKernelGGL(gemm_fixup_kernel, dim3(static_cast<unsigned>(16 * tiles)), dim3(256), 0, s, y, y_dtype,
+                         static_cast<int>(m), static_cast<int>(N), static_cast<int>(G), static_cast<int>(tn_count),
+                         static_cast<int>(chunk), ws);
+      rc = w4q_launch_status();
+    }
+    if (w4q_workspace_free(ws, s) != W4Q_OK && rc == W4Q_OK) rc = W4Q_EHIP;
+  }
+  return rc;
+}
+
 }  // namespace
 }  // namespace w4q
 
 using namespace w4q;
 
-int w4q_launch_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
-                    int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t s) {
+// exact weights, any shape: one K-group per step, scale applied per group on the vector ALUs
+static int launch_group(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
+                 int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t s) {
   if (d_in / kGroup > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
   const int64_t gn = (d_out + BN - 1) / BN;
   // 256-row tiles (8 wavefronts share one expansion of the codes) when they still give at
@@ -204,10 +516,32 @@ int w4q_launch_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const u
   if (8 * per_xcd > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
   const dim3 grid(static_cast<unsigned>(8 * per_xcd));
   if (big)
-    hipLaunchKernelGGL(gemm_kernel<4>, grid, dim3(64 * 4 * WN), 0, s, x, m, packed, s16, d_out, d_in, y,
+    hipLaunchKernelGGL(gemm_group_kernel<4>, grid, dim3(64 * 4 * WN), 0, s, x, m, packed, s16, d_out, d_in, y,
                        y_dtype, gn, tiles, per_xcd);
   else
-    hipLaunchKernelGGL(gemm_kernel<2>, grid, dim3(64 * 2 * WN), 0, s, x, m, packed, s16, d_out, d_in, y,
+    hipLaunchKernelGGL(gemm_group_kernel<2>, grid, dim3(64 * 2 * WN), 0, s, x, m, packed, s16, d_out, d_in, y,
                        y_dtype, gn, tiles, per_xcd);
   return w4q_launch_status();
+}
+
+int w4q_launch_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
+                    int64_t d_out, int64_t d_in, void* y, int y_dtype, int w_mode, hipStream_t s) {
+  // the matrix-core kernel needs 16-byte scale rows (d_in % 256 == 0) and 32-bit buffer offsets
+  // into the codes and scales; x is taken in passes of whole 256-row tiles that fit them too
+  const bool mma_ok = d_in % 256 == 0 && d_out * (d_in / 2) < 0x7FFFFFFF && 256 * d_in * 2 < 0x7FFFFFFF;
+  if (!mma_ok) {
+    if (w_mode != 0) return W4Q_EUNSUPPORTED;
+    return launch_group(x, m, packed, s16, d_out, d_in, y, y_dtype, s);
+  }
+  const int64_t rows = (0x7FFFFFFF / (2 * d_in)) / GT * GT;
+  const int64_t ob = y_dtype == 0 ? 4 : 2;
+  for (int64_t r0 = 0; r0 < m; r0 += rows) {
+    const int64_t mr = m - r0 < rows ? m - r0 : rows;
+    const uint16_t* xr = x + r0 * d_in;
+    void* yr = static_cast<uint8_t*>(y) + r0 * d_out * ob;
+    const int rc = w_mode == 0 ? launch_mma_pass<0>(xr, mr, packed, s16, d_out, d_in, yr, y_dtype, s)
+                               : launch_mma_pass<1>(xr, mr, packed, s16, d_out, d_in, yr, y_dtype, s);
+    if (rc != W4Q_OK) return rc;
+  }
+  return W4Q_OK;
 }

@@ -23,7 +23,6 @@
 // end of X return zeros, which pads the token tail without any test in the loop.
 #include "common.hpp"
 
-#include <mutex>
 #include <type_traits>
 
 namespace w4q {
@@ -31,12 +30,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int BT = 256;                // tile edge in features
-constexpr int BK = 64;                 // tokens per stage
+constexpr int BK = 32;                 // tokens per stage
+constexpr int NBUF = 4;                // LDS stage buffers: loads run NBUF - 1 stages ahead
 constexpr int kTileElems = BT * BT;    // floats per partial tile
-constexpr int kMinChunk = 8;           // stages per workgroup before more workgroups are used
+constexpr int kMinChunk = 16;          // stages per workgroup before more workgroups are used
 constexpr int kMaxBlocks = 256;        // one workgroup per compute unit (256 AGPR accumulators)
-constexpr uint32_t kBufferFlags = 0x00020000u;  // raw 32-bit buffer resource (gfx9 family)
-constexpr int kStageBytes = 2 * BK * BT * 2;    // I and J panels, bf16: 64 KB
+constexpr int kStageBytes = 2 * BK * BT * 2;    // I and J panels, bf16: 32 KB
+constexpr int kLoadsPerWave = kStageBytes / 1024 / 4;  // 1 KB per load instruction: 8
 
 // LDS stage layout: panel p (I = 0, J = 1), token t, 16-byte chunk position cp (32 per token row
 // of 256 features).  Chunk c (features 8c .. 8c + 7) of token t sits at position c ^ swz(t % 4).
@@ -98,18 +98,15 @@ __device__ __forceinline__ int64_t part_off(int w, int i, int j, int a, int lane
   return (int64_t)(((w * 16 + i * 4 + j) * 4 + a) * 256 + 4 * lane);
 }
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-#define W4Q_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 #define W4Q_LDS4(p) ((__attribute__((address_space(3))) v4i16*)(p))
+
+static_assert(kLoadsPerWave == 8, "one dma_x8 per stage and wave");
 
 __global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __restrict__ x, int n_tok, int d,
                                                               float* __restrict__ h, int accumulate, int nt,
                                                               int ns, int total, int chunk, int nblk,
                                                               int per_xcd, float* __restrict__ ws) {
-  // the two stage buffers are separate arrays, so the compiler can tell that reads of one need
-  // not wait for the loads in flight into the other
-  __shared__ __attribute__((aligned(16))) uint16_t L0[kStageBytes / 2];
-  __shared__ __attribute__((aligned(16))) uint16_t L1[kStageBytes / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t Ls[NBUF * kStageBytes / 2];
 
   // workgroups are dealt to the 8 XCDs round-robin; consecutive ranges (which share tiles and
   // hence I panels and partial tiles) go to the same XCD
@@ -123,15 +120,16 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid >> 1, wn = wid & 1;
 
-  // load role: load instruction q (0..15) of wave w fills the 1 KB of LDS at slot
-  // (16 w + q) * 64: panel w / 2, tokens 32 (w % 2) + 2 q + lane / 32, chunk position lane % 32
+  // load role: load q (0..7) of wave w fills the 1 KB of LDS at slot (8 w + q) * 64: panel w / 2,
+  // tokens 16 (w % 2) + 2 q + lane / 32, chunk position lane % 32
   const int ld_panel = wid >> 1;
-  int ld_tok[16], ld_chunk[16];
+  int ld_tok[kLoadsPerWave], ld_chunk[kLoadsPerWave];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    ld_tok[q] = 32 * (wid & 1) + 2 * q + (lane >> 5);
+  for (int q = 0; q < kLoadsPerWave; ++q) {
+    ld_tok[q] = 16 * (wid & 1) + 2 * q + (lane >> 5);
     ld_chunk[q] = (lane & 31) ^ swz(ld_tok[q]);
   }
+  const uint32_t lds_base = lds_addr(Ls);
 
   // read role (transposing reads): 16-lane group g = lane / 16, lane j = lane % 16 in it points
   // at token 8 (g / 2) + j / 4 (+ 4 for the second read) and at features 16 (g % 2) + 4 (j % 4)
@@ -156,87 +154,111 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __
     tile_coords(t, nt, ti, tj);
     const bool diag = ti == tj;
 
-    // byte offsets of this lane's 16 loads within a stage; features past d read into the next
-    // token or past the end (zeros): they only feed entries that are never stored
+    // byte offsets of this lane's loads within a stage; features past d read into the next token
+    // or past the end (zeros): they only feed entries that are never stored
     const int fbase = (ld_panel ? tj : ti) * BT;
-    int voff[16];
+    int voff[kLoadsPerWave];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) voff[q] = (ld_tok[q] * d + fbase + 8 * ld_chunk[q]) * 2;
+    for (int q = 0; q < kLoadsPerWave; ++q) voff[q] = (ld_tok[q] * d + fbase + 8 * ld_chunk[q]) * 2;
     // on a diagonal tile the J panel is the I panel: its loads are switched off
     const bool ld_on = !(diag && ld_panel == 1);
 
-    auto issue = [&](int s, uint16_t* L) {
+    auto issue = [&](int s) {
       const int64_t tok0 = (int64_t)s * BK;
       // bytes from the stage start to the end of X; 0 (every load returns zeros without touching
-      // memory) for stages outside this range.  All wave-uniform (readfirstlane keeps the buffer
-      // resource in SGPRs; it returns int, so each half is taken back as unsigned).
-      const int bytes =
-          __builtin_amdgcn_readfirstlane((s < s1 && ld_on) ? (n_tok - static_cast<int>(tok0)) * d * 2 : 0);
-      const uint64_t base = reinterpret_cast<uint64_t>(x + tok0 * d);
-      const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(base)));
-      const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(base >> 32)));
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), 0, bytes, kBufferFlags);
-#pragma unroll
-      for (int q = 0; q < 16; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, W4Q_LDS(L + (16 * wid + q) * 512), 16, voff[q], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);  // issue the loads here, ahead of the stage's products
+      // memory) for stages outside this range
+      const int bytes = (s < s1 && ld_on) ? (n_tok - static_cast<int>(tok0)) * d * 2 : 0;
+      const v4i32 rs = buffer_rsrc(x + tok0 * d, bytes);
+      const uint32_t m0 = lds_base + static_cast<uint32_t>(((s - s0) % NBUF) * kStageBytes + 8 * 1024 * wid);
+      dma_x8(m0, rs, voff);
+    };
+    // wait for this wave's loads of the stage about to be used (the NBUF - 2 younger stages stay
+    // in flight), then a barrier: the stage is in LDS for all wavefronts, and every wavefront is
+    // done with the buffer the next issue overwrites
+    auto stage_sync = [&]() {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerWave * (NBUF - 2)));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     };
 
     f32x16 acc[4][4];
     const int bpanel = diag ? 0 : 1;  // B fragments come from the I panel on diagonal tiles
-    // one stage: 4 steps of 16 tokens; `first` starts the sums from a zero accumulator.  (On a
-    // diagonal tile the (wm = 1, wn = 0) quadrant, the mirror of (0, 1), is computed as well,
-    // which keeps the loop free of branches around the accumulators, but never stored.)
-    auto compute = [&](const uint16_t* L, auto first) {
-      const char* Lb = reinterpret_cast<const char*>(L);
+    // fragments of one 16-token step of stage s (transposing reads)
+    struct Frag {
+      bf16x8 a[4], b[4];
+    };
+    auto load = [&](int s, int kk, Frag& F) {
+      const char* Lb = reinterpret_cast<const char*>(Ls) + ((s - s0) % NBUF) * kStageBytes + kk * 16 * 512;
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        bf16x8 a[4], b[4];
+      for (int i = 0; i < 4; ++i) {
+        const char* p = Lb + rd_off(0, 4 * wm + i);
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(W4Q_LDS4(p));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(W4Q_LDS4(p + 4 * 512));
+        F.a[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const char* p = Lb + rd_off(0, 4 * wm + i) + kk * 16 * 512;
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(W4Q_LDS4(p));
-          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(W4Q_LDS4(p + 4 * 512));
-          a[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const char* p = Lb + rd_off(bpanel, 4 * wn + j) + kk * 16 * 512;
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(W4Q_LDS4(p));
-          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(W4Q_LDS4(p + 4 * 512));
-          b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if constexpr (decltype(first)::value) {
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], kk == 0 ? zero16 : acc[i][j], 0, 0, 0);
-            } else {
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-            }
-          }
+      for (int j = 0; j < 4; ++j) {
+        const char* p = Lb + rd_off(bpanel, 4 * wn + j);
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(W4Q_LDS4(p));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(W4Q_LDS4(p + 4 * 512));
+        F.b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     };
+    // products of rows i0 .. i1 - 1 of the 4x4 blocks; `first` starts the sums from zero.  (On a
+    // diagonal tile the (wm = 1, wn = 0) quadrant, the mirror of (0, 1), is computed as well,
+    // which keeps the loop free of branches around the accumulators, but never stored.)
+    auto mma = [&](const Frag& F, int i0, int i1, auto first) {
+#pragma unroll
+      for (int i = i0; i < i1; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (decltype(first)::value) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[i], F.b[j], zero16, 0, 0, 0);
+          } else {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[i], F.b[j], acc[i][j], 0, 0, 0);
+          }
+        }
+    };
+    // the barrier sits between the products of a stage's last step, so the matrix cores stay
+    // busy while the wavefronts meet; right after it the first fragments of the next stage are
+    // read (the instruction order around it is pinned)
+    auto mid_sync = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      stage_sync();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    static_assert(BK == 32, "two 16-token steps per stage");
 
-    // stage s lives in L0 for s - s0 even and in L1 for s - s0 odd.  Each barrier (which waits
-    // for this wave's loads to LDS) makes the next stage visible to all wavefronts and frees the
-    // other buffer; the loads of stage s + 1 then run under the products of stage s.
-    issue(s0, L0);
-    __syncthreads();
-    issue(s0 + 1, L1);
-    compute(L0, std::true_type{});
-    for (int s = s0 + 1; s < s1; s += 2) {
-      __syncthreads();
-      issue(s + 1, L0);
-      compute(L1, std::false_type{});
-      if (s + 1 >= s1) break;  // uniform
-      __syncthreads();
-      issue(s + 2, L1);
-      compute(L0, std::false_type{});
+    // stage s lives in buffer (s - s0) % NBUF; its loads are issued NBUF - 1 stages ahead, into
+    // the buffer of stage s - 1, which every wavefront finished reading before the last barrier
+    Frag F0, F1;
+#pragma unroll
+    for (int p = 0; p < NBUF - 1; ++p) issue(s0 + p);
+    stage_sync();
+    load(s0, 0, F0);
+    issue(s0 + NBUF - 1);
+    load(s0, 1, F1);
+    mma(F0, 0, 4, std::true_type{});
+    mma(F1, 0, 2, std::false_type{});
+    mid_sync();
+    load(s0 + 1, 0, F0);  // (past the range: a stale buffer, never used)
+    mma(F1, 2, 4, std::false_type{});
+    for (int s = s0 + 1; s < s1; ++s) {
+      issue(s + NBUF - 1);
+      load(s, 1, F1);
+      mma(F0, 0, 4, std::false_type{});
+      mma(F1, 0, 2, std::false_type{});
+      mid_sync();
+      load(s + 1, 0, F0);
+      mma(F1, 2, 4, std::false_type{});
     }
-    __syncthreads();  // both buffers free for the next range
+    // every load of this range (including the empty ones past its end) has landed and every
+    // wavefront is done with the buffers before the next range refills them
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 
     const bool work = !(diag && wm == 1 && wn == 0);
     if (work) {
@@ -306,29 +328,6 @@ __global__ __launch_bounds__(kThreads) void hessian_fixup_kernel(float* __restri
   store_block(h, d, row0, col0, v, accumulate, lane);
 }
 
-// Library-owned stream-ordered pool per device for the partial tiles (kept, not released to
-// the system between calls).
-constexpr int kMaxDevices = 64;
-std::mutex g_pool_mu;
-hipMemPool_t g_pool[kMaxDevices];
-
-hipMemPool_t device_pool(int dev) {
-  std::lock_guard<std::mutex> lk(g_pool_mu);
-  if (dev < 0 || dev >= kMaxDevices) return nullptr;
-  if (!g_pool[dev]) {
-    hipMemPoolProps props = {};
-    props.allocType = hipMemAllocationTypePinned;
-    props.location.type = hipMemLocationTypeDevice;
-    props.location.id = dev;
-    hipMemPool_t p = nullptr;
-    if (hipMemPoolCreate(&p, &props) != hipSuccess) return nullptr;
-    uint64_t keep = UINT64_MAX;
-    hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
-    g_pool[dev] = p;
-  }
-  return g_pool[dev];
-}
-
 // One pass over at most 2^31 - 1 bytes of X (32-bit buffer offsets).
 int launch_pass(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accumulate, hipStream_t s) {
   const int64_t nt = (d + BT - 1) / BT;
@@ -345,12 +344,8 @@ int launch_pass(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accum
 
   float* ws = nullptr;
   if (split) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return W4Q_EHIP;
-    hipMemPool_t pool = device_pool(dev);
-    if (!pool) return W4Q_EHIP;
     const size_t bytes = (size_t)nblk * 2 * kTileElems * sizeof(float);
-    if (hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), bytes, pool, s) != hipSuccess) return W4Q_EHIP;
+    if (w4q_workspace_alloc(reinterpret_cast<void**>(&ws), bytes, s) != W4Q_OK) return W4Q_EHIP;
   }
   hipLaunchKernelGGL(hessian_kernel, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(kThreads), 0, s, x,
                      static_cast<int>(n_tok), static_cast<int>(d), h, accumulate, static_cast<int>(nt),
@@ -364,7 +359,7 @@ int launch_pass(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accum
                          static_cast<int>(chunk), ws);
       rc = w4q_launch_status();
     }
-    if (hipFreeAsync(ws, s) != hipSuccess && rc == W4Q_OK) rc = W4Q_EHIP;
+    if (w4q_workspace_free(ws, s) != W4Q_OK && rc == W4Q_OK) rc = W4Q_EHIP;
   }
   return rc;
 }

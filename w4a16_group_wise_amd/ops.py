@@ -123,9 +123,8 @@ def lsq_bwd(w: torch.Tensor, scale: torch.Tensor, grad_w_hat: torch.Tensor, grad
     return gw, gsc, wh
 
 
-def w4a16_gemm(x: torch.Tensor, packed: torch.Tensor, scale_f16: torch.Tensor,
-               out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None):
-    """y [m][d_out] = x [m][d_in] (bf16) times the dequantised packed weights, transposed."""
+def _gemm(name: str, x: torch.Tensor, packed: torch.Tensor, scale_f16: torch.Tensor,
+          out_dtype: torch.dtype, out: Optional[torch.Tensor]):
     _need(x, "x", torch.bfloat16)
     m, d_in = x.shape
     _need(packed, "packed", torch.uint8, device=x.device)
@@ -136,7 +135,21 @@ def w4a16_gemm(x: torch.Tensor, packed: torch.Tensor, scale_f16: torch.Tensor,
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be float32 or bfloat16")
     y = _out(out, "y", (m, d_out), out_dtype, x.device)
-    check("w4a16_gemm", lib().w4a16_gemm(x.data_ptr(), m, packed.data_ptr(), scale_f16.data_ptr(),
-                                         d_out, d_in, y.data_ptr(),
-                                         0 if out_dtype == torch.float32 else 1, _stream(x)))
+    check(name, getattr(lib(), name)(x.data_ptr(), m, packed.data_ptr(), scale_f16.data_ptr(),
+                                     d_out, d_in, y.data_ptr(),
+                                     0 if out_dtype == torch.float32 else 1, _stream(x)))
     return y
+
+
+def w4a16_gemm(x: torch.Tensor, packed: torch.Tensor, scale_f16: torch.Tensor,
+               out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None):
+    """y [m][d_out] = x [m][d_in] (bf16) times the dequantised packed weights (s16 * q, exact),
+    transposed."""
+    return _gemm("w4a16_gemm", x, packed, scale_f16, out_dtype, out)
+
+
+def w4a16_gemm_dq(x: torch.Tensor, packed: torch.Tensor, scale_f16: torch.Tensor,
+                  out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None):
+    """As w4a16_gemm with each weight dequantized to bf16 (RNE of s16 * q) before the product;
+    d_in must be a multiple of 256."""
+    return _gemm("w4a16_gemm_dq", x, packed, scale_f16, out_dtype, out)

@@ -191,7 +191,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_group_kernel(const uint16_t
 // Matrix-core kernel: 256x256 output tiles, 4 wavefronts of 128x128 (4x4 blocks of
 // v_mfma_f32_32x32x16_bf16, accumulators in AGPRs), one K-group (32 codes) per stage.
 //   x tile   : buffer loads straight to LDS, [row][16-byte chunk] with chunk c of row r at
-//              position c ^ ((r >> 1) & 3), 4 stage buffers (loads run 3 stages ahead).
+//              position c ^ f(r) (bank-conflict-free, see gswz), 4 stage buffers (loads run 3
+//              stages ahead).
 //   codes    : 16 bytes (the group's 32 nibbles) per column, loaded to LDS the same way and
 //              3 stages ahead; fp16 scales 16 bytes (8 groups) per column, every 8 groups.
 //   weights  : each thread owns one column: it reads its codes and scale from LDS, forms the
@@ -222,7 +223,11 @@ constexpr int kOffW = kOffJunk + 1024;              // 89 KB
 template <int kMode>
 constexpr int kGemmLds = kOffW + 2 * kWStage<kMode>;  // 121 KB (dequantized) or 153 KB (exact)
 
-__device__ __forceinline__ int gswz(int r, int c) { return 16 * (c ^ ((r >> 1) & 3)); }
+// byte offset of 16-byte chunk c within LDS row r (64-byte rows): position c ^ f(r) with
+// f(r) = ((r >> 1) ^ (r >> 3)) & 3, so the 8 rows of a 128-byte bank phase and the 16 rows of a
+// 256-byte phase read or written at one chunk all land on distinct 16-byte bank slots
+__device__ __forceinline__ int gswz_f(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int gswz(int r, int c) { return 16 * (c ^ gswz_f(r)); }
 
 // partial-tile layout of the accumulators (as for the Hessian): 1 KB per store instruction
 __device__ __forceinline__ int64_t gpart_off(int w, int i, int j, int a, int lane) {
@@ -267,12 +272,12 @@ __global__ __launch_bounds__(256, 1) void gemm_mma_kernel(const uint16_t* __rest
   const uint32_t lds0 = lds_addr(lds);
 
   // x loads: load q (0..3) of wave w fills rows 16 (4 w + q) .. + 15, lane l -> row + l / 4,
-  // position l % 4, which holds chunk (l % 4) ^ ((row >> 1) & 3)
+  // position l % 4, which holds chunk (l % 4) ^ f(row)
   int xvo[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int r = 16 * (4 * wid + q) + (lane >> 2);
-    xvo[q] = r * K * 2 + 16 * ((lane & 3) ^ ((r >> 1) & 3));
+    xvo[q] = r * K * 2 + 16 * ((lane & 3) ^ gswz_f(r));
   }
   // codes and scales: column 64 w + l of the tile, i.e. this thread's own column
   const int cvo = tid * (K >> 1);
@@ -337,71 +342,105 @@ __global__ __launch_bounds__(256, 1) void gemm_mma_kernel(const uint16_t* __rest
     };
 
     f32x16 acc[4][4];
-    auto compute = [&](int g, auto first) {
+    // fragments of one 16-code step (x rows and weight columns, and the lo plane when exact)
+    struct Frag {
+      bf16x8 a[4], b[4], bl[kMode == 0 ? 4 : 1];
+    };
+    auto load = [&](int g, int kk, Frag& F) {
       const uint8_t* xb = lds + (g % GNB) * kXStage;
       const uint8_t* wb = lds + kOffW + (g & 1) * kWStage<kMode>;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 a[4], b[4], bl[4];
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 128 + 32 * i + fr;
+        F.a[i] = *reinterpret_cast<const bf16x8*>(xb + r * 64 + gswz(r, 2 * kk + fh));
+      }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = wm * 128 + 32 * i + fr;
-          a[i] = *reinterpret_cast<const bf16x8*>(xb + r * 64 + gswz(r, 2 * kk + fh));
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int n = wn * 128 + 32 * j + fr;
+        F.b[j] = *reinterpret_cast<const bf16x8*>(wb + n * 64 + gswz(n, 2 * kk + fh));
+        if constexpr (kMode == 0)
+          F.bl[j] = *reinterpret_cast<const bf16x8*>(wb + GT * 64 + n * 64 + gswz(n, 2 * kk + fh));
+      }
+    };
+    // the products of one step; `first` starts the sums from zero
+    auto mma = [&](const Frag& F, auto first) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int n = wn * 128 + 32 * j + fr;
-          b[j] = *reinterpret_cast<const bf16x8*>(wb + n * 64 + gswz(n, 2 * kk + fh));
-          if constexpr (kMode == 0) bl[j] = *reinterpret_cast<const bf16x8*>(wb + GT * 64 + n * 64 + gswz(n, 2 * kk + fh));
+          if constexpr (decltype(first)::value)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[i], F.b[j], zero16, 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[i], F.b[j], acc[i][j], 0, 0, 0);
         }
+      if constexpr (kMode == 0) {
+        // the lo plane after all hi products: no back-to-back dependent products
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if constexpr (decltype(first)::value) {
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], kk == 0 ? zero16 : acc[i][j], 0, 0, 0);
-            } else {
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-            }
-          }
-        if constexpr (kMode == 0) {
-          // the lo plane after all hi products: no back-to-back dependent products
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bl[j], acc[i][j], 0, 0, 0);
-        }
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[i], F.bl[j], acc[i][j], 0, 0, 0);
       }
     };
-    // wait for this wave's loads of the x tile of group g and of the codes of group g + 1
-    // (the 6 loads of the stage after them stay in flight) and for its LDS writes, then a
-    // barrier: the x tile and the weights of group g are visible to all wavefronts, and the
-    // buffers the next loads and weights overwrite are free
-    auto stage_sync = [&]() {
+    constexpr int kReads = kMode == 0 ? 12 : 8;
+    // products interleaved with the fragment reads of the next step (one read between products)
+    // and with the vector work of the dequantization
+    auto pattern = [&](auto valu) {
+      constexpr int kM = kMode == 0 ? 32 : 16;
+      constexpr int kV = decltype(valu)::value;
+#pragma unroll
+      for (int i = 0; i < kM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if (i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        if constexpr (kV > 0) __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);  // VALU
+      }
+    };
+    // own loads: at most n outstanding (no barrier)
+    auto wait_vm = [&](auto n) {
       asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kOpsPerStage));
-      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(decltype(n)::value));
       asm volatile("" ::: "memory");
     };
+    // mid-stage synchronisation: this wave's loads of the next x tile have landed (the two
+    // younger stages of loads stay in flight) and its LDS reads and weight writes are done;
+    // after the barrier the next stage's x tile and weights are visible to all wavefronts and
+    // nobody reads the buffers the next loads and weights overwrite
+    auto mid_sync = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * kOpsPerStage));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
 
-    // group g: x in buffer g % GNB, codes in g % GNB, weights in g & 1; loads issued 3 stages
-    // ahead, weights formed one stage ahead
+    // group g: x in buffer g % GNB, codes in g % GNB, weights in g & 1.  Loads are issued 3
+    // stages ahead; the weights of g + 1 are formed during stage g; each stage is two steps of
+    // 16 codes, and the barrier sits between them, so the reads of every step overlap the
+    // products of the step before.
+    Frag F0, F1;
     issue(s0);
     issue(s0 + 1);
     issue(s0 + 2);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kOpsPerStage));  // own codes and scales of s0
-    asm volatile("" ::: "memory");
+    wait_vm(std::integral_constant<int, 2 * kOpsPerStage>{});  // own codes and scales of s0
     dequant(s0);
-    stage_sync();
-    issue(s0 + 3);
-    if (s0 + 1 < s1) dequant(s0 + 1);
-    compute(s0, std::true_type{});
-    for (int g = s0 + 1; g < s1; ++g) {
-      stage_sync();
+    mid_sync();
+    load(s0, 0, F0);
+    for (int g = s0; g < s1; ++g) {
       issue(g + 3);
-      if (g + 1 < s1) dequant(g + 1);
-      compute(g, std::false_type{});
+      wait_vm(std::integral_constant<int, 2 * kOpsPerStage>{});  // own codes of g + 1
+      load(g, 1, F1);
+      if (g == s0)
+        mma(F0, std::true_type{});
+      else
+        mma(F0, std::false_type{});
+      // (past the range the weights are formed from empty codes into a buffer nobody reads)
+      dequant(g + 1);
+      pattern(std::integral_constant<int, kMode == 0 ? 3 : 6>{});
+      mid_sync();
+      load(g + 1, 0, F0);  // (past the range: a stale buffer, never used)
+      mma(F1, std::false_type{});
+      pattern(std::integral_constant<int, 0>{});
     }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));

@@ -38,7 +38,7 @@ CSRC = os.path.join(ROOT, "w4a16_group_wise_amd", "csrc")
 
 # kernel family -> (source file, symbol substrings as they appear in a kernel trace)
 KERNELS = {
-    "hessian": ("hessian.hip", ["hessian_kernel", "hessian256_kernel"]),
+    "hessian": ("hessian.hip", ["hessian_kernel", "hessian_fixup_kernel"]),
     "scale_search": ("scale_search.hip", ["search_fp32_kernel", "search_fp64_kernel"]),
     "pack": ("pack_lsq.hip", ["pack_kernel"]),
     "lsq_fwd": ("pack_lsq.hip", ["lsq_fwd_kernel"]),
@@ -46,7 +46,8 @@ KERNELS = {
     "gemv_m1": ("gemv.hip", ["gemv_kernel<1,"]),
     "gemv_m4": ("gemv.hip", []),   # same kernel as the M=16 passes: not separable by name
     "gemv_m16": ("gemv.hip", []),
-    "gemm": ("gemm.hip", ["gemm_kernel"]),
+    "gemm": ("gemm.hip", ["gemm_group_kernel"]),
+    "gemm_dq": ("gemm.hip", ["gemm_dq_kernel", "gemm_fixup_kernel"]),
 }
 
 
@@ -104,8 +105,9 @@ class Step:
         self.w_hat2 = torch.empty_like(self.w)
         self.gemm_m = min(wl["gemm_m"], self.n_tok)
         self.y = {m: torch.empty((m, d_out), dtype=f32, device=dev) for m in (1, 4, 16, self.gemm_m)}
+        self.y_dq = torch.empty((self.gemm_m, d_out), dtype=f32, device=dev)
         self.names = ["hessian", "scale_search", "pack", "lsq_fwd", "lsq_bwd", "gemv_m1", "gemv_m4",
-                      "gemv_m16", "gemm"]
+                      "gemv_m16", "gemm", "gemm_dq"]
 
     def launches(self):
         import w4a16_group_wise_amd as w4q
@@ -119,6 +121,7 @@ class Step:
                                              out=(self.gw, self.gsc, self.w_hat2))
         for m, name in ((1, "gemv_m1"), (4, "gemv_m4"), (16, "gemv_m16"), (self.gemm_m, "gemm")):
             yield name, (lambda m=m: w4q.w4a16_gemm(self.x[:m], self.packed, self.s16, out=self.y[m]))
+        yield "gemm_dq", lambda: w4q.w4a16_gemm_dq(self.x[:self.gemm_m], self.packed, self.s16, out=self.y_dq)
 
     def work(self):
         """Algorithmic work per launch: (amount, unit, bound, peak)."""
@@ -139,6 +142,7 @@ class Step:
             "gemv_m4": (gemv_bytes(4), "byte", "hbm", PEAK_HBM_GBS * 1e9),
             "gemv_m16": (gemv_bytes(16), "byte", "hbm", PEAK_HBM_GBS * 1e9),
             "gemm": (2 * self.gemm_m * d_out * d_in, "flop", "mfma", PEAK_BF16_TFLOPS * 1e12),
+            "gemm_dq": (2 * self.gemm_m * d_out * d_in, "flop", "mfma", PEAK_BF16_TFLOPS * 1e12),
         }
 
 
@@ -275,6 +279,7 @@ def run(args):
             "search_groups_per_s": round(step.d_out * step.G / (comps["scale_search"]["us"] * 1e-6), 1),
             "hessian_mfma_frac": comps["hessian"]["frac"],
             "gemm_mfma_frac": comps["gemm"]["frac"],
+            "gemm_dq_mfma_frac": comps["gemm_dq"]["frac"],
         },
         "kernels": comps,
     }

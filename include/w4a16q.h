@@ -16,8 +16,8 @@
  *   - Tensors are caller-owned DEVICE memory, row-major, contiguous.  Every call only
  *     enqueues work on `stream` (0 = the legacy default stream) and returns; the library never
  *     synchronises.  Results are valid once the caller has synchronised that stream.  The
- *     library allocates nothing except, for quant_hessian and for w4a16_gemm / w4a16_gemm_dq
- *     with m > 16, partial-tile scratch taken from and returned to a library-owned
+ *     library allocates nothing except, for quant_hessian and w4a16_gemm_dq, partial-tile
+ *     scratch taken from and returned to a library-owned
  *     stream-ordered memory pool on the same stream (at most 128 MB per call; the pool keeps
  *     its memory for later calls).
  *   - Weights W are fp32 [d_out][d_in]; a group is 32 consecutive weights of one row along
@@ -161,9 +161,9 @@ int lsq_bwd(const float* w, const float* scale, const float* grad_w_hat, int64_t
  *   scale_f16 fp16 bits [d_out][G].
  *   y         [m][d_out], fp32 (y_dtype 0) or bf16 RNE of the fp32 result (y_dtype 1).
  *   m >= 1.  Small m (<= 16) streams the packed weights (bandwidth bound); larger m runs on
- *   the bf16 matrix cores: each weight s*q (at most 11 x 4 significant bits, exact in fp32) is
- *   split exactly into two bf16 values hi + lo in registers and both are multiplied, so the
- *   weights enter the products unrounded.
+ *   the bf16 matrix cores with the codes expanded to bf16 (exact small integers) and the fp32
+ *   scale applied once per group to the group's partial products, so the weights enter the
+ *   products unrounded.
  */
 int w4a16_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
                int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t stream);
@@ -174,9 +174,10 @@ int w4a16_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16
  * take bf16 operands):
  *   w_hat[n][k] = bf16_RNE(fp32(scale_f16[n][k/32]) * q[n][k])
  *   y[m][n]     = sum_k x[m][k] * w_hat[n][k]          (fp32 accumulation)
- * Arguments, layouts and y_dtype as for w4a16_gemm.  One bf16 matrix-core product per weight
- * (half the products of w4a16_gemm for m > 16); any m >= 1 runs on the matrix cores.
- * d_in must be a multiple of 256 (else W4Q_EUNSUPPORTED).
+ * Arguments, layouts and y_dtype as for w4a16_gemm.  The weights are formed in registers and
+ * go straight into the bf16 matrix-core products (no per-group scaling step); any m >= 1 runs
+ * on the matrix cores.  d_in must be a multiple of 256 and d_out * d_in / 2 below 2^31 (else
+ * W4Q_EUNSUPPORTED).
  */
 int w4a16_gemm_dq(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
                   int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t stream);

@@ -114,7 +114,6 @@ int w4a16_gemm_dq(const uint16_t* x, int64_t m, const uint8_t* packed, const uin
                   int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t stream) {
   const int rc = gemm_args(x, m, packed, scale_f16, d_out, d_in, y, y_dtype);
   if (rc != W4Q_OK) return rc;
-  if (d_in % 256 != 0) return W4Q_EUNSUPPORTED;
   return w4q_launch_gemm(x, m, packed, scale_f16, d_out, d_in, y, y_dtype, 1, stream);
 }
 

@@ -198,10 +198,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_group_kernel(const uint16_t
 //   weights  : each thread owns one column: it reads its codes and scale from LDS, forms the
 //              bf16 weights in registers and writes them to a double-buffered [column][chunk]
 //              LDS tile (same swizzle), one stage ahead of the products.
-// kMode 1 (dequantized to bf16): w = bf16_RNE(s * q), one product per step.
-// kMode 0 (exact): s * q (exact in fp32: at most 11 x 4 significant bits) = hi + lo with
-//              hi = bf16_RNE(s * q) and lo = s * q - hi, also exact in bf16 (at most 7 bits);
-//              two products per step, no per-group scaling on the vector ALUs.
+// The weights are dequantized to bf16: w = bf16_RNE(s * q), one product per weight.
 // Work split as for the Hessian: stream-K over (tile, group), partial tiles summed in a fixed
 // order by a second kernel.  All loads are the asm loads to LDS, so the explicit vmcnt waits
 // count exactly 6 loads per stage and wavefront (4 x rows, 1 codes, 1 scales or an empty load).
@@ -214,14 +211,12 @@ constexpr int kGTileElems = GT * GT;
 constexpr int kGMinChunk = 16;
 constexpr int kGMaxBlocks = 256;
 constexpr int kOpsPerStage = 6;
-template <int kMode>
-constexpr int kWStage = GT * 32 * 2 * (kMode == 0 ? 2 : 1);  // bf16 weights (hi, lo planes)
+constexpr int kWStage = GT * 32 * 2;  // 16 KB of bf16 weights
 constexpr int kOffC = GNB * kXStage;                // 64 KB
 constexpr int kOffS = kOffC + GNB * kCStage;        // 80 KB
 constexpr int kOffJunk = kOffS + 2 * kSBlock;       // 88 KB (target of the empty loads)
 constexpr int kOffW = kOffJunk + 1024;              // 89 KB
-template <int kMode>
-constexpr int kGemmLds = kOffW + 2 * kWStage<kMode>;  // 121 KB (dequantized) or 153 KB (exact)
+constexpr int kGemmLds = kOffW + 2 * kWStage;  // 121 KB
 
 // byte offset of 16-byte chunk c within LDS row r (64-byte rows): position c ^ f(r) with
 // f(r) = ((r >> 1) ^ (r >> 3)) & 3, so the 8 rows of a 128-byte bank phase and the 16 rows of a
@@ -251,14 +246,13 @@ __device__ __forceinline__ void gstore_block(void* __restrict__ y, int y_dtype, 
   }
 }
 
-template <int kMode>
-__global__ __launch_bounds__(256, 1) void gemm_mma_kernel(const uint16_t* __restrict__ x, int M,
+__global__ __launch_bounds__(256, 1) void gemm_dq_kernel(const uint16_t* __restrict__ x, int M,
                                                           const uint8_t* __restrict__ packed,
                                                           const uint16_t* __restrict__ s16, int N, int K,
                                                           void* __restrict__ y, int y_dtype, int tn_count,
                                                           int total, int chunk, int nblk, int per_xcd,
                                                           float* __restrict__ ws) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kGemmLds<kMode>];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kGemmLds];
   const int G = K >> 5;
   const int lb = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (lb >= nblk) return;
@@ -313,42 +307,34 @@ __global__ __launch_bounds__(256, 1) void gemm_mma_kernel(const uint16_t* __rest
       dma_x1(sl ? lds0 + kOffS + ((g >> 3) & 1) * kSBlock + wid * 1024 : lds0 + kOffJunk,
              buffer_rsrc(st + (g & ~7), sl ? sbytes - (g & ~7) * 2 : 0), svo);
     };
-    // this thread's column of group g as bf16 weights (hi plane, and lo plane in exact mode)
+    // this thread's column of group g as bf16 weights
     auto dequant = [&](int g) {
       const u32x4 c = *reinterpret_cast<const u32x4*>(lds + kOffC + (g % GNB) * kCStage + tid * 16);
       const float sc =
           f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(lds + kOffS + ((g >> 3) & 1) * kSBlock + tid * 16 + (g & 7) * 2));
-      uint8_t* wb = lds + kOffW + (g & 1) * kWStage<kMode>;
+      uint8_t* wb = lds + kOffW + (g & 1) * kWStage;
 #pragma unroll
       for (int ch = 0; ch < 4; ++ch) {  // 8 codes (k = 8 ch .. 8 ch + 7) per 16-byte chunk
         const uint32_t word = c[ch];
-        uint32_t hi[4], lo[4];
+        uint32_t hi[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const float w0 = static_cast<float>(static_cast<int>(word << (28 - 8 * p)) >> 28) * sc;
           const float w1 = static_cast<float>(static_cast<int>(word << (24 - 8 * p)) >> 28) * sc;
-          const bf16x2 h = __builtin_convertvector(f32x2{w0, w1}, bf16x2);
-          hi[p] = __builtin_bit_cast(uint32_t, h);
-          if constexpr (kMode == 0) {
-            const float r0 = w0 - __builtin_bit_cast(float, hi[p] << 16);
-            const float r1 = w1 - __builtin_bit_cast(float, hi[p] & 0xFFFF0000u);
-            lo[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
-          }
+          hi[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{w0, w1}, bf16x2));
         }
         *reinterpret_cast<u32x4*>(wb + tid * 64 + gswz(tid, ch)) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-        if constexpr (kMode == 0)
-          *reinterpret_cast<u32x4*>(wb + GT * 64 + tid * 64 + gswz(tid, ch)) = u32x4{lo[0], lo[1], lo[2], lo[3]};
       }
     };
 
     f32x16 acc[4][4];
-    // fragments of one 16-code step (x rows and weight columns, and the lo plane when exact)
+    // fragments of one 16-code step (x rows and weight columns)
     struct Frag {
-      bf16x8 a[4], b[4], bl[kMode == 0 ? 4 : 1];
+      bf16x8 a[4], b[4];
     };
     auto load = [&](int g, int kk, Frag& F) {
       const uint8_t* xb = lds + (g % GNB) * kXStage;
-      const uint8_t* wb = lds + kOffW + (g & 1) * kWStage<kMode>;
+      const uint8_t* wb = lds + kOffW + (g & 1) * kWStage;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = wm * 128 + 32 * i + fr;
@@ -358,8 +344,6 @@ __global__ __launch_bounds__(256, 1) void gemm_mma_kernel(const uint16_t* __rest
       for (int j = 0; j < 4; ++j) {
         const int n = wn * 128 + 32 * j + fr;
         F.b[j] = *reinterpret_cast<const bf16x8*>(wb + n * 64 + gswz(n, 2 * kk + fh));
-        if constexpr (kMode == 0)
-          F.bl[j] = *reinterpret_cast<const bf16x8*>(wb + GT * 64 + n * 64 + gswz(n, 2 * kk + fh));
       }
     };
     // the products of one step; `first` starts the sums from zero
@@ -373,20 +357,12 @@ __global__ __launch_bounds__(256, 1) void gemm_mma_kernel(const uint16_t* __rest
           else
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[i], F.b[j], acc[i][j], 0, 0, 0);
         }
-      if constexpr (kMode == 0) {
-        // the lo plane after all hi products: no back-to-back dependent products
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[i], F.bl[j], acc[i][j], 0, 0, 0);
-      }
     };
-    constexpr int kReads = kMode == 0 ? 12 : 8;
+    constexpr int kReads = 8;
     // products interleaved with the fragment reads of the next step (one read between products)
     // and with the vector work of the dequantization
     auto pattern = [&](auto valu) {
-      constexpr int kM = kMode == 0 ? 32 : 16;
+      constexpr int kM = 16;
       constexpr int kV = decltype(valu)::value;
 #pragma unroll
       for (int i = 0; i < kM; ++i) {
@@ -436,7 +412,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mma_kernel(const uint16_t* __rest
         mma(F0, std::false_type{});
       // (past the range the weights are formed from empty codes into a buffer nobody reads)
       dequant(g + 1);
-      pattern(std::integral_constant<int, kMode == 0 ? 3 : 6>{});
+      pattern(std::integral_constant<int, 6>{});
       mid_sync();
       load(g + 1, 0, F0);  // (past the range: a stale buffer, never used)
       mma(F1, std::false_type{});
@@ -501,8 +477,7 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(void* __restrict__ y, i
   gstore_block(y, y_dtype, M, N, tm * GT + wm * 128 + 32 * i, tn * GT + wn * 128 + 32 * j, v, lane);
 }
 
-template <int kMode>
-int launch_mma_pass(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16, int64_t N,
+int launch_dq_pass(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16, int64_t N,
                     int64_t K, void* y, int y_dtype, hipStream_t s) {
   const int64_t G = K / 32;
   const int64_t tm_count = (m + GT - 1) / GT, tn_count = (N + GT - 1) / GT;
@@ -519,7 +494,7 @@ int launch_mma_pass(const uint16_t* x, int64_t m, const uint8_t* packed, const u
   if (split && w4q_workspace_alloc(reinterpret_cast<void**>(&ws), (size_t)nblk * 2 * kGTileElems * sizeof(float), s) !=
                    W4Q_OK)
     return W4Q_EHIP;
-  hipLaunchKernelGGL(gemm_mma_kernel<kMode>, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(256), 0, s,
+  hipLaunchKernelGGL(gemm_dq_kernel, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(256), 0, s,
                      x, static_cast<int>(m), packed, s16, static_cast<int>(N), static_cast<int>(K), y, y_dtype,
                      static_cast<int>(tn_count), static_cast<int>(total), static_cast<int>(chunk),
                      static_cast<int>(nblk), static_cast<int>(per_xcd), ws);
@@ -565,21 +540,17 @@ static int launch_group(const uint16_t* x, int64_t m, const uint8_t* packed, con
 
 int w4q_launch_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
                     int64_t d_out, int64_t d_in, void* y, int y_dtype, int w_mode, hipStream_t s) {
-  // the matrix-core kernel needs 16-byte scale rows (d_in % 256 == 0) and 32-bit buffer offsets
+  if (w_mode == 0) return launch_group(x, m, packed, s16, d_out, d_in, y, y_dtype, s);
+  // the dequantizing kernel needs 16-byte scale rows (d_in % 256 == 0) and 32-bit buffer offsets
   // into the codes and scales; x is taken in passes of whole 256-row tiles that fit them too
-  const bool mma_ok = d_in % 256 == 0 && d_out * (d_in / 2) < 0x7FFFFFFF && 256 * d_in * 2 < 0x7FFFFFFF;
-  if (!mma_ok) {
-    if (w_mode != 0) return W4Q_EUNSUPPORTED;
-    return launch_group(x, m, packed, s16, d_out, d_in, y, y_dtype, s);
-  }
+  if (d_in % 256 != 0 || d_out * (d_in / 2) >= 0x7FFFFFFF || 256 * d_in * 2 >= 0x7FFFFFFF)
+    return W4Q_EUNSUPPORTED;
   const int64_t rows = (0x7FFFFFFF / (2 * d_in)) / GT * GT;
   const int64_t ob = y_dtype == 0 ? 4 : 2;
   for (int64_t r0 = 0; r0 < m; r0 += rows) {
     const int64_t mr = m - r0 < rows ? m - r0 : rows;
-    const uint16_t* xr = x + r0 * d_in;
-    void* yr = static_cast<uint8_t*>(y) + r0 * d_out * ob;
-    const int rc = w_mode == 0 ? launch_mma_pass<0>(xr, mr, packed, s16, d_out, d_in, yr, y_dtype, s)
-                               : launch_mma_pass<1>(xr, mr, packed, s16, d_out, d_in, yr, y_dtype, s);
+    const int rc = launch_dq_pass(x + r0 * d_in, mr, packed, s16, d_out, d_in,
+                                  static_cast<uint8_t*>(y) + r0 * d_out * ob, y_dtype, s);
     if (rc != W4Q_OK) return rc;
   }
   return W4Q_OK;

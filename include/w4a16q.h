@@ -16,10 +16,10 @@
  *   - Tensors are caller-owned DEVICE memory, row-major, contiguous.  Every call only
  *     enqueues work on `stream` (0 = the legacy default stream) and returns; the library never
  *     synchronises.  Results are valid once the caller has synchronised that stream.  The
- *     library allocates nothing except, for quant_hessian and w4a16_gemm_dq, partial-tile
- *     scratch taken from and returned to a library-owned
- *     stream-ordered memory pool on the same stream (at most 128 MB per call; the pool keeps
- *     its memory for later calls).
+ *     library allocates nothing except one 128 MB device scratch buffer per device (partial
+ *     tiles of quant_hessian and w4a16_gemm_dq), made by the first such call on the device and
+ *     kept until the process ends; the work of those two calls on one device is serialised on
+ *     it (a later call's stream waits for an event recorded after the earlier call's kernels).
  *   - Weights W are fp32 [d_out][d_in]; a group is 32 consecutive weights of one row along
  *     d_in, so d_in must be a positive multiple of 32 (W4Q_GROUP).  G = d_in / 32 groups/row.
  *   - Codes are integers in [-8, 7] (W4Q_QMIN..W4Q_QMAX).  code(w, D) is the code c that

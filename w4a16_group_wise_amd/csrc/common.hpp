@@ -153,9 +153,11 @@ __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u,
 
 }  // namespace w4q
 
-// Stream-ordered device scratch (partial tiles); return a w4q_status.
-int w4q_workspace_alloc(void** ptr, size_t bytes, hipStream_t s);
-int w4q_workspace_free(void* ptr, hipStream_t s);
+// Device scratch for partial tiles (one buffer per device, users serialised); return a
+// w4q_status.  Every successful acquire must be followed by a release on the same stream.
+constexpr size_t kWorkspaceBytes = size_t(256) * 2 * 256 * 256 * sizeof(float);  // 128 MB
+int w4q_workspace_acquire(void** ptr, size_t bytes, hipStream_t s);
+int w4q_workspace_release(hipStream_t s);
 
 // Launchers (one per source file); return a w4q_status.
 int w4q_launch_hessian(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accumulate,

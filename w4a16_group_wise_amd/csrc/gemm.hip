@@ -491,7 +491,7 @@ int launch_dq_pass(const uint16_t* x, int64_t m, const uint8_t* packed, const ui
   const bool split = nblk > 1 && chunk % G != 0;
   const int64_t per_xcd = (nblk + 7) / 8;
   float* ws = nullptr;
-  if (split && w4q_workspace_alloc(reinterpret_cast<void**>(&ws), (size_t)nblk * 2 * kGTileElems * sizeof(float), s) !=
+  if (split && w4q_workspace_acquire(reinterpret_cast<void**>(&ws), (size_t)nblk * 2 * kGTileElems * sizeof(float), s) !=
                    W4Q_OK)
     return W4Q_EHIP;
   hipLaunchKernelGGL(gemm_dq_kernel, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(256), 0, s,
@@ -506,7 +506,7 @@ int launch_dq_pass(const uint16_t* x, int64_t m, const uint8_t* packed, const ui
                          static_cast<int>(chunk), ws);
       rc = w4q_launch_status();
     }
-    if (w4q_workspace_free(ws, s) != W4Q_OK && rc == W4Q_OK) rc = W4Q_EHIP;
+    if (w4q_workspace_release(s) != W4Q_OK && rc == W4Q_OK) rc = W4Q_EHIP;
   }
   return rc;
 }

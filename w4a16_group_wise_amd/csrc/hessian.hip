@@ -335,17 +335,19 @@ int launch_pass(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accum
   const int64_t ns = (n_tok + BK - 1) / BK;
   const int64_t total = tiles * ns;
   if (total > 0x3FFFFFFF) return W4Q_EUNSUPPORTED;
-  int64_t nblk = (total + kMinChunk - 1) / kMinChunk;
-  if (nblk > kMaxBlocks) nblk = kMaxBlocks;
-  const int64_t chunk = (total + nblk - 1) / nblk;
-  nblk = (total + chunk - 1) / chunk;
+  // an even share of the stages for every compute unit, but at least kMinChunk stages (or a
+  // whole tile) per workgroup: short ranges cost more in partial tiles than they gain
+  const int64_t min_chunk = ns < kMinChunk ? ns : kMinChunk;
+  int64_t chunk = (total + kMaxBlocks - 1) / kMaxBlocks;
+  if (chunk < min_chunk) chunk = min_chunk;
+  const int64_t nblk = (total + chunk - 1) / chunk;
   const bool split = nblk > 1 && chunk % ns != 0;
   const int64_t per_xcd = (nblk + 7) / 8;
 
   float* ws = nullptr;
   if (split) {
     const size_t bytes = (size_t)nblk * 2 * kTileElems * sizeof(float);
-    if (w4q_workspace_alloc(reinterpret_cast<void**>(&ws), bytes, s) != W4Q_OK) return W4Q_EHIP;
+    if (w4q_workspace_acquire(reinterpret_cast<void**>(&ws), bytes, s) != W4Q_OK) return W4Q_EHIP;
   }
   hipLaunchKernelGGL(hessian_kernel, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(kThreads), 0, s, x,
                      static_cast<int>(n_tok), static_cast<int>(d), h, accumulate, static_cast<int>(nt),
@@ -359,7 +361,7 @@ int launch_pass(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accum
                          static_cast<int>(chunk), ws);
       rc = w4q_launch_status();
     }
-    if (w4q_workspace_free(ws, s) != W4Q_OK && rc == W4Q_OK) rc = W4Q_EHIP;
+    if (w4q_workspace_release(s) != W4Q_OK && rc == W4Q_OK) rc = W4Q_EHIP;
   }
   return rc;
 }

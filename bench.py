@@ -219,6 +219,77 @@ def traffic_for(workload, kernel):
     return k.get("bytes_per_launch")
 
 
+def decode_pass(dev, reps=3):
+    """The 36-layer decoder's decode pass: one M=1 W4A16 product per linear over all 252
+    linears (hidden 4096, intermediate 12288; 3.9 GB of packed codes and scales, far beyond the
+    256 MB Infinity Cache, so every pass streams the weights from HBM), on one stream and timed
+    as a whole with HIP events, three ways: one w4a16_gemm call per linear; w4a16_gemv_grouped
+    per decoder phase (q|k|v, o, gate|up, down: the order a decoder can issue them in); and
+    w4a16_gemv_grouped over all 252 linears.  Codes and scales are random: this measures
+    bandwidth only (parity of the same calls is tested separately)."""
+    import torch
+    import w4a16_group_wise_amd as w4q
+    from w4a16_group_wise_amd import synth
+
+    c = synth.CONFIGS[5]
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    mats, total = [], 0
+    for _layer in range(c.layers):
+        for lin in c.linears:
+            p = torch.randint(0, 256, (lin.d_out, lin.d_in // 2), dtype=torch.uint8, device=dev, generator=g)
+            sc = (torch.rand((lin.d_out, lin.d_in // 32), device=dev, generator=g) * 0.01 + 1e-3).half()
+            y = torch.empty((1, lin.d_out), dtype=torch.float32, device=dev)
+            mats.append((p, sc, lin.d_in, y))
+            total += lin.d_out * lin.d_in * 9 // 16 + 2 * lin.d_in + 4 * lin.d_out
+    xs = {d: torch.randn((1, d), device=dev, generator=g).to(torch.bfloat16) for d in {m[2] for m in mats}}
+
+    def single():
+        for p, sc, d, y in mats:
+            w4q.w4a16_gemm(xs[d], p, sc, out=y)
+
+    # the calls a decoder makes in dependency order: q|k|v and gate|up share an input, o and down
+    # follow their producers -> 4 grouped launches per layer
+    phases = []
+    per_layer = len(c.linears)
+    for l0 in range(0, len(mats), per_layer):
+        layer = mats[l0:l0 + per_layer]
+        for idx in ((0, 1, 2), (3,), (4, 5), (6,)):
+            sel = [layer[i] for i in idx]
+            phases.append(([xs[m[2]] for m in sel], [m[0] for m in sel], [m[1] for m in sel], [m[3] for m in sel]))
+
+    def grouped_layers():
+        for xg, pg, sg, yg in phases:
+            w4q.w4a16_gemv_grouped(xg, pg, sg, outs=yg)
+
+    everything = ([xs[m[2]] for m in mats], [m[0] for m in mats], [m[1] for m in mats], [m[3] for m in mats])
+
+    def grouped_all():
+        w4q.w4a16_gemv_grouped(*everything[:3], outs=everything[3])
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        return {"us_per_pass": round(us, 1), "GBps": round(total / (us * 1e-6) / 1e9, 1),
+                "frac_hbm": round(total / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
+    res = {"linears": len(mats), "bytes": total,
+           "one_call_per_linear": timed(single),
+           "grouped_per_layer_phase": timed(grouped_layers),
+           "grouped_whole_pass": timed(grouped_all)}
+    del mats, phases, everything
+    torch.cuda.empty_cache()
+    return res
+
+
 def run(args):
     import torch
 
@@ -283,6 +354,8 @@ def run(args):
         },
         "kernels": comps,
     }
+    if not args.no_decode:
+        out["components"]["decode_pass_36_layer"] = decode_pass(dev)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(step)
     print(json.dumps(out))
@@ -363,6 +436,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--pmc-copy", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the 36-layer decode-pass measurement")
     ap.add_argument("--copy-bytes", type=float, default=float(1 << 30))
     args = ap.parse_args()
     if args.pmc_summary:

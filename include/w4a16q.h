@@ -182,6 +182,32 @@ int w4a16_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16
 int w4a16_gemm_dq(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
                   int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t stream);
 
+/*
+ * w4a16_gemv_grouped -- many independent one-row W4A16 products (decode: one token through
+ * several linears, e.g. the q/k/v or gate/up projections that share an input, or a whole
+ * decoder's linears) in as few launches as possible: one launch per 32 problems.  Each problem
+ * is the product of w4a16_gemm with m = 1 and the same arithmetic (exact weights s16 * q, fp32
+ * accumulation); only the split of the row reduction over lanes may differ from the single
+ * call, so results agree with it to fp32 rounding, not bitwise.
+ *   problems   HOST array of n_problems descriptors; each x (bf16 [d_in], 16-B aligned),
+ *              packed ([d_out][d_in/2], 16-B aligned), scale_f16 ([d_out][d_in/32]) and
+ *              y ([d_out], fp32 or bf16 by y_dtype) is device memory as for w4a16_gemm.
+ *   n_problems >= 0 (0 enqueues nothing).  d_out <= 2^31 - 1 per problem.
+ * Problems may share inputs; outputs must not overlap.  Argument errors are reported before
+ * anything is enqueued.
+ */
+typedef struct w4q_gemv_problem {
+  const uint16_t* x;
+  const uint8_t* packed;
+  const uint16_t* scale_f16;
+  void* y;
+  int64_t d_out;
+  int64_t d_in;
+} w4q_gemv_problem;
+
+int w4a16_gemv_grouped(const w4q_gemv_problem* problems, int n_problems, int y_dtype,
+                       hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ def test_library_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"w4q_status_string", "w4q_version", "quant_hessian",
                           "quant_scale_search", "quant_pack", "lsq_fwd", "lsq_bwd", "w4a16_gemm",
-                          "w4a16_gemm_dq"}
+                          "w4a16_gemm_dq", "w4a16_gemv_grouped"}
     l = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(l, n), n
@@ -91,6 +91,20 @@ def test_pack_lsq_gemm_argument_errors():
     assert L.w4a16_gemm_dq(A, 0, A, A, 4, 256, A, 0, None) == w4q.W4Q_ESHAPE
     assert L.w4a16_gemm_dq(A + 2, 1, A, A, 4, 256, A, 0, None) == w4q.W4Q_EALIGN
     assert L.w4a16_gemm_dq(A, 1, A, A, 4, 64, A, 0, None) == w4q.W4Q_EUNSUPPORTED
+    from w4a16_group_wise_amd._lib import GemvProblem
+    probs = (GemvProblem * 2)(GemvProblem(A, A, A, A, 4, 64), GemvProblem(A, A, A, A, 4, 64))
+    pp = ctypes.cast(probs, ctypes.c_void_p)
+    assert L.w4a16_gemv_grouped(None, 0, 0, None) == w4q.W4Q_OK          # nothing to do
+    assert L.w4a16_gemv_grouped(None, 1, 0, None) == w4q.W4Q_EINVAL
+    assert L.w4a16_gemv_grouped(pp, -1, 0, None) == w4q.W4Q_EINVAL
+    assert L.w4a16_gemv_grouped(pp, 2, 3, None) == w4q.W4Q_EINVAL
+    probs[1].d_in = 65
+    assert L.w4a16_gemv_grouped(pp, 2, 0, None) == w4q.W4Q_ESHAPE
+    probs[1].d_in = 64
+    probs[1].x = A + 2
+    assert L.w4a16_gemv_grouped(pp, 2, 0, None) == w4q.W4Q_EALIGN
+    probs[1].x = 0
+    assert L.w4a16_gemv_grouped(pp, 2, 0, None) == w4q.W4Q_EINVAL
 
 
 def test_python_front_end_rejects_host_tensors():

@@ -316,3 +316,29 @@ def test_gemm_dq_config(dev, cfg, m, bf16_out):
         e_dq = np.max(np.abs(yg[:, cols] - yr) / ya)
         e_ex = np.max(np.abs(yg[:, cols] - ye) / ya)
         assert e_dq * 4 < e_ex, (e_dq, e_ex)
+
+
+# ------------------------------------------------------------ grouped one-row products (decode)
+@pytest.mark.parametrize("bf16_out", [False, True])
+def test_gemv_grouped(dev, bf16_out):
+    # the shapes of the 28-layer decoder's linears, a ragged one (3 groups per row: one lane per
+    # row) and enough problems for two launches
+    shapes = [(2048, 1024), (1024, 1024), (1024, 1024), (1024, 2048), (3072, 1024), (3072, 1024),
+              (1024, 3072), (77, 96)] * 5
+    xs, ps, ss, refs = [], [], [], []
+    for i, (d_out, d_in) in enumerate(shapes):
+        w = synth.weights(36, i, d_out, d_out, d_in, 0.01)
+        scale = (np.abs(w.reshape(d_out, -1, 32)).max(axis=2) / 7).astype(np.float32)
+        packed, s16 = oracle.pack(w, scale)
+        x = synth.calib_x(36, i, 0, 1, d_in, 1.0)
+        xs.append(dev_bf16(x, dev))
+        ps.append(torch.from_numpy(packed).to(dev))
+        ss.append(torch.from_numpy(s16.view(np.float16)).to(dev))
+        refs.append((x, packed, s16))
+    say("gemv grouped", len(shapes), "problems, bf16" if bf16_out else "fp32")
+    ys = w4q.w4a16_gemv_grouped(xs, ps, ss, out_dtype=torch.bfloat16 if bf16_out else torch.float32)
+    torch.cuda.synchronize()
+    for y, (x, packed, s16) in zip(ys, refs):
+        yg = bf16_bits_to_np(host_bf16_bits(y)) if bf16_out else y.cpu().numpy()
+        yr, ya = oracle.gemm_cols(x, packed, s16)
+        check_gemm(yg, yr, ya, bf16_out)

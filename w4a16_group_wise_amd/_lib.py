@@ -20,6 +20,12 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _INT = ctypes.c_int
 _F = ctypes.c_float
+class GemvProblem(ctypes.Structure):
+    """w4q_gemv_problem of w4a16q.h"""
+    _fields_ = [("x", ctypes.c_void_p), ("packed", ctypes.c_void_p), ("scale_f16", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("d_out", ctypes.c_int64), ("d_in", ctypes.c_int64)]
+
+
 SIGNATURES = {
     "w4q_status_string": (ctypes.c_char_p, [_INT]),
     "w4q_version": (_INT, []),
@@ -30,6 +36,7 @@ SIGNATURES = {
     "lsq_bwd": (_INT, [_P, _P, _P, _I64, _I64, _F, _P, _P, _P, _P]),
     "w4a16_gemm": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _INT, _P]),
     "w4a16_gemm_dq": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _INT, _P]),
+    "w4a16_gemv_grouped": (_INT, [_P, _INT, _INT, _P]),
 }
 
 

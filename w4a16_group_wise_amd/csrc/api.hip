@@ -117,4 +117,23 @@ int w4a16_gemm_dq(const uint16_t* x, int64_t m, const uint8_t* packed, const uin
   return w4q_launch_gemm(x, m, packed, scale_f16, d_out, d_in, y, y_dtype, 1, stream);
 }
 
+
+int w4a16_gemv_grouped(const w4q_gemv_problem* problems, int n_problems, int y_dtype,
+                       hipStream_t stream) {
+  if (n_problems < 0 || (y_dtype != 0 && y_dtype != 1)) return W4Q_EINVAL;
+  if (n_problems == 0) return W4Q_OK;
+  if (!problems) return W4Q_EINVAL;
+  for (int i = 0; i < n_problems; ++i) {
+    const w4q_gemv_problem& q = problems[i];
+    if (!q.x || !q.packed || !q.scale_f16 || !q.y) return W4Q_EINVAL;
+    const int rc = check_wshape(q.d_out, q.d_in);
+    if (rc != W4Q_OK) return rc;
+    if (q.d_out > 0x7FFFFFFF || q.d_in > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
+    if (!aligned(q.x, 16) || !aligned(q.packed, 16) || !aligned(q.scale_f16, 2) ||
+        !aligned(q.y, y_dtype == 0 ? 4 : 2))
+      return W4Q_EALIGN;
+  }
+  return w4q_launch_gemv_group(problems, n_problems, y_dtype, stream);
+}
+
 }  // extern "C"

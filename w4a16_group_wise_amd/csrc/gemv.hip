@@ -61,18 +61,17 @@ struct Chunk {
   u32x4 xv[MT][4];
 };
 
+// The product for the rows of workgroup `block` (of a grid covering d_out).
 template <int MT, int LPR, int RS>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(const uint16_t* __restrict__ x, int m_rows,
-                                                        const uint8_t* __restrict__ packed,
-                                                        const uint16_t* __restrict__ s16,
-                                                        int64_t d_out, int64_t d_in,
-                                                        void* __restrict__ y, int y_dtype,
-                                                        uint32_t mask) {
+__device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, int m_rows,
+                                          const uint8_t* __restrict__ packed,
+                                          const uint16_t* __restrict__ s16, int64_t d_out, int64_t d_in,
+                                          void* __restrict__ y, int y_dtype, uint32_t mask, int64_t block) {
   constexpr int RPS = 64 / LPR;  // rows per row-step
   const int lane = threadIdx.x & 63;
   const int sub = lane / LPR;
   const int j = lane % LPR;
-  const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + threadIdx.x / 64;
+  const int64_t wave = block * (kThreads / 64) + threadIdx.x / 64;
   const int64_t row0 = wave * (RPS * RS);
   if (row0 >= d_out) return;  // uniform per wavefront
   const int G = static_cast<int>(d_in / kGroup);
@@ -178,6 +177,45 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint16_t* __restri
   }
 }
 
+template <int MT, int LPR, int RS>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(const uint16_t* __restrict__ x, int m_rows,
+                                                        const uint8_t* __restrict__ packed,
+                                                        const uint16_t* __restrict__ s16,
+                                                        int64_t d_out, int64_t d_in,
+                                                        void* __restrict__ y, int y_dtype,
+                                                        uint32_t mask) {
+  gemv_body<MT, LPR, RS>(x, m_rows, packed, s16, d_out, d_in, y, y_dtype, mask, blockIdx.x);
+}
+
+// Many independent one-row products in one launch: workgroup b belongs to the problem p with
+// first[p] <= b < first[p + 1] and works on that problem's rows as its workgroup b - first[p].
+constexpr int kMaxGroup = 32;
+constexpr int64_t kGroupGrid = 256 * 12;  // workgroups of the grouped launch
+struct GroupArgs {
+  const uint16_t* x[kMaxGroup];
+  const uint8_t* packed[kMaxGroup];
+  const uint16_t* s16[kMaxGroup];
+  void* y[kMaxGroup];
+  int d_out[kMaxGroup];
+  int d_in[kMaxGroup];
+  int first[kMaxGroup + 1];
+  int n;
+  int y_dtype;
+  uint32_t mask;
+};
+
+// (the grid is a fixed number of workgroups that walk the row blocks with a stride, so the
+// wavefronts live long and keep loads in flight; problems are visited in order)
+template <int LPR, int RS>
+__global__ __launch_bounds__(kThreads) void gemv_group_kernel(const GroupArgs a) {
+  int p = 0;
+  for (int b = blockIdx.x; b < a.first[a.n]; b += gridDim.x) {
+    while (p + 1 < a.n && b >= a.first[p + 1]) ++p;  // uniform
+    gemv_body<1, LPR, RS>(a.x[p], 1, a.packed[p], a.s16[p], a.d_out[p], a.d_in[p], a.y[p], a.y_dtype,
+                          a.mask, b - a.first[p]);
+  }
+}
+
 template <int MT, int LPR>
 int launch_lpr(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
                int64_t d_out, int64_t d_in, void* y, int ydt, hipStream_t s) {
@@ -232,6 +270,51 @@ int w4q_launch_gemv(const uint16_t* x, int64_t m, const uint8_t* packed, const u
       rc = launch_mt<2>(xs, mt, packed, s16, d_out, d_in, ys, y_dtype, s);
     else
       rc = launch_mt<4>(xs, mt, packed, s16, d_out, d_in, ys, y_dtype, s);
+    if (rc != W4Q_OK) return rc;
+  }
+  return W4Q_OK;
+}
+
+// One launch for up to kMaxGroup one-row products (any d_out, d_in % 32 == 0).  Every problem
+// uses the lane split of the largest power of two (<= 64) that divides all their group counts
+// and four row-steps per wavefront.
+int w4q_launch_gemv_group(const w4q_gemv_problem* probs, int n, int y_dtype, hipStream_t s) {
+  for (int b = 0; b < n; b += kMaxGroup) {
+    const int cnt = n - b < kMaxGroup ? n - b : kMaxGroup;
+    GroupArgs a = {};
+    int lpr = 64;
+    for (int i = 0; i < cnt; ++i)
+      while ((probs[b + i].d_in / kGroup) % lpr != 0) lpr >>= 1;
+    const int rows_per_block = 4 * 4 * (64 / lpr);  // 4 wavefronts x 4 row-steps x rows per step
+    int64_t blocks = 0;
+    for (int i = 0; i < cnt; ++i) {
+      const w4q_gemv_problem& q = probs[b + i];
+      a.x[i] = q.x;
+      a.packed[i] = q.packed;
+      a.s16[i] = q.scale_f16;
+      a.y[i] = q.y;
+      a.d_out[i] = static_cast<int>(q.d_out);
+      a.d_in[i] = static_cast<int>(q.d_in);
+      a.first[i] = static_cast<int>(blocks);
+      blocks += (q.d_out + rows_per_block - 1) / rows_per_block;
+    }
+    if (blocks > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
+    a.first[cnt] = static_cast<int>(blocks);
+    a.n = cnt;
+    a.y_dtype = y_dtype;
+    a.mask = kMask;
+    // enough workgroups for every compute unit to hold a few, each walking many row blocks
+    const dim3 grid(static_cast<unsigned>(blocks < kGroupGrid ? blocks : kGroupGrid));
+    switch (lpr) {
+      case 64: hipLaunchKernelGGL((gemv_group_kernel<64, 4>), grid, dim3(kThreads), 0, s, a); break;
+      case 32: hipLaunchKernelGGL((gemv_group_kernel<32, 4>), grid, dim3(kThreads), 0, s, a); break;
+      case 16: hipLaunchKernelGGL((gemv_group_kernel<16, 4>), grid, dim3(kThreads), 0, s, a); break;
+      case 8: hipLaunchKernelGGL((gemv_group_kernel<8, 4>), grid, dim3(kThreads), 0, s, a); break;
+      case 4: hipLaunchKernelGGL((gemv_group_kernel<4, 4>), grid, dim3(kThreads), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((gemv_group_kernel<2, 4>), grid, dim3(kThreads), 0, s, a); break;
+      default: hipLaunchKernelGGL((gemv_group_kernel<1, 4>), grid, dim3(kThreads), 0, s, a); break;
+    }
+    const int rc = w4q_launch_status();
     if (rc != W4Q_OK) return rc;
   }
   return W4Q_OK;

@@ -7,6 +7,7 @@ from __future__ import annotations
 
 from typing import Optional, Tuple
 
+import ctypes
 import torch
 
 from ._lib import W4Q_GROUP, check, lib
@@ -153,3 +154,34 @@ def w4a16_gemm_dq(x: torch.Tensor, packed: torch.Tensor, scale_f16: torch.Tensor
     """As w4a16_gemm with each weight dequantized to bf16 (RNE of s16 * q) before the product;
     d_in must be a multiple of 256."""
     return _gemm("w4a16_gemm_dq", x, packed, scale_f16, out_dtype, out)
+
+
+def w4a16_gemv_grouped(xs, packeds, scales, out_dtype: torch.dtype = torch.float32, outs=None):
+    """One-row products y_i [1][d_out_i] = x_i [1][d_in_i] W_hat_i^T for several independent
+    problems in as few launches as possible (32 problems per launch)."""
+    from ._lib import GemvProblem
+    n = len(xs)
+    if not (len(packeds) == len(scales) == n) or (outs is not None and len(outs) != n):
+        raise ValueError("xs, packeds, scales (and outs) must have the same length")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    arr = (GemvProblem * max(n, 1))()
+    ys = []
+    for i in range(n):
+        x, p, s = xs[i], packeds[i], scales[i]
+        _need(x, "x", torch.bfloat16)
+        if x.dim() != 2 or x.shape[0] != 1:
+            raise ValueError("each x must be [1][d_in]")
+        d_in = x.shape[1]
+        _need(p, "packed", torch.uint8, device=x.device)
+        d_out = p.shape[0]
+        if p.dim() != 2 or p.shape[1] * 2 != d_in:
+            raise ValueError(f"packed must be [d_out][{d_in // 2}], got {tuple(p.shape)}")
+        _need(s, "scale_f16", torch.float16, (d_out, d_in // W4Q_GROUP), x.device)
+        y = _out(None if outs is None else outs[i], "y", (1, d_out), out_dtype, x.device)
+        ys.append(y)
+        arr[i] = GemvProblem(x.data_ptr(), p.data_ptr(), s.data_ptr(), y.data_ptr(), d_out, d_in)
+    stream = _stream(xs[0]) if n else 0
+    check("w4a16_gemv_grouped", lib().w4a16_gemv_grouped(ctypes.cast(arr, ctypes.c_void_p), n,
+                                                         0 if out_dtype == torch.float32 else 1, stream))
+    return ys

@@ -43,7 +43,7 @@ KERNELS = {
     "pack": ("pack_lsq.hip", ["pack_kernel"]),
     "lsq_fwd": ("pack_lsq.hip", ["lsq_fwd_kernel"]),
     "lsq_bwd": ("pack_lsq.hip", ["lsq_bwd_kernel"]),
-    "gemv_m1": ("gemv.hip", ["gemv_kernel<1,"]),
+    "gemv_m1": ("gemv.hip", ["gemv_stream_kernel"]),
     "gemv_m4": ("gemv.hip", []),   # same kernel as the M=16 passes: not separable by name
     "gemv_m16": ("gemv.hip", []),
     "gemm": ("gemm.hip", ["gemm_group_kernel"]),
@@ -225,8 +225,9 @@ def decode_pass(dev, reps=3):
     256 MB Infinity Cache, so every pass streams the weights from HBM), on one stream and timed
     as a whole with HIP events, three ways: one w4a16_gemm call per linear; w4a16_gemv_grouped
     per decoder phase (q|k|v, o, gate|up, down: the order a decoder can issue them in); and
-    w4a16_gemv_grouped over all 252 linears.  Codes and scales are random: this measures
-    bandwidth only (parity of the same calls is tested separately)."""
+    w4a16_gemv_grouped over all 252 linears (both grouped forms as prepared plans).  Codes and
+    scales are random: this measures bandwidth only (parity of the same calls is tested
+    separately)."""
     import torch
     import w4a16_group_wise_amd as w4q
     from w4a16_group_wise_amd import synth
@@ -249,23 +250,23 @@ def decode_pass(dev, reps=3):
             w4q.w4a16_gemm(xs[d], p, sc, out=y)
 
     # the calls a decoder makes in dependency order: q|k|v and gate|up share an input, o and down
-    # follow their producers -> 4 grouped launches per layer
-    phases = []
+    # follow their producers -> 4 grouped launches per layer.  A decoder reuses its weight, input
+    # and output buffers every step, so each grouped call is a plan marshalled once, here.
+    plans = []
     per_layer = len(c.linears)
     for l0 in range(0, len(mats), per_layer):
         layer = mats[l0:l0 + per_layer]
         for idx in ((0, 1, 2), (3,), (4, 5), (6,)):
             sel = [layer[i] for i in idx]
-            phases.append(([xs[m[2]] for m in sel], [m[0] for m in sel], [m[1] for m in sel], [m[3] for m in sel]))
+            plans.append(w4q.GemvGroupPlan([xs[m[2]] for m in sel], [m[0] for m in sel], [m[1] for m in sel],
+                                           outs=[m[3] for m in sel]))
 
     def grouped_layers():
-        for xg, pg, sg, yg in phases:
-            w4q.w4a16_gemv_grouped(xg, pg, sg, outs=yg)
+        for pl in plans:
+            pl()
 
-    everything = ([xs[m[2]] for m in mats], [m[0] for m in mats], [m[1] for m in mats], [m[3] for m in mats])
-
-    def grouped_all():
-        w4q.w4a16_gemv_grouped(*everything[:3], outs=everything[3])
+    whole = w4q.GemvGroupPlan([xs[m[2]] for m in mats], [m[0] for m in mats], [m[1] for m in mats],
+                              outs=[m[3] for m in mats])
 
     def timed(fn):
         fn()
@@ -284,8 +285,8 @@ def decode_pass(dev, reps=3):
     res = {"linears": len(mats), "bytes": total,
            "one_call_per_linear": timed(single),
            "grouped_per_layer_phase": timed(grouped_layers),
-           "grouped_whole_pass": timed(grouped_all)}
-    del mats, phases, everything
+           "grouped_whole_pass": timed(whole)}
+    del mats, plans, whole
     torch.cuda.empty_cache()
     return res
 

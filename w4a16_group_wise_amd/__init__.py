@@ -8,16 +8,16 @@ missing the calls raise.
 
 Entry points (same names as the C ABI):
   quant_hessian, quant_scale_search, quant_pack, lsq_fwd, lsq_bwd, w4a16_gemm, w4a16_gemm_dq,
-  w4a16_gemv_grouped
+  w4a16_gemv_grouped (and GemvGroupPlan, the same call with its problem table marshalled once)
 """
 from ._lib import (LIB_PATH, W4Q_EALIGN, W4Q_EHIP, W4Q_EINVAL, W4Q_ESHAPE, W4Q_EUNSUPPORTED,
                    W4Q_GROUP, W4Q_OK, W4QError, lib, status_string, version)
-from .ops import (lsq_bwd, lsq_fwd, quant_hessian, quant_pack, quant_scale_search, w4a16_gemm,
+from .ops import (GemvGroupPlan, lsq_bwd, lsq_fwd, quant_hessian, quant_pack, quant_scale_search, w4a16_gemm,
                   w4a16_gemm_dq, w4a16_gemv_grouped)
 
 __all__ = [
     "quant_hessian", "quant_scale_search", "quant_pack", "lsq_fwd", "lsq_bwd", "w4a16_gemm", "w4a16_gemm_dq",
-    "w4a16_gemv_grouped",
+    "w4a16_gemv_grouped", "GemvGroupPlan",
     "W4QError", "lib", "LIB_PATH", "status_string", "version", "W4Q_GROUP", "W4Q_OK",
     "W4Q_EINVAL", "W4Q_ESHAPE", "W4Q_EALIGN", "W4Q_EUNSUPPORTED", "W4Q_EHIP",
 ]

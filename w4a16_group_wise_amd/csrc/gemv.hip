@@ -19,6 +19,8 @@
 // and the factor 8 is removed (exactly) after the row reduction.  The bias is 24/|q| times the
 // signal, so the fp32 sum error stays near 2^-24 * 31 * sum|x| per group.  The next chunk's
 // codes, scales and activations are loaded while the current chunk is being reduced.
+#include <atomic>
+
 #include "common.hpp"
 
 namespace w4q {
@@ -187,10 +189,16 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint16_t* __restri
   gemv_body<MT, LPR, RS>(x, m_rows, packed, s16, d_out, d_in, y, y_dtype, mask, blockIdx.x);
 }
 
-// Many independent one-row products in one launch: workgroup b belongs to the problem p with
-// first[p] <= b < first[p + 1] and works on that problem's rows as its workgroup b - first[p].
-constexpr int kMaxGroup = 32;
-constexpr int64_t kGroupGrid = 256 * 12;  // workgroups of the grouped launch
+// ---- one activation row: a persistent stream over many problems --------------------------
+//
+// The rows of every problem are cut into items of RPS * RS rows (one wavefront's row-steps).
+// Each wavefront of a fixed, fully resident grid takes the items w, w + W, w + 2W, ... (W = all
+// wavefronts of the grid) and walks them as one stream of (item, chunk) units: the loads of the
+// next unit -- which may belong to the next item or the next problem -- are in flight while the
+// current unit is reduced, so the stream does not drain at item boundaries.  When the last chunk
+// of an item is reduced, its rows are finished (lane reduction, store) and the accumulators
+// restart.  Problems are numbered in the order given; first[p] is the first item of problem p.
+constexpr int kMaxGroup = 64;
 struct GroupArgs {
   const uint16_t* x[kMaxGroup];
   const uint8_t* packed[kMaxGroup];
@@ -201,18 +209,236 @@ struct GroupArgs {
   int first[kMaxGroup + 1];
   int n;
   int y_dtype;
-  uint32_t mask;
 };
 
-// (the grid is a fixed number of workgroups that walk the row blocks with a stride, so the
-// wavefronts live long and keep loads in flight; problems are visited in order)
+__device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(v))));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(v >> 32))));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// global (not generic) address space: loads through these are global_load with an SGPR base
+#define W4Q_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ W4Q_GLOBAL T* global_ptr(T* p) {
+  return (W4Q_GLOBAL T*)(p);
+}
+
+template <int RS>
+struct Src {  // where the loads of one item come from: wave-uniform bases, per-lane 32-bit offsets
+  const W4Q_GLOBAL uint8_t* pbase[RS];   // codes of each row (one row per row-step) or of the first
+  const W4Q_GLOBAL uint16_t* sbase[RS];  // scales likewise
+  const W4Q_GLOBAL uint16_t* xbase;      // activations
+  uint32_t poff[RS];                     // byte offset of (row, lane column) from pbase
+  uint32_t soff[RS];                     // element offset of (row, lane group) from sbase
+  int nchunk;
+};
+
+__device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_uint(float f) { return __builtin_bit_cast(uint32_t, f); }
+// lanes 32..63 of a trade places with lanes 0..31 of b
+__device__ __forceinline__ void swap_halves(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(as_uint(a), as_uint(b), false, false);
+  const uint32_t u0 = r[0], u1 = r[1];
+  a = as_float(u0);
+  b = as_float(u1);
+}
+// 16-lane rows 1 and 3 of a trade places with rows 0 and 2 of b
+__device__ __forceinline__ void swap_rows(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(as_uint(a), as_uint(b), false, false);
+  const uint32_t u0 = r[0], u1 = r[1];
+  a = as_float(u0);
+  b = as_float(u1);
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, false));
+}
+
+// The argument table is copied to LDS once per workgroup: the problem of an item is then one
+// ballot over first[] (the number of problems q >= 1 with first[q] <= item) and a few LDS reads.
 template <int LPR, int RS>
-__global__ __launch_bounds__(kThreads) void gemv_group_kernel(const GroupArgs a) {
-  int p = 0;
-  for (int b = blockIdx.x; b < a.first[a.n]; b += gridDim.x) {
-    while (p + 1 < a.n && b >= a.first[p + 1]) ++p;  // uniform
-    gemv_body<1, LPR, RS>(a.x[p], 1, a.packed[p], a.s16[p], a.d_out[p], a.d_in[p], a.y[p], a.y_dtype,
-                          a.mask, b - a.first[p]);
+__global__ __launch_bounds__(kThreads) void gemv_stream_kernel(const GroupArgs a) {
+  __shared__ GroupArgs t;
+  {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(&a);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(&t);
+    for (int i = threadIdx.x; i < static_cast<int>(sizeof(GroupArgs) / 4); i += kThreads) dst[i] = src[i];
+  }
+  __syncthreads();
+  constexpr int RPS = 64 / LPR;
+  constexpr int ROWS = RPS * RS;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane / LPR;
+  const int j = lane % LPR;
+  const int n = uniform_int(t.n);
+  const int64_t nitems = uniform_int(t.first[n]);
+  const int ydt = uniform_int(t.y_dtype);
+  const int fq = lane >= 1 && lane < n ? t.first[lane] : 0x7FFFFFFF;
+  const int64_t W = static_cast<int64_t>(uniform_int(static_cast<int>(gridDim.x))) * (kThreads / 64);
+  const int64_t w0 = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + uniform_int(threadIdx.x / 64);
+  if (w0 >= nitems) return;  // uniform per wavefront; no barrier follows
+  uint32_t c0 = kC0;
+  asm volatile("" : "+v"(c0));  // keep the constant in a VGPR so v_bitop3 can take it
+  const uint32_t mask = kMask;
+  const uint32_t xoff = static_cast<uint32_t>(j * kGroup);
+
+  auto problem_of = [&](int64_t item) { return __builtin_popcountll(__ballot(fq <= item)); };
+  auto setup = [&](int64_t item, Src<RS>& sr) {
+    const int p = problem_of(item);
+    const int64_t d_in = uniform_int(t.d_in[p]);
+    const int64_t d_out = uniform_int(t.d_out[p]);
+    const int G = static_cast<int>(d_in / kGroup);
+    const int64_t r0 = (item - uniform_int(t.first[p])) * ROWS;
+    const W4Q_GLOBAL uint8_t* pk = global_ptr(uniform_ptr(t.packed[p])) + r0 * (d_in / 2);
+    const W4Q_GLOBAL uint16_t* sk = global_ptr(uniform_ptr(t.s16[p])) + r0 * G;
+    sr.xbase = global_ptr(uniform_ptr(t.x[p]));
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs) {
+      if constexpr (RPS == 1) {
+        // one row per row-step: the row is wave-uniform, so it goes into the base
+        const int64_t r = r0 + rs < d_out ? rs : 0;  // rows past the end read the first row; never stored
+        sr.pbase[rs] = pk + r * (d_in / 2);
+        sr.sbase[rs] = sk + r * G;
+        sr.poff[rs] = static_cast<uint32_t>(j * 16);
+        sr.soff[rs] = static_cast<uint32_t>(j);
+      } else {
+        const int lr = rs * RPS + sub;
+        const uint32_t r = r0 + lr < d_out ? static_cast<uint32_t>(lr) : 0u;  // as above
+        sr.pbase[rs] = pk;
+        sr.sbase[rs] = sk;
+        sr.poff[rs] = r * static_cast<uint32_t>(d_in / 2) + static_cast<uint32_t>(j * 16);
+        sr.soff[rs] = r * static_cast<uint32_t>(G) + static_cast<uint32_t>(j);
+      }
+    }
+    sr.nchunk = G / LPR;
+  };
+  auto load = [&](const Src<RS>& sr, int c, Chunk<1, RS>& k) {
+    const W4Q_GLOBAL uint16_t* xb = sr.xbase + c * (LPR * kGroup);
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs) {
+      const W4Q_GLOBAL uint8_t* pb = sr.pbase[rs] + c * (LPR * 16);
+      const W4Q_GLOBAL uint16_t* sb = sr.sbase[rs] + c * LPR;
+      k.code[rs] = *reinterpret_cast<const W4Q_GLOBAL u32x4*>(pb + static_cast<uint64_t>(sr.poff[rs]));
+      k.sc[rs] = sb[static_cast<uint64_t>(sr.soff[rs])];
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      k.xv[0][b] = *reinterpret_cast<const W4Q_GLOBAL u32x4*>(xb + static_cast<uint64_t>(xoff + 8 * b));
+  };
+  float acc[RS];
+#pragma unroll
+  for (int rs = 0; rs < RS; ++rs) acc[rs] = 0.0f;
+  auto compute = [&](const Chunk<1, RS>& cur) {
+    uint32_t xp[16];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) pair_x(cur.xv[0][b], &xp[4 * b]);
+    float corr = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) corr = dot2(xp[i], kZero, corr);
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs) {
+      uint32_t cb[16];
+      const uint32_t words[4] = {cur.code[rs].x, cur.code[rs].y, cur.code[rs].z, cur.code[rs].w};
+#pragma unroll
+      for (int b = 0; b < 4; ++b) codes_bf16(words[b], mask, c0, &cb[4 * b]);
+      const float sc = f16_bits_to_f32(static_cast<uint16_t>(cur.sc[rs]));
+      float v = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v = dot2(xp[i], cb[i], v);
+      acc[rs] = __builtin_fmaf(sc, v - corr, acc[rs]);
+    }
+  };
+  auto store = [&](void* y, int64_t row, float v) {
+    if (ydt == 0)
+      global_ptr(reinterpret_cast<float*>(y))[row] = v;
+    else
+      global_ptr(reinterpret_cast<uint16_t*>(y))[row] = f32_to_bf16_bits(v);
+  };
+  // reduce the lane partials of each row of `item` (fixed order), undo the factor 8, store, and
+  // restart the accumulators
+  auto finish = [&](int64_t item) {
+    const int p = problem_of(item);
+    const int64_t d_out = uniform_int(t.d_out[p]);
+    void* y = uniform_ptr(t.y[p]);
+    const int64_t r0 = (item - uniform_int(t.first[p])) * ROWS;
+    if constexpr (LPR == 64 && RS == 4) {
+      // four rows, 64 lanes each: halves and 16-lane rows trade places so that two rows are
+      // summed per add; then 16-lane row k holds row k, reduced by rotations within the row
+      float a0 = acc[0], a1 = acc[1], a2 = acc[2], a3 = acc[3];
+      swap_halves(a0, a2);
+      swap_halves(a1, a3);
+      float s02 = a0 + a2;  // lanes 0..31: row 0, lanes 32..63: row 2
+      float s13 = a1 + a3;  // lanes 0..31: row 1, lanes 32..63: row 3
+      swap_rows(s02, s13);
+      float v = s02 + s13;  // 16-lane row k: row k
+      v += dpp<0x128>(v);   // row_ror:8
+      v += dpp<0x124>(v);   // row_ror:4
+      v += dpp<0x122>(v);   // row_ror:2
+      v += dpp<0x121>(v);   // row_ror:1
+      const int64_t row = r0 + (lane >> 4);
+      if ((lane & 15) == 0 && row < d_out) store(y, row, v * 0.125f);
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs) acc[rs] = 0.0f;
+    } else {
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs) {
+        float v = acc[rs];
+#pragma unroll
+        for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        acc[rs] = 0.0f;
+        const int64_t row = r0 + rs * RPS + sub;
+        if (j == 0 && row < d_out) store(y, row, v * 0.125f);
+      }
+    }
+  };
+
+  // load cursor (li, lc, ls) runs one unit ahead of the compute cursor (ci, cc, cn)
+  Src<RS> ls;
+  int64_t li = w0;
+  int lc = 0;
+  setup(li, ls);
+  int64_t ci = w0;
+  int cc = 0;
+  int cn = ls.nchunk;
+  auto advance_load = [&]() {
+    if (++lc == ls.nchunk) {
+      lc = 0;
+      li += W;
+      if (li < nitems) setup(li, ls);
+    }
+  };
+  // returns false when the wavefront's last unit has been reduced
+  auto advance_compute = [&]() {
+    if (++cc < cn) return true;
+    finish(ci);
+    ci += W;
+    if (ci >= nitems) return false;
+    cc = 0;
+    cn = uniform_int(t.d_in[problem_of(ci)]) / kGroup / LPR;
+    return true;
+  };
+  Chunk<1, RS> ca, cb;
+  load(ls, lc, ca);
+  advance_load();
+  while (true) {
+    if (li < nitems) {
+      load(ls, lc, cb);
+      advance_load();
+    }
+    asm volatile("" ::: "memory");
+    compute(ca);
+    if (!advance_compute()) break;
+    if (li < nitems) {
+      load(ls, lc, ca);
+      advance_load();
+    }
+    asm volatile("" ::: "memory");
+    compute(cb);
+    if (!advance_compute()) break;
   }
 }
 
@@ -255,7 +481,80 @@ int launch_mt(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_
 
 using namespace w4q;
 
-// Activation rows are processed four at a time; each slice of rows re-streams the weights.
+namespace w4q {
+namespace {
+
+// Workgroups of a kernel that fit on the device at once: compute units x resident workgroups per
+// compute unit, queried once per device and kernel.
+int resident_grid(const void* kernel, int slot) {
+  constexpr int kDevices = 64;
+  static std::atomic<int> cache[kDevices][8];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kDevices) {
+    const int v = cache[dev][slot].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kThreads, 0) != hipSuccess) return 0;
+  const int v = cus * (per > 0 ? per : 1);
+  if (dev < kDevices) cache[dev][slot].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+template <int LPR>
+int launch_stream(const GroupArgs& a, int64_t items, int slot, hipStream_t s) {
+  auto* k = &gemv_stream_kernel<LPR, 4>;
+  const int res = resident_grid(reinterpret_cast<const void*>(k), slot);
+  if (res <= 0) return W4Q_EHIP;
+  const int64_t need = (items + kThreads / 64 - 1) / (kThreads / 64);
+  const unsigned grid = static_cast<unsigned>(need < res ? need : res);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), 0, s, a);
+  return w4q_launch_status();
+}
+
+// problems [0, cnt) of `probs` in one launch: the lane split is the largest power of two
+// (<= 64) dividing every group count, and an item is 4 row-steps
+int launch_group_chunk(const w4q_gemv_problem* probs, int cnt, int y_dtype, hipStream_t s) {
+  GroupArgs a = {};
+  int lpr = 64;
+  for (int i = 0; i < cnt; ++i)
+    while ((probs[i].d_in / kGroup) % lpr != 0) lpr >>= 1;
+  const int rows_per_item = 4 * (64 / lpr);
+  int64_t items = 0;
+  for (int i = 0; i < cnt; ++i) {
+    const w4q_gemv_problem& q = probs[i];
+    a.x[i] = q.x;
+    a.packed[i] = q.packed;
+    a.s16[i] = q.scale_f16;
+    a.y[i] = q.y;
+    a.d_out[i] = static_cast<int>(q.d_out);
+    a.d_in[i] = static_cast<int>(q.d_in);
+    a.first[i] = static_cast<int>(items);
+    items += (q.d_out + rows_per_item - 1) / rows_per_item;
+    // lane offsets within an item are 32-bit
+    if (items > 0x7FFFFFFF || q.d_in / 2 * rows_per_item > 0xFFFFFFFFll) return W4Q_EUNSUPPORTED;
+  }
+  a.first[cnt] = static_cast<int>(items);
+  a.n = cnt;
+  a.y_dtype = y_dtype;
+  switch (lpr) {
+    case 64: return launch_stream<64>(a, items, 0, s);
+    case 32: return launch_stream<32>(a, items, 1, s);
+    case 16: return launch_stream<16>(a, items, 2, s);
+    case 8: return launch_stream<8>(a, items, 3, s);
+    case 4: return launch_stream<4>(a, items, 4, s);
+    case 2: return launch_stream<2>(a, items, 5, s);
+    default: return launch_stream<1>(a, items, 6, s);
+  }
+}
+
+}  // namespace
+}  // namespace w4q
+
+// Activation rows are processed four at a time; each slice of rows re-streams the weights.  A
+// single row takes the stream kernel (as a one-problem group) when its sizes fit 32 bits.
 int w4q_launch_gemv(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
                     int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t s) {
   const size_t ysz = y_dtype == 0 ? 4 : 2;
@@ -264,7 +563,10 @@ int w4q_launch_gemv(const uint16_t* x, int64_t m, const uint8_t* packed, const u
     const uint16_t* xs = x + m0 * d_in;
     void* ys = static_cast<char*>(y) + static_cast<size_t>(m0 * d_out) * ysz;
     int rc;
-    if (mt == 1)
+    if (mt == 1 && d_out <= 0x7FFFFFFF && d_in <= (1 << 24)) {
+      const w4q_gemv_problem one = {xs, packed, s16, ys, d_out, d_in};
+      rc = launch_group_chunk(&one, 1, y_dtype, s);
+    } else if (mt == 1)
       rc = launch_mt<1>(xs, mt, packed, s16, d_out, d_in, ys, y_dtype, s);
     else if (mt == 2)
       rc = launch_mt<2>(xs, mt, packed, s16, d_out, d_in, ys, y_dtype, s);
@@ -275,46 +577,10 @@ int w4q_launch_gemv(const uint16_t* x, int64_t m, const uint8_t* packed, const u
   return W4Q_OK;
 }
 
-// One launch for up to kMaxGroup one-row products (any d_out, d_in % 32 == 0).  Every problem
-// uses the lane split of the largest power of two (<= 64) that divides all their group counts
-// and four row-steps per wavefront.
+// One launch for up to kMaxGroup one-row products (any d_out, d_in % 32 == 0, both < 2^31).
 int w4q_launch_gemv_group(const w4q_gemv_problem* probs, int n, int y_dtype, hipStream_t s) {
   for (int b = 0; b < n; b += kMaxGroup) {
-    const int cnt = n - b < kMaxGroup ? n - b : kMaxGroup;
-    GroupArgs a = {};
-    int lpr = 64;
-    for (int i = 0; i < cnt; ++i)
-      while ((probs[b + i].d_in / kGroup) % lpr != 0) lpr >>= 1;
-    const int rows_per_block = 4 * 4 * (64 / lpr);  // 4 wavefronts x 4 row-steps x rows per step
-    int64_t blocks = 0;
-    for (int i = 0; i < cnt; ++i) {
-      const w4q_gemv_problem& q = probs[b + i];
-      a.x[i] = q.x;
-      a.packed[i] = q.packed;
-      a.s16[i] = q.scale_f16;
-      a.y[i] = q.y;
-      a.d_out[i] = static_cast<int>(q.d_out);
-      a.d_in[i] = static_cast<int>(q.d_in);
-      a.first[i] = static_cast<int>(blocks);
-      blocks += (q.d_out + rows_per_block - 1) / rows_per_block;
-    }
-    if (blocks > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
-    a.first[cnt] = static_cast<int>(blocks);
-    a.n = cnt;
-    a.y_dtype = y_dtype;
-    a.mask = kMask;
-    // enough workgroups for every compute unit to hold a few, each walking many row blocks
-    const dim3 grid(static_cast<unsigned>(blocks < kGroupGrid ? blocks : kGroupGrid));
-    switch (lpr) {
-      case 64: hipLaunchKernelGGL((gemv_group_kernel<64, 4>), grid, dim3(kThreads), 0, s, a); break;
-      case 32: hipLaunchKernelGGL((gemv_group_kernel<32, 4>), grid, dim3(kThreads), 0, s, a); break;
-      case 16: hipLaunchKernelGGL((gemv_group_kernel<16, 4>), grid, dim3(kThreads), 0, s, a); break;
-      case 8: hipLaunchKernelGGL((gemv_group_kernel<8, 4>), grid, dim3(kThreads), 0, s, a); break;
-      case 4: hipLaunchKernelGGL((gemv_group_kernel<4, 4>), grid, dim3(kThreads), 0, s, a); break;
-      case 2: hipLaunchKernelGGL((gemv_group_kernel<2, 4>), grid, dim3(kThreads), 0, s, a); break;
-      default: hipLaunchKernelGGL((gemv_group_kernel<1, 4>), grid, dim3(kThreads), 0, s, a); break;
-    }
-    const int rc = w4q_launch_status();
+    const int rc = launch_group_chunk(probs + b, n - b < kMaxGroup ? n - b : kMaxGroup, y_dtype, s);
     if (rc != W4Q_OK) return rc;
   }
   return W4Q_OK;

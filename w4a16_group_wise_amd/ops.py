@@ -156,32 +156,52 @@ def w4a16_gemm_dq(x: torch.Tensor, packed: torch.Tensor, scale_f16: torch.Tensor
     return _gemm("w4a16_gemm_dq", x, packed, scale_f16, out_dtype, out)
 
 
+class GemvGroupPlan:
+    """A prepared w4a16_gemv_grouped call: the problem table is checked and marshalled once, and
+    each call of the plan is a single library call (a decode step reuses the same weight, input
+    and output buffers, so the table does not change between steps).  The plan keeps references
+    to every tensor it points at."""
+
+    def __init__(self, xs, packeds, scales, out_dtype: torch.dtype = torch.float32, outs=None):
+        from ._lib import GemvProblem
+        n = len(xs)
+        if not (len(packeds) == len(scales) == n) or (outs is not None and len(outs) != n):
+            raise ValueError("xs, packeds, scales (and outs) must have the same length")
+        if out_dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("out_dtype must be float32 or bfloat16")
+        arr = (GemvProblem * max(n, 1))()
+        ys = []
+        for i in range(n):
+            x, p, s = xs[i], packeds[i], scales[i]
+            _need(x, "x", torch.bfloat16)
+            if x.dim() != 2 or x.shape[0] != 1:
+                raise ValueError("each x must be [1][d_in]")
+            d_in = x.shape[1]
+            _need(p, "packed", torch.uint8, device=x.device)
+            d_out = p.shape[0]
+            if p.dim() != 2 or p.shape[1] * 2 != d_in:
+                raise ValueError(f"packed must be [d_out][{d_in // 2}], got {tuple(p.shape)}")
+            _need(s, "scale_f16", torch.float16, (d_out, d_in // W4Q_GROUP), x.device)
+            y = _out(None if outs is None else outs[i], "y", (1, d_out), out_dtype, x.device)
+            ys.append(y)
+            arr[i] = GemvProblem(x.data_ptr(), p.data_ptr(), s.data_ptr(), y.data_ptr(), d_out, d_in)
+        self.outs = ys
+        self._keep = (list(xs), list(packeds), list(scales))
+        self._arr = arr
+        self._ptr = ctypes.cast(arr, ctypes.c_void_p)
+        self._n = n
+        self._ydt = 0 if out_dtype == torch.float32 else 1
+        self._device = xs[0].device if n else None
+        self._fn = lib().w4a16_gemv_grouped
+
+    def __call__(self):
+        stream = _stream(self._keep[0][0]) if self._n else 0
+        check("w4a16_gemv_grouped", self._fn(self._ptr, self._n, self._ydt, stream))
+        return self.outs
+
+
 def w4a16_gemv_grouped(xs, packeds, scales, out_dtype: torch.dtype = torch.float32, outs=None):
     """One-row products y_i [1][d_out_i] = x_i [1][d_in_i] W_hat_i^T for several independent
-    problems in as few launches as possible (32 problems per launch)."""
-    from ._lib import GemvProblem
-    n = len(xs)
-    if not (len(packeds) == len(scales) == n) or (outs is not None and len(outs) != n):
-        raise ValueError("xs, packeds, scales (and outs) must have the same length")
-    if out_dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError("out_dtype must be float32 or bfloat16")
-    arr = (GemvProblem * max(n, 1))()
-    ys = []
-    for i in range(n):
-        x, p, s = xs[i], packeds[i], scales[i]
-        _need(x, "x", torch.bfloat16)
-        if x.dim() != 2 or x.shape[0] != 1:
-            raise ValueError("each x must be [1][d_in]")
-        d_in = x.shape[1]
-        _need(p, "packed", torch.uint8, device=x.device)
-        d_out = p.shape[0]
-        if p.dim() != 2 or p.shape[1] * 2 != d_in:
-            raise ValueError(f"packed must be [d_out][{d_in // 2}], got {tuple(p.shape)}")
-        _need(s, "scale_f16", torch.float16, (d_out, d_in // W4Q_GROUP), x.device)
-        y = _out(None if outs is None else outs[i], "y", (1, d_out), out_dtype, x.device)
-        ys.append(y)
-        arr[i] = GemvProblem(x.data_ptr(), p.data_ptr(), s.data_ptr(), y.data_ptr(), d_out, d_in)
-    stream = _stream(xs[0]) if n else 0
-    check("w4a16_gemv_grouped", lib().w4a16_gemv_grouped(ctypes.cast(arr, ctypes.c_void_p), n,
-                                                         0 if out_dtype == torch.float32 else 1, stream))
-    return ys
+    problems in as few launches as possible (32 problems per launch).  For a call repeated on the
+    same buffers, GemvGroupPlan marshals the table once."""
+    return GemvGroupPlan(xs, packeds, scales, out_dtype, outs)()

@@ -224,8 +224,9 @@ def decode_pass(dev, reps=3):
     linears (hidden 4096, intermediate 12288; 3.9 GB of packed codes and scales, far beyond the
     256 MB Infinity Cache, so every pass streams the weights from HBM), on one stream and timed
     as a whole with HIP events, three ways: one w4a16_gemm call per linear; w4a16_gemv_grouped
-    per decoder phase (q|k|v, o, gate|up, down: the order a decoder can issue them in); and
-    w4a16_gemv_grouped over all 252 linears (both grouped forms as prepared plans).  Codes and
+    per decoder phase (q|k|v, o, gate|up, down: the order a decoder can issue them in), issued
+    from the host and replayed from a HIP graph; and w4a16_gemv_grouped over all 252 linears
+    (the grouped forms as prepared plans).  Codes and
     scales are random: this measures bandwidth only (parity of the same calls is tested
     separately)."""
     import torch
@@ -282,11 +283,19 @@ def decode_pass(dev, reps=3):
         return {"us_per_pass": round(us, 1), "GBps": round(total / (us * 1e-6) / 1e9, 1),
                 "frac_hbm": round(total / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
 
+    # the per-phase sequence captured once in a HIP graph and replayed (no host launch cost)
+    grouped_layers()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        grouped_layers()
+
     res = {"linears": len(mats), "bytes": total,
            "one_call_per_linear": timed(single),
            "grouped_per_layer_phase": timed(grouped_layers),
+           "grouped_per_layer_phase_graph": timed(graph.replay),
            "grouped_whole_pass": timed(whole)}
-    del mats, plans, whole
+    del mats, plans, whole, graph
     torch.cuda.empty_cache()
     return res
 

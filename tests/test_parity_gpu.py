@@ -322,9 +322,9 @@ def test_gemm_dq_config(dev, cfg, m, bf16_out):
 @pytest.mark.parametrize("bf16_out", [False, True])
 def test_gemv_grouped(dev, bf16_out):
     # the shapes of the 28-layer decoder's linears, a ragged one (3 groups per row: one lane per
-    # row) and enough problems for two launches
+    # row) and enough problems for two launches (64 per launch)
     shapes = [(2048, 1024), (1024, 1024), (1024, 1024), (1024, 2048), (3072, 1024), (3072, 1024),
-              (1024, 3072), (77, 96)] * 5
+              (1024, 3072), (77, 96)] * 9
     xs, ps, ss, refs = [], [], [], []
     for i, (d_out, d_in) in enumerate(shapes):
         w = synth.weights(36, i, d_out, d_out, d_in, 0.01)
@@ -342,3 +342,37 @@ def test_gemv_grouped(dev, bf16_out):
         yg = bf16_bits_to_np(host_bf16_bits(y)) if bf16_out else y.cpu().numpy()
         yr, ya = oracle.gemm_cols(x, packed, s16)
         check_gemm(yg, yr, ya, bf16_out)
+
+
+def test_gemv_plan_graph_replays(dev):
+    # a prepared grouped call captured in a HIP graph: every replay (with eager work on the same
+    # buffers between replays) gives the eager result, which matches the oracle
+    shapes = [(2048, 1024), (1024, 3072), (77, 96), (4096, 4096)]
+    xs, ps, ss, refs = [], [], [], []
+    for i, (d_out, d_in) in enumerate(shapes):
+        w = synth.weights(37, i, d_out, d_out, d_in, 0.01)
+        scale = (np.abs(w.reshape(d_out, -1, 32)).max(axis=2) / 7).astype(np.float32)
+        packed, s16 = oracle.pack(w, scale)
+        x = synth.calib_x(37, i, 0, 1, d_in, 1.0)
+        xs.append(dev_bf16(x, dev))
+        ps.append(torch.from_numpy(packed).to(dev))
+        ss.append(torch.from_numpy(s16.view(np.float16)).to(dev))
+        refs.append((x, packed, s16))
+    say("gemv plan in a graph", len(shapes), "problems")
+    plan = w4q.GemvGroupPlan(xs, ps, ss)
+    eager = [y.clone() for y in plan()]
+    torch.cuda.synchronize()
+    for y, (x, packed, s16) in zip(eager, refs):
+        yr, ya = oracle.gemm_cols(x, packed, s16)
+        check_gemm(y.cpu().numpy(), yr, ya, False)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan()
+    for rep in range(3):
+        for y in plan.outs:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for y, e in zip(plan.outs, eager):
+            assert torch.equal(y, e), f"replay {rep}"

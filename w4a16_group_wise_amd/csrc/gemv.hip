@@ -421,21 +421,20 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(const GroupArgs a
     cn = uniform_int(t.d_in[problem_of(ci)]) / kGroup / LPR;
     return true;
   };
+  // The loads are issued unconditionally: past the wavefront's last unit the cursor still holds
+  // the last item, so a spare (valid, unused) unit is loaded.  Every reduction then has the same
+  // number of loads after it, and the wait before it is a fixed count instead of a full drain.
   Chunk<1, RS> ca, cb;
   load(ls, lc, ca);
   advance_load();
   while (true) {
-    if (li < nitems) {
-      load(ls, lc, cb);
-      advance_load();
-    }
+    load(ls, lc, cb);
+    if (li < nitems) advance_load();
     asm volatile("" ::: "memory");
     compute(ca);
     if (!advance_compute()) break;
-    if (li < nitems) {
-      load(ls, lc, ca);
-      advance_load();
-    }
+    load(ls, lc, ca);
+    if (li < nitems) advance_load();
     asm volatile("" ::: "memory");
     compute(cb);
     if (!advance_compute()) break;

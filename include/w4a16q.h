@@ -185,16 +185,19 @@ int w4a16_gemm_dq(const uint16_t* x, int64_t m, const uint8_t* packed, const uin
 /*
  * w4a16_gemv_grouped -- many independent one-row W4A16 products (decode: one token through
  * several linears, e.g. the q/k/v or gate/up projections that share an input, or a whole
- * decoder's linears) in as few launches as possible: one launch per 32 problems.  Each problem
+ * decoder's linears) in as few launches as possible: one launch per 64 problems.  Each problem
  * is the product of w4a16_gemm with m = 1 and the same arithmetic (exact weights s16 * q, fp32
- * accumulation); only the split of the row reduction over lanes may differ from the single
- * call, so results agree with it to fp32 rounding, not bitwise.
+ * accumulation); only the split of the row reduction over lanes may differ from other launches,
+ * so results agree with them to fp32 rounding, not bitwise.
  *   problems   HOST array of n_problems descriptors; each x (bf16 [d_in], 16-B aligned),
  *              packed ([d_out][d_in/2], 16-B aligned), scale_f16 ([d_out][d_in/32]) and
  *              y ([d_out], fp32 or bf16 by y_dtype) is device memory as for w4a16_gemm.
- *   n_problems >= 0 (0 enqueues nothing).  d_out <= 2^31 - 1 per problem.
- * Problems may share inputs; outputs must not overlap.  Argument errors are reported before
- * anything is enqueued.
+ *   n_problems >= 0 (0 enqueues nothing).  Per problem d_out <= 2^31 - 1 and d_in <= 2^24
+ *              (W4Q_EUNSUPPORTED otherwise).
+ * Problems may share inputs; outputs must not overlap.  Argument errors (including
+ * W4Q_EUNSUPPORTED) are reported before anything is enqueued.  The problem table is read
+ * during the call only; the device memory it points to must stay valid until the stream
+ * reaches the launch.  No scratch memory is used.
  */
 typedef struct w4q_gemv_problem {
   const uint16_t* x;
@@ -207,6 +210,23 @@ typedef struct w4q_gemv_problem {
 
 int w4a16_gemv_grouped(const w4q_gemv_problem* problems, int n_problems, int y_dtype,
                        hipStream_t stream);
+
+/*
+ * Diagnostics (not part of the quantization path): measured peaks that rooflines are quoted
+ * against besides the chip's nominal ones.
+ *   w4q_probe_read       streams `bytes` (a multiple of 16, >= 16) of the 16-B aligned device
+ *                        buffer `buf` once with 16-byte loads, non-temporal if nontemporal is 1
+ *                        (0: ordinary loads, which also fill the caches); sink is device memory
+ *                        of W4Q_PROBE_SINK_WORDS words, written at most at a few words.
+ *   w4q_probe_mfma_bf16  runs `iters` (1 .. 2^24) rounds of 16 independent 32x32x16 bf16
+ *                        matrix-core products on every wavefront (one per SIMD); sink is device
+ *                        memory of W4Q_PROBE_SINK_WORDS floats; *flop (host, nullable) receives
+ *                        the flop count of the launch.
+ * Both enqueue one kernel on `stream` and return W4Q_EINVAL for bad arguments.
+ */
+#define W4Q_PROBE_SINK_WORDS 65536
+int w4q_probe_read(const void* buf, int64_t bytes, int nontemporal, uint32_t* sink, hipStream_t stream);
+int w4q_probe_mfma_bf16(float* sink, int64_t iters, double* flop, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,8 @@ def test_library_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"w4q_status_string", "w4q_version", "quant_hessian",
                           "quant_scale_search", "quant_pack", "lsq_fwd", "lsq_bwd", "w4a16_gemm",
-                          "w4a16_gemm_dq", "w4a16_gemv_grouped"}
+                          "w4a16_gemm_dq", "w4a16_gemv_grouped", "w4q_probe_read",
+                          "w4q_probe_mfma_bf16"}
     l = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(l, n), n
@@ -105,6 +106,21 @@ def test_pack_lsq_gemm_argument_errors():
     assert L.w4a16_gemv_grouped(pp, 2, 0, None) == w4q.W4Q_EALIGN
     probs[1].x = 0
     assert L.w4a16_gemv_grouped(pp, 2, 0, None) == w4q.W4Q_EINVAL
+    probs[1].x = A
+    probs[1].d_out, probs[1].d_in = 4, (1 << 24) + 32   # beyond the 32-bit lane offsets
+    assert L.w4a16_gemv_grouped(pp, 2, 0, None) == w4q.W4Q_EUNSUPPORTED
+
+
+def test_probe_argument_errors():
+    L = w4q.lib()
+    assert L.w4q_probe_read(None, 16, 1, A, None) == w4q.W4Q_EINVAL
+    assert L.w4q_probe_read(A, 24, 1, A, None) == w4q.W4Q_EINVAL
+    assert L.w4q_probe_read(A, 0, 1, A, None) == w4q.W4Q_EINVAL
+    assert L.w4q_probe_read(A, 16, 2, A, None) == w4q.W4Q_EINVAL
+    assert L.w4q_probe_read(A, 16, 1, None, None) == w4q.W4Q_EINVAL
+    assert L.w4q_probe_read(A + 8, 16, 1, A, None) == w4q.W4Q_EALIGN
+    assert L.w4q_probe_mfma_bf16(None, 10, None, None) == w4q.W4Q_EINVAL
+    assert L.w4q_probe_mfma_bf16(A, 0, None, None) == w4q.W4Q_EINVAL
 
 
 def test_python_front_end_rejects_host_tensors():

@@ -12,12 +12,12 @@ Entry points (same names as the C ABI):
 """
 from ._lib import (LIB_PATH, W4Q_EALIGN, W4Q_EHIP, W4Q_EINVAL, W4Q_ESHAPE, W4Q_EUNSUPPORTED,
                    W4Q_GROUP, W4Q_OK, W4QError, lib, status_string, version)
-from .ops import (GemvGroupPlan, lsq_bwd, lsq_fwd, quant_hessian, quant_pack, quant_scale_search, w4a16_gemm,
+from .ops import (GemvGroupPlan, lsq_bwd, probe_mfma_bf16, probe_read, lsq_fwd, quant_hessian, quant_pack, quant_scale_search, w4a16_gemm,
                   w4a16_gemm_dq, w4a16_gemv_grouped)
 
 __all__ = [
     "quant_hessian", "quant_scale_search", "quant_pack", "lsq_fwd", "lsq_bwd", "w4a16_gemm", "w4a16_gemm_dq",
-    "w4a16_gemv_grouped", "GemvGroupPlan",
+    "w4a16_gemv_grouped", "GemvGroupPlan", "probe_read", "probe_mfma_bf16",
     "W4QError", "lib", "LIB_PATH", "status_string", "version", "W4Q_GROUP", "W4Q_OK",
     "W4Q_EINVAL", "W4Q_ESHAPE", "W4Q_EALIGN", "W4Q_EUNSUPPORTED", "W4Q_EHIP",
 ]

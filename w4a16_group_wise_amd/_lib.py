@@ -37,7 +37,10 @@ SIGNATURES = {
     "w4a16_gemm": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _INT, _P]),
     "w4a16_gemm_dq": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _INT, _P]),
     "w4a16_gemv_grouped": (_INT, [_P, _INT, _INT, _P]),
+    "w4q_probe_read": (_INT, [_P, _I64, _INT, _P, _P]),
+    "w4q_probe_mfma_bf16": (_INT, [_P, _I64, _P, _P]),
 }
+W4Q_PROBE_SINK_WORDS = 65536
 
 
 class W4QError(RuntimeError):

@@ -128,11 +128,12 @@ int w4a16_gemv_grouped(const w4q_gemv_problem* problems, int n_problems, int y_d
     if (!q.x || !q.packed || !q.scale_f16 || !q.y) return W4Q_EINVAL;
     const int rc = check_wshape(q.d_out, q.d_in);
     if (rc != W4Q_OK) return rc;
-    if (q.d_out > 0x7FFFFFFF || q.d_in > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
+    if (q.d_out > 0x7FFFFFFF || q.d_in > (int64_t(1) << 24)) return W4Q_EUNSUPPORTED;
     if (!aligned(q.x, 16) || !aligned(q.packed, 16) || !aligned(q.scale_f16, 2) ||
         !aligned(q.y, y_dtype == 0 ? 4 : 2))
       return W4Q_EALIGN;
   }
+  if (!w4q_gemv_group_fits(problems, n_problems)) return W4Q_EUNSUPPORTED;
   return w4q_launch_gemv_group(problems, n_problems, y_dtype, stream);
 }
 

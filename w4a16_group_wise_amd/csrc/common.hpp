@@ -174,6 +174,7 @@ int w4q_launch_lsq_bwd(const float* w, const float* scale, const float* g, int64
                        hipStream_t s);
 int w4q_launch_gemv(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
                     int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t s);
+bool w4q_gemv_group_fits(const w4q_gemv_problem* probs, int n);
 int w4q_launch_gemv_group(const w4q_gemv_problem* probs, int n, int y_dtype, hipStream_t s);
 // w_mode: 0 = exact weights (s16 * q), 1 = weights dequantized to bf16 (RNE of s16 * q)
 int w4q_launch_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,

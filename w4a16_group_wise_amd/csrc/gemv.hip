@@ -322,8 +322,10 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(const GroupArgs a
     for (int rs = 0; rs < RS; ++rs) {
       const W4Q_GLOBAL uint8_t* pb = sr.pbase[rs] + c * (LPR * 16);
       const W4Q_GLOBAL uint16_t* sb = sr.sbase[rs] + c * LPR;
-      k.code[rs] = *reinterpret_cast<const W4Q_GLOBAL u32x4*>(pb + static_cast<uint64_t>(sr.poff[rs]));
-      k.sc[rs] = sb[static_cast<uint64_t>(sr.soff[rs])];
+      // codes and scales are read once: non-temporal loads keep them from displacing cached data
+      k.code[rs] = __builtin_nontemporal_load(
+          reinterpret_cast<const W4Q_GLOBAL u32x4*>(pb + static_cast<uint64_t>(sr.poff[rs])));
+      k.sc[rs] = __builtin_nontemporal_load(sb + static_cast<uint64_t>(sr.soff[rs]));
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b)
@@ -513,13 +515,26 @@ int launch_stream(const GroupArgs& a, int64_t items, int slot, hipStream_t s) {
   return w4q_launch_status();
 }
 
-// problems [0, cnt) of `probs` in one launch: the lane split is the largest power of two
-// (<= 64) dividing every group count, and an item is 4 row-steps
-int launch_group_chunk(const w4q_gemv_problem* probs, int cnt, int y_dtype, hipStream_t s) {
-  GroupArgs a = {};
+// lane split of a launch: the largest power of two (<= 64) dividing every group count
+int chunk_lpr(const w4q_gemv_problem* probs, int cnt) {
   int lpr = 64;
   for (int i = 0; i < cnt; ++i)
     while ((probs[i].d_in / kGroup) % lpr != 0) lpr >>= 1;
+  return lpr;
+}
+
+// items (4 row-steps of 64 / lpr rows) of problems [0, cnt)
+int64_t chunk_items(const w4q_gemv_problem* probs, int cnt, int lpr) {
+  const int rows_per_item = 4 * (64 / lpr);
+  int64_t items = 0;
+  for (int i = 0; i < cnt; ++i) items += (probs[i].d_out + rows_per_item - 1) / rows_per_item;
+  return items;
+}
+
+// problems [0, cnt) of `probs` in one launch (sizes checked by w4q_gemv_group_fits)
+int launch_group_chunk(const w4q_gemv_problem* probs, int cnt, int y_dtype, hipStream_t s) {
+  GroupArgs a = {};
+  const int lpr = chunk_lpr(probs, cnt);
   const int rows_per_item = 4 * (64 / lpr);
   int64_t items = 0;
   for (int i = 0; i < cnt; ++i) {
@@ -532,8 +547,6 @@ int launch_group_chunk(const w4q_gemv_problem* probs, int cnt, int y_dtype, hipS
     a.d_in[i] = static_cast<int>(q.d_in);
     a.first[i] = static_cast<int>(items);
     items += (q.d_out + rows_per_item - 1) / rows_per_item;
-    // lane offsets within an item are 32-bit
-    if (items > 0x7FFFFFFF || q.d_in / 2 * rows_per_item > 0xFFFFFFFFll) return W4Q_EUNSUPPORTED;
   }
   a.first[cnt] = static_cast<int>(items);
   a.n = cnt;
@@ -562,8 +575,8 @@ int w4q_launch_gemv(const uint16_t* x, int64_t m, const uint8_t* packed, const u
     const uint16_t* xs = x + m0 * d_in;
     void* ys = static_cast<char*>(y) + static_cast<size_t>(m0 * d_out) * ysz;
     int rc;
-    if (mt == 1 && d_out <= 0x7FFFFFFF && d_in <= (1 << 24)) {
-      const w4q_gemv_problem one = {xs, packed, s16, ys, d_out, d_in};
+    const w4q_gemv_problem one = {xs, packed, s16, ys, d_out, d_in};
+    if (mt == 1 && d_out <= 0x7FFFFFFF && d_in <= (1 << 24) && w4q_gemv_group_fits(&one, 1)) {
       rc = launch_group_chunk(&one, 1, y_dtype, s);
     } else if (mt == 1)
       rc = launch_mt<1>(xs, mt, packed, s16, d_out, d_in, ys, y_dtype, s);
@@ -576,7 +589,20 @@ int w4q_launch_gemv(const uint16_t* x, int64_t m, const uint8_t* packed, const u
   return W4Q_OK;
 }
 
-// One launch for up to kMaxGroup one-row products (any d_out, d_in % 32 == 0, both < 2^31).
+// Every launch's item count fits an int and every item's lane offsets fit 32 bits
+// (rows_per_item * d_in / 2 < 2^32, which d_in <= 2^24 guarantees).
+bool w4q_gemv_group_fits(const w4q_gemv_problem* probs, int n) {
+  for (int b = 0; b < n; b += kMaxGroup) {
+    const int cnt = n - b < kMaxGroup ? n - b : kMaxGroup;
+    const int lpr = chunk_lpr(probs + b, cnt);
+    for (int i = 0; i < cnt; ++i)
+      if (probs[b + i].d_in / 2 * (4 * (64 / lpr)) > 0xFFFFFFFFll) return false;
+    if (chunk_items(probs + b, cnt, lpr) > 0x7FFFFFFF) return false;
+  }
+  return true;
+}
+
+// One launch for up to kMaxGroup one-row products (any d_out, d_in % 32 == 0).
 int w4q_launch_gemv_group(const w4q_gemv_problem* probs, int n, int y_dtype, hipStream_t s) {
   for (int b = 0; b < n; b += kMaxGroup) {
     const int rc = launch_group_chunk(probs + b, n - b < kMaxGroup ? n - b : kMaxGroup, y_dtype, s);

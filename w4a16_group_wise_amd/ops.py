@@ -205,3 +205,27 @@ def w4a16_gemv_grouped(xs, packeds, scales, out_dtype: torch.dtype = torch.float
     problems in as few launches as possible (32 problems per launch).  For a call repeated on the
     same buffers, GemvGroupPlan marshals the table once."""
     return GemvGroupPlan(xs, packeds, scales, out_dtype, outs)()
+
+
+def probe_read(buf: torch.Tensor, nontemporal: bool = True, sink: Optional[torch.Tensor] = None) -> None:
+    """Enqueue one streaming read of the whole device tensor `buf` (diagnostic: measured HBM
+    peak with non-temporal loads; with ordinary loads it also refills the caches).  Time it with
+    events on the current stream."""
+    from ._lib import W4Q_PROBE_SINK_WORDS
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    sink = _out(sink, "sink", (W4Q_PROBE_SINK_WORDS,), torch.int32, buf.device)
+    check("w4q_probe_read", lib().w4q_probe_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                                 1 if nontemporal else 0, sink.data_ptr(), _stream(buf)))
+
+
+def probe_mfma_bf16(iters: int, device, sink: Optional[torch.Tensor] = None) -> float:
+    """Enqueue one launch of independent bf16 matrix-core products (diagnostic: measured MFMA
+    peak); returns its flop count."""
+    from ._lib import W4Q_PROBE_SINK_WORDS
+    device = torch.device(device)
+    sink = _out(sink, "sink", (W4Q_PROBE_SINK_WORDS,), torch.float32, device)
+    flop = ctypes.c_double(0.0)
+    check("w4q_probe_mfma_bf16", lib().w4q_probe_mfma_bf16(sink.data_ptr(), int(iters), ctypes.byref(flop),
+                                                           torch.cuda.current_stream(device).cuda_stream))
+    return flop.value

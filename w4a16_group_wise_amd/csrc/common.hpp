@@ -142,6 +142,20 @@ __device__ __forceinline__ void dma_x4(uint32_t lds, v4i32 rs, const int (&vo)[4
         [v0] "v"(vo[0]), [v1] "v"(vo[1]), [v2] "v"(vo[2]), [v3] "v"(vo[3])
       : "memory", "scc");
 }
+__device__ __forceinline__ void dma_x2(uint32_t lds, v4i32 rs, int v0, int v1) {
+  const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[m0]\n\t"
+      "buffer_load_dwordx4 %[v0], %[rs], 0 offen lds\n\t"
+      "s_mov_b32 m0, %[m1]\n\t"
+      "buffer_load_dwordx4 %[v1], %[rs], 0 offen lds\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [m0] "s"(l0), [m1] "s"(l0 + 1024), [rs] "s"(rs), [v0] "v"(v0), [v1] "v"(v1)
+      : "memory", "scc");
+}
 __device__ __forceinline__ void dma_x8(uint32_t lds, v4i32 rs, const int (&vo)[8]) {
   const int lo[4] = {vo[0], vo[1], vo[2], vo[3]};
   const int hi[4] = {vo[4], vo[5], vo[6], vo[7]};

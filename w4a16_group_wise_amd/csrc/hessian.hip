@@ -15,8 +15,11 @@
 // workgroups is finished by a second kernel that adds the partial tiles in the fixed order of
 // their token ranges: the result does not depend on scheduling.
 //
-// Per workgroup: 4 wavefronts of 128x128 (4x4 v_mfma_f32_32x32x16_bf16 blocks, accumulators in
-// AGPRs), 64 tokens per stage, two LDS stage buffers.  X is row-major [token][feature], the
+// Per workgroup: 8 wavefronts (two per SIMD) of 128x64 (4x2 v_mfma_f32_32x32x16_bf16 blocks),
+// 32 tokens per stage, four LDS stage buffers.  Two wavefronts per SIMD because the transposing
+// LDS reads below deliver almost twice the bytes per clock with two wavefronts per SIMD as with
+// one (about 180 vs 100 B/clk per compute unit measured on gfx950), and because vector and LDS
+// work of one wavefront only overlaps the matrix cores when it comes from another wavefront.  X is row-major [token][feature], the
 // layout in which it is copied straight from memory into LDS by buffer loads to LDS (16 bytes
 // per lane, no registers); the MFMA fragments, which want 8 consecutive tokens of one feature per
 // lane, are then read with the transposing LDS read ds_read_b64_tr_b16.  Buffer loads past the
@@ -28,15 +31,15 @@
 namespace w4q {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int BT = 256;                // tile edge in features
 constexpr int BK = 32;                 // tokens per stage
 constexpr int NBUF = 4;                // LDS stage buffers: loads run NBUF - 1 stages ahead
 constexpr int kTileElems = BT * BT;    // floats per partial tile
 constexpr int kMinChunk = 16;          // stages per workgroup before more workgroups are used
-constexpr int kMaxBlocks = 256;        // one workgroup per compute unit (256 AGPR accumulators)
+constexpr int kMaxBlocks = 256;        // one workgroup per compute unit
 constexpr int kStageBytes = 2 * BK * BT * 2;    // I and J panels, bf16: 32 KB
-constexpr int kLoadsPerWave = kStageBytes / 1024 / 4;  // 1 KB per load instruction: 8
+constexpr int kLoadsPerWave = kStageBytes / 1024 / 8;  // 1 KB per load instruction: 4
 
 // LDS stage layout: panel p (I = 0, J = 1), token t, 16-byte chunk position cp (32 per token row
 // of 256 features).  Chunk c (features 8c .. 8c + 7) of token t sits at position c ^ swz(t % 4).
@@ -93,14 +96,14 @@ __device__ __forceinline__ void store_block(float* __restrict__ h, int d, int ro
 }
 
 // partial-tile layout (per workgroup slot): wave w, block (i, j), register quad a, lane l ->
-// float4 at ((w * 16 + i * 4 + j) * 4 + a) * 256 + 4 l; each store instruction writes 1 KB.
+// float4 at ((w * 8 + i * 2 + j) * 4 + a) * 256 + 4 l; each store instruction writes 1 KB.
 __device__ __forceinline__ int64_t part_off(int w, int i, int j, int a, int lane) {
-  return (int64_t)(((w * 16 + i * 4 + j) * 4 + a) * 256 + 4 * lane);
+  return (int64_t)(((w * 8 + i * 2 + j) * 4 + a) * 256 + 4 * lane);
 }
 
 #define W4Q_LDS4(p) ((__attribute__((address_space(3))) v4i16*)(p))
 
-static_assert(kLoadsPerWave == 8, "one dma_x8 per stage and wave");
+static_assert(kLoadsPerWave == 4, "one dma_x4 per stage and wave");
 
 __global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __restrict__ x, int n_tok, int d,
                                                               float* __restrict__ h, int accumulate, int nt,
@@ -118,15 +121,15 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid >> 2, wn = wid & 3;
 
-  // load role: load q (0..7) of wave w fills the 1 KB of LDS at slot (8 w + q) * 64: panel w / 2,
-  // tokens 16 (w % 2) + 2 q + lane / 32, chunk position lane % 32
-  const int ld_panel = wid >> 1;
+  // load role: load q (0..3) of wave w fills the 1 KB of LDS at (4 w + q) KB: panel w / 4,
+  // tokens 8 (w % 4) + 2 q + lane / 32, chunk position lane % 32
+  const int ld_panel = wid >> 2;
   int ld_tok[kLoadsPerWave], ld_chunk[kLoadsPerWave];
 #pragma unroll
   for (int q = 0; q < kLoadsPerWave; ++q) {
-    ld_tok[q] = 16 * (wid & 1) + 2 * q + (lane >> 5);
+    ld_tok[q] = 8 * (wid & 3) + 2 * q + (lane >> 5);
     ld_chunk[q] = (lane & 31) ^ swz(ld_tok[q]);
   }
   const uint32_t lds_base = lds_addr(Ls);
@@ -169,8 +172,8 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __
       // memory) for stages outside this range
       const int bytes = (s < s1 && ld_on) ? (n_tok - static_cast<int>(tok0)) * d * 2 : 0;
       const v4i32 rs = buffer_rsrc(x + tok0 * d, bytes);
-      const uint32_t m0 = lds_base + static_cast<uint32_t>(((s - s0) % NBUF) * kStageBytes + 8 * 1024 * wid);
-      dma_x8(m0, rs, voff);
+      const uint32_t m0 = lds_base + static_cast<uint32_t>(((s - s0) % NBUF) * kStageBytes + 4 * 1024 * wid);
+      dma_x4(m0, rs, voff);
     };
     // wait for this wave's loads of the stage about to be used (the NBUF - 2 younger stages stay
     // in flight), then a barrier: the stage is in LDS for all wavefronts, and every wavefront is
@@ -182,11 +185,11 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __
       asm volatile("" ::: "memory");
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][2];
     const int bpanel = diag ? 0 : 1;  // B fragments come from the I panel on diagonal tiles
     // fragments of one 16-token step of stage s (transposing reads)
     struct Frag {
-      bf16x8 a[4], b[4];
+      bf16x8 a[4], b[2];
     };
     auto load = [&](int s, int kk, Frag& F) {
       const char* Lb = reinterpret_cast<const char*>(Ls) + ((s - s0) % NBUF) * kStageBytes + kk * 16 * 512;
@@ -198,21 +201,22 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __
         F.a[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const char* p = Lb + rd_off(bpanel, 4 * wn + j);
+      for (int j = 0; j < 2; ++j) {
+        const char* p = Lb + rd_off(bpanel, 2 * wn + j);
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(W4Q_LDS4(p));
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(W4Q_LDS4(p + 4 * 512));
         F.b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     };
-    // products of rows i0 .. i1 - 1 of the 4x4 blocks; `first` starts the sums from zero.  (On a
-    // diagonal tile the (wm = 1, wn = 0) quadrant, the mirror of (0, 1), is computed as well,
-    // which keeps the loop free of branches around the accumulators, but never stored.)
+    // products of rows i0 .. i1 - 1 of the 4x2 blocks; `first` starts the sums from zero.  (On a
+    // diagonal tile the wavefronts below the diagonal, wm = 1 with wn < 2, compute the mirror
+    // of others' blocks as well, which keeps the loop free of branches around the
+    // accumulators, but never store it.)
     auto mma = [&](const Frag& F, int i0, int i1, auto first) {
 #pragma unroll
       for (int i = i0; i < i1; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 2; ++j) {
           if constexpr (decltype(first)::value) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[i], F.b[j], zero16, 0, 0, 0);
           } else {
@@ -260,15 +264,15 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 
-    const bool work = !(diag && wm == 1 && wn == 0);
+    const bool work = !(diag && wm == 1 && wn < 2);
     if (work) {
       if (s0 == 0 && s1 == ns) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+          for (int j = 0; j < 2; ++j) {
             const int row0 = ti * BT + wm * 128 + 32 * i;
-            const int col0 = tj * BT + wn * 128 + 32 * j;
+            const int col0 = tj * BT + wn * 64 + 32 * j;
             if (row0 <= col0 && row0 < d) store_block(h, d, row0, col0, acc[i][j], accumulate, lane);
             asm volatile("" ::: "memory");  // one block at a time (bounds the live registers)
           }
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
               *reinterpret_cast<f32x4*>(slot + part_off(wid, i, j, a, lane)) =
@@ -293,11 +297,11 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_kernel(const uint16_t* __
 
 // Tiles whose stages were spread over several workgroups: sum the partial tiles in the order of
 // their token ranges (workgroup index), then store as the main kernel does.  One workgroup per
-// (tile, 32x32 block row i, block column j) of every wavefront's quadrant.
+// (tile, 32x32 block row i, block column j) of every wavefront's 128x64 part.
 __global__ __launch_bounds__(kThreads) void hessian_fixup_kernel(float* __restrict__ h, int d, int accumulate, int nt,
                                                                  int ns, int chunk, const float* __restrict__ ws) {
-  const int t = blockIdx.x >> 4;
-  const int i = (blockIdx.x >> 2) & 3, j = blockIdx.x & 3;
+  const int t = blockIdx.x >> 3;
+  const int i = (blockIdx.x >> 1) & 3, j = blockIdx.x & 1;
   const int first = static_cast<int>((int64_t)t * ns / chunk);
   const int last = static_cast<int>(((int64_t)t * ns + ns - 1) / chunk);
   if (first == last) return;  // written whole by the main kernel
@@ -306,10 +310,10 @@ __global__ __launch_bounds__(kThreads) void hessian_fixup_kernel(float* __restri
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wid >> 1, wn = wid & 1;
-  if (ti == tj && wm == 1 && wn == 0) return;
+  const int wm = wid >> 2, wn = wid & 3;
+  if (ti == tj && wm == 1 && wn < 2) return;
   const int row0 = ti * BT + wm * 128 + 32 * i;
-  const int col0 = tj * BT + wn * 128 + 32 * j;
+  const int col0 = tj * BT + wn * 64 + 32 * j;
   if (row0 > col0 || row0 >= d || col0 >= d) return;
   f32x16 v;
 #pragma unroll
@@ -356,7 +360,7 @@ int launch_pass(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accum
   int rc = w4q_launch_status();
   if (split) {
     if (rc == W4Q_OK) {
-      hipLaunchKernelGGL(hessian_fixup_kernel, dim3(static_cast<unsigned>(16 * tiles)), dim3(kThreads), 0, s, h,
+      hipLaunchKernelGGL(hessian_fixup_kernel, dim3(static_cast<unsigned>(8 * tiles)), dim3(kThreads), 0, s, h,
                          static_cast<int>(d), accumulate, static_cast<int>(nt), static_cast<int>(ns),
                          static_cast<int>(chunk), ws);
       rc = w4q_launch_status();

@@ -33,6 +33,7 @@ METRIC = "W4A16 GEMV GB/s (% HBM peak); scale-search groups/s; Hessian+GEMM MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 PEAK_FP32_VALU_TFLOPS = 157.3  # fp32 vector (published; counts packed FP32)
+PEAK_FP32_MFMA_TFLOPS = 157.3  # fp32 matrix cores (dense)
 GS = 1.0 / np.sqrt(32 * 7)
 FLUSH_BYTES = 1 << 30
 
@@ -163,7 +164,10 @@ class Step:
 
         return {
             "hessian": (N * d_in * (d_in + 1), "flop", "mfma", PEAK_BF16_TFLOPS * 1e12),
-            "scale_search": (ng * K * 1056, "flop", "alu", PEAK_FP32_VALU_TFLOPS * 1e12),
+            # pass 1 scores on the fp32 matrix cores (v_mfma_f32_32x32x2_f32); the algorithmic
+            # count is the symmetric form (K * 1056 flop per group), half the full 32x32 form
+            # the matrix cores evaluate
+            "scale_search": (ng * K * 1056, "flop", "mfma", PEAK_FP32_MFMA_TFLOPS * 1e12),
             "pack": (nw * 4.5 + ng * 6, "byte", "hbm", PEAK_HBM_GBS * 1e9),
             "lsq_fwd": (nw * 8 + ng * 4, "byte", "hbm", PEAK_HBM_GBS * 1e9),
             "lsq_bwd": (nw * 16 + ng * 8, "byte", "hbm", PEAK_HBM_GBS * 1e9),
@@ -390,10 +394,12 @@ def run(args):
         amt, unit, bound, peak = work[name]
         rate = amt / (us * 1e-6)
         comps[name] = dict(us=round(us, 3), work=amt, work_unit=unit, bound=bound,
+                           peak=round(peak / (1e9 if unit == "byte" else 1e12), 1),
                            achieved=round(rate / (1e9 if unit == "byte" else 1e12), 3),
                            rate_unit="GB/s" if unit == "byte" else "TFLOP/s",
                            frac=round(rate / peak, 4))
-        mp = peaks.get(bound)
+        # measured peaks exist for HBM streaming and bf16 matrix cores only
+        mp = peaks.get(bound) if (bound == "hbm" or peak == PEAK_BF16_TFLOPS * 1e12) else None
         if mp:
             comps[name]["frac_of_measured_peak"] = round(rate / mp, 4)
         ut = float(np.mean([a.elapsed_time(b) for a, b in ev_t[name]])) * 1e3
@@ -401,7 +407,7 @@ def run(args):
         comps[name]["achieved_timed_region"] = round(amt / (ut * 1e-6) / (1e9 if unit == "byte" else 1e12), 3)
     dom = max(comps, key=lambda n: comps[n]["us_timed_region"])
     d = comps[dom]
-    pk = PEAK_HBM_GBS if d["bound"] == "hbm" else (PEAK_BF16_TFLOPS if d["bound"] == "mfma" else PEAK_FP32_VALU_TFLOPS)
+    pk = d["peak"]
     roof = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved_timed_region"], "peak": pk,
             "unit": d["rate_unit"], "frac": round(d["achieved_timed_region"] / pk, 4),
             "traffic": traffic_for(args.workload, dom),

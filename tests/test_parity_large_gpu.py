@@ -63,15 +63,16 @@ def _pack_rows(w, sc, dev, rows):
     return p, s16
 
 
-def _gemm_cols(x, p, s16, dev, cols, bf16_out=False):
-    y = w4q.w4a16_gemm(dev_bf16(x, dev), p, s16, out_dtype=torch.bfloat16 if bf16_out else torch.float32)
+def _gemm_cols(x, p, s16, dev, cols, bf16_out=False, dq=False):
+    fn = w4q.w4a16_gemm_dq if dq else w4q.w4a16_gemm
+    y = fn(dev_bf16(x, dev), p, s16, out_dtype=torch.bfloat16 if bf16_out else torch.float32)
     if bf16_out:
         yg = bf16_bits_to_np(y.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
     else:
         yg = y.cpu().numpy()
     pn = p.cpu().numpy()
     sn = host_f16_bits(s16)
-    yr, ya = oracle.gemm_cols(x, pn, sn, cols)
+    yr, ya = oracle.gemm_cols(x, pn, sn, cols, dequant_bf16=dq)
     check_gemm(yg[:, cols], yr, ya, bf16_out)
 
 
@@ -111,6 +112,7 @@ def test_config3_mlp(dev, name):
     cols = np.sort(rng.choice(lin.d_out, 48, replace=False))
     for m in c.gemm_m:                    # 1, 16, 256
         _gemm_cols(x[:m], p, s16, dev, cols)
+    _gemm_cols(x[:256], p, s16, dev, cols, dq=True)
 
 
 # ---------------------------------------------- config 4: 28-layer stack, search + decode
@@ -120,6 +122,7 @@ def test_config4_stack_search_pack_decode(dev):
     alpha = c.alpha()
     at = dev_f32(alpha, dev)
     n_lin = 0
+    decode = []  # (x, packed, scales, y of the single call) of every linear
     for layer in range(c.layers):
         xs = {inp: c.x(layer, inp) for inp in c.inputs()}
         hs = {inp: w4q.quant_hessian(dev_bf16(xv, dev)) for inp, xv in xs.items()}
@@ -145,8 +148,16 @@ def test_config4_stack_search_pack_decode(dev):
             cols = rng.integers(0, lin.d_out, 16)
             yr, ya = oracle.gemm_cols(xs[lin.inp][:1], p.cpu().numpy(), host_f16_bits(s16), cols)
             check_gemm(y.cpu().numpy()[:, cols], yr, ya)
+            decode.append((dev_bf16(xs[lin.inp][:1], dev), p, s16, y))
             n_lin += 1
     assert n_lin == 196
+    # the whole decode pass as grouped launches (64 problems each): every output agrees with the
+    # single call to fp32 rounding of the lane split (relative to the sum of |terms|)
+    say("cfg4 grouped decode over", n_lin, "linears")
+    ys = w4q.w4a16_gemv_grouped([d[0] for d in decode], [d[1] for d in decode], [d[2] for d in decode])
+    for (xd, p, s16, y1), yg in zip(decode, ys):
+        a, b = y1.cpu().numpy().astype(np.float64), yg.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(a - b) <= 1e-5 * (np.abs(a).max() + 1e-30)), np.abs(a - b).max()
 
 
 # ------------------------------------ config 5: 36-layer stack, representative layers
@@ -173,3 +184,4 @@ def test_config5_layer(dev, layer):
         _gemm_cols(x[:1], p, s16, dev, cols)                    # decode
         if lin.name in ("gate", "down"):
             _gemm_cols(x[:2048], p, s16, dev, cols, bf16_out=(lin.name == "down"))   # prefill
+            _gemm_cols(x[:2048], p, s16, dev, cols, bf16_out=(lin.name == "gate"), dq=True)

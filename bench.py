@@ -33,7 +33,6 @@ METRIC = "W4A16 GEMV GB/s (% HBM peak); scale-search groups/s; Hessian+GEMM MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 PEAK_FP32_VALU_TFLOPS = 157.3  # fp32 vector (published; counts packed FP32)
-PEAK_FP32_MFMA_TFLOPS = 157.3  # fp32 matrix cores (dense)
 GS = 1.0 / np.sqrt(32 * 7)
 FLUSH_BYTES = 1 << 30
 
@@ -69,7 +68,7 @@ CSRC = os.path.join(ROOT, "w4a16_group_wise_amd", "csrc")
 # kernel family -> (source file, symbol substrings as they appear in a kernel trace)
 KERNELS = {
     "hessian": ("hessian.hip", ["hessian_kernel", "hessian_fixup_kernel"]),
-    "scale_search": ("scale_search.hip", ["search_fp32_kernel", "search_fp64_kernel"]),
+    "scale_search": ("scale_search.hip", ["search_split_kernel", "search_fp64_kernel"]),
     "pack": ("pack_lsq.hip", ["pack_kernel"]),
     "lsq_fwd": ("pack_lsq.hip", ["lsq_fwd_kernel"]),
     "lsq_bwd": ("pack_lsq.hip", ["lsq_bwd_kernel"]),
@@ -164,10 +163,11 @@ class Step:
 
         return {
             "hessian": (N * d_in * (d_in + 1), "flop", "mfma", PEAK_BF16_TFLOPS * 1e12),
-            # pass 1 scores on the fp32 matrix cores (v_mfma_f32_32x32x2_f32); the algorithmic
-            # count is the symmetric form (K * 1056 flop per group), half the full 32x32 form
-            # the matrix cores evaluate
-            "scale_search": (ng * K * 1056, "flop", "mfma", PEAK_FP32_MFMA_TFLOPS * 1e12),
+            # pass 1 scores with fp32 accuracy from fp16-split products on the matrix cores; its
+            # time goes mostly to vector instructions (codes, splits, dots), so it is priced
+            # against the fp32 vector peak.  The algorithmic count is the symmetric form
+            # (K * 1056 flop per group), half the full 32x32 form the matrix cores evaluate
+            "scale_search": (ng * K * 1056, "flop", "alu", PEAK_FP32_VALU_TFLOPS * 1e12),
             "pack": (nw * 4.5 + ng * 6, "byte", "hbm", PEAK_HBM_GBS * 1e9),
             "lsq_fwd": (nw * 8 + ng * 4, "byte", "hbm", PEAK_HBM_GBS * 1e9),
             "lsq_bwd": (nw * 16 + ng * 8, "byte", "hbm", PEAK_HBM_GBS * 1e9),

@@ -117,6 +117,21 @@ def test_search_ragged_and_single_candidate(dev):
         check_search(ix, sc, ob, io, so, oo, oao, _cand_fn(w, alpha))
 
 
+@pytest.mark.parametrize("sigma", [1.5, 2.5])
+def test_search_wide_channel_spread(dev, sigma):
+    # lognormal(0, sigma) channel scales spread each H_gg over many binades (about 2^40 between
+    # its largest and smallest entries at sigma 2.5), the hard case for a split-precision score
+    x = synth.calib_x(32, 0, 0, 1024, 1024, sigma)
+    h = w4q.quant_hessian(dev_bf16(x, dev)).cpu().numpy()
+    w = synth.weights(32, 0, 1, 192, 1024, 0.005)
+    alpha = synth.alpha_grid(40, 0.4, 1.0)
+    say("search channel spread", sigma)
+    sc, ix, ob, oa, so, io, oo, oao = _search_both(w, h, alpha, dev)
+    check_search(ix, sc, ob, io, so, oo, oao, _cand_fn(w, alpha))
+    err = np.abs(oa.astype(np.float64) - oao)
+    assert np.all(err <= 1e-5 * oao + 1e-30), f"worst rel {np.max(err / (oao + 1e-30)):.3g}"
+
+
 def test_search_deterministic(dev):
     c = synth.CONFIGS[1]
     w = c.weight(0, c.linears[0])

@@ -28,6 +28,11 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+# per-source additions: the scale search reads its matrix-core accumulators with vector
+# instructions after every candidate, so they are kept in ordinary VGPRs (no accvgpr copies)
+FILE_FLAGS = {
+    "scale_search.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def sources():
@@ -47,7 +52,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     def one(src):
         obj = os.path.join(OUT, os.path.basename(src)[:-4] + ".o")
-        cmd = [cc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -7,19 +7,23 @@
 // H = X^T X: obj_k = e_k^T Hg e_k, e_k = w - D_k code(w, D_k), D_k on the fp16 grid.
 //
 // Work: K * 1056 flop per group (the symmetric quadratic form) against 137 bytes of HBM
-// traffic, so the step is bound by arithmetic, not memory.  Pass 1 runs the quadratic forms
-// on the fp32 matrix cores (v_mfma_f32_32x32x2_f32, full 32x32 block) with the block held in
-// registers for the whole candidate loop; the mapping is described above the kernel.
+// traffic, so the step is bound by arithmetic, not memory.  Pass 1 forms the full 32x32
+// quadratic forms on the fp16 matrix cores (v_mfma_f32_32x32x16_f16) with fp32 accuracy: the
+// errors and the block are each split into two fp16 parts and three part products accumulate
+// in fp32 (the mapping and the error bound are described above the kernel); the block's parts
+// stay in registers for the whole candidate loop.  The vector instructions (codes, splits,
+// the final dot) take most of the time.
 //
 // Codes: rint(w * rcp(D)) clamped to [-8, 7] is the exact code unless w / D lies within 1e-5
 // of a half-integer (the rcp estimate is within ~2e-6 of w / D on the grid's range); when any
 // lane of the wavefront hits that window, the wavefront recomputes the candidate's codes with
 // the exact midpoint comparisons of code_correct.
 //
-// Precision: pass 1 scores in fp32.  A group whose two best fp32 scores are within a relative
-// 1e-5 (this includes exact ties and all-zero groups) is marked (index value 255, which
-// n_cand <= 255 keeps free), and pass 2 re-scores every candidate of each marked group in fp64,
-// one candidate per lane of a wavefront, and takes the first minimum.
+// Precision: pass 1 scores with fp32-level error (a few 2^-22 relative).  A group whose two
+// best pass-1 scores are within a relative 1e-5 (this includes exact ties and all-zero groups)
+// is marked (index value 255, which n_cand <= 255 keeps free), and pass 2 re-scores every
+// candidate of each marked group in fp64, one candidate per lane of a wavefront, and takes the
+// first minimum.
 #include "common.hpp"
 
 namespace w4q {
@@ -29,14 +33,6 @@ constexpr int kThreads = 256;
 constexpr uint8_t kMarked = 255;
 constexpr float kTieRel = 1e-5f;
 constexpr float kNear = 0.5f - 1e-5f;
-
-// Returns p unchanged through a VGPR, opaque to the optimiser: loads through it are vector
-// loads that cannot be hoisted out of the loop that produced it.
-__device__ __forceinline__ const float* vopaque(const float* p) {
-  uint64_t v = reinterpret_cast<uint64_t>(p);
-  asm volatile("" : "+v"(v));
-  return reinterpret_cast<const float*>(v);
-}
 
 __device__ __forceinline__ void load_group(const float* __restrict__ wp, float (&wv)[32]) {
 #pragma unroll
@@ -50,7 +46,7 @@ __device__ __forceinline__ void load_group(const float* __restrict__ wp, float (
 }
 
 // Codes of N weights at step d (d == 0 -> all 0), as floats.
-template <int N>
+template <int N, bool kZeroCodes = true>
 __device__ __forceinline__ void codes(const float (&wv)[N], float d, float (&c)[N]) {
   const bool zero = !(d > 0.0f);
   const float inv = __builtin_amdgcn_rcpf(zero ? 1.0f : d);
@@ -67,21 +63,68 @@ __device__ __forceinline__ void codes(const float (&wv)[N], float d, float (&c)[
 #pragma unroll
     for (int i = 0; i < N; ++i) c[i] = code_rcp(wv[i], d, inv);
   }
-  if (zero) {
+  if (kZeroCodes && zero) {
 #pragma unroll
     for (int i = 0; i < N; ++i) c[i] = 0.0f;
   }
 }
 
-// Pass 1 on the fp32 matrix cores.  A wavefront scores 32 rows (m = lane % 32) of one group
-// column g; the two lanes of a row (h = lane / 32) each own 16 of the group's 32 positions,
-// k = 8 q + 4 h + r (q, r in 0..3).  For a candidate, v_mfma_f32_32x32x2_f32 accumulates
-// D = Hg * E^T over 16 steps; step s pairs position p(s, h) = 8 (s/4) + 4 h + s % 4 of every
-// row, so lane (h, m) feeds e_m[p(s, h)] as the B operand and Hg[m][p(s, h)] as the A operand
-// (Hg stays in 16 VGPRs for the whole candidate loop), and receives D[k][m] = (Hg e_m)[k] for
-// exactly its own 16 positions k.  obj_m = sum_k e_m[k] D[k][m] is then a 16-term dot per lane
-// plus one exchange with the partner lane.
-__global__ __launch_bounds__(kThreads) void search_fp32_kernel(
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Splits 8 fp32 values into two fp16 parts, x = hi + lo + r: hi = x rounded to fp16, lo = the
+// exact fp32 difference x - hi rounded to fp16, so |lo| <= 2^-11 |x| and |r| <= 2^-22 |x| while
+// the values stay in fp16's normal range (below it the parts lose at most 2^-25 absolutely).
+// The values must be scaled so that |x| < 2^15.  Pairs go through v_cvt_pk_f16_f32.
+__device__ __forceinline__ void split8(const float* x, f16x8& hi, f16x8& lo) {
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const float a = x[j], b = x[j + 1];
+    uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+    asm volatile("" : "+v"(u));  // the parts are read back from the packed pair
+    const f16x2 hp = __builtin_bit_cast(f16x2, u);
+    const f16x2 lp = __builtin_convertvector(
+        (f32x2){a - static_cast<float>(hp[0]), b - static_cast<float>(hp[1])}, f16x2);
+    hi[j] = hp[0];
+    hi[j + 1] = hp[1];
+    lo[j] = lp[0];
+    lo[j + 1] = lp[1];
+  }
+}
+
+// 2^e as a float (e in [-126, 127])
+__device__ __forceinline__ float pow2(int e) { return __builtin_bit_cast(float, (e + 127) << 23); }
+
+// Exponent that scales values whose largest magnitude is m into [2^14, 2^15): the top of
+// fp16's range, so that entries far below the largest keep their bits (fp16's normal range
+// ends 2^28 below the top).  Clamped to a normal power of two for m == 0 or extreme m.
+__device__ __forceinline__ int scale_exp(float m) {
+  const int e = __builtin_amdgcn_frexp_expf(m);  // m in [2^(e-1), 2^e)
+  const int s = 15 - e;
+  return s > 127 ? 127 : (s < -126 ? -126 : s);
+}
+
+// Pass 1 on the fp16 matrix cores, fp32-accurate.  A wavefront scores 32 rows (m = lane % 32)
+// of one group column g; the two lanes of a row (h = lane / 32) each own 16 of the group's 32
+// positions, p = 8 q + 4 h + r (q, r in 0..3), held as element 4 q + r of the lane's arrays.
+// For a candidate, D = Hg * E^T (32 positions x 32 rows) is formed by
+// v_mfma_f32_32x32x16_f16 over two halves u of the reduction: in half u, reduction slot
+// 8 h + t of lane (h, m) is position p with 4 q + r = 8 u + t, so the lane feeds its own
+// elements 8u..8u+7 of e_m (B operand) and of Hg row m (A operand), and receives
+// D[p][m] = (Hg e_m)[p] for exactly its own 16 positions.  obj_m = sum_p e_m[p] D[p][m] is a
+// 16-term fp32 dot per lane plus one exchange with the partner lane.
+//
+// Precision: w is scaled by a power of two per row (sw) and Hg by one per block (sh), both
+// exactly, so that their largest magnitudes sit in [2^14, 2^15); the scaled error
+// e = sw w - code * (sw D) is exact in fp32 and |e| <= |sw w| (a code never overshoots w by
+// more than D / 2 <= |w|, and a clamped or zero code only shrinks w), so nothing overflows fp16.
+// e and Hg are each split into two fp16 parts (relative residual <= 2^-22 in fp16's normal
+// range), and D accumulates hi*lo, lo*hi, then hi*hi in fp32 (products of fp16 values are
+// exact; the dropped lo*lo term is <= 2^-22 relative), so the score carries an error of a few
+// 2^-22 of the form's magnitude before the exact rescale by 2^-(2 log2 sw + log2 sh).  The
+// headroom matters when the channel scales of X spread widely: the block's small entries then
+// lie many binades below its largest one and still need their full 22 bits.
+__global__ __launch_bounds__(kThreads) void search_split_kernel(
     const float* __restrict__ w, int64_t d_out, int64_t d_in, const float* __restrict__ h,
     int64_t ldh, const float* __restrict__ alpha, int n_cand, float* __restrict__ scale,
     uint8_t* __restrict__ idx, float* __restrict__ obj, float* __restrict__ obj_all) {
@@ -105,34 +148,71 @@ __global__ __launch_bounds__(kThreads) void search_fp32_kernel(
     wv[4 * q + 0] = a.x; wv[4 * q + 1] = a.y; wv[4 * q + 2] = a.z; wv[4 * q + 3] = a.w;
     ha[4 * q + 0] = b.x; ha[4 * q + 1] = b.y; ha[4 * q + 2] = b.z; ha[4 * q + 3] = b.w;
   }
-  float amax = 0.0f;
+  float amax = 0.0f, hmax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(wv[i]));
+  for (int i = 0; i < 16; ++i) {
+    amax = __builtin_fmaxf(amax, __builtin_fabsf(wv[i]));
+    hmax = __builtin_fmaxf(hmax, __builtin_fabsf(ha[i]));
+  }
   amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) hmax = __builtin_fmaxf(hmax, __shfl_xor(hmax, off));
+
+  // exact power-of-two scalings, then the two fp16 parts of the block (A operands)
+  const int ew = scale_exp(amax), eh = scale_exp(hmax);
+  const float sw = pow2(ew), sh = pow2(eh);
+  const int unscale = -(2 * ew + eh);  // obj = score * 2^unscale
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    wv[i] *= sw;
+    ha[i] *= sh;
+  }
+  f16x8 hhi[2], hlo[2];
+  split8(ha, hhi[0], hlo[0]);
+  split8(ha + 8, hhi[1], hlo[1]);
 
   float best = __builtin_inff(), second = __builtin_inff(), dbest = 0.0f;
   int kbest = 0;
-  float a_next = alpha[0];
+  float d_next = candidate(amax, alpha[0]);
 #pragma unroll 1
   for (int k = 0; k < n_cand; ++k) {
-    const float a = a_next;
-    a_next = alpha[k + 1 < n_cand ? k + 1 : k];  // scalar prefetch for the next candidate
-    const float d = candidate(amax, a);
+    const float d = d_next;
+    // the next candidate's step, off this candidate's dependency chain
+    d_next = candidate(amax, alpha[k + 1 < n_cand ? k + 1 : k]);
+    const float ds = d * sw;  // exact; the codes of sw w at ds are those of w at d
     float e[16];
-    codes<16>(wv, d, e);
+    // at a zero step the error is w whatever the codes are (w - c * 0), so the codes need not
+    // be cleared for it
+    codes<16, false>(wv, ds, e);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) e[i] = __builtin_fmaf(-e[i], d, wv[i]);
+    for (int i = 0; i < 16; ++i) {
+      e[i] = __builtin_fmaf(-e[i], ds, wv[i]);
+      asm volatile("" : "+v"(e[i]));  // e is formed once in fp32, then split
+    }
+    f16x8 ehi[2], elo[2];
+    split8(e, ehi[0], elo[0]);
+    split8(e + 8, ehi[1], elo[1]);
     f32x16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ha[s], e[s], acc, 0, 0, 0);
-    float part = 0.0f;
+    for (int u = 0; u < 2; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(hhi[u], elo[u], acc, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) part = __builtin_fmaf(e[i], acc[i], part);
-    // both lanes of a row get the sum of the two halves (fp32 addition is commutative, so
-    // both see the same bits)
-    const float o = part + __shfl_xor(part, 32);
+    for (int u = 0; u < 2; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(hlo[u], ehi[u], acc, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(hhi[u], ehi[u], acc, 0, 0, 0);
+    float p0 = 0.0f, p1 = 0.0f;  // two chains: even and odd positions of the lane
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      p0 = __builtin_fmaf(e[i], acc[i], p0);
+      p1 = __builtin_fmaf(e[i + 1], acc[i + 1], p1);
+    }
+    const float part = p0 + p1;
+    // both lanes of a row get lo-half + hi-half of the two partial dots (same bits in both)
+    const auto pr = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, part),
+                                                     __builtin_bit_cast(uint32_t, part), false, false);
+    const uint32_t u0 = pr[0], u1 = pr[1];
+    const float o = __builtin_ldexpf(__builtin_bit_cast(float, u0) + __builtin_bit_cast(float, u1), unscale);
     if (obj_all != nullptr && live && hh == 0) obj_all[(r * G + g) * n_cand + k] = o;
     // running first minimum and second-smallest score (branch-free)
     const bool better = o < best;
@@ -153,84 +233,117 @@ __global__ __launch_bounds__(kThreads) void search_fp32_kernel(
   }
 }
 
-// Pass 2: fp64 re-scoring of the marked groups, one wavefront per marked group and one
-// candidate per lane (same grid, same codes, fp64 sums, first minimum).
+// Pass 2 helper: wavefront Q's share of o = sum_i e_i sum_j H_ij e_j, the positions
+// i = 8Q..8Q+7 (hs holds Hg transposed: hs[j * 32 + i] = H_ij).
+template <int Q>
+__device__ __forceinline__ double partial_form(const double* hs, const double (&e)[32]) {
+  constexpr int kRows = kGroup / 4;
+  double sv[kRows];
+#pragma unroll
+  for (int t = 0; t < kRows; ++t) sv[t] = 0.0;
+#pragma unroll
+  for (int j = 0; j < kGroup; ++j) {
+    const double* hc = hs + j * kGroup + Q * kRows;
+#pragma unroll
+    for (int t = 0; t < kRows; ++t) sv[t] = __builtin_fma(hc[t], e[j], sv[t]);
+  }
+  double o = 0.0;
+#pragma unroll
+  for (int t = 0; t < kRows; ++t) o = __builtin_fma(e[Q * kRows + t], sv[t], o);
+  return o;
+}
+
+// Pass 2: fp64 re-scoring of the marked groups, one candidate per lane (same grid, same codes,
+// fp64 sums, first minimum).  A block covers 256 rows of one group column g; when any of them
+// is marked, the block stages Hg in LDS as fp64 and its four wavefronts score each marked row
+// together: wavefront q forms s_i = sum_j H_ij e_j and the partial sum of e_i s_i for the
+// positions i = 8q..8q+7, and the four partials are added in a fixed order.
 __global__ __launch_bounds__(kThreads) void search_fp64_kernel(
     const float* __restrict__ w, int64_t d_out, int64_t d_in, const float* __restrict__ h,
     int64_t ldh, const float* __restrict__ alpha, int n_cand, float* __restrict__ scale,
     uint8_t* __restrict__ idx, float* __restrict__ obj, float* __restrict__ obj_all) {
+  static_assert(kThreads == 256, "four wavefronts share a marked row's positions");
+  constexpr int kWaves = kThreads / 64;
+  __shared__ double hs[kGroup * kGroup];
+  __shared__ double part[kWaves][64];
+  __shared__ uint64_t marks[kWaves];
   const int64_t G = d_in / kGroup;
   const int64_t g = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int wid = threadIdx.x >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * kThreads;
+  const int64_t r = r0 + threadIdx.x;
   const bool marked = r < d_out && idx[r * G + g] == kMarked;
-  uint64_t mask = __builtin_amdgcn_ballot_w64(marked);
+  if (!__syncthreads_or(marked)) return;  // block-uniform
+  const uint64_t mask = __builtin_amdgcn_ballot_w64(marked);
+  if (lane == 0) marks[wid] = mask;
   const float* __restrict__ hg = h + g * kGroup * ldh + g * kGroup;
-  while (mask != 0) {
-    const int src = __builtin_ctzll(mask);
-    mask &= mask - 1;
-    const int64_t rs = r - lane + src;  // the marked row (wave-uniform)
-    const int64_t o_ = rs * G + g;
-    float wv[32];
-    load_group(w + rs * d_in + g * kGroup, wv);
-    float amax = 0.0f;
+  for (int t = threadIdx.x; t < kGroup * kGroup; t += kThreads)
+    hs[(t % kGroup) * kGroup + t / kGroup] = static_cast<double>(hg[(t / kGroup) * ldh + t % kGroup]);
+  __syncthreads();
+  // every wavefront walks the same list of marked rows, so the barriers below are uniform
+  for (int q = 0; q < kWaves; ++q) {
+    uint64_t m = marks[q];
+    while (m != 0) {
+      const int src = __builtin_ctzll(m);
+      m &= m - 1;
+      const int64_t rs = r0 + q * 64 + src;
+      const int64_t o_ = rs * G + g;
+      float wv[32];
+      load_group(w + rs * d_in + g * kGroup, wv);
+      float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(wv[i]));
-    double best = __builtin_inf();
-    int kbest = 0x7FFFFFFF;
-    float dbest = 0.0f;
-    for (int k0 = 0; k0 < n_cand; k0 += 64) {
-      const int k = k0 + lane;
-      const bool kv = k < n_cand;
-      const float d = candidate(amax, alpha[kv ? k : 0]);
-      float c[32];
-      codes<32>(wv, d, c);  // same codes as pass 1
-      double e[32];
+      for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(wv[i]));
+      double best = __builtin_inf();
+      int kbest = 0x7FFFFFFF;
+      float dbest = 0.0f;
+      for (int k0 = 0; k0 < n_cand; k0 += 64) {
+        const int k = k0 + lane;
+        const bool kv = k < n_cand;
+        const float d = candidate(amax, alpha[kv ? k : 0]);
+        float c[32];
+        codes<32>(wv, d, c);  // same codes as pass 1
+        double e[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i)
-        e[i] = __builtin_fma(-static_cast<double>(c[i]), static_cast<double>(d), static_cast<double>(wv[i]));
-      // o = sum_i e_i sum_j H_ij e_j over the full block, like pass 1; the outer loop stays
-      // rolled and recomputes e_i from memory so no register array is indexed dynamically
-      const float* hk = vopaque(hg);
-      const float* wk = vopaque(w + rs * d_in + g * kGroup);
-      const bool zero = !(d > 0.0f);
-      const float inv = __builtin_amdgcn_rcpf(zero ? 1.0f : d);
-      double o = 0.0;
-#pragma unroll 1
-      for (int i = 0; i < 32; ++i) {
-        const float* hr = hk + i * ldh;
-        double si = 0.0;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) si = __builtin_fma(static_cast<double>(hr[j]), e[j], si);
-        const float wi = wk[i];
-        const float ci = zero ? 0.0f : code_rcp(wi, d, inv);
-        const double ei = __builtin_fma(-static_cast<double>(ci), static_cast<double>(d), static_cast<double>(wi));
-        o = __builtin_fma(ei, si, o);
-      }
-      if (kv) {
-        if (obj_all != nullptr) obj_all[o_ * n_cand + k] = static_cast<float>(o);
-        if (o < best) {  // a lane's candidates rise with k0: strict keeps the first
-          best = o;
-          kbest = k;
-          dbest = d;
+        for (int i = 0; i < 32; ++i)
+          e[i] = __builtin_fma(-static_cast<double>(c[i]), static_cast<double>(d), static_cast<double>(wv[i]));
+        double op;
+        switch (wid) {
+          case 0: op = partial_form<0>(hs, e); break;
+          case 1: op = partial_form<1>(hs, e); break;
+          case 2: op = partial_form<2>(hs, e); break;
+          default: op = partial_form<3>(hs, e); break;
+        }
+        part[wid][lane] = op;
+        __syncthreads();
+        const double o = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+        __syncthreads();  // part is rewritten by the next chunk or row
+        if (kv) {
+          if (obj_all != nullptr && wid == 0) obj_all[o_ * n_cand + k] = static_cast<float>(o);
+          if (o < best) {  // a lane's candidates rise with k0: strict keeps the first
+            best = o;
+            kbest = k;
+            dbest = d;
+          }
         }
       }
-    }
-    // wavefront argmin, ties to the lowest candidate index
+      // wavefront argmin, ties to the lowest candidate index (every wavefront holds the same
+      // scores; the first one writes)
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double ob = __shfl_xor(best, off);
-      const int ok = __shfl_xor(kbest, off);
-      const float od = __shfl_xor(dbest, off);
-      const bool take = (ob < best) || (ob == best && ok < kbest);
-      best = take ? ob : best;
-      kbest = take ? ok : kbest;
-      dbest = take ? od : dbest;
-    }
-    if (lane == 0) {
-      scale[o_] = dbest;
-      idx[o_] = static_cast<uint8_t>(kbest);
-      if (obj != nullptr) obj[o_] = static_cast<float>(best);
+      for (int off = 32; off >= 1; off >>= 1) {
+        const double ob = __shfl_xor(best, off);
+        const int ok = __shfl_xor(kbest, off);
+        const float od = __shfl_xor(dbest, off);
+        const bool take = (ob < best) || (ob == best && ok < kbest);
+        best = take ? ob : best;
+        kbest = take ? ok : kbest;
+        dbest = take ? od : dbest;
+      }
+      if (threadIdx.x == 0) {
+        scale[o_] = dbest;
+        idx[o_] = static_cast<uint8_t>(kbest);
+        if (obj != nullptr) obj[o_] = static_cast<float>(best);
+      }
     }
   }
 }
@@ -247,7 +360,7 @@ int w4q_launch_scale_search(const float* w, int64_t d_out, int64_t d_in, const f
   if (G > 65535) return W4Q_EUNSUPPORTED;
   const dim3 grid1(static_cast<unsigned>((d_out + kThreads / 2 - 1) / (kThreads / 2)),
                    static_cast<unsigned>(G));
-  hipLaunchKernelGGL(search_fp32_kernel, grid1, dim3(kThreads), 0, s, w, d_out, d_in, h, ldh, alpha,
+  hipLaunchKernelGGL(search_split_kernel, grid1, dim3(kThreads), 0, s, w, d_out, d_in, h, ldh, alpha,
                      n_cand, scale, idx, obj, obj_all);
   if (hipGetLastError() != hipSuccess) return W4Q_EHIP;
   const dim3 grid(static_cast<unsigned>((d_out + kThreads - 1) / kThreads), static_cast<unsigned>(G));

@@ -160,9 +160,10 @@ int lsq_bwd(const float* w, const float* scale, const float* grad_w_hat, int64_t
  *   packed    uint8 [d_out][d_in/2] as written by quant_pack, 16-B aligned.
  *   scale_f16 fp16 bits [d_out][G].
  *   y         [m][d_out], fp32 (y_dtype 0) or bf16 RNE of the fp32 result (y_dtype 1).
- *   m >= 1.  Small m (<= 16) streams the packed weights (bandwidth bound); larger m runs on
- *   the bf16 matrix cores with the codes expanded to bf16 (exact small integers) and the fp32
- *   scale applied once per group to the group's partial products, so the weights enter the
+ *   m >= 1.  Small m (<= 16) streams the packed weights once (bandwidth bound): m = 1 on the
+ *   vector ALUs, 2..16 on the bf16 matrix cores; larger m is a tiled product on the matrix
+ *   cores.  On the matrix cores the codes enter as exact small bf16 integers and the fp32
+ *   scale is applied once per group to the group's partial products, so the weights enter the
  *   products unrounded.
  */
 int w4a16_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,

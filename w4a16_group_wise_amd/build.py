@@ -28,10 +28,12 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
-# per-source additions: the scale search reads its matrix-core accumulators with vector
-# instructions after every candidate, so they are kept in ordinary VGPRs (no accvgpr copies)
+# per-source additions: the scale search and the few-row W4A16 product read their matrix-core
+# results with vector instructions right after each product, so those stay in ordinary VGPRs
+# (no accvgpr copies)
 FILE_FLAGS = {
     "scale_search.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -1,12 +1,14 @@
-// gemv.hip -- W4A16 product for a few activation rows (decode): streams the packed INT4 codes
-// and fp16 scales from HBM once and keeps the activations in registers.
+// gemv.hip -- W4A16 product for 1..16 activation rows (decode): streams the packed INT4 codes
+// and fp16 scales from HBM once.  One row runs on the vector ALUs (below, and the persistent
+// stream kernel further down); 2..16 rows run on the matrix cores (the section "2..16
+// activation rows").
 //
 // Method: model card "Opt.Gear-1B-qat-int4-per-channel-unquantized" (W4A16: INT4 weights with
 // 16-bit activations; weight memory and bandwidth set the speed) with the group-32 symmetric
 // grid of blog "Opt.Gear-QAT: Preserving On-Device Performance with QAT".
 //   y[m][n] = sum_g s[n][g] * sum_{k in g} x[m][k] * q[n][k]
 //
-// Mapping: a group of 32 codes is one 16-byte load, so a lane owns one group column; LPR lanes
+// Vector mapping: a group of 32 codes is one 16-byte load, so a lane owns one group column; LPR lanes
 // (a power of two dividing G) cover one row per chunk of LPR groups, and a wavefront works on
 // 64 / LPR rows at once, RS row-steps deep, walking the chunks along d_in.  Loads of a row are
 // contiguous (LPR * 16 bytes).  The lane keeps its group's activations as bf16 pairs in
@@ -187,6 +189,218 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint16_t* __restri
                                                         void* __restrict__ y, int y_dtype,
                                                         uint32_t mask) {
   gemv_body<MT, LPR, RS>(x, m_rows, packed, s16, d_out, d_in, y, y_dtype, mask, blockIdx.x);
+}
+
+// ---- 2..16 activation rows on the matrix cores ------------------------------------------
+//
+// One v_mfma_f32_16x16x32_bf16 per (group, 16 rows of W) forms the 16 x 16 block of per-group
+// sums sum_{k in g} x[m][k] * 8 (24 + q[n][k]) for all activation rows at once (rows past
+// m_rows repeat the last one and are never stored); the code-0 product of the same activations
+// (one more product per group, shared by the tiles) is subtracted and the group's scale applied
+// in fp32, exactly as in the vector kernels above.  A operand: lane (q, m) = (lane / 16,
+// lane % 16) holds x[m][32 g + 8 q + e]; B operand: lane (q, n) holds the 8 codes of W row n
+// at the same offsets, as the nibble pairs of codes_bf16 (the activations are paired to match,
+// so the order of the 8 products inside the group is the same on both sides).  The result:
+// lane (q, n) holds rows m = 4 q + r of column n.
+//
+// A workgroup owns 32 rows of W (two tiles); its wavefronts take d_in's 8-group batches
+// round-robin.  Each wavefront keeps two batches of codes and scales in flight: those of its next
+// batch are issued before the current one is reduced; the activations (L2-resident) are loaded
+// one batch ahead, right after the previous batch's products.  Codes: lane (q, n) loads the whole group 4 h + q of row n
+// (16 rows x 64 contiguous bytes per instruction), and a 4 x 4 transpose across the lanes q
+// gives every lane dword q of each of the four groups.  Scales: one 16-byte load of the batch's
+// 8 scales per row when G % 8 == 0 (then every batch start is 16-byte aligned), else one
+// 2-byte load per group.  The wavefronts' partial results are added in LDS in a fixed order.
+constexpr int kMmaWaves = 8;
+constexpr int kMmaTiles = 2;
+constexpr int kMmaBatch = 8;
+
+// 4 x 4 transpose across the 16-lane rows R = lane / 16: on entry v[j] of row R holds element
+// (R, j), on exit element (j, R).  The 32-lane swap exchanges the off-diagonal 2 x 2 blocks,
+// the 16-lane swap the off-diagonal elements inside each block.
+__device__ __forceinline__ void transpose4(u32x4& v) {
+  uint32_t a0 = v.x, a1 = v.y, a2 = v.z, a3 = v.w;
+  auto s32 = [](uint32_t& a, uint32_t& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    a = r0;
+    b = r1;
+  };
+  auto s16 = [](uint32_t& a, uint32_t& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    a = r0;
+    b = r1;
+  };
+  s32(a0, a2);
+  s32(a1, a3);
+  s16(a0, a1);
+  s16(a2, a3);
+  v = u32x4{a0, a1, a2, a3};
+}
+
+struct MmaBatch {
+  u32x4 cv[kMmaBatch / 4][kMmaTiles];  // codes (transposed after arrival)
+  u32x4 sc[kMmaTiles];                 // 8 scales per row (vector path)
+  uint32_t s1[kMmaBatch][kMmaTiles];   // one scale per group (2-byte path)
+};
+
+template <bool kVecScales>
+__global__ __launch_bounds__(kMmaWaves * 64) void gemv_mma_kernel(const uint16_t* __restrict__ x, int m_rows,
+                                                                  const uint8_t* __restrict__ packed,
+                                                                  const uint16_t* __restrict__ s16,
+                                                                  int64_t d_out, int64_t d_in,
+                                                                  void* __restrict__ y, int y_dtype) {
+  __shared__ float part[kMmaWaves][kMmaTiles][4][64];
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = lane >> 4, nl = lane & 15;
+  const int G = static_cast<int>(d_in / kGroup);
+  const int nbat = (G + kMmaBatch - 1) / kMmaBatch;
+  const int64_t nbase = (int64_t)blockIdx.x * (16 * kMmaTiles);
+  uint32_t c0 = kC0;
+  asm volatile("" : "+v"(c0));  // keep the constant in a VGPR so v_bitop3 can take it
+
+  // rows of W past d_out read the last row (their columns are never stored)
+  const uint8_t* prow[kMmaTiles];
+  const uint16_t* srow[kMmaTiles];
+#pragma unroll
+  for (int t = 0; t < kMmaTiles; ++t) {
+    const int64_t n = nbase + 16 * t + nl;
+    const int64_t nn = n < d_out ? n : d_out - 1;
+    prow[t] = packed + nn * (d_in / 2);
+    srow[t] = s16 + nn * G;
+  }
+  const int mr = nl < m_rows ? nl : m_rows - 1;
+  const uint16_t* xrow = x + (int64_t)mr * d_in + 8 * q;
+  const u32x4 zero_codes = {kZero, kZero, kZero, kZero};
+  const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+
+  // the loads of batch b, all issued at once; groups past G repeat the last one.  Every loaded
+  // value passes through an empty asm, so no load can sink into the product of its group.
+  auto load = [&](int b, MmaBatch& B) {
+    const int gb = b * kMmaBatch;
+#pragma unroll
+    for (int h = 0; h < kMmaBatch / 4; ++h) {
+      const int g = gb + 4 * h + q < G ? gb + 4 * h + q : G - 1;
+#pragma unroll
+      for (int t = 0; t < kMmaTiles; ++t) B.cv[h][t] = *reinterpret_cast<const u32x4*>(prow[t] + (int64_t)g * 16);
+    }
+    if constexpr (kVecScales) {
+#pragma unroll
+      for (int t = 0; t < kMmaTiles; ++t) B.sc[t] = *reinterpret_cast<const u32x4*>(srow[t] + gb);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kMmaBatch; ++i) {
+        const int g = gb + i < G ? gb + i : G - 1;
+#pragma unroll
+        for (int t = 0; t < kMmaTiles; ++t) B.s1[i][t] = srow[t][g];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < kMmaBatch / 4; ++h)
+#pragma unroll
+      for (int t = 0; t < kMmaTiles; ++t) asm volatile("" : "+v"(B.cv[h][t]));
+    if constexpr (kVecScales) {
+#pragma unroll
+      for (int t = 0; t < kMmaTiles; ++t) asm volatile("" : "+v"(B.sc[t]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < kMmaBatch; ++i)
+#pragma unroll
+        for (int t = 0; t < kMmaTiles; ++t) asm volatile("" : "+v"(B.s1[i][t]));
+    }
+  };
+  // the activations of batch b (from L2: issued after the previous batch's products, they land
+  // while the codes, loaded a batch earlier, are still arriving)
+  u32x4 xv[kMmaBatch];
+  auto load_x = [&](int b) {
+    const int gb = b * kMmaBatch;
+#pragma unroll
+    for (int i = 0; i < kMmaBatch; ++i) {
+      const int g = gb + i < G ? gb + i : G - 1;
+      xv[i] = *reinterpret_cast<const u32x4*>(xrow + (int64_t)g * kGroup);
+    }
+#pragma unroll
+    for (int i = 0; i < kMmaBatch; ++i) asm volatile("" : "+v"(xv[i]));
+  };
+
+  f32x4 acc[kMmaTiles];
+#pragma unroll
+  for (int t = 0; t < kMmaTiles; ++t) acc[t] = zero4;
+
+  auto compute = [&](int b, MmaBatch& B) {
+    const int nb = G - b * kMmaBatch < kMmaBatch ? G - b * kMmaBatch : kMmaBatch;
+#pragma unroll
+    for (int h = 0; h < kMmaBatch / 4; ++h)
+#pragma unroll
+      for (int t = 0; t < kMmaTiles; ++t) transpose4(B.cv[h][t]);
+#pragma unroll
+    for (int i = 0; i < kMmaBatch; ++i) {
+      if (i >= nb) break;  // wavefront-uniform
+      uint32_t xp[4];
+      pair_x(xv[i], xp);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{xp[0], xp[1], xp[2], xp[3]});
+      const f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, zero_codes), zero4, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < kMmaTiles; ++t) {
+        uint32_t cb[4];
+        codes_bf16(B.cv[i / 4][t][i % 4], kMask, c0, cb);
+        const f32x4 dv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            a, __builtin_bit_cast(bf16x8, u32x4{cb[0], cb[1], cb[2], cb[3]}), zero4, 0, 0, 0);
+        uint32_t sbits;
+        if constexpr (kVecScales)
+          sbits = B.sc[t][i / 2] >> (16 * (i % 2));
+        else
+          sbits = B.s1[i][t];
+        const float sc = f16_bits_to_f32(static_cast<uint16_t>(sbits));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][r] = __builtin_fmaf(sc, dv[r] - d0[r], acc[t][r]);
+      }
+    }
+  };
+
+  // the wavefronts take the batches round-robin (wavefront w: w, w + 4, ...), so at any time a
+  // workgroup reads a few hundred contiguous bytes of each of its rows; two register sets: the
+  // next batch is in flight while the current one is reduced
+  constexpr int S = kMmaWaves;
+  MmaBatch B0, B1;
+  if (wid < nbat) {
+    load(wid, B0);
+    load_x(wid);
+  }
+  for (int b = wid; b < nbat; b += 2 * S) {
+    if (b + S < nbat) load(b + S, B1);
+    compute(b, B0);
+    if (b + S >= nbat) break;
+    load_x(b + S);
+    if (b + 2 * S < nbat) load(b + 2 * S, B0);
+    compute(b + S, B1);
+    if (b + 2 * S < nbat) load_x(b + 2 * S);
+  }
+
+#pragma unroll
+  for (int t = 0; t < kMmaTiles; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[wid][t][r][lane] = acc[t][r];
+  __syncthreads();
+  // outputs: tile t, activation row m, column c; wavefront partials in order, then the factor
+  // 8 removed (exactly)
+  for (int o = threadIdx.x; o < kMmaTiles * 256; o += kMmaWaves * 64) {
+    const int t = o >> 8, m = (o >> 4) & 15, c = o & 15;
+    const int src = 16 * (m >> 2) + c;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMmaWaves; ++w) v += part[w][t][m & 3][src];
+    v *= 0.125f;
+    const int64_t n = nbase + 16 * t + c;
+    if (m < m_rows && n < d_out) {
+      if (y_dtype == 0)
+        reinterpret_cast<float*>(y)[m * d_out + n] = v;
+      else
+        reinterpret_cast<uint16_t*>(y)[m * d_out + n] = f32_to_bf16_bits(v);
+    }
+  }
 }
 
 // ---- one activation row: a persistent stream over many problems --------------------------
@@ -565,28 +779,27 @@ int launch_group_chunk(const w4q_gemv_problem* probs, int cnt, int y_dtype, hipS
 }  // namespace
 }  // namespace w4q
 
-// Activation rows are processed four at a time; each slice of rows re-streams the weights.  A
-// single row takes the stream kernel (as a one-problem group) when its sizes fit 32 bits.
+// 2..16 activation rows: one matrix-core launch.  A single row takes the stream kernel (as a
+// one-problem group) when its sizes fit 32 bits, else the vector kernel.
 int w4q_launch_gemv(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
                     int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t s) {
-  const size_t ysz = y_dtype == 0 ? 4 : 2;
-  for (int64_t m0 = 0; m0 < m; m0 += 4) {
-    const int64_t mt = (m - m0) < 4 ? (m - m0) : 4;
-    const uint16_t* xs = x + m0 * d_in;
-    void* ys = static_cast<char*>(y) + static_cast<size_t>(m0 * d_out) * ysz;
-    int rc;
-    const w4q_gemv_problem one = {xs, packed, s16, ys, d_out, d_in};
-    if (mt == 1 && d_out <= 0x7FFFFFFF && d_in <= (1 << 24) && w4q_gemv_group_fits(&one, 1)) {
-      rc = launch_group_chunk(&one, 1, y_dtype, s);
-    } else if (mt == 1)
-      rc = launch_mt<1>(xs, mt, packed, s16, d_out, d_in, ys, y_dtype, s);
-    else if (mt == 2)
-      rc = launch_mt<2>(xs, mt, packed, s16, d_out, d_in, ys, y_dtype, s);
+  if (m >= 2 && m <= 16) {
+    const int64_t blocks = (d_out + 16 * kMmaTiles - 1) / (16 * kMmaTiles);
+    if (blocks > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
+    if ((d_in / kGroup) % kMmaBatch == 0)
+      hipLaunchKernelGGL(gemv_mma_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kMmaWaves * 64), 0, s,
+                         x, static_cast<int>(m), packed, s16, d_out, d_in, y, y_dtype);
     else
-      rc = launch_mt<4>(xs, mt, packed, s16, d_out, d_in, ys, y_dtype, s);
-    if (rc != W4Q_OK) return rc;
+      hipLaunchKernelGGL(gemv_mma_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kMmaWaves * 64), 0, s,
+                         x, static_cast<int>(m), packed, s16, d_out, d_in, y, y_dtype);
+    return w4q_launch_status();
   }
-  return W4Q_OK;
+  // one activation row: the persistent stream kernel, or the plain vector kernel when the
+  // stream's 32-bit offsets do not cover the shape
+  const w4q_gemv_problem one = {x, packed, s16, y, d_out, d_in};
+  if (d_out <= 0x7FFFFFFF && d_in <= (1 << 24) && w4q_gemv_group_fits(&one, 1))
+    return launch_group_chunk(&one, 1, y_dtype, s);
+  return launch_mt<1>(x, 1, packed, s16, d_out, d_in, y, y_dtype, s);
 }
 
 // Every launch's item count fits an int and every item's lane offsets fit 32 bits

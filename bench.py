@@ -73,7 +73,7 @@ KERNELS = {
     "lsq_fwd": ("pack_lsq.hip", ["lsq_fwd_kernel"]),
     "lsq_bwd": ("pack_lsq.hip", ["lsq_bwd_kernel"]),
     "gemv_m1": ("gemv.hip", ["gemv_stream_kernel"]),
-    "gemv_m4": ("gemv.hip", []),   # same kernel as the M=16 passes: not separable by name
+    "gemv_m4": ("gemv.hip", []),   # the matrix-core kernel also runs M=16: not separable by name
     "gemv_m16": ("gemv.hip", []),
     "gemm": ("gemm.hip", ["gemm_group_kernel"]),
     "gemm_dq": ("gemm.hip", ["gemm_dq_kernel", "gemm_fixup_kernel"]),

@@ -33,6 +33,8 @@ constexpr int kThreads = 256;
 constexpr uint8_t kMarked = 255;
 constexpr float kTieRel = 1e-5f;
 constexpr float kNear = 0.5f - 1e-5f;
+// below this many 32-row wavefronts pass 1 runs 16 rows per wavefront
+constexpr int64_t kWaves16Below = 2048;
 
 __device__ __forceinline__ void load_group(const float* __restrict__ wp, float (&wv)[32]) {
 #pragma unroll
@@ -83,8 +85,11 @@ __device__ __forceinline__ void split8(const float* x, f16x8& hi, f16x8& lo) {
     uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
     asm volatile("" : "+v"(u));  // the parts are read back from the packed pair
     const f16x2 hp = __builtin_bit_cast(f16x2, u);
-    const f16x2 lp = __builtin_convertvector(
-        (f32x2){a - static_cast<float>(hp[0]), b - static_cast<float>(hp[1])}, f16x2);
+    // x - hi as one mixed-precision fma per element (exact: hi holds x's leading 11 bits)
+    float ra, rb;
+    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(ra) : "v"(u), "v"(a));
+    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(rb) : "v"(u), "v"(b));
+    const f16x2 lp = __builtin_convertvector((f32x2){ra, rb}, f16x2);
     hi[j] = hp[0];
     hi[j + 1] = hp[1];
     lo[j] = lp[0];
@@ -233,6 +238,132 @@ __global__ __launch_bounds__(kThreads) void search_split_kernel(
   }
 }
 
+// Pass 1 for small grids: 16 rows per wavefront (twice the wavefronts of the kernel above, so
+// short problems still fill the SIMDs).  Lane (q, j) = (lane / 16, lane % 16) owns positions
+// p = 8 q + e (e = 0..7) of row j.  v_mfma_f32_32x32x16_f16 is replaced by pairs of
+// v_mfma_f32_16x16x32_f16: product u (0, 1) has output rows i = 0..15 standing for positions
+// 8 (i / 4) + 4 u + i % 4 and the reduction slot 8 q + e standing for position 8 q + e, so the
+// lane feeds its own 8 errors as the B operand and Hg[8 (i / 4) + 4 u + i % 4][8 q + e] (i = the
+// lane's j) as the A operand, and receives D[p][j] for exactly its own positions
+// p = 8 q + 4 u + r (r = 0..3).  Scaling, splitting and accumulation order as above.
+__global__ __launch_bounds__(kThreads) void search_split16_kernel(
+    const float* __restrict__ w, int64_t d_out, int64_t d_in, const float* __restrict__ h,
+    int64_t ldh, const float* __restrict__ alpha, int n_cand, float* __restrict__ scale,
+    uint8_t* __restrict__ idx, float* __restrict__ obj, float* __restrict__ obj_all) {
+  const int64_t G = d_in / kGroup;
+  const int64_t g = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4;
+  const int j = lane & 15;
+  const int64_t r = (int64_t)blockIdx.x * (kThreads / 4) + (threadIdx.x >> 6) * 16 + j;
+  const bool live = r < d_out;
+  const int64_t rr = live ? r : d_out - 1;
+
+  // this lane's 8 weights (positions 8q .. 8q+7) and, for u = 0, 1, the same 8 columns of Hg
+  // row 8 (j / 4) + 4 u + j % 4
+  float wv[8], ha[2][8];
+  {
+    const float* wp = w + rr * d_in + g * kGroup + 8 * q;
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(wp);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(wp + 4);
+    wv[0] = a0.x; wv[1] = a0.y; wv[2] = a0.z; wv[3] = a0.w;
+    wv[4] = a1.x; wv[5] = a1.y; wv[6] = a1.z; wv[7] = a1.w;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int prow = 8 * (j >> 2) + 4 * u + (j & 3);
+      const float* hp = h + (g * kGroup + prow) * ldh + g * kGroup + 8 * q;
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(hp);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(hp + 4);
+      ha[u][0] = b0.x; ha[u][1] = b0.y; ha[u][2] = b0.z; ha[u][3] = b0.w;
+      ha[u][4] = b1.x; ha[u][5] = b1.y; ha[u][6] = b1.z; ha[u][7] = b1.w;
+    }
+  }
+  float amax = 0.0f, hmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    amax = __builtin_fmaxf(amax, __builtin_fabsf(wv[i]));
+    hmax = __builtin_fmaxf(hmax, __builtin_fmaxf(__builtin_fabsf(ha[0][i]), __builtin_fabsf(ha[1][i])));
+  }
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) hmax = __builtin_fmaxf(hmax, __shfl_xor(hmax, off));
+
+  const int ew = scale_exp(amax), eh = scale_exp(hmax);
+  const float sw = pow2(ew), sh = pow2(eh);
+  const int unscale = -(2 * ew + eh);  // obj = score * 2^unscale
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    wv[i] *= sw;
+    ha[0][i] *= sh;
+    ha[1][i] *= sh;
+  }
+  f16x8 hhi[2], hlo[2];
+  split8(ha[0], hhi[0], hlo[0]);
+  split8(ha[1], hhi[1], hlo[1]);
+
+  float best = __builtin_inff(), second = __builtin_inff(), dbest = 0.0f;
+  int kbest = 0;
+  float d_next = candidate(amax, alpha[0]);
+  const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 1
+  for (int k = 0; k < n_cand; ++k) {
+    const float d = d_next;
+    // the next candidate's step, off this candidate's dependency chain
+    d_next = candidate(amax, alpha[k + 1 < n_cand ? k + 1 : k]);
+    const float ds = d * sw;  // exact; the codes of sw w at ds are those of w at d
+    float e[8];
+    codes<8, false>(wv, ds, e);  // at a zero step the error is w whatever the codes are
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      e[i] = __builtin_fmaf(-e[i], ds, wv[i]);
+      asm volatile("" : "+v"(e[i]));  // e is formed once in fp32, then split
+    }
+    f16x8 ehi, elo;
+    split8(e, ehi, elo);
+    f32x4 acc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hhi[u], elo, zero4, 0, 0, 0);
+      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hlo[u], ehi, acc[u], 0, 0, 0);
+      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hhi[u], ehi, acc[u], 0, 0, 0);
+    }
+    float p0 = 0.0f, p1 = 0.0f;  // two chains: the two products
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p0 = __builtin_fmaf(e[i], acc[0][i], p0);
+      p1 = __builtin_fmaf(e[4 + i], acc[1][i], p1);
+    }
+    const float part = p0 + p1;
+    // the four lanes of a row add their partial dots pairwise: (q0 + q1) + (q2 + q3) in all of
+    // them (same bits in each)
+    const auto s1 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, part),
+                                                     __builtin_bit_cast(uint32_t, part), false, false);
+    const uint32_t a0 = s1[0], a1 = s1[1];
+    const float half = __builtin_bit_cast(float, a0) + __builtin_bit_cast(float, a1);
+    const auto s2 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, half),
+                                                     __builtin_bit_cast(uint32_t, half), false, false);
+    const uint32_t b0 = s2[0], b1 = s2[1];
+    const float o = __builtin_ldexpf(__builtin_bit_cast(float, b0) + __builtin_bit_cast(float, b1), unscale);
+    if (obj_all != nullptr && live && q == 0) obj_all[(r * G + g) * n_cand + k] = o;
+    const bool better = o < best;
+    second = better ? best : __builtin_fminf(second, o);
+    kbest = better ? k : kbest;
+    dbest = better ? d : dbest;
+    best = better ? o : best;
+  }
+  if (!live || q != 0) return;
+  const int64_t o_ = r * G + g;
+  const bool clear = (second - best) > kTieRel * best;  // false for ties, zeros and NaN
+  if (clear) {
+    scale[o_] = dbest;
+    idx[o_] = static_cast<uint8_t>(kbest);
+    if (obj != nullptr) obj[o_] = best;
+  } else {
+    idx[o_] = kMarked;
+  }
+}
+
 // Pass 2 helper: wavefront Q's share of o = sum_i e_i sum_j H_ij e_j, the positions
 // i = 8Q..8Q+7 (hs holds Hg transposed: hs[j * 32 + i] = H_ij).
 template <int Q>
@@ -358,10 +489,19 @@ int w4q_launch_scale_search(const float* w, int64_t d_out, int64_t d_in, const f
                             uint8_t* idx, float* obj, float* obj_all, hipStream_t s) {
   const int64_t G = d_in / kGroup;
   if (G > 65535) return W4Q_EUNSUPPORTED;
-  const dim3 grid1(static_cast<unsigned>((d_out + kThreads / 2 - 1) / (kThreads / 2)),
-                   static_cast<unsigned>(G));
-  hipLaunchKernelGGL(search_split_kernel, grid1, dim3(kThreads), 0, s, w, d_out, d_in, h, ldh, alpha,
-                     n_cand, scale, idx, obj, obj_all);
+  // 32 rows per wavefront, or 16 when that leaves too few wavefronts to fill the SIMDs
+  const int64_t waves32 = (d_out + 31) / 32 * G;
+  if (waves32 >= kWaves16Below) {
+    const dim3 grid1(static_cast<unsigned>((d_out + kThreads / 2 - 1) / (kThreads / 2)),
+                     static_cast<unsigned>(G));
+    hipLaunchKernelGGL(search_split_kernel, grid1, dim3(kThreads), 0, s, w, d_out, d_in, h, ldh, alpha,
+                       n_cand, scale, idx, obj, obj_all);
+  } else {
+    const dim3 grid1(static_cast<unsigned>((d_out + kThreads / 4 - 1) / (kThreads / 4)),
+                     static_cast<unsigned>(G));
+    hipLaunchKernelGGL(search_split16_kernel, grid1, dim3(kThreads), 0, s, w, d_out, d_in, h, ldh,
+                       alpha, n_cand, scale, idx, obj, obj_all);
+  }
   if (hipGetLastError() != hipSuccess) return W4Q_EHIP;
   const dim3 grid(static_cast<unsigned>((d_out + kThreads - 1) / kThreads), static_cast<unsigned>(G));
   hipLaunchKernelGGL(search_fp64_kernel, grid, dim3(kThreads), 0, s, w, d_out, d_in, h, ldh, alpha,

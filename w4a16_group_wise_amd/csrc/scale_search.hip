@@ -71,6 +71,19 @@ __device__ __forceinline__ void codes(const float (&wv)[N], float d, float (&c)[
   }
 }
 
+// candidate(amax, alpha) without the IEEE division sequence: t / 7 correctly rounded as
+// q0 = RN(t * RN(1/7)) followed by one fma correction with the exact remainder t - 7 q0.  Checked
+// exhaustively against RN(t / 7) for every normal fp32 t (quotients below fp16's range become 0
+// in the conversion either way); an infinite t (alpha * amax beyond fp32) keeps t / 7 = t.
+__device__ __forceinline__ float candidate_fast(float amax, float alpha) {
+  const float t = alpha * amax;
+  constexpr float c = 1.0f / 7.0f;
+  const float q0 = t * c;
+  float q = __builtin_fmaf(__builtin_fmaf(-q0, 7.0f, t), c, q0);
+  q = __builtin_fabsf(t) == __builtin_inff() ? t : q;
+  return f16_bits_to_f32(f32_to_f16_bits(q));
+}
+
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
@@ -178,12 +191,12 @@ __global__ __launch_bounds__(kThreads) void search_split_kernel(
 
   float best = __builtin_inff(), second = __builtin_inff(), dbest = 0.0f;
   int kbest = 0;
-  float d_next = candidate(amax, alpha[0]);
+  float d_next = candidate_fast(amax, alpha[0]);
 #pragma unroll 1
   for (int k = 0; k < n_cand; ++k) {
     const float d = d_next;
     // the next candidate's step, off this candidate's dependency chain
-    d_next = candidate(amax, alpha[k + 1 < n_cand ? k + 1 : k]);
+    d_next = candidate_fast(amax, alpha[k + 1 < n_cand ? k + 1 : k]);
     const float ds = d * sw;  // exact; the codes of sw w at ds are those of w at d
     float e[16];
     // at a zero step the error is w whatever the codes are (w - c * 0), so the codes need not
@@ -304,13 +317,13 @@ __global__ __launch_bounds__(kThreads) void search_split16_kernel(
 
   float best = __builtin_inff(), second = __builtin_inff(), dbest = 0.0f;
   int kbest = 0;
-  float d_next = candidate(amax, alpha[0]);
+  float d_next = candidate_fast(amax, alpha[0]);
   const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 1
   for (int k = 0; k < n_cand; ++k) {
     const float d = d_next;
     // the next candidate's step, off this candidate's dependency chain
-    d_next = candidate(amax, alpha[k + 1 < n_cand ? k + 1 : k]);
+    d_next = candidate_fast(amax, alpha[k + 1 < n_cand ? k + 1 : k]);
     const float ds = d * sw;  // exact; the codes of sw w at ds are those of w at d
     float e[8];
     codes<8, false>(wv, ds, e);  // at a zero step the error is w whatever the codes are

@@ -84,6 +84,19 @@ __device__ __forceinline__ float candidate_fast(float amax, float alpha) {
   return f16_bits_to_f32(f32_to_f16_bits(q));
 }
 
+// Running first minimum (score, index, step) and second-smallest score of a candidate loop,
+// without branches: best = min(best, o), second = min(max(best, o), second) (a tie with the
+// best makes second equal to it; NaN scores leave both unchanged), and the index and step move
+// only on a strictly smaller score, so the first of equal minima is kept.
+__device__ __forceinline__ void track(float o, int k, float d, float& best, float& second, int& kbest,
+                                      float& dbest) {
+  const bool better = o < best;
+  kbest = better ? k : kbest;
+  dbest = better ? d : dbest;
+  second = __builtin_fminf(__builtin_fmaxf(best, o), second);
+  best = __builtin_fminf(best, o);
+}
+
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
@@ -142,6 +155,7 @@ __device__ __forceinline__ int scale_exp(float m) {
 // 2^-22 of the form's magnitude before the exact rescale by 2^-(2 log2 sw + log2 sh).  The
 // headroom matters when the channel scales of X spread widely: the block's small entries then
 // lie many binades below its largest one and still need their full 22 bits.
+template <bool kAll>
 __global__ __launch_bounds__(kThreads) void search_split_kernel(
     const float* __restrict__ w, int64_t d_out, int64_t d_in, const float* __restrict__ h,
     int64_t ldh, const float* __restrict__ alpha, int n_cand, float* __restrict__ scale,
@@ -231,13 +245,8 @@ __global__ __launch_bounds__(kThreads) void search_split_kernel(
                                                      __builtin_bit_cast(uint32_t, part), false, false);
     const uint32_t u0 = pr[0], u1 = pr[1];
     const float o = __builtin_ldexpf(__builtin_bit_cast(float, u0) + __builtin_bit_cast(float, u1), unscale);
-    if (obj_all != nullptr && live && hh == 0) obj_all[(r * G + g) * n_cand + k] = o;
-    // running first minimum and second-smallest score (branch-free)
-    const bool better = o < best;
-    second = better ? best : __builtin_fminf(second, o);
-    kbest = better ? k : kbest;
-    dbest = better ? d : dbest;
-    best = better ? o : best;
+    if (kAll && live && hh == 0) obj_all[(r * G + g) * n_cand + k] = o;
+    track(o, k, d, best, second, kbest, dbest);
   }
   if (!live || hh != 0) return;
   const int64_t o_ = r * G + g;
@@ -259,6 +268,7 @@ __global__ __launch_bounds__(kThreads) void search_split_kernel(
 // lane feeds its own 8 errors as the B operand and Hg[8 (i / 4) + 4 u + i % 4][8 q + e] (i = the
 // lane's j) as the A operand, and receives D[p][j] for exactly its own positions
 // p = 8 q + 4 u + r (r = 0..3).  Scaling, splitting and accumulation order as above.
+template <bool kAll>
 __global__ __launch_bounds__(kThreads) void search_split16_kernel(
     const float* __restrict__ w, int64_t d_out, int64_t d_in, const float* __restrict__ h,
     int64_t ldh, const float* __restrict__ alpha, int n_cand, float* __restrict__ scale,
@@ -358,12 +368,8 @@ __global__ __launch_bounds__(kThreads) void search_split16_kernel(
                                                      __builtin_bit_cast(uint32_t, half), false, false);
     const uint32_t b0 = s2[0], b1 = s2[1];
     const float o = __builtin_ldexpf(__builtin_bit_cast(float, b0) + __builtin_bit_cast(float, b1), unscale);
-    if (obj_all != nullptr && live && q == 0) obj_all[(r * G + g) * n_cand + k] = o;
-    const bool better = o < best;
-    second = better ? best : __builtin_fminf(second, o);
-    kbest = better ? k : kbest;
-    dbest = better ? d : dbest;
-    best = better ? o : best;
+    if (kAll && live && q == 0) obj_all[(r * G + g) * n_cand + k] = o;
+    track(o, k, d, best, second, kbest, dbest);
   }
   if (!live || q != 0) return;
   const int64_t o_ = r * G + g;
@@ -507,13 +513,21 @@ int w4q_launch_scale_search(const float* w, int64_t d_out, int64_t d_in, const f
   if (waves32 >= kWaves16Below) {
     const dim3 grid1(static_cast<unsigned>((d_out + kThreads / 2 - 1) / (kThreads / 2)),
                      static_cast<unsigned>(G));
-    hipLaunchKernelGGL(search_split_kernel, grid1, dim3(kThreads), 0, s, w, d_out, d_in, h, ldh, alpha,
-                       n_cand, scale, idx, obj, obj_all);
+    if (obj_all != nullptr)
+      hipLaunchKernelGGL(search_split_kernel<true>, grid1, dim3(kThreads), 0, s, w, d_out, d_in, h, ldh,
+                         alpha, n_cand, scale, idx, obj, obj_all);
+    else
+      hipLaunchKernelGGL(search_split_kernel<false>, grid1, dim3(kThreads), 0, s, w, d_out, d_in, h, ldh,
+                         alpha, n_cand, scale, idx, obj, obj_all);
   } else {
     const dim3 grid1(static_cast<unsigned>((d_out + kThreads / 4 - 1) / (kThreads / 4)),
                      static_cast<unsigned>(G));
-    hipLaunchKernelGGL(search_split16_kernel, grid1, dim3(kThreads), 0, s, w, d_out, d_in, h, ldh,
-                       alpha, n_cand, scale, idx, obj, obj_all);
+    if (obj_all != nullptr)
+      hipLaunchKernelGGL(search_split16_kernel<true>, grid1, dim3(kThreads), 0, s, w, d_out, d_in, h, ldh,
+                         alpha, n_cand, scale, idx, obj, obj_all);
+    else
+      hipLaunchKernelGGL(search_split16_kernel<false>, grid1, dim3(kThreads), 0, s, w, d_out, d_in, h, ldh,
+                         alpha, n_cand, scale, idx, obj, obj_all);
   }
   if (hipGetLastError() != hipSuccess) return W4Q_EHIP;
   const dim3 grid(static_cast<unsigned>((d_out + kThreads - 1) / kThreads), static_cast<unsigned>(G));

@@ -21,16 +21,14 @@
 //
 // Precision: pass 1 scores with fp32-level error (a few 2^-22 relative).  A group whose two
 // best pass-1 scores are within a relative 1e-5 (this includes exact ties and all-zero groups)
-// is marked (index value 255, which n_cand <= 255 keeps free), and pass 2 re-scores every
-// candidate of each marked group in fp64, one candidate per lane of a wavefront, and takes the
-// first minimum.
+// is re-scored at the end of the same workgroup: every candidate again in fp64, one candidate
+// per lane, first minimum.
 #include "common.hpp"
 
 namespace w4q {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr uint8_t kMarked = 255;
 constexpr float kTieRel = 1e-5f;
 constexpr float kNear = 0.5f - 1e-5f;
 // below this many 32-row wavefronts pass 1 runs 16 rows per wavefront
@@ -135,6 +133,112 @@ __device__ __forceinline__ int scale_exp(float m) {
   return s > 127 ? 127 : (s < -126 ? -126 : s);
 }
 
+// Pass 2, inside the pass-1 block: fp64 re-scoring of the rows the block marked (their two best
+// pass-1 scores within kTieRel), every candidate again, one candidate per lane (same grid, same
+// codes, fp64 sums, first minimum).  A block covers one group column g, so it stages Hg in LDS
+// as fp64 (transposed: column j of Hg is contiguous) when any of its rows is marked, and its
+// four wavefronts score each marked row together: wavefront q forms s_i = sum_j H_ij e_j and
+// the partial sum of e_i s_i for the positions i = 8q .. 8q + 7, the four partials added in a
+// fixed order.  e_j is recomputed from the staged weights where it is needed, so the re-scoring
+// holds few registers.  Every thread of the block calls this; `marked` flags this lane's row
+// (lanes below rows_per_wave own rows row0 + wavefront * rows_per_wave + lane).
+__device__ __forceinline__ void rescore_marked(const float* __restrict__ w, int64_t d_in,
+                                               const float* __restrict__ h, int64_t ldh,
+                                               const float* __restrict__ alpha, int n_cand,
+                                               float* __restrict__ scale, uint8_t* __restrict__ idx,
+                                               float* __restrict__ obj, float* __restrict__ obj_all,
+                                               int64_t g, int64_t row0, int rows_per_wave, bool marked) {
+  static_assert(kThreads == 256, "four wavefronts share a marked row's positions");
+  constexpr int kWaves = kThreads / 64;
+  constexpr int kPos = kGroup / kWaves;  // positions per wavefront
+  __shared__ double hs[kGroup * kGroup];
+  __shared__ double part[kWaves][64];
+  __shared__ uint64_t marks[kWaves];
+  __shared__ float wl[kGroup];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const uint64_t mask = __builtin_amdgcn_ballot_w64(marked);
+  if (!__syncthreads_or(marked)) return;  // block-uniform
+  if (lane == 0) marks[wid] = mask;
+  const int64_t G = d_in / kGroup;
+  const float* __restrict__ hg = h + g * kGroup * ldh + g * kGroup;
+  for (int t = threadIdx.x; t < kGroup * kGroup; t += kThreads)
+    hs[(t % kGroup) * kGroup + t / kGroup] = static_cast<double>(hg[(t / kGroup) * ldh + t % kGroup]);
+  __syncthreads();
+  // every wavefront walks the same list of marked rows, so the barriers below are uniform
+  for (int q = 0; q < kWaves; ++q) {
+    uint64_t m = marks[q];
+    while (m != 0) {
+      const int src = __builtin_ctzll(m);
+      m &= m - 1;
+      const int64_t rs = row0 + q * rows_per_wave + src;
+      const int64_t o_ = rs * G + g;
+      if (threadIdx.x < kGroup) wl[threadIdx.x] = w[rs * d_in + g * kGroup + threadIdx.x];
+      __syncthreads();
+      float amax = __builtin_fabsf(wl[lane & (kGroup - 1)]);
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
+      double best = __builtin_inf();
+      int kbest = 0x7FFFFFFF;
+      float dbest = 0.0f;
+      for (int k0 = 0; k0 < n_cand; k0 += 64) {
+        const int k = k0 + lane;
+        const bool kv = k < n_cand;
+        const float d = candidate_fast(amax, alpha[kv ? k : 0]);  // the step pass 1 used
+        const bool zero = !(d > 0.0f);
+        const float inv = __builtin_amdgcn_rcpf(zero ? 1.0f : d);
+        auto err = [&](float wi) {  // e = w - code(w, d) d, exact in fp64
+          const float ci = zero ? 0.0f : code_rcp(wi, d, inv);
+          return __builtin_fma(-static_cast<double>(ci), static_cast<double>(d), static_cast<double>(wi));
+        };
+        double sv[kPos];
+#pragma unroll
+        for (int t = 0; t < kPos; ++t) sv[t] = 0.0;
+#pragma unroll 1
+        for (int j = 0; j < kGroup; ++j) {
+          const double ej = err(wl[j]);
+          const double* hc = hs + j * kGroup + kPos * wid;
+#pragma unroll
+          for (int t = 0; t < kPos; ++t) sv[t] = __builtin_fma(hc[t], ej, sv[t]);
+        }
+        double op = 0.0;
+#pragma unroll
+        for (int t = 0; t < kPos; ++t) op = __builtin_fma(err(wl[kPos * wid + t]), sv[t], op);
+        part[wid][lane] = op;
+        __syncthreads();
+        const double o = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+        __syncthreads();  // part is rewritten by the next chunk
+        if (kv) {
+          if (obj_all != nullptr && wid == 0) obj_all[o_ * n_cand + k] = static_cast<float>(o);
+          if (o < best) {  // a lane's candidates rise with k0: strict keeps the first
+            best = o;
+            kbest = k;
+            dbest = d;
+          }
+        }
+      }
+      // wavefront argmin, ties to the lowest candidate index (every wavefront holds the same
+      // scores; the first thread writes)
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const double ob = __shfl_xor(best, off);
+        const int ok = __shfl_xor(kbest, off);
+        const float od = __shfl_xor(dbest, off);
+        const bool take = (ob < best) || (ob == best && ok < kbest);
+        best = take ? ob : best;
+        kbest = take ? ok : kbest;
+        dbest = take ? od : dbest;
+      }
+      if (threadIdx.x == 0) {
+        scale[o_] = dbest;
+        idx[o_] = static_cast<uint8_t>(kbest);
+        if (obj != nullptr) obj[o_] = static_cast<float>(best);
+      }
+      __syncthreads();  // wl is rewritten for the next marked row
+    }
+  }
+}
+
 // Pass 1 on the fp16 matrix cores, fp32-accurate.  A wavefront scores 32 rows (m = lane % 32)
 // of one group column g; the two lanes of a row (h = lane / 32) each own 16 of the group's 32
 // positions, p = 8 q + 4 h + r (q, r in 0..3), held as element 4 q + r of the lane's arrays.
@@ -156,7 +260,7 @@ __device__ __forceinline__ int scale_exp(float m) {
 // headroom matters when the channel scales of X spread widely: the block's small entries then
 // lie many binades below its largest one and still need their full 22 bits.
 template <bool kAll>
-__global__ __launch_bounds__(kThreads) void search_split_kernel(
+__global__ __launch_bounds__(kThreads, 5) void search_split_kernel(
     const float* __restrict__ w, int64_t d_out, int64_t d_in, const float* __restrict__ h,
     int64_t ldh, const float* __restrict__ alpha, int n_cand, float* __restrict__ scale,
     uint8_t* __restrict__ idx, float* __restrict__ obj, float* __restrict__ obj_all) {
@@ -248,16 +352,15 @@ __global__ __launch_bounds__(kThreads) void search_split_kernel(
     if (kAll && live && hh == 0) obj_all[(r * G + g) * n_cand + k] = o;
     track(o, k, d, best, second, kbest, dbest);
   }
-  if (!live || hh != 0) return;
-  const int64_t o_ = r * G + g;
   const bool clear = (second - best) > kTieRel * best;  // false for ties, zeros and NaN
-  if (clear) {
+  if (live && hh == 0 && clear) {
+    const int64_t o_ = r * G + g;
     scale[o_] = dbest;
     idx[o_] = static_cast<uint8_t>(kbest);
     if (obj != nullptr) obj[o_] = best;
-  } else {
-    idx[o_] = kMarked;
   }
+  rescore_marked(w, d_in, h, ldh, alpha, n_cand, scale, idx, obj, obj_all, g,
+                 (int64_t)blockIdx.x * (kThreads / 2), 32, live && hh == 0 && !clear);
 }
 
 // Pass 1 for small grids: 16 rows per wavefront (twice the wavefronts of the kernel above, so
@@ -371,131 +474,15 @@ __global__ __launch_bounds__(kThreads) void search_split16_kernel(
     if (kAll && live && q == 0) obj_all[(r * G + g) * n_cand + k] = o;
     track(o, k, d, best, second, kbest, dbest);
   }
-  if (!live || q != 0) return;
-  const int64_t o_ = r * G + g;
   const bool clear = (second - best) > kTieRel * best;  // false for ties, zeros and NaN
-  if (clear) {
+  if (live && q == 0 && clear) {
+    const int64_t o_ = r * G + g;
     scale[o_] = dbest;
     idx[o_] = static_cast<uint8_t>(kbest);
     if (obj != nullptr) obj[o_] = best;
-  } else {
-    idx[o_] = kMarked;
   }
-}
-
-// Pass 2 helper: wavefront Q's share of o = sum_i e_i sum_j H_ij e_j, the positions
-// i = 8Q..8Q+7 (hs holds Hg transposed: hs[j * 32 + i] = H_ij).
-template <int Q>
-__device__ __forceinline__ double partial_form(const double* hs, const double (&e)[32]) {
-  constexpr int kRows = kGroup / 4;
-  double sv[kRows];
-#pragma unroll
-  for (int t = 0; t < kRows; ++t) sv[t] = 0.0;
-#pragma unroll
-  for (int j = 0; j < kGroup; ++j) {
-    const double* hc = hs + j * kGroup + Q * kRows;
-#pragma unroll
-    for (int t = 0; t < kRows; ++t) sv[t] = __builtin_fma(hc[t], e[j], sv[t]);
-  }
-  double o = 0.0;
-#pragma unroll
-  for (int t = 0; t < kRows; ++t) o = __builtin_fma(e[Q * kRows + t], sv[t], o);
-  return o;
-}
-
-// Pass 2: fp64 re-scoring of the marked groups, one candidate per lane (same grid, same codes,
-// fp64 sums, first minimum).  A block covers 256 rows of one group column g; when any of them
-// is marked, the block stages Hg in LDS as fp64 and its four wavefronts score each marked row
-// together: wavefront q forms s_i = sum_j H_ij e_j and the partial sum of e_i s_i for the
-// positions i = 8q..8q+7, and the four partials are added in a fixed order.
-__global__ __launch_bounds__(kThreads) void search_fp64_kernel(
-    const float* __restrict__ w, int64_t d_out, int64_t d_in, const float* __restrict__ h,
-    int64_t ldh, const float* __restrict__ alpha, int n_cand, float* __restrict__ scale,
-    uint8_t* __restrict__ idx, float* __restrict__ obj, float* __restrict__ obj_all) {
-  static_assert(kThreads == 256, "four wavefronts share a marked row's positions");
-  constexpr int kWaves = kThreads / 64;
-  __shared__ double hs[kGroup * kGroup];
-  __shared__ double part[kWaves][64];
-  __shared__ uint64_t marks[kWaves];
-  const int64_t G = d_in / kGroup;
-  const int64_t g = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int64_t r0 = (int64_t)blockIdx.x * kThreads;
-  const int64_t r = r0 + threadIdx.x;
-  const bool marked = r < d_out && idx[r * G + g] == kMarked;
-  if (!__syncthreads_or(marked)) return;  // block-uniform
-  const uint64_t mask = __builtin_amdgcn_ballot_w64(marked);
-  if (lane == 0) marks[wid] = mask;
-  const float* __restrict__ hg = h + g * kGroup * ldh + g * kGroup;
-  for (int t = threadIdx.x; t < kGroup * kGroup; t += kThreads)
-    hs[(t % kGroup) * kGroup + t / kGroup] = static_cast<double>(hg[(t / kGroup) * ldh + t % kGroup]);
-  __syncthreads();
-  // every wavefront walks the same list of marked rows, so the barriers below are uniform
-  for (int q = 0; q < kWaves; ++q) {
-    uint64_t m = marks[q];
-    while (m != 0) {
-      const int src = __builtin_ctzll(m);
-      m &= m - 1;
-      const int64_t rs = r0 + q * 64 + src;
-      const int64_t o_ = rs * G + g;
-      float wv[32];
-      load_group(w + rs * d_in + g * kGroup, wv);
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(wv[i]));
-      double best = __builtin_inf();
-      int kbest = 0x7FFFFFFF;
-      float dbest = 0.0f;
-      for (int k0 = 0; k0 < n_cand; k0 += 64) {
-        const int k = k0 + lane;
-        const bool kv = k < n_cand;
-        const float d = candidate(amax, alpha[kv ? k : 0]);
-        float c[32];
-        codes<32>(wv, d, c);  // same codes as pass 1
-        double e[32];
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-          e[i] = __builtin_fma(-static_cast<double>(c[i]), static_cast<double>(d), static_cast<double>(wv[i]));
-        double op;
-        switch (wid) {
-          case 0: op = partial_form<0>(hs, e); break;
-          case 1: op = partial_form<1>(hs, e); break;
-          case 2: op = partial_form<2>(hs, e); break;
-          default: op = partial_form<3>(hs, e); break;
-        }
-        part[wid][lane] = op;
-        __syncthreads();
-        const double o = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
-        __syncthreads();  // part is rewritten by the next chunk or row
-        if (kv) {
-          if (obj_all != nullptr && wid == 0) obj_all[o_ * n_cand + k] = static_cast<float>(o);
-          if (o < best) {  // a lane's candidates rise with k0: strict keeps the first
-            best = o;
-            kbest = k;
-            dbest = d;
-          }
-        }
-      }
-      // wavefront argmin, ties to the lowest candidate index (every wavefront holds the same
-      // scores; the first one writes)
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const double ob = __shfl_xor(best, off);
-        const int ok = __shfl_xor(kbest, off);
-        const float od = __shfl_xor(dbest, off);
-        const bool take = (ob < best) || (ob == best && ok < kbest);
-        best = take ? ob : best;
-        kbest = take ? ok : kbest;
-        dbest = take ? od : dbest;
-      }
-      if (threadIdx.x == 0) {
-        scale[o_] = dbest;
-        idx[o_] = static_cast<uint8_t>(kbest);
-        if (obj != nullptr) obj[o_] = static_cast<float>(best);
-      }
-    }
-  }
+  rescore_marked(w, d_in, h, ldh, alpha, n_cand, scale, idx, obj, obj_all, g,
+                 (int64_t)blockIdx.x * (kThreads / 4), 16, live && q == 0 && !clear);
 }
 
 }  // namespace
@@ -529,9 +516,5 @@ int w4q_launch_scale_search(const float* w, int64_t d_out, int64_t d_in, const f
       hipLaunchKernelGGL(search_split16_kernel<false>, grid1, dim3(kThreads), 0, s, w, d_out, d_in, h, ldh,
                          alpha, n_cand, scale, idx, obj, obj_all);
   }
-  if (hipGetLastError() != hipSuccess) return W4Q_EHIP;
-  const dim3 grid(static_cast<unsigned>((d_out + kThreads - 1) / kThreads), static_cast<unsigned>(G));
-  hipLaunchKernelGGL(search_fp64_kernel, grid, dim3(kThreads), 0, s, w, d_out, d_in, h, ldh, alpha,
-                     n_cand, scale, idx, obj, obj_all);
   return w4q_launch_status();
 }

@@ -68,7 +68,7 @@ CSRC = os.path.join(ROOT, "w4a16_group_wise_amd", "csrc")
 # kernel family -> (source file, symbol substrings as they appear in a kernel trace)
 KERNELS = {
     "hessian": ("hessian.hip", ["hessian_kernel", "hessian_fixup_kernel"]),
-    "scale_search": ("scale_search.hip", ["search_split_kernel", "search_fp64_kernel"]),
+    "scale_search": ("scale_search.hip", ["search_split_kernel", "search_split16_kernel"]),
     "pack": ("pack_lsq.hip", ["pack_kernel"]),
     "lsq_fwd": ("pack_lsq.hip", ["lsq_fwd_kernel"]),
     "lsq_bwd": ("pack_lsq.hip", ["lsq_bwd_kernel"]),

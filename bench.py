@@ -374,10 +374,13 @@ def run(args):
     #     over repetitions is reported
     flush_buf = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     flush_sink = torch.empty(65536, dtype=torch.int32, device=dev)
+    # the floor of this protocol: a kernel that reads 4 KB, timed the same way
+    tiny_buf = torch.ones(4096, dtype=torch.uint8, device=dev)
+    floor = [("_floor", lambda: w4q.probe_read(tiny_buf, nontemporal=False, sink=flush_sink))]
     reps = max(args.steps, 20)
-    ev = {n: [] for n, _ in launches}
+    ev = {n: [] for n, _ in launches + floor}
     for _ in range(reps):
-        for name, fn in launches:
+        for name, fn in launches + floor:
             w4q.probe_read(flush_buf, nontemporal=False, sink=flush_sink)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -386,7 +389,8 @@ def run(args):
             e1.record()
             ev[name].append((e0, e1))
     torch.cuda.synchronize()
-    del flush_buf, flush_sink
+    del flush_buf, flush_sink, tiny_buf
+    floor_us = float(np.median([a.elapsed_time(b) for a, b in ev.pop("_floor")])) * 1e3
     peaks = measured_peaks(dev)
     comps = {}
     for name, pairs in ev.items():
@@ -428,6 +432,7 @@ def run(args):
                                   "best of 5, HIP events"},
         "timing": f"per launch: median of {reps} repetitions, each after a 1 GiB read of other data "
                   "(cold Infinity Cache), HIP events on the launch stream",
+        "launch_floor_us": round(floor_us, 3),  # a 4 KB read kernel timed the same way
         "components": {
             "gemv_m1_frac_hbm": gv["frac"],
             "search_groups_per_s": round(step.d_out * step.G / (comps["scale_search"]["us"] * 1e-6), 1),

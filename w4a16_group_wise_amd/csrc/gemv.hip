@@ -203,7 +203,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint16_t* __restri
 // so the order of the 8 products inside the group is the same on both sides).  The result:
 // lane (q, n) holds rows m = 4 q + r of column n.
 //
-// A workgroup owns 32 rows of W (two tiles); its wavefronts take d_in's 8-group batches
+// A workgroup owns 32 rows of W (two tiles; 16 rows, one tile, when d_out < 8192, where two
+// would leave too few workgroups); its wavefronts take d_in's 8-group batches
 // round-robin.  Each wavefront keeps two batches of codes and scales in flight: those of its next
 // batch are issued before the current one is reduced; the activations (L2-resident) are loaded
 // one batch ahead, right after the previous batch's products.  Codes: lane (q, n) loads the whole group 4 h + q of row n
@@ -212,7 +213,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint16_t* __restri
 // 8 scales per row when G % 8 == 0 (then every batch start is 16-byte aligned), else one
 // 2-byte load per group.  The wavefronts' partial results are added in LDS in a fixed order.
 constexpr int kMmaWaves = 8;
-constexpr int kMmaTiles = 2;
 constexpr int kMmaBatch = 8;
 
 // 4 x 4 transpose across the 16-lane rows R = lane / 16: on entry v[j] of row R holds element
@@ -239,13 +239,15 @@ __device__ __forceinline__ void transpose4(u32x4& v) {
   v = u32x4{a0, a1, a2, a3};
 }
 
+template <int kMmaTiles>
 struct MmaBatch {
   u32x4 cv[kMmaBatch / 4][kMmaTiles];  // codes (transposed after arrival)
   u32x4 sc[kMmaTiles];                 // 8 scales per row (vector path)
   uint32_t s1[kMmaBatch][kMmaTiles];   // one scale per group (2-byte path)
 };
 
-template <bool kVecScales>
+// kMmaTiles: 16-row tiles of W per workgroup (1 or 2)
+template <bool kVecScales, int kMmaTiles>
 __global__ __launch_bounds__(kMmaWaves * 64) void gemv_mma_kernel(const uint16_t* __restrict__ x, int m_rows,
                                                                   const uint8_t* __restrict__ packed,
                                                                   const uint16_t* __restrict__ s16,
@@ -278,7 +280,7 @@ __global__ __launch_bounds__(kMmaWaves * 64) void gemv_mma_kernel(const uint16_t
 
   // the loads of batch b, all issued at once; groups past G repeat the last one.  Every loaded
   // value passes through an empty asm, so no load can sink into the product of its group.
-  auto load = [&](int b, MmaBatch& B) {
+  auto load = [&](int b, MmaBatch<kMmaTiles>& B) {
     const int gb = b * kMmaBatch;
 #pragma unroll
     for (int h = 0; h < kMmaBatch / 4; ++h) {
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(kMmaWaves * 64) void gemv_mma_kernel(const uint16_t
 #pragma unroll
   for (int t = 0; t < kMmaTiles; ++t) acc[t] = zero4;
 
-  auto compute = [&](int b, MmaBatch& B) {
+  auto compute = [&](int b, MmaBatch<kMmaTiles>& B) {
     const int nb = G - b * kMmaBatch < kMmaBatch ? G - b * kMmaBatch : kMmaBatch;
 #pragma unroll
     for (int h = 0; h < kMmaBatch / 4; ++h)
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(kMmaWaves * 64) void gemv_mma_kernel(const uint16_t
   // workgroup reads a few hundred contiguous bytes of each of its rows; two register sets: the
   // next batch is in flight while the current one is reduced
   constexpr int S = kMmaWaves;
-  MmaBatch B0, B1;
+  MmaBatch<kMmaTiles> B0, B1;
   if (wid < nbat) {
     load(wid, B0);
     load_x(wid);
@@ -784,14 +786,20 @@ int launch_group_chunk(const w4q_gemv_problem* probs, int cnt, int y_dtype, hipS
 int w4q_launch_gemv(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
                     int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t s) {
   if (m >= 2 && m <= 16) {
-    const int64_t blocks = (d_out + 16 * kMmaTiles - 1) / (16 * kMmaTiles);
+    const int tiles = d_out < 8192 ? 1 : 2;
+    const int64_t blocks = (d_out + 16 * tiles - 1) / (16 * tiles);
     if (blocks > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
-    if ((d_in / kGroup) % kMmaBatch == 0)
-      hipLaunchKernelGGL(gemv_mma_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kMmaWaves * 64), 0, s,
-                         x, static_cast<int>(m), packed, s16, d_out, d_in, y, y_dtype);
+    const bool vec = (d_in / kGroup) % kMmaBatch == 0;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kMmaWaves * 64);
+    const int mr = static_cast<int>(m);
+    if (vec && tiles == 2)
+      hipLaunchKernelGGL((gemv_mma_kernel<true, 2>), grid, block, 0, s, x, mr, packed, s16, d_out, d_in, y, y_dtype);
+    else if (vec)
+      hipLaunchKernelGGL((gemv_mma_kernel<true, 1>), grid, block, 0, s, x, mr, packed, s16, d_out, d_in, y, y_dtype);
+    else if (tiles == 2)
+      hipLaunchKernelGGL((gemv_mma_kernel<false, 2>), grid, block, 0, s, x, mr, packed, s16, d_out, d_in, y, y_dtype);
     else
-      hipLaunchKernelGGL(gemv_mma_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kMmaWaves * 64), 0, s,
-                         x, static_cast<int>(m), packed, s16, d_out, d_in, y, y_dtype);
+      hipLaunchKernelGGL((gemv_mma_kernel<false, 1>), grid, block, 0, s, x, mr, packed, s16, d_out, d_in, y, y_dtype);
     return w4q_launch_status();
   }
   // one activation row: the persistent stream kernel, or the plain vector kernel when the

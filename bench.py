@@ -10,7 +10,8 @@ K = 40 candidates over alpha in [0.4, 1.0]).  Every kernel is timed with HIP eve
 stream it runs on; the JSON line reports the M=1 GEMV bandwidth as `value`, each kernel's
 rate against its roofline, and the CPU oracle timed on a bounded sample of the same work.
 
-    python bench.py [--steps K] [--warmup W] [--workload cfg2|cfg3|cfg5] [--no-cpu]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload proj_2048x2048|mlp_gate_8192x2048|decoder36_gate_12288x4096] [--no-cpu]
     python bench.py --pmc-summary FETCH_DIR WRITE_DIR   (writes profiles/traffic_<workload>.json)
 """
 from __future__ import annotations
@@ -89,12 +90,12 @@ def src_hash(fname: str) -> str:
 
 
 WORKLOADS = {
-    "cfg2": dict(cfg=2, lin=0, desc="2048x2048 attention-projection layer; X 2048 tok x 2048 bf16 "
+    "proj_2048x2048": dict(synth="proj_2048x2048", lin=0, desc="2048x2048 attention-projection layer; X 2048 tok x 2048 bf16 "
                  "(lognormal(0,1) channel scales); K=40, alpha in [0.4,1.0]; GEMV M=1,4,16; "
                  "GEMM M=2048", gemm_m=2048),
-    "cfg3": dict(cfg=3, lin=0, desc="MLP gate 8192x2048; X 4096 tok x 2048 bf16 (lognormal(0,1.5)); "
+    "mlp_gate_8192x2048": dict(synth="mlp_8192x2048", lin=0, desc="MLP gate 8192x2048; X 4096 tok x 2048 bf16 (lognormal(0,1.5)); "
                  "K=40; GEMV M=1,4,16; GEMM M=256", gemm_m=256),
-    "cfg5": dict(cfg=5, lin=4, desc="36-layer stack's gate projection 12288x4096; X 8192 tok x 4096 "
+    "decoder36_gate_12288x4096": dict(synth="decoder36_h4096", lin=4, desc="36-layer stack's gate projection 12288x4096; X 8192 tok x 4096 "
                  "bf16; K=40; GEMV M=1,4,16; GEMM M=2048", gemm_m=2048),
 }
 
@@ -106,7 +107,7 @@ class Step:
         import torch
         from w4a16_group_wise_amd import synth
 
-        c = synth.CONFIGS[wl["cfg"]]
+        c = synth.WORKLOADS[wl["synth"]]
         lin = c.linears[wl["lin"]]
         self.c, self.lin = c, lin
         w = c.weight(0, lin)
@@ -266,7 +267,7 @@ def decode_pass(dev, reps=3):
     import w4a16_group_wise_amd as w4q
     from w4a16_group_wise_amd import synth
 
-    c = synth.CONFIGS[5]
+    c = synth.WORKLOADS["decoder36_h4096"]
     g = torch.Generator(device=dev)
     g.manual_seed(5)
     mats, total = [], 0
@@ -338,8 +339,8 @@ def run(args):
     import w4a16_group_wise_amd as w4q
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                          "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        print(json.dumps({"error": "runs on one GPU only; --gpus must be 1 "
+                          "(sharding over several GPUs is not implemented)"}))
         sys.exit(2)
     dev = torch.device("cuda:0")
     wl = WORKLOADS[args.workload]
@@ -520,7 +521,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="cfg2", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="proj_2048x2048", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--pmc-copy", action="store_true")

@@ -1,5 +1,5 @@
-"""GPU parity of every step against the CPU oracle (configs 1-2 in full, edge cases, ragged
-shapes).  Inputs are the seeded synthetic layers of w4a16_group_wise_amd.synth; each stage is
+"""GPU parity of every step against the CPU oracle (the 256x512 and 2048x2048 layers in full, edge
+cases, ragged shapes).  Inputs are the seeded synthetic layers of w4a16_group_wise_amd.synth; each stage is
 fed identical inputs on both sides (e.g. the search gets the GPU's fp32 H on both sides)."""
 import sys
 
@@ -38,11 +38,11 @@ def _cand_fn(w, alpha):
 
 
 # ---------------------------------------------------------------------------------- Hessian
-@pytest.mark.parametrize("cfg", [1, 2])
-def test_hessian_config(dev, cfg):
-    c = synth.CONFIGS[cfg]
+@pytest.mark.parametrize("wl", ["linear_256x512", "proj_2048x2048"])
+def test_hessian_workload(dev, wl):
+    c = synth.WORKLOADS[wl]
     x = c.x(0, "attn")
-    say("hessian cfg", cfg, x.shape)
+    say("hessian", wl, x.shape)
     h = w4q.quant_hessian(dev_bf16(x, dev)).cpu().numpy()
     assert np.array_equal(h, h.T)
     check_hessian(h, oracle.hessian(x))
@@ -70,13 +70,13 @@ def test_hessian_accumulate(dev, d):
 
 
 # ------------------------------------------------------------------------------ scale search
-@pytest.mark.parametrize("cfg", [1, 2])
-def test_search_config(dev, cfg):
-    c = synth.CONFIGS[cfg]
+@pytest.mark.parametrize("wl", ["linear_256x512", "proj_2048x2048"])
+def test_search_workload(dev, wl):
+    c = synth.WORKLOADS[wl]
     lin = c.linears[0]
     w = c.weight(0, lin)
     x = c.x(0, lin.inp)
-    say("search cfg", cfg, w.shape)
+    say("search", wl, w.shape)
     h = w4q.quant_hessian(dev_bf16(x, dev)).cpu().numpy()
     alpha = c.alpha()
     sc, ix, ob, oa, so, io, oo, oao = _search_both(w, h, alpha, dev)
@@ -133,7 +133,7 @@ def test_search_wide_channel_spread(dev, sigma):
 
 
 def test_search_deterministic(dev):
-    c = synth.CONFIGS[1]
+    c = synth.WORKLOADS["linear_256x512"]
     w = c.weight(0, c.linears[0])
     h = w4q.quant_hessian(dev_bf16(c.x(0, "attn"), dev))
     wt, at = dev_f32(w, dev), dev_f32(c.alpha(), dev)
@@ -145,15 +145,15 @@ def test_search_deterministic(dev):
 
 
 # ---------------------------------------------------------------------------------- pack
-@pytest.mark.parametrize("cfg", [1, 2])
-def test_pack_config(dev, cfg):
-    c = synth.CONFIGS[cfg]
+@pytest.mark.parametrize("wl", ["linear_256x512", "proj_2048x2048"])
+def test_pack_workload(dev, wl):
+    c = synth.WORKLOADS[wl]
     w = c.weight(0, c.linears[0])
     G = w.shape[1] // 32
     # scales: max-based candidates stretched per group (fp32, not yet on the fp16 grid)
-    rng = np.random.default_rng(cfg)
+    rng = np.random.default_rng(c.stream)
     scale = (np.abs(w.reshape(-1, G, 32)).max(axis=2) / 7 * rng.uniform(0.4, 1.0, (w.shape[0], G))).astype(np.float32)
-    say("pack cfg", cfg)
+    say("pack", wl)
     p, s16 = w4q.quant_pack(dev_f32(w, dev), dev_f32(scale, dev))
     po, so = oracle.pack(w, scale)
     assert np.array_equal(p.cpu().numpy(), po)
@@ -200,15 +200,15 @@ def _lsq_check(w, scale, g, dev, fused):
 
 
 @pytest.mark.parametrize("fused", [False, True])
-def test_lsq_config1(dev, fused):
-    c = synth.CONFIGS[1]
+def test_lsq_linear_256x512(dev, fused):
+    c = synth.WORKLOADS["linear_256x512"]
     lin = c.linears[0]
     w = c.weight(0, lin)
     g = c.grad(0, lin)
     G = w.shape[1] // 32
     rng = np.random.default_rng(5)
     scale = (np.abs(w.reshape(-1, G, 32)).max(axis=2) / 7 * rng.uniform(0.3, 1.1, (w.shape[0], G))).astype(np.float32)
-    say("lsq cfg1 fused", fused)
+    say("lsq linear_256x512 fused", fused)
     _lsq_check(w, scale, g, dev, fused)
 
 
@@ -225,8 +225,8 @@ def test_lsq_edges(dev):
 
 
 # ----------------------------------------------------------------------------------- GEMM
-def _packed_layer(cfg, layer=0):
-    c = synth.CONFIGS[cfg]
+def _packed_layer(wl, layer=0):
+    c = synth.WORKLOADS[wl]
     lin = c.linears[0]
     w = c.weight(layer, lin)
     G = w.shape[1] // 32
@@ -235,12 +235,14 @@ def _packed_layer(cfg, layer=0):
     return c, lin, packed, s16
 
 
-@pytest.mark.parametrize("cfg,m", [(1, 1), (2, 1), (2, 4), (2, 16), (2, 3), (2, 17), (2, 256)])
+@pytest.mark.parametrize("wl,m", [("linear_256x512", 1), ("proj_2048x2048", 1), ("proj_2048x2048", 4),
+                                  ("proj_2048x2048", 16), ("proj_2048x2048", 3), ("proj_2048x2048", 17),
+                                  ("proj_2048x2048", 256)])
 @pytest.mark.parametrize("bf16_out", [False, True])
-def test_gemm_config(dev, cfg, m, bf16_out):
-    c, lin, packed, s16 = _packed_layer(cfg)
+def test_gemm_workload(dev, wl, m, bf16_out):
+    c, lin, packed, s16 = _packed_layer(wl)
     x = c.x(0, lin.inp)[:m]
-    say("gemm cfg", cfg, "m", m, "bf16", bf16_out)
+    say("gemm", wl, "m", m, "bf16", bf16_out)
     y = w4q.w4a16_gemm(dev_bf16(x, dev), torch.from_numpy(packed).to(dev),
                        torch.from_numpy(s16.view(np.float16)).to(dev),
                        out_dtype=torch.bfloat16 if bf16_out else torch.float32)
@@ -271,7 +273,7 @@ def test_gemm_ragged(dev, m, d_out, d_in):
 
 
 def test_gemm_rows_agree_with_m1(dev):
-    c, lin, packed, s16 = _packed_layer(2)
+    c, lin, packed, s16 = _packed_layer("proj_2048x2048")
     x = c.x(0, lin.inp)[:40]
     pt = torch.from_numpy(packed).to(dev)
     st = torch.from_numpy(s16.view(np.float16)).to(dev)
@@ -316,12 +318,12 @@ def test_gemm_mma_shapes(dev, m, d_out, d_in, dq):
     check_gemm(yg[:, cols], yr, ya)
 
 
-@pytest.mark.parametrize("cfg,m", [(1, 1), (2, 16), (2, 2048)])
+@pytest.mark.parametrize("wl,m", [("linear_256x512", 1), ("proj_2048x2048", 16), ("proj_2048x2048", 2048)])
 @pytest.mark.parametrize("bf16_out", [False, True])
-def test_gemm_dq_config(dev, cfg, m, bf16_out):
-    c, lin, packed, s16 = _packed_layer(cfg)
+def test_gemm_dq_workload(dev, wl, m, bf16_out):
+    c, lin, packed, s16 = _packed_layer(wl)
     x = c.x(0, lin.inp)[:m]
-    say("gemm dq cfg", cfg, "m", m, "bf16", bf16_out)
+    say("gemm dq", wl, "m", m, "bf16", bf16_out)
     y = w4q.w4a16_gemm_dq(dev_bf16(x, dev), torch.from_numpy(packed).to(dev),
                           torch.from_numpy(s16.view(np.float16)).to(dev),
                           out_dtype=torch.bfloat16 if bf16_out else torch.float32)

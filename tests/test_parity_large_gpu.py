@@ -1,7 +1,7 @@
-"""GPU parity at the full synthetic sizes (configs 3-5), in the launch configuration the
-benchmark uses: the GPU computes every output, the oracle recomputes a seeded sample of them
-one by one (entries of H, groups of the search, rows of pack/LSQ, output columns of the
-W4A16 product), plus properties that hold at any size (bitwise symmetry of H)."""
+"""GPU parity at the full synthetic sizes (MLP block, 28- and 36-layer decoders), in the launch
+configuration the benchmark uses: the GPU computes every output, the oracle recomputes a seeded
+sample of them one by one (entries of H, groups of the search, rows of pack/LSQ, output columns
+of the W4A16 product), plus properties that hold at any size (bitwise symmetry of H)."""
 import sys
 
 import numpy as np
@@ -95,12 +95,12 @@ def _lsq_rows(w, sc, g, dev, rows):
     assert np.all(np.abs(gsc[rows] - gso) <= LSQ_REL * GS * gf + GS * 2.0 ** -20 * ga)
 
 
-# ------------------------------------------------------------------- config 3: MLP block
+# ------------------------------------------------------------- MLP block (8192x2048 gate/up)
 @pytest.mark.parametrize("name", ["gate", "down"])
-def test_config3_mlp(dev, name):
-    c = synth.CONFIGS[3]
+def test_mlp_block(dev, name):
+    c = synth.WORKLOADS["mlp_8192x2048"]
     lin = {l.name: l for l in c.linears}[name]
-    say("cfg3", name, lin.d_out, lin.d_in)
+    say("mlp_8192x2048", name, lin.d_out, lin.d_in)
     x = c.x(0, lin.inp)
     w = c.weight(0, lin)
     h = _hessian_sampled(x, dev)
@@ -115,9 +115,9 @@ def test_config3_mlp(dev, name):
     _gemm_cols(x[:256], p, s16, dev, cols, dq=True)
 
 
-# ---------------------------------------------- config 4: 28-layer stack, search + decode
-def test_config4_stack_search_pack_decode(dev):
-    c = synth.CONFIGS[4]
+# ------------------------------------------- 28-layer decoder stack: search, pack, decode
+def test_decoder28_stack_search_pack_decode(dev):
+    c = synth.WORKLOADS["decoder28_h1024"]
     rng = np.random.default_rng(4)
     alpha = c.alpha()
     at = dev_f32(alpha, dev)
@@ -127,7 +127,7 @@ def test_config4_stack_search_pack_decode(dev):
         xs = {inp: c.x(layer, inp) for inp in c.inputs()}
         hs = {inp: w4q.quant_hessian(dev_bf16(xv, dev)) for inp, xv in xs.items()}
         for lin in c.linears:
-            say("cfg4 layer", layer, lin.name)
+            say("decoder28_h1024 layer", layer, lin.name)
             w = c.weight(layer, lin)
             G = lin.d_in // 32
             sc, ix, ob, _ = w4q.quant_scale_search(dev_f32(w, dev), hs[lin.inp], at)
@@ -153,26 +153,26 @@ def test_config4_stack_search_pack_decode(dev):
     assert n_lin == 196
     # the whole decode pass as grouped launches (64 problems each): every output agrees with the
     # single call to fp32 rounding of the lane split (relative to the sum of |terms|)
-    say("cfg4 grouped decode over", n_lin, "linears")
+    say("decoder28_h1024 grouped decode over", n_lin, "linears")
     ys = w4q.w4a16_gemv_grouped([d[0] for d in decode], [d[1] for d in decode], [d[2] for d in decode])
     for (xd, p, s16, y1), yg in zip(decode, ys):
         a, b = y1.cpu().numpy().astype(np.float64), yg.cpu().numpy().astype(np.float64)
         assert np.all(np.abs(a - b) <= 1e-5 * (np.abs(a).max() + 1e-30)), np.abs(a - b).max()
 
 
-# ------------------------------------ config 5: 36-layer stack, representative layers
+# ------------------------------------ 36-layer decoder stack, representative layers
 @pytest.mark.parametrize("layer", [0, 35])
-def test_config5_layer(dev, layer):
-    c = synth.CONFIGS[5]
+def test_decoder36_layer(dev, layer):
+    c = synth.WORKLOADS["decoder36_h4096"]
     rng = np.random.default_rng(50 + layer)
     alpha = c.alpha()
     hs, xs = {}, {}
     for inp in c.inputs():
-        say("cfg5 layer", layer, "hessian", inp)
+        say("decoder36_h4096 layer", layer, "hessian", inp)
         xs[inp] = c.x(layer, inp)
         hs[inp] = _hessian_sampled(xs[inp], dev, n_samples=1500, seed=layer)
     for lin in c.linears:
-        say("cfg5 layer", layer, lin.name, lin.d_out, lin.d_in)
+        say("decoder36_h4096 layer", layer, lin.name, lin.d_out, lin.d_in)
         w = c.weight(layer, lin)
         sc = _search_sampled(w, hs[lin.inp], alpha, dev, n_samples=1000, seed=layer)
         rows = np.sort(rng.choice(lin.d_out, 8, replace=False))

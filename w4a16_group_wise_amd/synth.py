@@ -15,7 +15,8 @@ text that are not available here; these seeded layers stand in for them:
   alpha_k = lo + (hi - lo) * k / (K - 1) in fp64, stored as fp32.
   G  = N(0, 1) fp32 upstream gradient with the shape of W.
 
-Every tensor has its own generator: PCG64(SeedSequence([0, cfg, layer, tensor_id])).
+Every tensor has its own generator: PCG64(SeedSequence([0, stream, layer, tensor_id])), where
+`stream` is the integer that identifies a workload's family of generators (see WORKLOADS).
 """
 from __future__ import annotations
 
@@ -24,20 +25,20 @@ from typing import Dict, List, Tuple
 
 import numpy as np
 
-# tensor ids inside one (cfg, layer)
+# tensor ids inside one (stream, layer)
 LINEAR_IDS = {"w": 0, "q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6}
 INPUT_IDS = {"attn": 10, "o": 11, "mlp": 12, "down": 13}
 GRAD_BASE = 20
 
 
-def rng(cfg: int, layer: int, tensor_id: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([0, cfg, layer, tensor_id])))
+def rng(stream: int, layer: int, tensor_id: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([0, stream, layer, tensor_id])))
 
 
-def weights(cfg: int, layer: int, tensor_id: int, d_out: int, d_in: int,
+def weights(stream: int, layer: int, tensor_id: int, d_out: int, d_in: int,
             outlier_frac: float) -> np.ndarray:
     """fp32 [d_out][d_in] = 0.02 * N(0,1) with round(p * numel) entries scaled by 10."""
-    g = rng(cfg, layer, tensor_id)
+    g = rng(stream, layer, tensor_id)
     w = g.standard_normal((d_out, d_in), dtype=np.float32)
     w *= np.float32(0.02)
     n_out = int(round(outlier_frac * w.size))
@@ -60,9 +61,9 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def calib_x(cfg: int, layer: int, tensor_id: int, n_tok: int, d: int, sigma: float) -> np.ndarray:
+def calib_x(stream: int, layer: int, tensor_id: int, n_tok: int, d: int, sigma: float) -> np.ndarray:
     """bf16 bits [n_tok][d]: N(0,1) times a lognormal(0, sigma) factor per input channel."""
-    g = rng(cfg, layer, tensor_id)
+    g = rng(stream, layer, tensor_id)
     c = np.exp(sigma * g.standard_normal(d)).astype(np.float32)
     z = g.standard_normal((n_tok, d), dtype=np.float32)
     z *= c[None, :]
@@ -76,8 +77,8 @@ def alpha_grid(k: int, lo: float, hi: float) -> np.ndarray:
     return a.astype(np.float32)
 
 
-def upstream_grad(cfg: int, layer: int, tensor_id: int, d_out: int, d_in: int) -> np.ndarray:
-    g = rng(cfg, layer, GRAD_BASE + tensor_id)
+def upstream_grad(stream: int, layer: int, tensor_id: int, d_out: int, d_in: int) -> np.ndarray:
+    g = rng(stream, layer, GRAD_BASE + tensor_id)
     return g.standard_normal((d_out, d_in), dtype=np.float32)
 
 
@@ -90,8 +91,8 @@ class Linear:
 
 
 @dataclass(frozen=True)
-class Config:
-    cfg: int
+class Workload:
+    stream: int    # generator family of its tensors
     title: str
     layers: int
     linears: Tuple[Linear, ...]
@@ -115,15 +116,15 @@ class Config:
         return alpha_grid(self.n_cand, self.alpha_lo, self.alpha_hi)
 
     def weight(self, layer: int, lin: Linear) -> np.ndarray:
-        return weights(self.cfg, layer, LINEAR_IDS[lin.name], lin.d_out, lin.d_in,
+        return weights(self.stream, layer, LINEAR_IDS[lin.name], lin.d_out, lin.d_in,
                        self.outlier_frac)
 
     def x(self, layer: int, inp: str) -> np.ndarray:
-        return calib_x(self.cfg, layer, INPUT_IDS[inp], self.n_tok, self.inputs()[inp],
+        return calib_x(self.stream, layer, INPUT_IDS[inp], self.n_tok, self.inputs()[inp],
                        self.sigma)
 
     def grad(self, layer: int, lin: Linear) -> np.ndarray:
-        return upstream_grad(self.cfg, layer, LINEAR_IDS[lin.name], lin.d_out, lin.d_in)
+        return upstream_grad(self.stream, layer, LINEAR_IDS[lin.name], lin.d_out, lin.d_in)
 
 
 def _decoder(hidden: int, heads: int, kv_heads: int, head_dim: int, inter: int) -> Tuple[Linear, ...]:
@@ -140,22 +141,28 @@ def _decoder(hidden: int, heads: int, kv_heads: int, head_dim: int, inter: int) 
     )
 
 
-CONFIGS: Dict[int, Config] = {
-    1: Config(1, "single linear 256x512", 1, (Linear("w", 256, 512, "attn"),), 128, 1.0, 0.01,
-              20, 0.5, 1.0, (1,), ("w",)),
-    2: Config(2, "attention projection 2048x2048", 1, (Linear("w", 2048, 2048, "attn"),), 2048,
-              1.0, 0.005, 40, 0.4, 1.0, (1, 4, 16)),
-    3: Config(3, "MLP block gate/up 8192x2048, down 2048x8192", 1,
-              (Linear("gate", 8192, 2048, "mlp"), Linear("up", 8192, 2048, "mlp"),
-               Linear("down", 2048, 8192, "down")),
-              4096, 1.5, 0.005, 40, 0.4, 1.0, (1, 16, 256), ("gate", "up", "down")),
-    4: Config(4, "28-layer decoder, hidden 1024", 28, _decoder(1024, 16, 8, 128, 3072), 4096, 1.0,
-              0.005, 40, 0.4, 1.0, (1,)),
-    5: Config(5, "36-layer decoder, hidden 4096", 36, _decoder(4096, 32, 8, 128, 12288), 8192, 1.0,
-              0.005, 40, 0.4, 1.0, (1, 2048), ("gate", "up")),
+# the five workloads, by what they are
+WORKLOADS: Dict[str, Workload] = {
+    "linear_256x512": Workload(
+        1, "single linear 256x512", 1, (Linear("w", 256, 512, "attn"),), 128, 1.0, 0.01,
+        20, 0.5, 1.0, (1,), ("w",)),
+    "proj_2048x2048": Workload(
+        2, "attention projection 2048x2048", 1, (Linear("w", 2048, 2048, "attn"),), 2048,
+        1.0, 0.005, 40, 0.4, 1.0, (1, 4, 16)),
+    "mlp_8192x2048": Workload(
+        3, "MLP block gate/up 8192x2048, down 2048x8192", 1,
+        (Linear("gate", 8192, 2048, "mlp"), Linear("up", 8192, 2048, "mlp"),
+         Linear("down", 2048, 8192, "down")),
+        4096, 1.5, 0.005, 40, 0.4, 1.0, (1, 16, 256), ("gate", "up", "down")),
+    "decoder28_h1024": Workload(
+        4, "28-layer decoder, hidden 1024", 28, _decoder(1024, 16, 8, 128, 3072), 4096, 1.0,
+        0.005, 40, 0.4, 1.0, (1,)),
+    "decoder36_h4096": Workload(
+        5, "36-layer decoder, hidden 4096", 36, _decoder(4096, 32, 8, 128, 12288), 8192, 1.0,
+        0.005, 40, 0.4, 1.0, (1, 2048), ("gate", "up")),
 }
 
 
-def linears_of(cfg: int) -> List[Tuple[int, Linear]]:
-    c = CONFIGS[cfg]
+def linears_of(name: str) -> List[Tuple[int, Linear]]:
+    c = WORKLOADS[name]
     return [(layer, lin) for layer in range(c.layers) for lin in c.linears]

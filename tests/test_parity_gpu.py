@@ -299,9 +299,10 @@ def test_gemm_zero_codes_exact(dev):
 
 # ------------------------------------------------ matrix-core product, both weight readings
 # shapes on the 256x256-tile kernel (d_in % 256 == 0): ragged rows / columns, K split over
-# workgroups (partial tiles) or not, and several tiles per workgroup
+# workgroups (partial tiles) or not, and several tiles per workgroup; the last shape has enough
+# output tiles that exact weights take the per-group kernel instead
 @pytest.mark.parametrize("m,d_out,d_in", [(17, 40, 256), (300, 520, 512), (64, 256, 4096),
-                                          (513, 1000, 768), (256, 2304, 1024)])
+                                          (513, 1000, 768), (256, 2304, 1024), (1100, 4100, 256)])
 @pytest.mark.parametrize("dq", [False, True])
 def test_gemm_mma_shapes(dev, m, d_out, d_in, dq):
     w = synth.weights(34, 0, d_out, d_out, d_in, 0.01)
@@ -316,6 +317,12 @@ def test_gemm_mma_shapes(dev, m, d_out, d_in, dq):
     cols = np.arange(d_out) if d_out * m <= 200000 else np.arange(0, d_out, 5)
     yr, ya = oracle.gemm_cols(x, packed, s16, cols, dequant_bf16=dq)
     check_gemm(yg[:, cols], yr, ya)
+    # each entry point follows its own weight reading: its distance to the other reading's
+    # reference is far above its distance to its own (fp32 accumulation only)
+    yo, _ = oracle.gemm_cols(x, packed, s16, cols, dequant_bf16=not dq)
+    e_own = np.max(np.abs(yg[:, cols] - yr) / ya)
+    e_other = np.max(np.abs(yg[:, cols] - yo) / ya)
+    assert e_own * 4 < e_other, (e_own, e_other)
 
 
 @pytest.mark.parametrize("wl,m", [("linear_256x512", 1), ("proj_2048x2048", 16), ("proj_2048x2048", 2048)])

@@ -256,6 +256,12 @@ __device__ __forceinline__ void gstore_block(void* __restrict__ y, int y_dtype, 
   }
 }
 
+// kSplit: exact weights.  s * q is formed as two bf16 parts, s_hi * q and s_lo * q, with s_hi = s
+// rounded to 5 significant bits and s_lo = s - s_hi (at most 5 significant bits too, since
+// |s - s_hi| <= 32 units of s's 11-bit significand): each part times a code (at most 3
+// significant bits) fits bf16's 8 bits exactly, so the two products per weight enter the fp32
+// sums unrounded.  Otherwise the weights are dequantized to bf16: w = bf16_RNE(s * q).
+template <bool kSplit>
 __global__ __launch_bounds__(kGThreads, 1) void gemm_dq_kernel(const uint16_t* __restrict__ x, int M,
                                                                 const uint8_t* __restrict__ packed,
                                                                 const uint16_t* __restrict__ s16, int N, int K,
@@ -339,20 +345,39 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_dq_kernel(const uint16_t* _
     // bf16 B fragment of step kk: per 8 codes, the even and odd nibbles as bytes in offset
     // binary (q + 8), each converted to float, and s * (q + 8) - 8 s in one fma (exact: it
     // equals s * q, which fp32 holds), rounded to bf16 in pairs
-    auto make_b = [&](const Codes& cd, int kk, bf16x8& bf) {
+    struct BFrag {
+      bf16x8 v[kSplit ? 2 : 1];  // [0]: s * q (or s_hi * q), [1]: s_lo * q
+    };
+    auto make_b = [&](const Codes& cd, int kk, BFrag& bf) {
       const float sc = f16_bits_to_f32(static_cast<uint16_t>(cd.s));
-      const float ms = -8.0f * sc;
       const uint32_t word = cd.w[kk];
       const uint32_t ev = (word & 0x0F0F0F0Fu) ^ 0x08080808u;
       const uint32_t od = ((word >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
-      uint32_t hi[4];
+      float qe[4], qo[4];  // q + 8 of the even and odd nibbles
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const float w0 = __builtin_fmaf(sc, static_cast<float>((ev >> (8 * p)) & 0xFFu), ms);
-        const float w1 = __builtin_fmaf(sc, static_cast<float>((od >> (8 * p)) & 0xFFu), ms);
-        hi[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{w0, w1}, bf16x2));
+        qe[p] = static_cast<float>((ev >> (8 * p)) & 0xFFu);
+        qo[p] = static_cast<float>((od >> (8 * p)) & 0xFFu);
       }
-      bf = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+      auto part = [&](float s, bf16x8& out) {  // bf16 of s * q (exact when s * q fits bf16)
+        const float ms = -8.0f * s;
+        uint32_t h[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float w0 = __builtin_fmaf(s, qe[p], ms);
+          const float w1 = __builtin_fmaf(s, qo[p], ms);
+          h[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{w0, w1}, bf16x2));
+        }
+        out = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+      };
+      if constexpr (kSplit) {
+        // s rounded to 5 significant bits (fraction bits below the top 4 cleared, half rounded up)
+        const float s_hi = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, sc) + 0x00040000u) & 0xFFF80000u);
+        part(s_hi, bf.v[0]);
+        part(sc - s_hi, bf.v[1]);
+      } else {
+        part(sc, bf.v[0]);
+      }
     };
 
     f32x16 acc[8];
@@ -366,13 +391,14 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_dq_kernel(const uint16_t* _
       }
     };
     // the products of one step; `first` starts the sums from zero
-    auto mma = [&](const bf16x8 (&af)[8], const bf16x8& bf, auto first) {
+    auto mma = [&](const bf16x8 (&af)[8], const BFrag& bf, auto first) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         if constexpr (decltype(first)::value)
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf, zero16, 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf.v[0], zero16, 0, 0, 0);
         else
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf, acc[i], 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf.v[0], acc[i], 0, 0, 0);
+        if constexpr (kSplit) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf.v[1], acc[i], 0, 0, 0);
       }
     };
     // each product followed by one LDS read of the next step and kV vector instructions of the
@@ -381,9 +407,9 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_dq_kernel(const uint16_t* _
       constexpr int V = decltype(kv)::value;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, kSplit ? 2 : 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);               // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, kSplit ? V + 2 : V, 0);  // VALU
       }
     };
     // stage synchronisation: this wave's loads up to two stages back have landed and its LDS
@@ -404,7 +430,8 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_dq_kernel(const uint16_t* _
     // nobody reads any more.  Step 0 multiplies the fragments of kk = 0 of g (set X, prepared
     // during stage g - 1) while those of kk = 1 (set Y) are prepared and the codes of g + 1 are
     // read; step 1 multiplies set Y while set X is refilled with kk = 0 of g + 1.
-    bf16x8 ax[8], ay[8], bx, by;
+    bf16x8 ax[8], ay[8];
+    BFrag bx, by;
     Codes cg, cn;
     int gb = s0 % GNB;  // stage buffer of group g
     issue(s0, gb);
@@ -495,7 +522,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_fixup_kernel(void* __restrict_
 }
 
 int launch_dq_pass(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16, int64_t N,
-                    int64_t K, void* y, int y_dtype, hipStream_t s) {
+                    int64_t K, void* y, int y_dtype, bool exact, hipStream_t s) {
   const int64_t G = K / 32;
   const int64_t tm_count = (m + GT - 1) / GT, tn_count = (N + GT - 1) / GT;
   const int64_t tiles = tm_count * tn_count;
@@ -505,18 +532,25 @@ int launch_dq_pass(const uint16_t* x, int64_t m, const uint8_t* packed, const ui
   if (nblk > kGMaxBlocks) nblk = kGMaxBlocks;
   const int64_t chunk = (total + nblk - 1) / nblk;
   nblk = (total + chunk - 1) / chunk;
-  const bool split = nblk > 1 && chunk % G != 0;
+  const bool partial = nblk > 1 && chunk % G != 0;
   const int64_t per_xcd = (nblk + 7) / 8;
   float* ws = nullptr;
-  if (split && w4q_workspace_acquire(reinterpret_cast<void**>(&ws), (size_t)nblk * 2 * kGTileElems * sizeof(float), s) !=
+  if (partial && w4q_workspace_acquire(reinterpret_cast<void**>(&ws), (size_t)nblk * 2 * kGTileElems * sizeof(float), s) !=
                    W4Q_OK)
     return W4Q_EHIP;
-  hipLaunchKernelGGL(gemm_dq_kernel, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(kGThreads), 0, s,
-                     x, static_cast<int>(m), packed, s16, static_cast<int>(N), static_cast<int>(K), y, y_dtype,
-                     static_cast<int>(tn_count), static_cast<int>(total), static_cast<int>(chunk),
-                     static_cast<int>(nblk), static_cast<int>(per_xcd), ws);
+  const dim3 grid(static_cast<unsigned>(8 * per_xcd));
+  if (exact)
+    hipLaunchKernelGGL(gemm_dq_kernel<true>, grid, dim3(kGThreads), 0, s, x, static_cast<int>(m), packed, s16,
+                       static_cast<int>(N), static_cast<int>(K), y, y_dtype, static_cast<int>(tn_count),
+                       static_cast<int>(total), static_cast<int>(chunk), static_cast<int>(nblk),
+                       static_cast<int>(per_xcd), ws);
+  else
+    hipLaunchKernelGGL(gemm_dq_kernel<false>, grid, dim3(kGThreads), 0, s, x, static_cast<int>(m), packed, s16,
+                       static_cast<int>(N), static_cast<int>(K), y, y_dtype, static_cast<int>(tn_count),
+                       static_cast<int>(total), static_cast<int>(chunk), static_cast<int>(nblk),
+                       static_cast<int>(per_xcd), ws);
   int rc = w4q_launch_status();
-  if (split) {
+  if (partial) {
     if (rc == W4Q_OK) {
       hipLaunchKernelGGL(gemm_fixup_kernel, dim3(static_cast<unsigned>(8 * tiles)), dim3(kGThreads), 0, s, y,
                          y_dtype, static_cast<int>(m), static_cast<int>(N), static_cast<int>(G),
@@ -533,16 +567,22 @@ int launch_dq_pass(const uint16_t* x, int64_t m, const uint8_t* packed, const ui
 
 using namespace w4q;
 
+// output tiles of the per-group kernel: 256-row tiles (8 wavefronts share one expansion of the
+// codes) when they still give at least one tile per compute unit, 128-row tiles otherwise
+static int64_t group_tiles(int64_t m, int64_t d_out, bool* big) {
+  const int64_t gn = (d_out + BN - 1) / BN;
+  const int64_t gm4 = (m + 255) / 256, gm2 = (m + 127) / 128;
+  *big = gm4 * gn >= 256;
+  return (*big ? gm4 : gm2) * gn;
+}
+
 // exact weights, any shape: one K-group per step, scale applied per group on the vector ALUs
 static int launch_group(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
                  int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t s) {
   if (d_in / kGroup > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
   const int64_t gn = (d_out + BN - 1) / BN;
-  // 256-row tiles (8 wavefronts share one expansion of the codes) when they still give at
-  // least one tile per compute unit, 128-row tiles otherwise
-  const int64_t gm4 = (m + 255) / 256, gm2 = (m + 127) / 128;
-  const bool big = gm4 * gn >= 256;
-  const int64_t tiles = (big ? gm4 : gm2) * gn;
+  bool big;
+  const int64_t tiles = group_tiles(m, d_out, &big);
   const int64_t per_xcd = (tiles + 7) / 8;
   if (8 * per_xcd > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
   const dim3 grid(static_cast<unsigned>(8 * per_xcd));
@@ -557,17 +597,24 @@ static int launch_group(const uint16_t* x, int64_t m, const uint8_t* packed, con
 
 int w4q_launch_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
                     int64_t d_out, int64_t d_in, void* y, int y_dtype, int w_mode, hipStream_t s) {
-  if (w_mode == 0) return launch_group(x, m, packed, s16, d_out, d_in, y, y_dtype, s);
-  // the dequantizing kernel needs 16-byte scale rows (d_in % 256 == 0) and 32-bit buffer offsets
-  // into the codes and scales; x is taken in passes of whole 256-row tiles that fit them too
-  if (d_in % 256 != 0 || d_out * (d_in / 2) >= 0x7FFFFFFF || 256 * d_in * 2 >= 0x7FFFFFFF)
-    return W4Q_EUNSUPPORTED;
+  // the tiled kernel needs 16-byte scale rows (d_in % 256 == 0) and 32-bit buffer offsets into
+  // the codes and scales; x is taken in passes of whole 256-row tiles that fit them too
+  const bool tiled = d_in % 256 == 0 && d_out * (d_in / 2) < 0x7FFFFFFF && 256 * d_in * 2 < 0x7FFFFFFF;
+  if (w_mode == 0) {
+    // exact weights: the per-group kernel while it has a tile for every compute unit; below
+    // that, the stream-K tiled kernel with split weights (twice the matrix-core work, but the
+    // K dimension spread over all compute units)
+    bool big;
+    if (!tiled || group_tiles(m, d_out, &big) >= 256)
+      return launch_group(x, m, packed, s16, d_out, d_in, y, y_dtype, s);
+  }
+  if (!tiled) return W4Q_EUNSUPPORTED;
   const int64_t rows = (0x7FFFFFFF / (2 * d_in)) / GT * GT;
   const int64_t ob = y_dtype == 0 ? 4 : 2;
   for (int64_t r0 = 0; r0 < m; r0 += rows) {
     const int64_t mr = m - r0 < rows ? m - r0 : rows;
     const int rc = launch_dq_pass(x + r0 * d_in, mr, packed, s16, d_out, d_in,
-                                  static_cast<uint8_t*>(y) + r0 * d_out * ob, y_dtype, s);
+                                  static_cast<uint8_t*>(y) + r0 * d_out * ob, y_dtype, w_mode == 0, s);
     if (rc != W4Q_OK) return rc;
   }
   return W4Q_OK;

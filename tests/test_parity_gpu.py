@@ -214,12 +214,17 @@ def test_lsq_linear_256x512(dev, fused):
 
 def test_lsq_edges(dev):
     d = np.float32(0.25)
-    w = np.zeros((2, 64), np.float32)
+    w = np.zeros((3, 64), np.float32)
     w[0, :8] = [0.375, 1.875, 1.75, -2.125, -2.0, 0.1, 7 * 0.25, -8 * 0.25]
     w[0, 8:32] = ((np.arange(24) - 12) * 0.125).astype(np.float32)
     w[1, :] = np.linspace(-3, 3, 64, dtype=np.float32)
-    scale = np.array([[d, np.float32(0.013)], [np.float32(1e-30), np.float32(100.0)]], np.float32)
-    g = np.random.default_rng(9).standard_normal((2, 64)).astype(np.float32)
+    # fp32-subnormal steps: 2^-127 (its reciprocal 2^127 is finite) and 1e-40 (reciprocal overflows)
+    tiny = [np.float32(2.0 ** -127), np.float32(1e-40)]
+    for j in range(2):
+        k = np.arange(32) - 16.0
+        w[2, 32 * j:32 * j + 32] = (k * 0.7 * np.float64(tiny[j])).astype(np.float32)
+    scale = np.array([[d, np.float32(0.013)], [np.float32(1e-30), np.float32(100.0)], tiny], np.float32)
+    g = np.random.default_rng(9).standard_normal((3, 64)).astype(np.float32)
     say("lsq edges")
     _lsq_check(w, scale, g, dev, True)
 

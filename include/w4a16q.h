@@ -115,7 +115,7 @@ int quant_scale_search(const float* w, int64_t d_out, int64_t d_in, const float*
  *   s16 = fp16_RNE(scale);  q = code(w, s16);  byte j of a packed row holds
  *   (q[2j] & 0xF) | (q[2j+1] & 0xF) << 4  (two's-complement nibbles, low nibble = even k).
  *
- *   w         fp32 [d_out][d_in], 16-B aligned.    scale  fp32 [d_out][G] (>= 0, finite).
+ *   w         fp32 [d_out][d_in] (finite), 16-B aligned.    scale  fp32 [d_out][G] (>= 0, finite).
  *   packed    uint8 [d_out][d_in/2] out, 16-B aligned.
  *   scale_f16 fp16 bits [d_out][G] out.
  */

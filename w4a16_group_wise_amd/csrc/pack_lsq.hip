@@ -12,6 +12,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPer = 8;  // weights per thread
+constexpr float kNearTie = 0.5f - 1e-5f;
 
 // The codes of a thread's weights at step d.  The estimate comes from one reciprocal per thread
 // (w * RN(1/d) is within a few units in the last place of w / d, so its nearest integer is off
@@ -27,6 +28,28 @@ struct Coder {
   __device__ __forceinline__ float operator()(float w) const { return rcp ? code_rcp(w, d, inv) : code_div(w, d); }
 };
 
+// Codes of 8 weights at step d as clamp(rint(w * rcp(d))).  For d in [2^-126, 2^125] the
+// reciprocal is normal and w * rcp(d) is within 2e-7 relative of w / d, so that is the code
+// unless w / d lies within 1e-5 of a half-integer (below 9 in magnitude; beyond, the clamp
+// decides).  A wavefront with such a lane, or with a step outside that range (0 and fp32
+// subnormals included), takes the exact per-weight path for all its lanes.
+__device__ __forceinline__ void fast_codes(const float (&v)[8], float d, float (&c)[8]) {
+  const bool ok = d >= 0x1p-126f && d <= 0x1p125f;
+  const float inv = __builtin_amdgcn_rcpf(ok ? d : 1.0f);
+  bool near = !ok;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float t = v[i] * inv;
+    const float r = __builtin_rintf(t);
+    near |= __builtin_fabsf(t - r) > kNearTie;
+    c[i] = __builtin_fminf(__builtin_fmaxf(r, -8.0f), 7.0f);
+  }
+  if (__builtin_amdgcn_ballot_w64(near) != 0) {  // wave-uniform, rare
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = code_div(v[i], d);
+  }
+}
+
 // Export ([card] "QAT Highlights" / "Quickstart", [blog] "Conclusion"): fp16 scale, codes on
 // that scale, two's-complement nibbles with the even index in the low nibble.
 __global__ __launch_bounds__(kThreads) void pack_kernel(const float* __restrict__ w,
@@ -41,12 +64,30 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const float* __restrict_
   const f32x4 a = *reinterpret_cast<const f32x4*>(w + e0);
   const f32x4 b = *reinterpret_cast<const f32x4*>(w + e0 + 4);
   const uint16_t hs = f32_to_f16_bits(scale[grp]);
-  const Coder code(f16_bits_to_f32(hs));
+  const float d = f16_bits_to_f32(hs);  // an fp16 value: 0, inf or normal in fp32
   const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  // Codes as clamp(rint(w * rcp(d))).  With w * rcp(d) within 2e-7 relative of w / d, that is the
+  // code unless w / d lies within 1e-5 of a half-integer (below 9 in magnitude; beyond, the clamp
+  // decides); a wavefront with such a lane takes the exact correction step for all its lanes.
+  const bool pos = d > 0.0f;
+  const float inv = __builtin_amdgcn_rcpf(pos ? d : 1.0f);
+  float c[8];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float t = v[i] * inv;
+    const float r = __builtin_rintf(t);
+    near |= __builtin_fabsf(t - r) > kNearTie;
+    c[i] = __builtin_fminf(__builtin_fmaxf(r, -8.0f), 7.0f);
+  }
+  if (__builtin_amdgcn_ballot_w64(near && pos) != 0) {  // wave-uniform, rare
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = code_rcp(v[i], d, inv);
+  }
   uint32_t word = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int q = static_cast<int>(code(v[i]));
+    const int q = pos ? static_cast<int>(c[i]) : 0;
     word |= (static_cast<uint32_t>(q) & 0xFu) << (4 * i);
   }
   packed[t] = word;
@@ -61,16 +102,14 @@ __global__ __launch_bounds__(kThreads) void lsq_fwd_kernel(const float* __restri
   const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (t >= n8) return;
   const int64_t e0 = t * kPer;
-  // (one division per weight: measured faster in this kernel than the reciprocal estimate)
   const float d = scale[e0 / kGroup];
-  f32x4 a = *reinterpret_cast<const f32x4*>(w + e0);
-  f32x4 b = *reinterpret_cast<const f32x4*>(w + e0 + 4);
-  a.x = d * code_div(a.x, d); a.y = d * code_div(a.y, d);
-  a.z = d * code_div(a.z, d); a.w = d * code_div(a.w, d);
-  b.x = d * code_div(b.x, d); b.y = d * code_div(b.y, d);
-  b.z = d * code_div(b.z, d); b.w = d * code_div(b.w, d);
-  *reinterpret_cast<f32x4*>(w_hat + e0) = a;
-  *reinterpret_cast<f32x4*>(w_hat + e0 + 4) = b;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(w + e0);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(w + e0 + 4);
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  float c[8];
+  fast_codes(v, d, c);
+  *reinterpret_cast<f32x4*>(w_hat + e0) = f32x4{d * c[0], d * c[1], d * c[2], d * c[3]};
+  *reinterpret_cast<f32x4*>(w_hat + e0 + 4) = f32x4{d * c[4], d * c[5], d * c[6], d * c[7]};
 }
 
 // [blog] section 3 backward.  m = [-8 D <= w <= 7 D] (signs from fma, exact);

@@ -259,10 +259,11 @@ def test_gemm_workload(dev, wl, m, bf16_out):
 
 # 2..16 rows run on the matrix-core kernel: G % 8 == 0 (16-byte scale loads) or not, fewer
 # groups than wavefronts, ragged weight rows, one or two 16-row tiles per workgroup
-# (d_out below or above 8192)
+# (d_out below or above 8192), 8 or 16 wavefronts per workgroup (d_in >= 8192 with M <= 8)
 @pytest.mark.parametrize("m,d_out,d_in", [(1, 1, 32), (1, 3, 96), (2, 130, 224), (5, 64, 1056),
                                           (3, 1000, 256), (16, 33, 8192), (9, 257, 2048), (16, 31, 64),
                                           (4, 8200, 64), (11, 8224, 512),
+                                          (5, 40, 8192), (3, 50, 8224), (8, 17, 16384), (2, 9, 12320),
                                           (1, 77, 3072), (33, 200, 160), (130, 129, 96)])
 def test_gemm_ragged(dev, m, d_out, d_in):
     w = synth.weights(32, 0, d_out, d_out, d_in, 0.01)

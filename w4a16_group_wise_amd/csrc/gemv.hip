@@ -246,14 +246,15 @@ struct MmaBatch {
   uint32_t s1[kMmaBatch][kMmaTiles];   // one scale per group (2-byte path)
 };
 
-// kMmaTiles: 16-row tiles of W per workgroup (1 or 2)
-template <bool kVecScales, int kMmaTiles>
-__global__ __launch_bounds__(kMmaWaves * 64) void gemv_mma_kernel(const uint16_t* __restrict__ x, int m_rows,
+// kMmaTiles: 16-row tiles of W per workgroup (1 or 2); kWaves: wavefronts per workgroup (8, or
+// 16 for long rows, where each still gets two batches or more)
+template <bool kVecScales, int kMmaTiles, int kWaves = kMmaWaves>
+__global__ __launch_bounds__(kWaves * 64) void gemv_mma_kernel(const uint16_t* __restrict__ x, int m_rows,
                                                                   const uint8_t* __restrict__ packed,
                                                                   const uint16_t* __restrict__ s16,
                                                                   int64_t d_out, int64_t d_in,
                                                                   void* __restrict__ y, int y_dtype) {
-  __shared__ float part[kMmaWaves][kMmaTiles][4][64];
+  __shared__ float part[kWaves][kMmaTiles][4][64];
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4, nl = lane & 15;
@@ -362,10 +363,10 @@ __global__ __launch_bounds__(kMmaWaves * 64) void gemv_mma_kernel(const uint16_t
     }
   };
 
-  // the wavefronts take the batches round-robin (wavefront w: w, w + 4, ...), so at any time a
+  // the wavefronts take the batches round-robin (wavefront w: w, w + S, ... for S wavefronts), so at any time a
   // workgroup reads a few hundred contiguous bytes of each of its rows; two register sets: the
   // next batch is in flight while the current one is reduced
-  constexpr int S = kMmaWaves;
+  constexpr int S = kWaves;
   MmaBatch<kMmaTiles> B0, B1;
   if (wid < nbat) {
     load(wid, B0);
@@ -388,12 +389,12 @@ __global__ __launch_bounds__(kMmaWaves * 64) void gemv_mma_kernel(const uint16_t
   __syncthreads();
   // outputs: tile t, activation row m, column c; wavefront partials in order, then the factor
   // 8 removed (exactly)
-  for (int o = threadIdx.x; o < kMmaTiles * 256; o += kMmaWaves * 64) {
+  for (int o = threadIdx.x; o < kMmaTiles * 256; o += kWaves * 64) {
     const int t = o >> 8, m = (o >> 4) & 15, c = o & 15;
     const int src = 16 * (m >> 2) + c;
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kMmaWaves; ++w) v += part[w][t][m & 3][src];
+    for (int w = 0; w < kWaves; ++w) v += part[w][t][m & 3][src];
     v *= 0.125f;
     const int64_t n = nbase + 16 * t + c;
     if (m < m_rows && n < d_out) {
@@ -792,6 +793,20 @@ int w4q_launch_gemv(const uint16_t* x, int64_t m, const uint8_t* packed, const u
     const bool vec = (d_in / kGroup) % kMmaBatch == 0;
     const dim3 grid(static_cast<unsigned>(blocks)), block(kMmaWaves * 64);
     const int mr = static_cast<int>(m);
+    // 16 wavefronts per workgroup (twice the loads in flight per compute unit) on long rows with
+    // one tile per workgroup: d_in >= 8192 gives each wavefront two 8-group batches or more
+    // (measured at 4096x12288, M = 2..8: 17.6 -> 15.5 us at M = 2; no gain at M = 16, and a loss
+    // where the wavefronts get one batch each)
+    if (tiles == 1 && d_in >= 8192 && m <= 8) {
+      const dim3 block16(16 * 64);
+      if (vec)
+        hipLaunchKernelGGL((gemv_mma_kernel<true, 1, 16>), grid, block16, 0, s, x, mr, packed, s16, d_out, d_in, y,
+                           y_dtype);
+      else
+        hipLaunchKernelGGL((gemv_mma_kernel<false, 1, 16>), grid, block16, 0, s, x, mr, packed, s16, d_out, d_in, y,
+                           y_dtype);
+      return w4q_launch_status();
+    }
     if (vec && tiles == 2)
       hipLaunchKernelGGL((gemv_mma_kernel<true, 2>), grid, block, 0, s, x, mr, packed, s16, d_out, d_in, y, y_dtype);
     else if (vec)

@@ -162,9 +162,12 @@ int lsq_bwd(const float* w, const float* scale, const float* grad_w_hat, int64_t
  *   y         [m][d_out], fp32 (y_dtype 0) or bf16 RNE of the fp32 result (y_dtype 1).
  *   m >= 1.  Small m (<= 16) streams the packed weights once (bandwidth bound): m = 1 on the
  *   vector ALUs, 2..16 on the bf16 matrix cores; larger m is a tiled product on the matrix
- *   cores.  On the matrix cores the codes enter as exact small bf16 integers and the fp32
- *   scale is applied once per group to the group's partial products, so the weights enter the
- *   products unrounded.
+ *   cores.  On the matrix cores the weights enter the products unrounded: either the codes
+ *   enter as exact small bf16 integers and the fp32 scale is applied once per group to the
+ *   group's partial products, or (shapes with few output tiles, d_in % 256 == 0) each weight
+ *   is split into two bf16-exact parts, scale_hi * q + scale_lo * q, with scale_hi the fp16
+ *   scale rounded to 5 significant bits.  Either way only the fp32 summation order differs
+ *   from the definition above.
  */
 int w4a16_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
                int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t stream);

@@ -15,6 +15,8 @@
 // barrier per group, and a register ring that keeps the global loads of the next PD - 1
 // groups in flight (one group of compute is far shorter than a memory round trip).  LDS rows
 // are XOR-swizzled in 16-byte chunks so fragment reads and tile writes are bank-conflict free.
+// Where this kernel would have fewer tiles than compute units, the exact product runs instead
+// on the stream-K kernel further down, with each weight split into two bf16-exact parts.
 #include "common.hpp"
 
 namespace w4q {
@@ -195,11 +197,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_group_kernel(const uint16_t
 
 // ---------------------------------------------------------------------------------------
 // Matrix-core kernel: 256x256 output tiles, 8 wavefronts (two per SIMD) of 256x32 (8 blocks of
-// v_mfma_f32_32x32x16_bf16 down the rows), one K-group (32 codes) per stage.  Two wavefronts
-// per SIMD because on gfx950 vector instructions overlap the matrix cores only when they come
-// from another wavefront: the dequantization of one wavefront hides behind the products of the
-// other.  Each wavefront owns 32 whole columns, so every code is dequantized exactly once (the
-// vector work per code, about three instructions, is what bounds this kernel otherwise).
+// v_mfma_f32_32x32x16_bf16 down the rows), one K-group (32 codes) per stage, two wavefronts per
+// SIMD.  Each wavefront owns 32 whole columns, so every code is dequantized exactly once (about
+// three vector instructions per code; with the vector work removed the kernel is only about
+// 11 % faster).
 //   x tile   : buffer loads straight to LDS, [row][16-byte chunk] with chunk c of row r at
 //              position c ^ swz_f(r), 5 stage buffers (loads run 4 stages ahead); each
 //              wavefront loads 32 rows and reads its A fragments from there.
@@ -210,7 +211,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_group_kernel(const uint16_t
 //              in registers, one step ahead of the products.  (LDS writes are the
 //              scarce resource on gfx950 -- about a third of the read bandwidth -- so only the
 //              activations go through LDS as bf16.)
-// The weights are dequantized to bf16: w = bf16_RNE(s * q), one product per weight.
+// The weights are dequantized to bf16, w = bf16_RNE(s * q) (w4a16_gemm_dq), or split into two
+// exact bf16 parts (w4a16_gemm below 256 tiles of the per-group kernel; see kSplit).
 // Work split as for the Hessian: stream-K over (tile, group), partial tiles summed in a fixed
 // order by a second kernel.  All global loads are the asm loads to LDS, so the explicit vmcnt
 // waits count exactly 3 loads per stage and wavefront (2 x rows, 1 codes or scales or empty).

@@ -17,9 +17,10 @@
  *     enqueues work on `stream` (0 = the legacy default stream) and returns; the library never
  *     synchronises.  Results are valid once the caller has synchronised that stream.  The
  *     library allocates nothing except one 128 MB device scratch buffer per device (partial
- *     tiles of quant_hessian and w4a16_gemm_dq), made by the first such call on the device and
- *     kept until the process ends; the work of those two calls on one device is serialised on
- *     it (a later call's stream waits for an event recorded after the earlier call's kernels).
+ *     tiles of quant_hessian, w4a16_gemm_dq, and w4a16_gemm when m > 16 runs the split-scale
+ *     tiled kernel), made by the first such call on the device and kept until the process
+ *     ends; the work of those calls on one device is serialised on it (a later call's stream
+ *     waits for an event recorded after the earlier call's kernels).
  *   - Weights W are fp32 [d_out][d_in]; a group is 32 consecutive weights of one row along
  *     d_in, so d_in must be a positive multiple of 32 (W4Q_GROUP).  G = d_in / 32 groups/row.
  *   - Codes are integers in [-8, 7] (W4Q_QMIN..W4Q_QMAX).  code(w, D) is the code c that

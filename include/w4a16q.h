@@ -159,7 +159,7 @@ int lsq_bwd(const float* w, const float* scale, const float* grad_w_hat, int64_t
  *   y[m][n]     = sum_k x[m][k] * w_hat[n][k]          (fp32 accumulation)
  *   x         bf16 [m][d_in], 16-B aligned.
  *   packed    uint8 [d_out][d_in/2] as written by quant_pack, 16-B aligned.
- *   scale_f16 fp16 bits [d_out][G].
+ *   scale_f16 fp16 bits [d_out][G], finite (an infinite scale gives undefined outputs).
  *   y         [m][d_out], fp32 (y_dtype 0) or bf16 RNE of the fp32 result (y_dtype 1).
  *   m >= 1.  Small m (<= 16) streams the packed weights once (bandwidth bound): m = 1 on the
  *   vector ALUs, 2..16 on the bf16 matrix cores; larger m is a tiled product on the matrix

@@ -15,12 +15,18 @@
  * Common conventions for every entry point:
  *   - Tensors are caller-owned DEVICE memory, row-major, contiguous.  Every call only
  *     enqueues work on `stream` (0 = the legacy default stream) and returns; the library never
- *     synchronises.  Results are valid once the caller has synchronised that stream.  The
- *     library allocates nothing except one 128 MB device scratch buffer per device (partial
- *     tiles of quant_hessian, w4a16_gemm_dq, and w4a16_gemm when m > 16 runs the split-scale
- *     tiled kernel), made by the first such call on the device and kept until the process
- *     ends; the work of those calls on one device is serialised on it (a later call's stream
- *     waits for an event recorded after the earlier call's kernels).
+ *     synchronises, allocates nothing and keeps no mutable state between calls.  Results are
+ *     valid once the caller has synchronised that stream.
+ *   - Scratch: quant_hessian, w4a16_gemm and w4a16_gemm_dq split output tiles over workgroups
+ *     and keep the partial tiles in a caller-owned device workspace (workspace,
+ *     workspace_bytes): NULL with 0 bytes, or 256-B aligned memory (W4Q_EINVAL for NULL with a
+ *     non-zero size, W4Q_EALIGN if misaligned).  The matching *_workspace_size call returns the
+ *     bytes the fastest schedule uses; with less, the call runs a schedule whose partial tiles
+ *     fit (down to none: no scratch at all, fewer workgroups on small problems), with the same
+ *     arithmetic up to the fp32 summation order.  The workspace is in use from the call until
+ *     the stream has run its work: calls that may overlap (different streams, graph replays)
+ *     need distinct workspaces.  The calls can be captured in HIP graphs (no allocation and no
+ *     memset inside).
  *   - Weights W are fp32 [d_out][d_in]; a group is 32 consecutive weights of one row along
  *     d_in, so d_in must be a positive multiple of 32 (W4Q_GROUP).  G = d_in / 32 groups/row.
  *   - Codes are integers in [-8, 7] (W4Q_QMIN..W4Q_QMAX).  code(w, D) is the code c that
@@ -73,11 +79,16 @@ int w4q_version(void);
  *   h        fp32 [d][d] output, H[i][j] = sum_t x[t][i] * x[t][j], unnormalised.
  *            H is written exactly symmetric (bitwise).  16-B aligned.
  *   accumulate  0: H = X^T X.   1: H += X^T X (H must hold a symmetric matrix on entry).
+ *   workspace, workspace_bytes  caller-owned scratch (see the conventions above).
  *   Products bf16 x bf16 are exact in fp32; sums are accumulated in fp32 on the matrix cores.
  *   Limits: 1 <= n_tok, 1 <= d <= 65536, d % 8 == 0 (else W4Q_ESHAPE).
  */
 int quant_hessian(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accumulate,
-                  hipStream_t stream);
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Scratch bytes of quant_hessian's fastest schedule for this shape (0: none), in *bytes (host).
+ * Argument errors as for quant_hessian.  At most 128 MB. */
+int quant_hessian_workspace_size(int64_t n_tok, int64_t d, size_t* bytes);
 
 /*
  * quant_scale_search -- Hessian-weighted choice of one scale per group.
@@ -94,15 +105,20 @@ int quant_hessian(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int acc
  *   idx     = the first k with the smallest obj_k.
  *
  *   w        fp32 [d_out][d_in], 16-B aligned.
- *   h        fp32 [d_in][ldh]; only the 32x32 diagonal blocks are read, and each block is
- *            taken to be symmetric (its upper triangle, diagonal included, is read).
+ *   h        fp32 [d_in][ldh], 16-B aligned, ldh >= d_in and a multiple of 4; only the 32x32
+ *            diagonal blocks are read, all 32x32 entries of each (the form e^T Hg e uses both
+ *            triangles, so a caller passing a triangle-only H gets wrong scores).
  *   alpha    fp32 [n_cand] DEVICE array of candidate multipliers (> 0, finite).
  *   scale    fp32 [d_out][G] out: Delta_idx (an fp16-representable value).
  *   idx      uint8 [d_out][G] out: chosen candidate index.
  *   obj      fp32 [d_out][G] out or NULL: objective of the chosen candidate.
  *   obj_all  fp32 [d_out][G][n_cand] out or NULL: objective of every candidate.
- *   Objectives are scored in fp32; every group whose two best fp32 scores lie within a
- *   relative 1e-5 of each other is re-scored in fp64 before the choice is made.
+ *   Objectives are first scored with fp32-level error, each with an error radius
+ *   2^-18 * |e|^T |Hg| |e|.  A group is re-scored in fp64 (the candidates whose interval
+ *   reaches below the best one's; all of them when obj_all is requested) unless the best
+ *   interval lies below every other and the reported objectives' radii are below 9e-6 of
+ *   them.  So the chosen index is the exact first minimum up to fp64 rounding, and every
+ *   reported objective is within 1e-5 relative of e^T Hg e.
  *   Precondition (not checked on the device): amax * alpha / 7 <= 65504.
  */
 int quant_scale_search(const float* w, int64_t d_out, int64_t d_in, const float* h, int64_t ldh,
@@ -171,7 +187,13 @@ int lsq_bwd(const float* w, const float* scale, const float* grad_w_hat, int64_t
  *   from the definition above.
  */
 int w4a16_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
-               int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t stream);
+               int64_t d_out, int64_t d_in, void* y, int y_dtype, void* workspace,
+               size_t workspace_bytes, hipStream_t stream);
+
+/* Scratch bytes of w4a16_gemm's fastest schedule (0: none; the split-weight tiled kernel for
+ * m > 16 with fewer output tiles than compute units is the only user; without its full scratch
+ * the per-group kernel runs), in *bytes (host).  At most 128 MB. */
+int w4a16_gemm_workspace_size(int64_t m, int64_t d_out, int64_t d_in, size_t* bytes);
 
 /*
  * w4a16_gemm_dq -- the same product with the weights dequantized to the 16-bit activation
@@ -185,7 +207,12 @@ int w4a16_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16
  * W4Q_EUNSUPPORTED).
  */
 int w4a16_gemm_dq(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
-                  int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t stream);
+                  int64_t d_out, int64_t d_in, void* y, int y_dtype, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+
+/* Scratch bytes of w4a16_gemm_dq's fastest schedule (0: none), in *bytes (host).  At most
+ * 128 MB. */
+int w4a16_gemm_dq_workspace_size(int64_t m, int64_t d_out, int64_t d_in, size_t* bytes);
 
 /*
  * w4a16_gemv_grouped -- many independent one-row W4A16 products (decode: one token through

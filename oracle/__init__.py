@@ -69,7 +69,6 @@ def _L():
         lib.orc_pack.argtypes = [P, P, I, I, P, P]
         lib.orc_lsq_fwd.argtypes = [P, P, I, I, P]
         lib.orc_lsq_bwd.argtypes = [P, P, P, I, I, ctypes.c_double, P, P, P]
-        lib.orc_gemm_cols.argtypes = [P, I, P, P, I, P, I, P, P]
         lib.orc_gemm_cols_mode.argtypes = [P, I, P, P, I, P, I, ctypes.c_int, P, P]
         lib.orc_round_bf16.restype = ctypes.c_double
         lib.orc_round_bf16.argtypes = [ctypes.c_double]

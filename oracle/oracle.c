@@ -337,24 +337,3 @@ void orc_gemm_cols_mode(const uint16_t* x, int64_t m, const uint8_t* packed, con
     }
   }
 }
-
-void orc_gemm_cols(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
-                   int64_t d_in, const int64_t* cols, int64_t ncols, double* y, double* yabs) {
-  int64_t G = d_in / GROUP;
-#pragma omp parallel for schedule(static)
-  for (int64_t c = 0; c < ncols; ++c) {
-    int64_t n = cols[c];
-    const uint8_t* prow = packed + n * (d_in / 2);
-    for (int64_t mi = 0; mi < m; ++mi) {
-      double s = 0.0, sa = 0.0;
-      for (int64_t k = 0; k < d_in; ++k) {
-        double wh = orc_f16_to_f64(s16[n * G + k / GROUP]) * (double)orc_unpack(prow, k);
-        double p = orc_bf16_to_f64(x[mi * d_in + k]) * wh;
-        s += p;
-        sa += fabs(p);
-      }
-      y[mi * ncols + c] = s;
-      if (yabs) yabs[mi * ncols + c] = sa;
-    }
-  }
-}

@@ -89,3 +89,21 @@ def check_gemm(y_gpu, y_ref, yabs, bf16_out=False):
     assert not bad.any(), f"{bad.sum()} outputs out of tolerance; worst ratio {np.max(err / (bound + 1e-300)):.3g}"
     rel2 = np.linalg.norm(y_gpu - y_ref) / max(np.linalg.norm(y_ref), 1e-300)
     return float(np.max(err / (bound + 1e-300))), float(rel2)
+
+
+def search_bound(w, h, alpha, cand_fn):
+    """B[r][g][k] = |e|^T |H_gg| |e| for every group and candidate (the scale of a pass-1 score's
+    rounding error), e = w - d_k * code(w, d_k) with the oracle's candidate steps cand_fn(i, k)
+    (flat group index i) and nearest-even codes clamped to [-8, 7]."""
+    d_out, d_in = w.shape
+    G, K = d_in // 32, alpha.shape[0]
+    wg = w.reshape(d_out, G, 32).astype(np.float64)
+    out = np.empty((d_out, G, K))
+    for g in range(G):
+        ha = np.abs(np.asarray(h, dtype=np.float64)[32 * g:32 * g + 32, 32 * g:32 * g + 32])
+        d = np.array([[cand_fn(r * G + g, k) for k in range(K)] for r in range(d_out)])  # [r][k]
+        safe = np.where(d == 0, 1.0, d)
+        q = np.clip(np.rint(wg[:, g, None, :] / safe[:, :, None]), -8, 7)
+        e = np.abs(wg[:, g, None, :] - d[:, :, None] * q)
+        out[:, g, :] = np.einsum("rki,ij,rkj->rk", e, ha, e)
+    return out

@@ -23,9 +23,10 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"w4q_status_string", "w4q_version", "quant_hessian",
-                          "quant_scale_search", "quant_pack", "lsq_fwd", "lsq_bwd", "w4a16_gemm",
-                          "w4a16_gemm_dq", "w4a16_gemv_grouped", "w4q_probe_read",
-                          "w4q_probe_mfma_bf16"}
+                          "quant_hessian_workspace_size", "quant_scale_search", "quant_pack",
+                          "lsq_fwd", "lsq_bwd", "w4a16_gemm", "w4a16_gemm_workspace_size",
+                          "w4a16_gemm_dq", "w4a16_gemm_dq_workspace_size", "w4a16_gemv_grouped",
+                          "w4q_probe_read", "w4q_probe_mfma_bf16"}
     l = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(l, n), n
@@ -45,14 +46,50 @@ B = 4097  # misaligned
 
 def test_hessian_argument_errors():
     L = w4q.lib()
-    assert L.quant_hessian(None, 8, 8, A, 0, None) == w4q.W4Q_EINVAL
-    assert L.quant_hessian(A, 8, 8, None, 0, None) == w4q.W4Q_EINVAL
-    assert L.quant_hessian(A, 8, 8, A, 2, None) == w4q.W4Q_EINVAL
-    assert L.quant_hessian(A, 0, 8, A, 0, None) == w4q.W4Q_ESHAPE
-    assert L.quant_hessian(A, 8, 12, A, 0, None) == w4q.W4Q_ESHAPE
-    assert L.quant_hessian(A, 8, -8, A, 0, None) == w4q.W4Q_ESHAPE
-    assert L.quant_hessian(A, 8, 65544, A, 0, None) == w4q.W4Q_ESHAPE
-    assert L.quant_hessian(B, 8, 8, A, 0, None) == w4q.W4Q_EALIGN
+    assert L.quant_hessian(None, 8, 8, A, 0, None, 0, None) == w4q.W4Q_EINVAL
+    assert L.quant_hessian(A, 8, 8, None, 0, None, 0, None) == w4q.W4Q_EINVAL
+    assert L.quant_hessian(A, 8, 8, A, 2, None, 0, None) == w4q.W4Q_EINVAL
+    assert L.quant_hessian(A, 0, 8, A, 0, None, 0, None) == w4q.W4Q_ESHAPE
+    assert L.quant_hessian(A, 8, 12, A, 0, None, 0, None) == w4q.W4Q_ESHAPE
+    assert L.quant_hessian(A, 8, -8, A, 0, None, 0, None) == w4q.W4Q_ESHAPE
+    assert L.quant_hessian(A, 8, 65544, A, 0, None, 0, None) == w4q.W4Q_ESHAPE
+    assert L.quant_hessian(B, 8, 8, A, 0, None, 0, None) == w4q.W4Q_EALIGN
+
+
+def test_workspace_arguments():
+    L = w4q.lib()
+    n = ctypes.c_size_t(7)
+    assert L.quant_hessian_workspace_size(8, 8, None) == w4q.W4Q_EINVAL
+    assert L.quant_hessian_workspace_size(0, 8, ctypes.byref(n)) == w4q.W4Q_ESHAPE
+    assert L.w4a16_gemm_workspace_size(0, 4, 64, ctypes.byref(n)) == w4q.W4Q_ESHAPE
+    assert L.w4a16_gemm_dq_workspace_size(4, 4, 48, ctypes.byref(n)) == w4q.W4Q_ESHAPE
+    # NULL scratch with a size, and misaligned scratch, are refused before anything is enqueued
+    assert L.quant_hessian(A, 8, 8, A, 0, None, 64, None) == w4q.W4Q_EINVAL
+    assert L.quant_hessian(A, 8, 8, A, 0, A + 16, 64, None) == w4q.W4Q_EALIGN
+    assert L.w4a16_gemm(A, 32, A, A, 4, 256, A, 0, None, 16, None) == w4q.W4Q_EINVAL
+    assert L.w4a16_gemm_dq(A, 32, A, A, 4, 256, A, 0, A + 128, 1 << 20, None) == w4q.W4Q_EALIGN
+
+
+@pytest.mark.parametrize("n_tok,d,want", [(8, 8, 0), (8192, 4096, 256 * 2 * 256 * 256 * 4),
+                                          (1 << 20, 12288, 256 * 2 * 256 * 256 * 4)])
+def test_hessian_workspace_size(n_tok, d, want):
+    # the fastest schedule keeps two 256x256 fp32 partial tiles per workgroup that shares a tile;
+    # a single small tile needs none; never more than 128 MB
+    n = ctypes.c_size_t(0)
+    assert w4q.lib().quant_hessian_workspace_size(n_tok, d, ctypes.byref(n)) == w4q.W4Q_OK
+    assert n.value == want
+    assert w4q.workspace_size("quant_hessian", n_tok, d) == want
+
+
+def test_gemm_workspace_size():
+    # exact weights use scratch only for m > 16 below 256 output tiles on the tiled kernel; the
+    # dequantizing product for its stream-K split
+    assert w4q.workspace_size("w4a16_gemm", 16, 4096, 4096) == 0
+    assert w4q.workspace_size("w4a16_gemm", 2048, 12288, 4096) == 0          # 384 tiles: per-group kernel
+    assert w4q.workspace_size("w4a16_gemm", 256, 8192, 2048) > 0             # 32 tiles: split weights
+    assert w4q.workspace_size("w4a16_gemm", 256, 8192, 2080) == 0            # d_in % 256 != 0
+    assert 0 < w4q.workspace_size("w4a16_gemm_dq", 2048, 12288, 4096) <= 128 << 20
+    assert w4q.workspace_size("w4a16_gemm_dq", 1, 256, 256) == 0             # one tile, no split
 
 
 def test_search_argument_errors():
@@ -71,7 +108,9 @@ def test_search_argument_errors():
     assert call(d_in=48) == w4q.W4Q_ESHAPE
     assert call(d_out=0) == w4q.W4Q_ESHAPE
     assert call(ldh=32) == w4q.W4Q_ESHAPE
+    assert call(ldh=66) == w4q.W4Q_ESHAPE                  # rows of H must stay 16-byte aligned
     assert call(w=A + 4) == w4q.W4Q_EALIGN
+    assert call(h=A + 4) == w4q.W4Q_EALIGN
 
 
 def test_pack_lsq_gemm_argument_errors():
@@ -83,15 +122,15 @@ def test_pack_lsq_gemm_argument_errors():
     assert L.lsq_fwd(A, A, -1, 64, A, None) == w4q.W4Q_ESHAPE
     assert L.lsq_bwd(A, A, A, 4, 64, 0.5, A, None, None, None) == w4q.W4Q_EINVAL
     assert L.lsq_bwd(A, A, A, 4, 96, 0.5, A + 4, A, None, None) == w4q.W4Q_EALIGN
-    assert L.w4a16_gemm(A, 1, A, A, 4, 64, A, 2, None) == w4q.W4Q_EINVAL
-    assert L.w4a16_gemm(A, 0, A, A, 4, 64, A, 0, None) == w4q.W4Q_ESHAPE
-    assert L.w4a16_gemm(A, 1, A, A, 4, 65, A, 0, None) == w4q.W4Q_ESHAPE
-    assert L.w4a16_gemm(A + 2, 1, A, A, 4, 64, A, 0, None) == w4q.W4Q_EALIGN
-    assert L.w4a16_gemm(A, 1, A, A, 4, 64, A + 1, 1, None) == w4q.W4Q_EALIGN
-    assert L.w4a16_gemm_dq(A, 1, A, A, 4, 256, A, 2, None) == w4q.W4Q_EINVAL
-    assert L.w4a16_gemm_dq(A, 0, A, A, 4, 256, A, 0, None) == w4q.W4Q_ESHAPE
-    assert L.w4a16_gemm_dq(A + 2, 1, A, A, 4, 256, A, 0, None) == w4q.W4Q_EALIGN
-    assert L.w4a16_gemm_dq(A, 1, A, A, 4, 64, A, 0, None) == w4q.W4Q_EUNSUPPORTED
+    assert L.w4a16_gemm(A, 1, A, A, 4, 64, A, 2, None, 0, None) == w4q.W4Q_EINVAL
+    assert L.w4a16_gemm(A, 0, A, A, 4, 64, A, 0, None, 0, None) == w4q.W4Q_ESHAPE
+    assert L.w4a16_gemm(A, 1, A, A, 4, 65, A, 0, None, 0, None) == w4q.W4Q_ESHAPE
+    assert L.w4a16_gemm(A + 2, 1, A, A, 4, 64, A, 0, None, 0, None) == w4q.W4Q_EALIGN
+    assert L.w4a16_gemm(A, 1, A, A, 4, 64, A + 1, 1, None, 0, None) == w4q.W4Q_EALIGN
+    assert L.w4a16_gemm_dq(A, 1, A, A, 4, 256, A, 2, None, 0, None) == w4q.W4Q_EINVAL
+    assert L.w4a16_gemm_dq(A, 0, A, A, 4, 256, A, 0, None, 0, None) == w4q.W4Q_ESHAPE
+    assert L.w4a16_gemm_dq(A + 2, 1, A, A, 4, 256, A, 0, None, 0, None) == w4q.W4Q_EALIGN
+    assert L.w4a16_gemm_dq(A, 1, A, A, 4, 64, A, 0, None, 0, None) == w4q.W4Q_EUNSUPPORTED
     from w4a16_group_wise_amd._lib import GemvProblem
     probs = (GemvProblem * 2)(GemvProblem(A, A, A, A, 4, 64), GemvProblem(A, A, A, A, 4, 64))
     pp = ctypes.cast(probs, ctypes.c_void_p)

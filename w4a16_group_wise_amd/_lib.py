@@ -20,6 +20,7 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _INT = ctypes.c_int
 _F = ctypes.c_float
+_SZ = ctypes.c_size_t
 class GemvProblem(ctypes.Structure):
     """w4q_gemv_problem of w4a16q.h"""
     _fields_ = [("x", ctypes.c_void_p), ("packed", ctypes.c_void_p), ("scale_f16", ctypes.c_void_p),
@@ -29,13 +30,16 @@ class GemvProblem(ctypes.Structure):
 SIGNATURES = {
     "w4q_status_string": (ctypes.c_char_p, [_INT]),
     "w4q_version": (_INT, []),
-    "quant_hessian": (_INT, [_P, _I64, _I64, _P, _INT, _P]),
+    "quant_hessian": (_INT, [_P, _I64, _I64, _P, _INT, _P, _SZ, _P]),
+    "quant_hessian_workspace_size": (_INT, [_I64, _I64, _P]),
     "quant_scale_search": (_INT, [_P, _I64, _I64, _P, _I64, _P, _INT, _P, _P, _P, _P, _P]),
     "quant_pack": (_INT, [_P, _P, _I64, _I64, _P, _P, _P]),
     "lsq_fwd": (_INT, [_P, _P, _I64, _I64, _P, _P]),
     "lsq_bwd": (_INT, [_P, _P, _P, _I64, _I64, _F, _P, _P, _P, _P]),
-    "w4a16_gemm": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _INT, _P]),
-    "w4a16_gemm_dq": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _INT, _P]),
+    "w4a16_gemm": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _INT, _P, _SZ, _P]),
+    "w4a16_gemm_workspace_size": (_INT, [_I64, _I64, _I64, _P]),
+    "w4a16_gemm_dq": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _INT, _P, _SZ, _P]),
+    "w4a16_gemm_dq_workspace_size": (_INT, [_I64, _I64, _I64, _P]),
     "w4a16_gemv_grouped": (_INT, [_P, _INT, _INT, _P]),
     "w4q_probe_read": (_INT, [_P, _I64, _INT, _P, _P]),
     "w4q_probe_mfma_bf16": (_INT, [_P, _I64, _P, _P]),

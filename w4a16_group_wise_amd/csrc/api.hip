@@ -1,5 +1,6 @@
 // api.hip -- the extern "C" entry points of libw4a16q: argument checks on the host, then one
-// launcher per step.  No allocation, no synchronisation, no global mutable state.
+// launcher per step.  No allocation, no synchronisation, no global mutable state: scratch memory
+// is the caller's (workspace arguments), and every call only enqueues on the caller's stream.
 #include "common.hpp"
 
 namespace {
@@ -23,7 +24,7 @@ const char* w4q_status_string(int status) {
   switch (status) {
     case W4Q_OK: return "ok";
     case W4Q_EINVAL: return "invalid argument (null pointer, bad enum value or n_cand outside [1, 255])";
-    case W4Q_ESHAPE: return "bad shape (non-positive size, d_in not a multiple of 32, ldh < d_in, d % 8 != 0 or size overflow)";
+    case W4Q_ESHAPE: return "bad shape (non-positive size, d_in not a multiple of 32, ldh < d_in or not a multiple of 4, d % 8 != 0 or size overflow)";
     case W4Q_EALIGN: return "misaligned pointer (tensor data must be 16-byte aligned)";
     case W4Q_EUNSUPPORTED: return "size beyond the supported range";
     case W4Q_EHIP: return "HIP launch error";
@@ -33,13 +34,35 @@ const char* w4q_status_string(int status) {
 
 int w4q_version(void) { return kVersion; }
 
-int quant_hessian(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accumulate,
-                  hipStream_t stream) {
-  if (!x || !h || (accumulate != 0 && accumulate != 1)) return W4Q_EINVAL;
+static int hessian_args(int64_t n_tok, int64_t d) {
   if (n_tok <= 0 || d <= 0 || d % 8 != 0 || d > 65536) return W4Q_ESHAPE;
   if (n_tok > (int64_t(1) << 40) / d) return W4Q_ESHAPE;
+  return W4Q_OK;
+}
+
+// scratch: NULL with 0 bytes, or 256-byte aligned memory of ws_bytes
+static int ws_args(const void* ws, size_t ws_bytes) {
+  if (ws == nullptr && ws_bytes != 0) return W4Q_EINVAL;
+  if (ws != nullptr && !aligned(ws, 256)) return W4Q_EALIGN;
+  return W4Q_OK;
+}
+
+int quant_hessian_workspace_size(int64_t n_tok, int64_t d, size_t* bytes) {
+  if (!bytes) return W4Q_EINVAL;
+  const int rc = hessian_args(n_tok, d);
+  if (rc != W4Q_OK) return rc;
+  *bytes = w4q_hessian_workspace(n_tok, d);
+  return W4Q_OK;
+}
+
+int quant_hessian(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accumulate,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!x || !h || (accumulate != 0 && accumulate != 1)) return W4Q_EINVAL;
+  int rc = hessian_args(n_tok, d);
+  if (rc != W4Q_OK) return rc;
+  if ((rc = ws_args(workspace, workspace_bytes)) != W4Q_OK) return rc;
   if (!aligned(x, 16) || !aligned(h, 16)) return W4Q_EALIGN;
-  return w4q_launch_hessian(x, n_tok, d, h, accumulate, stream);
+  return w4q_launch_hessian(x, n_tok, d, h, accumulate, workspace, workspace_bytes, stream);
 }
 
 int quant_scale_search(const float* w, int64_t d_out, int64_t d_in, const float* h, int64_t ldh,
@@ -49,8 +72,8 @@ int quant_scale_search(const float* w, int64_t d_out, int64_t d_in, const float*
   if (n_cand < 1 || n_cand > W4Q_MAX_CAND) return W4Q_EINVAL;
   int rc = check_wshape(d_out, d_in);
   if (rc != W4Q_OK) return rc;
-  if (ldh < d_in) return W4Q_ESHAPE;
-  if (!aligned(w, 16) || !aligned(h, 4) || !aligned(alpha, 4) || !aligned(scale, 4) ||
+  if (ldh < d_in || ldh % 4 != 0) return W4Q_ESHAPE;
+  if (!aligned(w, 16) || !aligned(h, 16) || !aligned(alpha, 4) || !aligned(scale, 4) ||
       (obj && !aligned(obj, 4)) || (obj_all && !aligned(obj_all, 4)))
     return W4Q_EALIGN;
   return w4q_launch_scale_search(w, d_out, d_in, h, ldh, alpha, n_cand, scale, idx, obj, obj_all,
@@ -89,32 +112,62 @@ int lsq_bwd(const float* w, const float* scale, const float* grad_w_hat, int64_t
                             w_hat, stream);
 }
 
+static int gemm_shape(int64_t m, int64_t d_out, int64_t d_in);
+
 static int gemm_args(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
                      int64_t d_out, int64_t d_in, void* y, int y_dtype) {
   if (!x || !packed || !scale_f16 || !y || (y_dtype != 0 && y_dtype != 1)) return W4Q_EINVAL;
-  if (m <= 0) return W4Q_ESHAPE;
-  int rc = check_wshape(d_out, d_in);
+  const int rc = gemm_shape(m, d_out, d_in);
   if (rc != W4Q_OK) return rc;
-  if (m > (int64_t(1) << 40) / d_in || m > (int64_t(1) << 40) / d_out) return W4Q_ESHAPE;
   if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scale_f16, 2) ||
       !aligned(y, y_dtype == 0 ? 4 : 2))
     return W4Q_EALIGN;
   return W4Q_OK;
 }
 
-int w4a16_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
-               int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t stream) {
-  const int rc = gemm_args(x, m, packed, scale_f16, d_out, d_in, y, y_dtype);
+static int gemm_shape(int64_t m, int64_t d_out, int64_t d_in) {
+  if (m <= 0) return W4Q_ESHAPE;
+  const int rc = check_wshape(d_out, d_in);
   if (rc != W4Q_OK) return rc;
+  if (m > (int64_t(1) << 40) / d_in || m > (int64_t(1) << 40) / d_out) return W4Q_ESHAPE;
+  return W4Q_OK;
+}
+
+int w4a16_gemm_workspace_size(int64_t m, int64_t d_out, int64_t d_in, size_t* bytes) {
+  if (!bytes) return W4Q_EINVAL;
+  const int rc = gemm_shape(m, d_out, d_in);
+  if (rc != W4Q_OK) return rc;
+  *bytes = w4q_gemm_workspace(m, d_out, d_in, 0);
+  return W4Q_OK;
+}
+
+int w4a16_gemm_dq_workspace_size(int64_t m, int64_t d_out, int64_t d_in, size_t* bytes) {
+  if (!bytes) return W4Q_EINVAL;
+  const int rc = gemm_shape(m, d_out, d_in);
+  if (rc != W4Q_OK) return rc;
+  *bytes = w4q_gemm_workspace(m, d_out, d_in, 1);
+  return W4Q_OK;
+}
+
+int w4a16_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
+               int64_t d_out, int64_t d_in, void* y, int y_dtype, void* workspace,
+               size_t workspace_bytes, hipStream_t stream) {
+  int rc = gemm_args(x, m, packed, scale_f16, d_out, d_in, y, y_dtype);
+  if (rc != W4Q_OK) return rc;
+  if ((rc = ws_args(workspace, workspace_bytes)) != W4Q_OK) return rc;
   if (m <= 16) return w4q_launch_gemv(x, m, packed, scale_f16, d_out, d_in, y, y_dtype, stream);
-  return w4q_launch_gemm(x, m, packed, scale_f16, d_out, d_in, y, y_dtype, 0, stream);
+  return w4q_launch_gemm(x, m, packed, scale_f16, d_out, d_in, y, y_dtype, 0, workspace,
+                         workspace_bytes, stream);
 }
 
 int w4a16_gemm_dq(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
-                  int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t stream) {
-  const int rc = gemm_args(x, m, packed, scale_f16, d_out, d_in, y, y_dtype);
+                  int64_t d_out, int64_t d_in, void* y, int y_dtype, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  int rc = gemm_args(x, m, packed, scale_f16, d_out, d_in, y, y_dtype);
   if (rc != W4Q_OK) return rc;
-  return w4q_launch_gemm(x, m, packed, scale_f16, d_out, d_in, y, y_dtype, 1, stream);
+  if ((rc = ws_args(workspace, workspace_bytes)) != W4Q_OK) return rc;
+  return w4q_launch_gemm(x, m, packed, scale_f16, d_out, d_in, y, y_dtype, 1, workspace,
+                         workspace_bytes, stream);
 }
 
 

@@ -167,15 +167,14 @@ __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u,
 
 }  // namespace w4q
 
-// Device scratch for partial tiles (one buffer per device, users serialised); return a
-// w4q_status.  Every successful acquire must be followed by a release on the same stream.
-constexpr size_t kWorkspaceBytes = size_t(256) * 2 * 256 * 256 * sizeof(float);  // 128 MB
-int w4q_workspace_acquire(void** ptr, size_t bytes, hipStream_t s);
-int w4q_workspace_release(hipStream_t s);
-
 // Launchers (one per source file); return a w4q_status.
+// Scratch: the Hessian and the tiled W4A16 product split output tiles over workgroups (stream-K)
+// and keep the partial tiles in scratch memory the caller passes (ws, ws_bytes); with less than
+// the *_workspace size (the fastest schedule's need) they run a schedule whose partial tiles fit.
+size_t w4q_hessian_workspace(int64_t n_tok, int64_t d);
+size_t w4q_gemm_workspace(int64_t m, int64_t d_out, int64_t d_in, int w_mode);
 int w4q_launch_hessian(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accumulate,
-                       hipStream_t s);
+                       void* ws, size_t ws_bytes, hipStream_t s);
 int w4q_launch_scale_search(const float* w, int64_t d_out, int64_t d_in, const float* h,
                             int64_t ldh, const float* alpha, int n_cand, float* scale,
                             uint8_t* idx, float* obj, float* obj_all, hipStream_t s);
@@ -192,7 +191,8 @@ bool w4q_gemv_group_fits(const w4q_gemv_problem* probs, int n);
 int w4q_launch_gemv_group(const w4q_gemv_problem* probs, int n, int y_dtype, hipStream_t s);
 // w_mode: 0 = exact weights (s16 * q), 1 = weights dequantized to bf16 (RNE of s16 * q)
 int w4q_launch_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
-                    int64_t d_out, int64_t d_in, void* y, int y_dtype, int w_mode, hipStream_t s);
+                    int64_t d_out, int64_t d_in, void* y, int y_dtype, int w_mode, void* ws,
+                    size_t ws_bytes, hipStream_t s);
 
 static inline int w4q_launch_status() {
   return hipGetLastError() == hipSuccess ? W4Q_OK : W4Q_EHIP;

@@ -523,43 +523,74 @@ __global__ __launch_bounds__(kGThreads) void gemm_fixup_kernel(void* __restrict_
   gstore_block(y, y_dtype, M, N, tm * GT + 32 * i, tn * GT + 32 * wid, v, lane);
 }
 
-int launch_dq_pass(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16, int64_t N,
-                    int64_t K, void* y, int y_dtype, bool exact, hipStream_t s) {
-  const int64_t G = K / 32;
-  const int64_t tm_count = (m + GT - 1) / GT, tn_count = (N + GT - 1) / GT;
-  const int64_t tiles = tm_count * tn_count;
-  const int64_t total = tiles * G;
-  if (total > 0x3FFFFFFF) return W4Q_EUNSUPPORTED;
-  int64_t nblk = (total + kGMinChunk - 1) / kGMinChunk;
+// Schedule of one pass of the tiled kernel: stream-K ranges of `chunk` (tile, K-group)
+// iterations, one per workgroup, and the scratch their partial tiles need (two fp32 tiles per
+// workgroup, only when some tile is split over workgroups).
+struct DqPlan {
+  int64_t tn_count, tiles, G, total, chunk, nblk, per_xcd;
+  bool partial;
+  size_t ws_need;
+};
+
+constexpr size_t kGSlotPair = size_t(2) * kGTileElems * sizeof(float);
+
+void dq_finish(DqPlan& p) {
+  p.nblk = (p.total + p.chunk - 1) / p.chunk;
+  p.partial = p.nblk > 1 && p.chunk % p.G != 0;
+  p.ws_need = p.partial ? size_t(p.nblk) * kGSlotPair : 0;
+  p.per_xcd = (p.nblk + 7) / 8;
+}
+
+// The fastest schedule (SIZE_MAX) or the fastest whose scratch fits ws_bytes: the most
+// workgroups whose partial tiles fit, or one whole tile per workgroup (no scratch), whichever
+// runs more workgroups.
+DqPlan plan_dq(int64_t m, int64_t N, int64_t K, size_t ws_bytes) {
+  DqPlan p;
+  p.G = K / 32;
+  const int64_t tm_count = (m + GT - 1) / GT;
+  p.tn_count = (N + GT - 1) / GT;
+  p.tiles = tm_count * p.tn_count;
+  p.total = p.tiles * p.G;
+  int64_t nblk = (p.total + kGMinChunk - 1) / kGMinChunk;
   if (nblk > kGMaxBlocks) nblk = kGMaxBlocks;
-  const int64_t chunk = (total + nblk - 1) / nblk;
-  nblk = (total + chunk - 1) / chunk;
-  const bool partial = nblk > 1 && chunk % G != 0;
-  const int64_t per_xcd = (nblk + 7) / 8;
-  float* ws = nullptr;
-  if (partial && w4q_workspace_acquire(reinterpret_cast<void**>(&ws), (size_t)nblk * 2 * kGTileElems * sizeof(float), s) !=
-                   W4Q_OK)
-    return W4Q_EHIP;
-  const dim3 grid(static_cast<unsigned>(8 * per_xcd));
+  p.chunk = (p.total + nblk - 1) / nblk;
+  dq_finish(p);
+  if (p.ws_need <= ws_bytes) return p;
+  const int64_t fit = static_cast<int64_t>(ws_bytes / kGSlotPair);
+  DqPlan q = p;
+  q.chunk = q.G;
+  dq_finish(q);
+  if (fit >= 2) {
+    DqPlan r = p;
+    r.chunk = (r.total + fit - 1) / fit;
+    dq_finish(r);
+    if (r.ws_need <= ws_bytes && r.nblk > q.nblk) return r;
+  }
+  return q;
+}
+
+int launch_dq_pass(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16, int64_t N,
+                    int64_t K, void* y, int y_dtype, bool exact, void* ws_ptr, size_t ws_bytes, hipStream_t s) {
+  const DqPlan p = plan_dq(m, N, K, ws_ptr != nullptr ? ws_bytes : 0);
+  if (p.total > 0x3FFFFFFF) return W4Q_EUNSUPPORTED;
+  float* ws = p.partial ? static_cast<float*>(ws_ptr) : nullptr;
+  const dim3 grid(static_cast<unsigned>(8 * p.per_xcd));
   if (exact)
     hipLaunchKernelGGL(gemm_dq_kernel<true>, grid, dim3(kGThreads), 0, s, x, static_cast<int>(m), packed, s16,
-                       static_cast<int>(N), static_cast<int>(K), y, y_dtype, static_cast<int>(tn_count),
-                       static_cast<int>(total), static_cast<int>(chunk), static_cast<int>(nblk),
-                       static_cast<int>(per_xcd), ws);
+                       static_cast<int>(N), static_cast<int>(K), y, y_dtype, static_cast<int>(p.tn_count),
+                       static_cast<int>(p.total), static_cast<int>(p.chunk), static_cast<int>(p.nblk),
+                       static_cast<int>(p.per_xcd), ws);
   else
     hipLaunchKernelGGL(gemm_dq_kernel<false>, grid, dim3(kGThreads), 0, s, x, static_cast<int>(m), packed, s16,
-                       static_cast<int>(N), static_cast<int>(K), y, y_dtype, static_cast<int>(tn_count),
-                       static_cast<int>(total), static_cast<int>(chunk), static_cast<int>(nblk),
-                       static_cast<int>(per_xcd), ws);
+                       static_cast<int>(N), static_cast<int>(K), y, y_dtype, static_cast<int>(p.tn_count),
+                       static_cast<int>(p.total), static_cast<int>(p.chunk), static_cast<int>(p.nblk),
+                       static_cast<int>(p.per_xcd), ws);
   int rc = w4q_launch_status();
-  if (partial) {
-    if (rc == W4Q_OK) {
-      hipLaunchKernelGGL(gemm_fixup_kernel, dim3(static_cast<unsigned>(8 * tiles)), dim3(kGThreads), 0, s, y,
-                         y_dtype, static_cast<int>(m), static_cast<int>(N), static_cast<int>(G),
-                         static_cast<int>(tn_count), static_cast<int>(chunk), ws);
-      rc = w4q_launch_status();
-    }
-    if (w4q_workspace_release(s) != W4Q_OK && rc == W4Q_OK) rc = W4Q_EHIP;
+  if (p.partial && rc == W4Q_OK) {
+    hipLaunchKernelGGL(gemm_fixup_kernel, dim3(static_cast<unsigned>(8 * p.tiles)), dim3(kGThreads), 0, s, y,
+                       y_dtype, static_cast<int>(m), static_cast<int>(N), static_cast<int>(p.G),
+                       static_cast<int>(p.tn_count), static_cast<int>(p.chunk), ws);
+    rc = w4q_launch_status();
   }
   return rc;
 }
@@ -597,26 +628,50 @@ static int launch_group(const uint16_t* x, int64_t m, const uint8_t* packed, con
   return w4q_launch_status();
 }
 
+// the tiled kernel needs 16-byte scale rows (d_in % 256 == 0) and 32-bit buffer offsets into
+// the codes and scales; x is taken in passes of whole 256-row tiles that fit them too
+static bool tiled_ok(int64_t d_out, int64_t d_in) {
+  return d_in % 256 == 0 && d_out * (d_in / 2) < 0x7FFFFFFF && 256 * d_in * 2 < 0x7FFFFFFF;
+}
+static int64_t pass_rows(int64_t d_in) { return (0x7FFFFFFF / (2 * d_in)) / GT * GT; }
+
+// exact weights go to the split-scale tiled kernel only while the per-group kernel would leave
+// compute units idle (fewer than 256 output tiles) and the tiled kernel can take the shape
+static bool exact_on_tiled(int64_t m, int64_t d_out, int64_t d_in) {
+  bool big;
+  return tiled_ok(d_out, d_in) && group_tiles(m, d_out, &big) < 256;
+}
+
+size_t w4q_gemm_workspace(int64_t m, int64_t d_out, int64_t d_in, int w_mode) {
+  if (w_mode == 0 && (m <= 16 || !exact_on_tiled(m, d_out, d_in))) return 0;
+  if (!tiled_ok(d_out, d_in)) return 0;
+  const int64_t rows = pass_rows(d_in);
+  const int64_t first = m < rows ? m : rows;
+  const int64_t last = m % rows == 0 ? first : m % rows;
+  const size_t a = plan_dq(first, d_out, d_in, SIZE_MAX).ws_need;
+  const size_t b = plan_dq(last, d_out, d_in, SIZE_MAX).ws_need;
+  return a > b ? a : b;
+}
+
 int w4q_launch_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
-                    int64_t d_out, int64_t d_in, void* y, int y_dtype, int w_mode, hipStream_t s) {
-  // the tiled kernel needs 16-byte scale rows (d_in % 256 == 0) and 32-bit buffer offsets into
-  // the codes and scales; x is taken in passes of whole 256-row tiles that fit them too
-  const bool tiled = d_in % 256 == 0 && d_out * (d_in / 2) < 0x7FFFFFFF && 256 * d_in * 2 < 0x7FFFFFFF;
+                    int64_t d_out, int64_t d_in, void* y, int y_dtype, int w_mode, void* ws,
+                    size_t ws_bytes, hipStream_t s) {
   if (w_mode == 0) {
     // exact weights: the per-group kernel while it has a tile for every compute unit; below
     // that, the stream-K tiled kernel with split weights (twice the matrix-core work, but the
-    // K dimension spread over all compute units)
-    bool big;
-    if (!tiled || group_tiles(m, d_out, &big) >= 256)
+    // K dimension spread over all compute units) when the caller's scratch holds its partial
+    // tiles
+    if (!exact_on_tiled(m, d_out, d_in) || ws == nullptr || ws_bytes < w4q_gemm_workspace(m, d_out, d_in, 0))
       return launch_group(x, m, packed, s16, d_out, d_in, y, y_dtype, s);
   }
-  if (!tiled) return W4Q_EUNSUPPORTED;
-  const int64_t rows = (0x7FFFFFFF / (2 * d_in)) / GT * GT;
+  if (!tiled_ok(d_out, d_in)) return W4Q_EUNSUPPORTED;
+  const int64_t rows = pass_rows(d_in);
   const int64_t ob = y_dtype == 0 ? 4 : 2;
   for (int64_t r0 = 0; r0 < m; r0 += rows) {
     const int64_t mr = m - r0 < rows ? m - r0 : rows;
     const int rc = launch_dq_pass(x + r0 * d_in, mr, packed, s16, d_out, d_in,
-                                  static_cast<uint8_t*>(y) + r0 * d_out * ob, y_dtype, w_mode == 0, s);
+                                  static_cast<uint8_t*>(y) + r0 * d_out * ob, y_dtype, w_mode == 0, ws,
+                                  ws_bytes, s);
     if (rc != W4Q_OK) return rc;
   }
   return W4Q_OK;

@@ -13,7 +13,9 @@
 // are cut into one contiguous range per workgroup, so every compute unit gets the same number of
 // matrix-core steps whatever the tile count.  A tile whose stages are spread over several
 // workgroups is finished by a second kernel that adds the partial tiles in the fixed order of
-// their token ranges: the result does not depend on scheduling.
+// their token ranges: the result does not depend on scheduling.  The partial tiles live in
+// scratch memory the caller passes; with less scratch than the even split wants, the ranges are
+// lengthened until their partial tiles fit, or become whole tiles (no scratch at all).
 //
 // Per workgroup: 8 wavefronts (two per SIMD) of 128x64 (4x2 v_mfma_f32_32x32x16_bf16 blocks),
 // 32 tokens per stage, four LDS stage buffers.  Two wavefronts per SIMD because the transposing
@@ -332,60 +334,101 @@ __global__ __launch_bounds__(kThreads) void hessian_fixup_kernel(float* __restri
   store_block(h, d, row0, col0, v, accumulate, lane);
 }
 
-// One pass over at most 2^31 - 1 bytes of X (32-bit buffer offsets).
-int launch_pass(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accumulate, hipStream_t s) {
-  const int64_t nt = (d + BT - 1) / BT;
-  const int64_t tiles = nt * (nt + 1) / 2;
-  const int64_t ns = (n_tok + BK - 1) / BK;
-  const int64_t total = tiles * ns;
-  if (total > 0x3FFFFFFF) return W4Q_EUNSUPPORTED;
+// Schedule of one pass: stream-K ranges of `chunk` (tile, stage) iterations, one per workgroup,
+// and the scratch their partial tiles need (two 256x256 fp32 slots per workgroup, only when some
+// tile is split over workgroups).
+struct Plan {
+  int64_t nt, tiles, ns, total, chunk, nblk, per_xcd;
+  bool split;
+  size_t ws_need;
+};
+
+constexpr size_t kSlotPair = size_t(2) * kTileElems * sizeof(float);  // 512 KB per workgroup
+
+void finish(Plan& p) {
+  p.nblk = (p.total + p.chunk - 1) / p.chunk;
+  p.split = p.nblk > 1 && p.chunk % p.ns != 0;
+  p.ws_need = p.split ? size_t(p.nblk) * kSlotPair : 0;
+  p.per_xcd = (p.nblk + 7) / 8;
+}
+
+// The fastest schedule whose scratch fits ws_bytes (SIZE_MAX: the fastest one).
+Plan plan_pass(int64_t n_tok, int64_t d, size_t ws_bytes) {
+  Plan p;
+  p.nt = (d + BT - 1) / BT;
+  p.tiles = p.nt * (p.nt + 1) / 2;
+  p.ns = (n_tok + BK - 1) / BK;
+  p.total = p.tiles * p.ns;
   // an even share of the stages for every compute unit, but at least kMinChunk stages (or a
   // whole tile) per workgroup: short ranges cost more in partial tiles than they gain.  Shares
   // shorter than 2 kMinChunk are lengthened to that while at least half the compute units stay
   // busy (measured: 4096 x 2048 tokens x features 60 -> 52 us)
-  const int64_t min_chunk = ns < kMinChunk ? ns : kMinChunk;
-  int64_t chunk = (total + kMaxBlocks - 1) / kMaxBlocks;
-  if (chunk < 2 * kMinChunk && total / (2 * kMinChunk) >= kMaxBlocks / 2 && ns >= 2 * kMinChunk)
-    chunk = 2 * kMinChunk;
-  if (chunk < min_chunk) chunk = min_chunk;
-  const int64_t nblk = (total + chunk - 1) / chunk;
-  const bool split = nblk > 1 && chunk % ns != 0;
-  const int64_t per_xcd = (nblk + 7) / 8;
-
-  float* ws = nullptr;
-  if (split) {
-    const size_t bytes = (size_t)nblk * 2 * kTileElems * sizeof(float);
-    if (w4q_workspace_acquire(reinterpret_cast<void**>(&ws), bytes, s) != W4Q_OK) return W4Q_EHIP;
+  const int64_t min_chunk = p.ns < kMinChunk ? p.ns : kMinChunk;
+  p.chunk = (p.total + kMaxBlocks - 1) / kMaxBlocks;
+  if (p.chunk < 2 * kMinChunk && p.total / (2 * kMinChunk) >= kMaxBlocks / 2 && p.ns >= 2 * kMinChunk)
+    p.chunk = 2 * kMinChunk;
+  if (p.chunk < min_chunk) p.chunk = min_chunk;
+  finish(p);
+  if (p.ws_need <= ws_bytes) return p;
+  // not enough scratch: the most workgroups whose partial tiles fit, or one whole tile per
+  // workgroup (no scratch), whichever runs more workgroups
+  const int64_t fit = static_cast<int64_t>(ws_bytes / kSlotPair);
+  Plan q = p;
+  q.chunk = q.ns;
+  finish(q);
+  if (fit >= 2) {
+    Plan r = p;
+    r.chunk = (r.total + fit - 1) / fit;
+    finish(r);
+    if (r.ws_need <= ws_bytes && r.nblk > q.nblk) return r;
   }
-  hipLaunchKernelGGL(hessian_kernel, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(kThreads), 0, s, x,
-                     static_cast<int>(n_tok), static_cast<int>(d), h, accumulate, static_cast<int>(nt),
-                     static_cast<int>(ns), static_cast<int>(total), static_cast<int>(chunk),
-                     static_cast<int>(nblk), static_cast<int>(per_xcd), ws);
+  return q;
+}
+
+// One pass over at most 2^31 - 1 bytes of X (32-bit buffer offsets).
+int launch_pass(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accumulate, void* ws_ptr,
+                size_t ws_bytes, hipStream_t s) {
+  const Plan p = plan_pass(n_tok, d, ws_ptr != nullptr ? ws_bytes : 0);
+  if (p.total > 0x3FFFFFFF) return W4Q_EUNSUPPORTED;
+  float* ws = p.split ? static_cast<float*>(ws_ptr) : nullptr;
+  hipLaunchKernelGGL(hessian_kernel, dim3(static_cast<unsigned>(8 * p.per_xcd)), dim3(kThreads), 0, s, x,
+                     static_cast<int>(n_tok), static_cast<int>(d), h, accumulate, static_cast<int>(p.nt),
+                     static_cast<int>(p.ns), static_cast<int>(p.total), static_cast<int>(p.chunk),
+                     static_cast<int>(p.nblk), static_cast<int>(p.per_xcd), ws);
   int rc = w4q_launch_status();
-  if (split) {
-    if (rc == W4Q_OK) {
-      hipLaunchKernelGGL(hessian_fixup_kernel, dim3(static_cast<unsigned>(8 * tiles)), dim3(kThreads), 0, s, h,
-                         static_cast<int>(d), accumulate, static_cast<int>(nt), static_cast<int>(ns),
-                         static_cast<int>(chunk), ws);
-      rc = w4q_launch_status();
-    }
-    if (w4q_workspace_release(s) != W4Q_OK && rc == W4Q_OK) rc = W4Q_EHIP;
+  if (p.split && rc == W4Q_OK) {
+    hipLaunchKernelGGL(hessian_fixup_kernel, dim3(static_cast<unsigned>(8 * p.tiles)), dim3(kThreads), 0, s, h,
+                       static_cast<int>(d), accumulate, static_cast<int>(p.nt), static_cast<int>(p.ns),
+                       static_cast<int>(p.chunk), ws);
+    rc = w4q_launch_status();
   }
   return rc;
 }
+
+// tokens per pass: whole tokens within 32-bit buffer offsets
+int64_t pass_tokens(int64_t d) { return 0x7FFFFFFF / (2 * d); }
 
 }  // namespace
 }  // namespace w4q
 
 using namespace w4q;
 
+size_t w4q_hessian_workspace(int64_t n_tok, int64_t d) {
+  const int64_t max_tok = pass_tokens(d);
+  const int64_t first = n_tok < max_tok ? n_tok : max_tok;
+  const int64_t last = n_tok % max_tok == 0 ? first : n_tok % max_tok;
+  const size_t a = plan_pass(first, d, SIZE_MAX).ws_need, b = plan_pass(last, d, SIZE_MAX).ws_need;
+  return a > b ? a : b;
+}
+
 int w4q_launch_hessian(const uint16_t* x, int64_t n_tok, int64_t d, float* h, int accumulate,
-                       hipStream_t s) {
+                       void* ws, size_t ws_bytes, hipStream_t s) {
   // X is taken in passes of whole tokens that fit 32-bit buffer offsets; later passes add on
-  const int64_t max_tok = 0x7FFFFFFF / (2 * d);
+  // (stream order lets every pass reuse the same scratch)
+  const int64_t max_tok = pass_tokens(d);
   for (int64_t t0 = 0; t0 < n_tok; t0 += max_tok) {
     const int64_t n = n_tok - t0 < max_tok ? n_tok - t0 : max_tok;
-    const int rc = launch_pass(x + t0 * d, n, d, h, t0 == 0 ? accumulate : 1, s);
+    const int rc = launch_pass(x + t0 * d, n, d, h, t0 == 0 ? accumulate : 1, ws, ws_bytes, s);
     if (rc != W4Q_OK) return rc;
   }
   return W4Q_OK;

@@ -19,31 +19,28 @@
 // lane of the wavefront hits that window, the wavefront recomputes the candidate's codes with
 // the exact midpoint comparisons of code_correct.
 //
-// Precision: pass 1 scores with fp32-level error (a few 2^-22 relative).  A group whose two
-// best pass-1 scores are within a relative 1e-5 (this includes exact ties and all-zero groups)
-// is re-scored at the end of the same workgroup: every candidate again in fp64, one candidate
-// per lane, first minimum.
+// Precision: pass 1 scores with fp32-level error and bounds it: with each score o it forms
+// B = |e|^T |Hg| |e| on the matrix cores and takes r = 2^-18 B as the score's radius (the
+// exact objective lies within o +- r).  A group's choice is kept when the best candidate's
+// interval lies below every other candidate's interval and its radius is below 9e-6 of its
+// score; otherwise (near-ties, exact ties, all-zero groups, ill-conditioned blocks where the
+// form cancels) the candidates whose intervals reach below the best one are re-scored in fp64
+// at the end of the same workgroup, and the first minimum among them is taken.
 #include "common.hpp"
+
+#include <utility>
+
+// every multiply and add below rounds as written (no contraction into fused operations): the
+// radii and interval tests are evaluated exactly as the error analysis states them
+#pragma clang fp contract(off)
 
 namespace w4q {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr float kTieRel = 1e-5f;
 constexpr float kNear = 0.5f - 1e-5f;
 // below this many 32-row wavefronts pass 1 runs 16 rows per wavefront
 constexpr int64_t kWaves16Below = 2048;
-
-__device__ __forceinline__ void load_group(const float* __restrict__ wp, float (&wv)[32]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(wp + 4 * i);
-    wv[4 * i + 0] = v.x;
-    wv[4 * i + 1] = v.y;
-    wv[4 * i + 2] = v.z;
-    wv[4 * i + 3] = v.w;
-  }
-}
 
 // Codes of N weights at step d (d == 0 -> all 0), as floats.
 template <int N, bool kZeroCodes = true>
@@ -59,7 +56,9 @@ __device__ __forceinline__ void codes(const float (&wv)[N], float d, float (&c)[
     c[i] = __builtin_fminf(__builtin_fmaxf(r, -8.0f), 7.0f);
   }
   near &= !zero;
-  if (__builtin_amdgcn_ballot_w64(near) != 0) {  // wave-uniform, rare
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(near) != 0, 0)) {  // wave-uniform, rare
+    // (the empty asm keeps this a branch: as selects, the exact rule would run every time)
+    asm volatile("");
 #pragma unroll
     for (int i = 0; i < N; ++i) c[i] = code_rcp(wv[i], d, inv);
   }
@@ -80,19 +79,6 @@ __device__ __forceinline__ float candidate_fast(float amax, float alpha) {
   float q = __builtin_fmaf(__builtin_fmaf(-q0, 7.0f, t), c, q0);
   q = __builtin_fabsf(t) == __builtin_inff() ? t : q;
   return f16_bits_to_f32(f32_to_f16_bits(q));
-}
-
-// Running first minimum (score, index, step) and second-smallest score of a candidate loop,
-// without branches: best = min(best, o), second = min(max(best, o), second) (a tie with the
-// best makes second equal to it; NaN scores leave both unchanged), and the index and step move
-// only on a strictly smaller score, so the first of equal minima is kept.
-__device__ __forceinline__ void track(float o, int k, float d, float& best, float& second, int& kbest,
-                                      float& dbest) {
-  const bool better = o < best;
-  kbest = better ? k : kbest;
-  dbest = better ? d : dbest;
-  second = __builtin_fminf(__builtin_fmaxf(best, o), second);
-  best = __builtin_fminf(best, o);
 }
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -133,109 +119,252 @@ __device__ __forceinline__ int scale_exp(float m) {
   return s > 127 ? 127 : (s < -126 ? -126 : s);
 }
 
-// Pass 2, inside the pass-1 block: fp64 re-scoring of the rows the block marked (their two best
-// pass-1 scores within kTieRel), every candidate again, one candidate per lane (same grid, same
-// codes, fp64 sums, first minimum).  A block covers one group column g, so it stages Hg in LDS
-// as fp64 (transposed: column j of Hg is contiguous) when any of its rows is marked, and its
-// four wavefronts score each marked row together: wavefront q forms s_i = sum_j H_ij e_j and
-// the partial sum of e_i s_i for the positions i = 8q .. 8q + 7, the four partials added in a
-// fixed order.  e_j is recomputed from the staged weights where it is needed, so the re-scoring
-// holds few registers.  Every thread of the block calls this; `marked` flags this lane's row
-// (lanes below rows_per_wave own rows row0 + wavefront * rows_per_wave + lane).
-__device__ __forceinline__ void rescore_marked(const float* __restrict__ w, int64_t d_in,
-                                               const float* __restrict__ h, int64_t ldh,
-                                               const float* __restrict__ alpha, int n_cand,
-                                               float* __restrict__ scale, uint8_t* __restrict__ idx,
-                                               float* __restrict__ obj, float* __restrict__ obj_all,
-                                               int64_t g, int64_t row0, int rows_per_wave, bool marked) {
-  static_assert(kThreads == 256, "four wavefronts share a marked row's positions");
-  constexpr int kWaves = kThreads / 64;
-  constexpr int kPos = kGroup / kWaves;  // positions per wavefront
+// |x| of eight fp16 values (sign bits cleared)
+__device__ __forceinline__ f16x8 abs8(f16x8 x) {
+  u32x4 u = __builtin_bit_cast(u32x4, x);
+  u &= 0x7FFF7FFFu;
+  return __builtin_bit_cast(f16x8, u);
+}
+
+// a + (the same quantity in the lane 32 apart): both lanes of a row get lo-half + hi-half of the
+// two partial dots (the same bits in both)
+__device__ __forceinline__ float pair_sum32(float part) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, part),
+                                                   __builtin_bit_cast(uint32_t, part), false, false);
+  const uint32_t u0 = pr[0], u1 = pr[1];
+  return __builtin_bit_cast(float, u0) + __builtin_bit_cast(float, u1);
+}
+
+// sum over the four lanes 16 apart, added pairwise: (q0 + q1) + (q2 + q3) in all of them (same
+// bits in each)
+__device__ __forceinline__ float quad_sum(float part) {
+  const auto s1 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, part),
+                                                   __builtin_bit_cast(uint32_t, part), false, false);
+  const uint32_t a0 = s1[0], a1 = s1[1];
+  return pair_sum32(__builtin_bit_cast(float, a0) + __builtin_bit_cast(float, a1));
+}
+
+// Error radius of a pass-1 score.  Pass 1 evaluates e^T Hg e from fp16 parts (two per value,
+// relative residual <= 2^-22), dropping the lo*lo product, with fp32 accumulation in six
+// matrix-core products of 16 terms each and a final 16-term fp32 dot.  Every one of these
+// errors is a small multiple of 2^-24 or 2^-22 times a sum of |e_i| |H_ij| |e_j| terms, so
+// the score's error is at most a constant times B = |e|^T |Hg| |e| (with one rounding per
+// matrix-core product the constant is about 7 * 2^-22).  Pass 1 also evaluates B, from the hi
+// parts of |Hg| and |e| on the matrix cores (accurate to about 2^-10, ample for a bound), and
+// takes kRad * B as the radius of the score: the exact objective lies in [o - r, o + r].
+// kRad = 2^-18 = 16 * 2^-22 is three times the largest error measured against the fp64 oracle
+// (5.3 * 2^-22 B, over every candidate of iid, lognormal(0, 2.5) and correlated calibration
+// data), and above the model's constant.
+constexpr float kRad = 1.0f / 262144.0f;  // 2^-18
+// A pass-1 objective is returned only if its radius is below this fraction of it (the
+// objective is then within 1e-5 relative of the exact value, fp32 output rounding included).
+constexpr float kObjRel = 9e-6f;
+
+// Running state of a candidate loop over one row (all values in the row's scaled units):
+// the first minimum (best, kbest, dbest) with its radius, and the three smallest lower ends
+// o - r of the candidates' intervals (the two smallest with their indices).
+struct Track {
+  float best = __builtin_inff(), rbest = 0.0f, dbest = 0.0f;
+  int kbest = 0;
+  float l1 = __builtin_inff(), l2 = __builtin_inff(), l3 = __builtin_inff();
+  int k1 = -1, k2 = -1;
+  bool loose = false;  // some candidate's radius exceeds kObjRel of its score
+
+  __device__ __forceinline__ void add(float o, float r, int k, float d) {
+    const bool better = o < best;  // strict: the first of equal minima is kept
+    kbest = better ? k : kbest;
+    dbest = better ? d : dbest;
+    rbest = better ? r : rbest;
+    best = better ? o : best;
+    const float l = o - r;
+    const bool lt1 = l < l1, lt2 = l < l2, lt3 = l < l3;
+    l3 = lt2 ? l2 : (lt3 ? l : l3);
+    k2 = lt1 ? k1 : (lt2 ? k : k2);
+    l2 = lt1 ? l1 : (lt2 ? l : l2);
+    k1 = lt1 ? k : k1;
+    l1 = lt1 ? l : l1;
+    loose |= r > kObjRel * o;
+  }
+  // The choice is certain when the best interval lies strictly below every other candidate's
+  // lower end, and its objective is accurate when its radius is small enough.  False for
+  // exact ties, all-zero groups and NaN scores: those groups are re-scored in fp64.
+  __device__ __forceinline__ bool clear(bool all_accurate) const {
+    const float lo_other = k1 == kbest ? l2 : l1;
+    return (best + rbest < lo_other) && (rbest <= kObjRel * best) && !(all_accurate && loose);
+  }
+};
+
+// Candidates a marked row re-scores: those whose interval reaches below the best interval's
+// upper end (the exact minimiser is among them).  Usually that is the best and at most one
+// more, which the two smallest lower ends name; when the third smallest also reaches below, or
+// every objective is wanted, it is all of them.  The `parts` lanes of a row share the work:
+// lane `part` takes the part-th named candidate, or every parts-th index.
+struct CandSet {
+  int c[2] = {-1, -1};
+  bool all = false;
+  __device__ __forceinline__ void from(const Track& t) {
+    const float upper = t.best + t.rbest;
+    all = !(t.l3 > upper);
+    c[0] = t.l1 <= upper ? t.k1 : -1;
+    c[1] = t.l2 <= upper ? t.k2 : -1;
+  }
+  // the candidate indices of lane `part`: k = first(), then next(k) until -1
+  __device__ __forceinline__ int first(int part, int n_cand) const {
+    if (all) return part < n_cand ? part : -1;
+    return part < 2 ? c[part] : -1;
+  }
+  __device__ __forceinline__ int next(int k, int parts, int n_cand) const {
+    return (all && k + parts < n_cand) ? k + parts : -1;
+  }
+};
+
+// Entry p of the upper triangle of a 32x32 block (diagonal included) in row-major order:
+// row tri_row(p), column tri_col(p), LDS index 32 row + column.  Compile-time after unrolling.
+constexpr int kTri = kGroup * (kGroup + 1) / 2;  // 528
+__host__ __device__ constexpr int tri_row(int p) {
+  int i = 0;
+  while (p >= kGroup - i) {
+    p -= kGroup - i;
+    ++i;
+  }
+  return i;
+}
+__host__ __device__ constexpr int tri_col(int p) {
+  int i = 0;
+  while (p >= kGroup - i) {
+    p -= kGroup - i;
+    ++i;
+  }
+  return i + p;
+}
+__host__ __device__ constexpr int tri_index(int p) { return kGroup * tri_row(p) + tri_col(p); }
+static_assert(tri_row(0) == 0 && tri_col(31) == 31 && tri_row(32) == 1 && tri_col(32) == 1 &&
+              tri_row(kTri - 1) == 31 && tri_col(kTri - 1) == 31, "triangle order");
+
+constexpr int kTriChunk = 8, kTriChunks = kTri / kTriChunk;
+static_assert(kTri % kTriChunk == 0, "whole chunks");
+
+// one entry of the form: start of row i (diagonal), an off-diagonal term, end of row i
+template <int P>
+__device__ __forceinline__ void tri_step(double hv, const float (&e)[kGroup], double& s, double& o) {
+  constexpr int i = tri_row(P), j = tri_col(P);
+  if constexpr (j == i) s = hv * static_cast<double>(e[i]);
+  else s = __builtin_fma(hv, static_cast<double>(e[j]), s);
+  if constexpr (j == kGroup - 1) o = __builtin_fma(static_cast<double>(e[i]), s, o);
+}
+template <int P>
+constexpr int kTriIndex = tri_index(P);  // a constant expression: never evaluated at run time
+template <int C, int... T>
+__device__ __forceinline__ void tri_load(const double* hs, int off, double (&b)[kTriChunk],
+                                         std::integer_sequence<int, T...>) {
+  ((b[T] = hs[off + kTriIndex<C * kTriChunk + T>]), ...);
+}
+template <int C, int... T>
+__device__ __forceinline__ void tri_compute(const double (&b)[kTriChunk], const float (&e)[kGroup],
+                                            double& s, double& o, std::integer_sequence<int, T...>) {
+  (tri_step<C * kTriChunk + T>(b[T], e, s, o), ...);
+}
+template <int C>
+__device__ __forceinline__ void tri_chunks(const double* hs, int& off, const float (&e)[kGroup],
+                                           double (&buf)[2][kTriChunk], double& s, double& o) {
+  if constexpr (C + 1 < kTriChunks) {
+    asm volatile("" : "+v"(off) : "v"(o), "v"(s));
+    tri_load<C + 1>(hs, off, buf[(C + 1) & 1], std::make_integer_sequence<int, kTriChunk>{});
+  }
+  tri_compute<C>(buf[C & 1], e, s, o, std::make_integer_sequence<int, kTriChunk>{});
+  if constexpr (C + 1 < kTriChunks) tri_chunks<C + 1>(hs, off, e, buf, s, o);
+}
+
+// fp64 objective of one candidate of one row: e_i = w_i - d * code(w_i, d) (exact in fp32 and
+// fp64), obj = sum_i e_i (H_ii e_i + sum_{j > i} (H_ij + H_ji) e_j) in fp64.  hs holds that
+// form of the block in LDS: hs[32 i + i] = H_ii, hs[32 i + j] = H_ij + H_ji for j > i (every
+// lane reads the same entry at the same time, so the reads are broadcasts).  The errors stay in
+// fp32 registers and are widened where they are used, so that the rare re-scoring does not
+// raise the register count of the pass-1 loop it shares a kernel with.
+__device__ __forceinline__ double score_f64(const float* __restrict__ wrow, float d, const double* hs) {
+  // at a zero step e = w whatever the (finite) codes are, so the codes need no special case
+  const float inv = __builtin_amdgcn_rcpf(d > 0.0f ? d : 1.0f);
+  float e[kGroup];
+#pragma unroll
+  for (int i = 0; i < kGroup; i += 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(wrow + i);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t)  // exact: |c| <= 8 and d on the fp16 grid
+      e[i + t] = __builtin_fmaf(-code_rcp(vv[t], d, inv), d, vv[t]);
+  }
+  // The 528 entries of the triangle are taken in row-major order in chunks of 8: the loads of
+  // chunk c + 1 are issued before chunk c is computed, at an LDS offset that depends (through an
+  // empty asm) on the sums after chunk c - 1, so the compiler can neither hoist them out of the
+  // caller's candidate loop nor pull more than two chunks into registers.  The chunks and their
+  // entries are expanded at compile time (templates), so every index below is a constant.
+  double buf[2][kTriChunk];
+  double o = 0.0, s = 0.0;
+  int off = 0;
+  tri_load<0>(hs, 0, buf[0], std::make_integer_sequence<int, kTriChunk>{});
+  tri_chunks<0>(hs, off, e, buf, s, o);
+  return o;
+}
+
+// Pass 2, at the end of the pass-1 block: fp64 re-scoring of the rows whose pass-1 choice is
+// not certain (or whose objective is not accurate enough).  A block covers one group column g,
+// so when any of its rows is marked it stages Hg in LDS in fp64 (the symmetric form of
+// score_f64).  Each lane then scores, in fp64, the candidates of its row in `cand` that belong
+// to its share (the `parts` lanes of a row take every parts-th index), keeping the first
+// minimum; the shares are combined across the row's lanes (lane distance `stride`), lowest
+// index first on equal objectives, and the first lane of the row writes the results.
+// Every thread of the block calls this.
+__device__ __forceinline__ void rescore(const float* __restrict__ w, int64_t d_in,
+                                        const float* __restrict__ h, int64_t ldh,
+                                        const float* __restrict__ alpha, int n_cand,
+                                        float* __restrict__ scale, uint8_t* __restrict__ idx,
+                                        float* __restrict__ obj, float* __restrict__ obj_all,
+                                        int64_t g, int64_t row, float amax, bool marked, bool writer,
+                                        const CandSet& cand, int part, int parts, int stride) {
   __shared__ double hs[kGroup * kGroup];
-  __shared__ double part[kWaves][64];
-  __shared__ uint64_t marks[kWaves];
-  __shared__ float wl[kGroup];
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const uint64_t mask = __builtin_amdgcn_ballot_w64(marked);
   if (!__syncthreads_or(marked)) return;  // block-uniform
-  if (lane == 0) marks[wid] = mask;
   const int64_t G = d_in / kGroup;
   const float* __restrict__ hg = h + g * kGroup * ldh + g * kGroup;
-  for (int t = threadIdx.x; t < kGroup * kGroup; t += kThreads)
-    hs[(t % kGroup) * kGroup + t / kGroup] = static_cast<double>(hg[(t / kGroup) * ldh + t % kGroup]);
+  for (int t = threadIdx.x; t < kGroup * kGroup; t += kThreads) {
+    const int i = t / kGroup, j = t % kGroup;
+    double v = 0.0;
+    if (j == i) v = static_cast<double>(hg[i * ldh + i]);
+    else if (j > i) v = static_cast<double>(hg[i * ldh + j]) + static_cast<double>(hg[j * ldh + i]);
+    hs[t] = v;
+  }
   __syncthreads();
-  // every wavefront walks the same list of marked rows, so the barriers below are uniform
-  for (int q = 0; q < kWaves; ++q) {
-    uint64_t m = marks[q];
-    while (m != 0) {
-      const int src = __builtin_ctzll(m);
-      m &= m - 1;
-      const int64_t rs = row0 + q * rows_per_wave + src;
-      const int64_t o_ = rs * G + g;
-      if (threadIdx.x < kGroup) wl[threadIdx.x] = w[rs * d_in + g * kGroup + threadIdx.x];
-      __syncthreads();
-      float amax = __builtin_fabsf(wl[lane & (kGroup - 1)]);
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
-      double best = __builtin_inf();
-      int kbest = 0x7FFFFFFF;
-      float dbest = 0.0f;
-      for (int k0 = 0; k0 < n_cand; k0 += 64) {
-        const int k = k0 + lane;
-        const bool kv = k < n_cand;
-        const float d = candidate_fast(amax, alpha[kv ? k : 0]);  // the step pass 1 used
-        const bool zero = !(d > 0.0f);
-        const float inv = __builtin_amdgcn_rcpf(zero ? 1.0f : d);
-        auto err = [&](float wi) {  // e = w - code(w, d) d, exact in fp64
-          const float ci = zero ? 0.0f : code_rcp(wi, d, inv);
-          return __builtin_fma(-static_cast<double>(ci), static_cast<double>(d), static_cast<double>(wi));
-        };
-        double sv[kPos];
-#pragma unroll
-        for (int t = 0; t < kPos; ++t) sv[t] = 0.0;
-#pragma unroll 1
-        for (int j = 0; j < kGroup; ++j) {
-          const double ej = err(wl[j]);
-          const double* hc = hs + j * kGroup + kPos * wid;
-#pragma unroll
-          for (int t = 0; t < kPos; ++t) sv[t] = __builtin_fma(hc[t], ej, sv[t]);
-        }
-        double op = 0.0;
-#pragma unroll
-        for (int t = 0; t < kPos; ++t) op = __builtin_fma(err(wl[kPos * wid + t]), sv[t], op);
-        part[wid][lane] = op;
-        __syncthreads();
-        const double o = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
-        __syncthreads();  // part is rewritten by the next chunk
-        if (kv) {
-          if (obj_all != nullptr && wid == 0) obj_all[o_ * n_cand + k] = static_cast<float>(o);
-          if (o < best) {  // a lane's candidates rise with k0: strict keeps the first
-            best = o;
-            kbest = k;
-            dbest = d;
-          }
-        }
+  const float* __restrict__ wrow = w + row * d_in + g * kGroup;
+  const int64_t o_ = row * G + g;
+  double best = __builtin_inf();
+  int kbest = 0x7FFFFFFF;
+  float dbest = 0.0f;
+  int k = marked ? cand.first(part, n_cand) : -1;
+  while (__builtin_amdgcn_ballot_w64(k >= 0) != 0) {  // wave-uniform exit
+    if (k >= 0) {
+      const float d = candidate_fast(amax, alpha[k]);  // the step pass 1 used
+      const double o = score_f64(wrow, d, hs);
+      if (obj_all != nullptr) obj_all[o_ * n_cand + k] = static_cast<float>(o);
+      if (o < best || (o == best && k < kbest)) {
+        best = o;
+        kbest = k;
+        dbest = d;
       }
-      // wavefront argmin, ties to the lowest candidate index (every wavefront holds the same
-      // scores; the first thread writes)
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const double ob = __shfl_xor(best, off);
-        const int ok = __shfl_xor(kbest, off);
-        const float od = __shfl_xor(dbest, off);
-        const bool take = (ob < best) || (ob == best && ok < kbest);
-        best = take ? ob : best;
-        kbest = take ? ok : kbest;
-        dbest = take ? od : dbest;
-      }
-      if (threadIdx.x == 0) {
-        scale[o_] = dbest;
-        idx[o_] = static_cast<uint8_t>(kbest);
-        if (obj != nullptr) obj[o_] = static_cast<float>(best);
-      }
-      __syncthreads();  // wl is rewritten for the next marked row
+      k = cand.next(k, parts, n_cand);
     }
+  }
+  for (int off = stride; off < stride * parts; off <<= 1) {
+    const double ob = __shfl_xor(best, off);
+    const int ok = __shfl_xor(kbest, off);
+    const float od = __shfl_xor(dbest, off);
+    const bool take = (ob < best) || (ob == best && ok < kbest);
+    best = take ? ob : best;
+    kbest = take ? ok : kbest;
+    dbest = take ? od : dbest;
+  }
+  if (marked && writer) {
+    scale[o_] = dbest;
+    idx[o_] = static_cast<uint8_t>(kbest);
+    if (obj != nullptr) obj[o_] = static_cast<float>(best);
   }
 }
 
@@ -247,7 +376,8 @@ __device__ __forceinline__ void rescore_marked(const float* __restrict__ w, int6
 // 8 h + t of lane (h, m) is position p with 4 q + r = 8 u + t, so the lane feeds its own
 // elements 8u..8u+7 of e_m (B operand) and of Hg row m (A operand), and receives
 // D[p][m] = (Hg e_m)[p] for exactly its own 16 positions.  obj_m = sum_p e_m[p] D[p][m] is a
-// 16-term fp32 dot per lane plus one exchange with the partner lane.
+// 16-term fp32 dot per lane plus one exchange with the partner lane.  The same mapping with
+// the hi parts of |Hg| and |e| gives B = |e|^T |Hg| |e|, the scale of the score's error.
 //
 // Precision: w is scaled by a power of two per row (sw) and Hg by one per block (sh), both
 // exactly, so that their largest magnitudes sit in [2^14, 2^15); the scaled error
@@ -255,12 +385,17 @@ __device__ __forceinline__ void rescore_marked(const float* __restrict__ w, int6
 // more than D / 2 <= |w|, and a clamped or zero code only shrinks w), so nothing overflows fp16.
 // e and Hg are each split into two fp16 parts (relative residual <= 2^-22 in fp16's normal
 // range), and D accumulates hi*lo, lo*hi, then hi*hi in fp32 (products of fp16 values are
-// exact; the dropped lo*lo term is <= 2^-22 relative), so the score carries an error of a few
-// 2^-22 of the form's magnitude before the exact rescale by 2^-(2 log2 sw + log2 sh).  The
-// headroom matters when the channel scales of X spread widely: the block's small entries then
-// lie many binades below its largest one and still need their full 22 bits.
+// exact; the dropped lo*lo term is <= 2^-22 relative).  Scores are compared in the scaled
+// units (the same factor 2^-(2 log2 sw + log2 sh) for every candidate of a row) and unscaled
+// exactly for the outputs.  The headroom matters when the channel scales of X spread widely:
+// the block's small entries then lie many binades below its largest one.
+//
+// Marking: a row is re-scored in fp64 (pass 2) unless its choice is certain and its objective
+// accurate by the radii (Track::clear).  Pass 2 scores the candidates of CandSet.  With
+// obj_all, every candidate's objective must be accurate, and a marked row's candidates are all
+// re-scored.
 template <bool kAll>
-__global__ __launch_bounds__(kThreads, 5) void search_split_kernel(
+__global__ __launch_bounds__(kThreads, 4) void search_split_kernel(
     const float* __restrict__ w, int64_t d_out, int64_t d_in, const float* __restrict__ h,
     int64_t ldh, const float* __restrict__ alpha, int n_cand, float* __restrict__ scale,
     uint8_t* __restrict__ idx, float* __restrict__ obj, float* __restrict__ obj_all) {
@@ -294,7 +429,8 @@ __global__ __launch_bounds__(kThreads, 5) void search_split_kernel(
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) hmax = __builtin_fmaxf(hmax, __shfl_xor(hmax, off));
 
-  // exact power-of-two scalings, then the two fp16 parts of the block (A operands)
+  // exact power-of-two scalings, then the two fp16 parts of the block (A operands) and the
+  // magnitudes of the hi parts (A operands of the bound)
   const int ew = scale_exp(amax), eh = scale_exp(hmax);
   const float sw = pow2(ew), sh = pow2(eh);
   const int unscale = -(2 * ew + eh);  // obj = score * 2^unscale
@@ -303,18 +439,14 @@ __global__ __launch_bounds__(kThreads, 5) void search_split_kernel(
     wv[i] *= sw;
     ha[i] *= sh;
   }
-  f16x8 hhi[2], hlo[2];
+  f16x8 hhi[2], hlo[2], habs[2];
   split8(ha, hhi[0], hlo[0]);
   split8(ha + 8, hhi[1], hlo[1]);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) habs[u] = abs8(hhi[u]);
 
-  float best = __builtin_inff(), second = __builtin_inff(), dbest = 0.0f;
-  int kbest = 0;
-  float d_next = candidate_fast(amax, alpha[0]);
-#pragma unroll 1
-  for (int k = 0; k < n_cand; ++k) {
-    const float d = d_next;
-    // the next candidate's step, off this candidate's dependency chain
-    d_next = candidate_fast(amax, alpha[k + 1 < n_cand ? k + 1 : k]);
+  // score and radius of candidate step d (scaled units; same bits in both lanes of a row)
+  auto eval = [&](float d, float& o, float& rad) {
     const float ds = d * sw;  // exact; the codes of sw w at ds are those of w at d
     float e[16];
     // at a zero step the error is w whatever the codes are (w - c * 0), so the codes need not
@@ -337,30 +469,55 @@ __global__ __launch_bounds__(kThreads, 5) void search_split_kernel(
     for (int u = 0; u < 2; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(hlo[u], ehi[u], acc, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < 2; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(hhi[u], ehi[u], acc, 0, 0, 0);
-    float p0 = 0.0f, p1 = 0.0f;  // two chains: even and odd positions of the lane
+    const f16x8 eabs[2] = {abs8(ehi[0]), abs8(ehi[1])};
+    float p0 = 0.0f, p1 = 0.0f;  // even and odd positions of the lane
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
       p0 = __builtin_fmaf(e[i], acc[i], p0);
       p1 = __builtin_fmaf(e[i + 1], acc[i + 1], p1);
     }
-    const float part = p0 + p1;
-    // both lanes of a row get lo-half + hi-half of the two partial dots (same bits in both)
-    const auto pr = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, part),
-                                                     __builtin_bit_cast(uint32_t, part), false, false);
-    const uint32_t u0 = pr[0], u1 = pr[1];
-    const float o = __builtin_ldexpf(__builtin_bit_cast(float, u0) + __builtin_bit_cast(float, u1), unscale);
-    if (kAll && live && hh == 0) obj_all[(r * G + g) * n_cand + k] = o;
-    track(o, k, d, best, second, kbest, dbest);
+    // the bound's products reuse the registers of the score's accumulator
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(habs[u], eabs[u], acc, 0, 0, 0);
+    float b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      b0 = __builtin_fmaf(__builtin_fabsf(e[i]), acc[i], b0);
+      b1 = __builtin_fmaf(__builtin_fabsf(e[i + 1]), acc[i + 1], b1);
+    }
+    o = pair_sum32(p0 + p1);
+    rad = kRad * pair_sum32(b0 + b1);
+  };
+
+  Track t;
+  float d_next = candidate_fast(amax, alpha[0]);
+#pragma unroll 1
+  for (int k = 0; k < n_cand; ++k) {
+    const float d = d_next;
+    // the next candidate's step, off this candidate's dependency chain
+    d_next = candidate_fast(amax, alpha[k + 1 < n_cand ? k + 1 : k]);
+    float o, rad;
+    eval(d, o, rad);
+    if (kAll && live && hh == 0) obj_all[(r * G + g) * n_cand + k] = __builtin_ldexpf(o, unscale);
+    t.add(o, rad, k, d);
   }
-  const bool clear = (second - best) > kTieRel * best;  // false for ties, zeros and NaN
-  if (live && hh == 0 && clear) {
+  const bool clear = t.clear(kAll);
+  const bool writer = live && hh == 0;
+  if (writer && clear) {
     const int64_t o_ = r * G + g;
-    scale[o_] = dbest;
-    idx[o_] = static_cast<uint8_t>(kbest);
-    if (obj != nullptr) obj[o_] = best;
+    scale[o_] = t.dbest;
+    idx[o_] = static_cast<uint8_t>(t.kbest);
+    if (obj != nullptr) obj[o_] = __builtin_ldexpf(t.best, unscale);
   }
-  rescore_marked(w, d_in, h, ldh, alpha, n_cand, scale, idx, obj, obj_all, g,
-                 (int64_t)blockIdx.x * (kThreads / 2), 32, live && hh == 0 && !clear);
+  const bool marked = live && !clear;
+  CandSet cand;
+  cand.from(t);
+  cand.all |= kAll;
+  rescore(w, d_in, h, ldh, alpha, n_cand, scale, idx, obj, obj_all, g, rr, amax, marked, writer,
+          cand, hh, 2, 32);
 }
 
 // Pass 1 for small grids: 16 rows per wavefront (twice the wavefronts of the kernel above, so
@@ -370,9 +527,10 @@ __global__ __launch_bounds__(kThreads, 5) void search_split_kernel(
 // 8 (i / 4) + 4 u + i % 4 and the reduction slot 8 q + e standing for position 8 q + e, so the
 // lane feeds its own 8 errors as the B operand and Hg[8 (i / 4) + 4 u + i % 4][8 q + e] (i = the
 // lane's j) as the A operand, and receives D[p][j] for exactly its own positions
-// p = 8 q + 4 u + r (r = 0..3).  Scaling, splitting and accumulation order as above.
+// p = 8 q + 4 u + r (r = 0..3).  Scaling, splitting, accumulation order, radii and marking as
+// above; the four lanes of a row share pass 2's candidates.
 template <bool kAll>
-__global__ __launch_bounds__(kThreads) void search_split16_kernel(
+__global__ __launch_bounds__(kThreads, 4) void search_split16_kernel(
     const float* __restrict__ w, int64_t d_out, int64_t d_in, const float* __restrict__ h,
     int64_t ldh, const float* __restrict__ alpha, int n_cand, float* __restrict__ scale,
     uint8_t* __restrict__ idx, float* __restrict__ obj, float* __restrict__ obj_all) {
@@ -424,19 +582,14 @@ __global__ __launch_bounds__(kThreads) void search_split16_kernel(
     ha[0][i] *= sh;
     ha[1][i] *= sh;
   }
-  f16x8 hhi[2], hlo[2];
+  f16x8 hhi[2], hlo[2], habs[2];
   split8(ha[0], hhi[0], hlo[0]);
   split8(ha[1], hhi[1], hlo[1]);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) habs[u] = abs8(hhi[u]);
 
-  float best = __builtin_inff(), second = __builtin_inff(), dbest = 0.0f;
-  int kbest = 0;
-  float d_next = candidate_fast(amax, alpha[0]);
   const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 1
-  for (int k = 0; k < n_cand; ++k) {
-    const float d = d_next;
-    // the next candidate's step, off this candidate's dependency chain
-    d_next = candidate_fast(amax, alpha[k + 1 < n_cand ? k + 1 : k]);
+  auto eval = [&](float d, float& o, float& rad) {
     const float ds = d * sw;  // exact; the codes of sw w at ds are those of w at d
     float e[8];
     codes<8, false>(wv, ds, e);  // at a zero step the error is w whatever the codes are
@@ -447,42 +600,53 @@ __global__ __launch_bounds__(kThreads) void search_split16_kernel(
     }
     f16x8 ehi, elo;
     split8(e, ehi, elo);
-    f32x4 acc[2];
+    const f16x8 eabs = abs8(ehi);
+    f32x4 acc[2], accb[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hhi[u], elo, zero4, 0, 0, 0);
       acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hlo[u], ehi, acc[u], 0, 0, 0);
       acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hhi[u], ehi, acc[u], 0, 0, 0);
+      accb[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(habs[u], eabs, zero4, 0, 0, 0);
     }
-    float p0 = 0.0f, p1 = 0.0f;  // two chains: the two products
+    float p0 = 0.0f, p1 = 0.0f, b0 = 0.0f, b1 = 0.0f;  // two chains: the two products
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       p0 = __builtin_fmaf(e[i], acc[0][i], p0);
       p1 = __builtin_fmaf(e[4 + i], acc[1][i], p1);
+      b0 = __builtin_fmaf(__builtin_fabsf(e[i]), accb[0][i], b0);
+      b1 = __builtin_fmaf(__builtin_fabsf(e[4 + i]), accb[1][i], b1);
     }
-    const float part = p0 + p1;
-    // the four lanes of a row add their partial dots pairwise: (q0 + q1) + (q2 + q3) in all of
-    // them (same bits in each)
-    const auto s1 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, part),
-                                                     __builtin_bit_cast(uint32_t, part), false, false);
-    const uint32_t a0 = s1[0], a1 = s1[1];
-    const float half = __builtin_bit_cast(float, a0) + __builtin_bit_cast(float, a1);
-    const auto s2 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, half),
-                                                     __builtin_bit_cast(uint32_t, half), false, false);
-    const uint32_t b0 = s2[0], b1 = s2[1];
-    const float o = __builtin_ldexpf(__builtin_bit_cast(float, b0) + __builtin_bit_cast(float, b1), unscale);
-    if (kAll && live && q == 0) obj_all[(r * G + g) * n_cand + k] = o;
-    track(o, k, d, best, second, kbest, dbest);
+    o = quad_sum(p0 + p1);
+    rad = kRad * quad_sum(b0 + b1);
+  };
+
+  Track t;
+  float d_next = candidate_fast(amax, alpha[0]);
+#pragma unroll 1
+  for (int k = 0; k < n_cand; ++k) {
+    const float d = d_next;
+    // the next candidate's step, off this candidate's dependency chain
+    d_next = candidate_fast(amax, alpha[k + 1 < n_cand ? k + 1 : k]);
+    float o, rad;
+    eval(d, o, rad);
+    if (kAll && live && q == 0) obj_all[(r * G + g) * n_cand + k] = __builtin_ldexpf(o, unscale);
+    t.add(o, rad, k, d);
   }
-  const bool clear = (second - best) > kTieRel * best;  // false for ties, zeros and NaN
-  if (live && q == 0 && clear) {
+  const bool clear = t.clear(kAll);
+  const bool writer = live && q == 0;
+  if (writer && clear) {
     const int64_t o_ = r * G + g;
-    scale[o_] = dbest;
-    idx[o_] = static_cast<uint8_t>(kbest);
-    if (obj != nullptr) obj[o_] = best;
+    scale[o_] = t.dbest;
+    idx[o_] = static_cast<uint8_t>(t.kbest);
+    if (obj != nullptr) obj[o_] = __builtin_ldexpf(t.best, unscale);
   }
-  rescore_marked(w, d_in, h, ldh, alpha, n_cand, scale, idx, obj, obj_all, g,
-                 (int64_t)blockIdx.x * (kThreads / 4), 16, live && q == 0 && !clear);
+  const bool marked = live && !clear;
+  CandSet cand;
+  cand.from(t);
+  cand.all |= kAll;
+  rescore(w, d_in, h, ldh, alpha, n_cand, scale, idx, obj, obj_all, g, rr, amax, marked, writer,
+          cand, q, 4, 16);
 }
 
 }  // namespace

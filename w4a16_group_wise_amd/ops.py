@@ -39,16 +39,41 @@ def _out(t: Optional[torch.Tensor], name, shape, dtype, device) -> torch.Tensor:
     return t
 
 
+def _workspace(query: str, sizes, device, workspace: Optional[torch.Tensor]):
+    """(pointer, bytes, tensor) of the scratch for one call: the caller's uint8 device tensor, or
+    a fresh one of the size the library asks for (torch's caching allocator, on the current
+    stream; none when the library needs none)."""
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, device=device)
+        return workspace.data_ptr(), workspace.numel(), workspace
+    n = ctypes.c_size_t(0)
+    check(query, getattr(lib(), query)(*sizes, ctypes.byref(n)))
+    if n.value == 0:
+        return None, 0, None
+    buf = torch.empty(n.value, dtype=torch.uint8, device=device)
+    return buf.data_ptr(), n.value, buf
+
+
+def workspace_size(op: str, *sizes) -> int:
+    """Scratch bytes of the fastest schedule: op in ("quant_hessian", "w4a16_gemm",
+    "w4a16_gemm_dq") with (n_tok, d) or (m, d_out, d_in)."""
+    n = ctypes.c_size_t(0)
+    check(op + "_workspace_size", getattr(lib(), op + "_workspace_size")(*sizes, ctypes.byref(n)))
+    return n.value
+
+
 def quant_hessian(x: torch.Tensor, h: Optional[torch.Tensor] = None,
-                  accumulate: bool = False) -> torch.Tensor:
-    """H = X^T X (or H += X^T X) for bf16 X [n_tok][d]; returns fp32 H [d][d]."""
+                  accumulate: bool = False, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """H = X^T X (or H += X^T X) for bf16 X [n_tok][d]; returns fp32 H [d][d].  workspace: a
+    uint8 device tensor of scratch (default: allocated per call with torch)."""
     _need(x, "x", torch.bfloat16)
     n_tok, d = x.shape
     if accumulate and h is None:
         raise ValueError("accumulate=True needs h")
     h = _out(h, "h", (d, d), torch.float32, x.device)
+    wp, wb, _keep = _workspace("quant_hessian_workspace_size", (n_tok, d), x.device, workspace)
     check("quant_hessian", lib().quant_hessian(x.data_ptr(), n_tok, d, h.data_ptr(),
-                                               1 if accumulate else 0, _stream(x)))
+                                               1 if accumulate else 0, wp, wb, _stream(x)))
     return h
 
 
@@ -65,13 +90,18 @@ def quant_scale_search(w: torch.Tensor, h: torch.Tensor, alpha: torch.Tensor,
     G, K = d_in // W4Q_GROUP, alpha.numel()
     dev = w.device
     if out is None:
-        scale = torch.empty((d_out, G), dtype=torch.float32, device=dev)
-        idx = torch.empty((d_out, G), dtype=torch.uint8, device=dev)
-        obj = torch.empty((d_out, G), dtype=torch.float32, device=dev) if with_obj else None
-        obj_all = (torch.empty((d_out, G, K), dtype=torch.float32, device=dev)
-                   if with_obj_all else None)
-    else:
-        scale, idx, obj, obj_all = out
+        out = (None, None, None, None)
+    if len(out) != 4:
+        raise ValueError("out must be (scale, idx, obj | None, obj_all | None)")
+    scale = _out(out[0], "scale", (d_out, G), torch.float32, dev)
+    idx = _out(out[1], "idx", (d_out, G), torch.uint8, dev)
+    obj = out[2] if out[2] is not None or not with_obj else torch.empty((d_out, G), dtype=torch.float32, device=dev)
+    if obj is not None:
+        _need(obj, "obj", torch.float32, (d_out, G), dev)
+    obj_all = (out[3] if out[3] is not None or not with_obj_all
+               else torch.empty((d_out, G, K), dtype=torch.float32, device=dev))
+    if obj_all is not None:
+        _need(obj_all, "obj_all", torch.float32, (d_out, G, K), dev)
     check("quant_scale_search", lib().quant_scale_search(
         w.data_ptr(), d_out, d_in, h.data_ptr(), h.shape[1], alpha.data_ptr(), K,
         scale.data_ptr(), idx.data_ptr(), obj.data_ptr() if obj is not None else None,
@@ -85,11 +115,9 @@ def quant_pack(w: torch.Tensor, scale: torch.Tensor,
     _need(w, "w", torch.float32)
     d_out, d_in = w.shape
     _need(scale, "scale", torch.float32, (d_out, d_in // W4Q_GROUP), w.device)
-    if out is None:
-        packed = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=w.device)
-        s16 = torch.empty((d_out, d_in // W4Q_GROUP), dtype=torch.float16, device=w.device)
-    else:
-        packed, s16 = out
+    packed, s16 = (None, None) if out is None else out
+    packed = _out(packed, "packed", (d_out, d_in // 2), torch.uint8, w.device)
+    s16 = _out(s16, "scale_f16", (d_out, d_in // W4Q_GROUP), torch.float16, w.device)
     check("quant_pack", lib().quant_pack(w.data_ptr(), scale.data_ptr(), d_out, d_in,
                                          packed.data_ptr(), s16.data_ptr(), _stream(w)))
     return packed, s16
@@ -112,12 +140,13 @@ def lsq_bwd(w: torch.Tensor, scale: torch.Tensor, grad_w_hat: torch.Tensor, grad
     d_out, d_in = w.shape
     _need(scale, "scale", torch.float32, (d_out, d_in // W4Q_GROUP), w.device)
     _need(grad_w_hat, "grad_w_hat", torch.float32, (d_out, d_in), w.device)
-    if out is None:
-        gw = torch.empty_like(w)
-        gsc = torch.empty((d_out, d_in // W4Q_GROUP), dtype=torch.float32, device=w.device)
-        wh = torch.empty_like(w) if with_w_hat else None
-    else:
-        gw, gsc, wh = out
+    gw, gsc, wh = (None, None, None) if out is None else out
+    gw = _out(gw, "grad_w", (d_out, d_in), torch.float32, w.device)
+    gsc = _out(gsc, "grad_scale_out", (d_out, d_in // W4Q_GROUP), torch.float32, w.device)
+    if wh is None and with_w_hat:
+        wh = torch.empty_like(w)
+    if wh is not None:
+        _need(wh, "w_hat", torch.float32, (d_out, d_in), w.device)
     check("lsq_bwd", lib().lsq_bwd(w.data_ptr(), scale.data_ptr(), grad_w_hat.data_ptr(), d_out,
                                    d_in, float(grad_scale), gw.data_ptr(), gsc.data_ptr(),
                                    wh.data_ptr() if wh is not None else None, _stream(w)))
@@ -125,7 +154,7 @@ def lsq_bwd(w: torch.Tensor, scale: torch.Tensor, grad_w_hat: torch.Tensor, grad
 
 
 def _gemm(name: str, x: torch.Tensor, packed: torch.Tensor, scale_f16: torch.Tensor,
-          out_dtype: torch.dtype, out: Optional[torch.Tensor]):
+          out_dtype: torch.dtype, out: Optional[torch.Tensor], workspace: Optional[torch.Tensor] = None):
     _need(x, "x", torch.bfloat16)
     m, d_in = x.shape
     _need(packed, "packed", torch.uint8, device=x.device)
@@ -136,24 +165,27 @@ def _gemm(name: str, x: torch.Tensor, packed: torch.Tensor, scale_f16: torch.Ten
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be float32 or bfloat16")
     y = _out(out, "y", (m, d_out), out_dtype, x.device)
+    wp, wb, _keep = _workspace(name + "_workspace_size", (m, d_out, d_in), x.device, workspace)
     check(name, getattr(lib(), name)(x.data_ptr(), m, packed.data_ptr(), scale_f16.data_ptr(),
                                      d_out, d_in, y.data_ptr(),
-                                     0 if out_dtype == torch.float32 else 1, _stream(x)))
+                                     0 if out_dtype == torch.float32 else 1, wp, wb, _stream(x)))
     return y
 
 
 def w4a16_gemm(x: torch.Tensor, packed: torch.Tensor, scale_f16: torch.Tensor,
-               out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None):
+               out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None):
     """y [m][d_out] = x [m][d_in] (bf16) times the dequantised packed weights (s16 * q, exact),
     transposed."""
-    return _gemm("w4a16_gemm", x, packed, scale_f16, out_dtype, out)
+    return _gemm("w4a16_gemm", x, packed, scale_f16, out_dtype, out, workspace)
 
 
 def w4a16_gemm_dq(x: torch.Tensor, packed: torch.Tensor, scale_f16: torch.Tensor,
-                  out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None):
+                  out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None):
     """As w4a16_gemm with each weight dequantized to bf16 (RNE of s16 * q) before the product;
     d_in must be a multiple of 256."""
-    return _gemm("w4a16_gemm_dq", x, packed, scale_f16, out_dtype, out)
+    return _gemm("w4a16_gemm_dq", x, packed, scale_f16, out_dtype, out, workspace)
 
 
 class GemvGroupPlan:
@@ -202,7 +234,7 @@ class GemvGroupPlan:
 
 def w4a16_gemv_grouped(xs, packeds, scales, out_dtype: torch.dtype = torch.float32, outs=None):
     """One-row products y_i [1][d_out_i] = x_i [1][d_in_i] W_hat_i^T for several independent
-    problems in as few launches as possible (32 problems per launch).  For a call repeated on the
+    problems in as few launches as possible (64 problems per launch).  For a call repeated on the
     same buffers, GemvGroupPlan marshals the table once."""
     return GemvGroupPlan(xs, packeds, scales, out_dtype, outs)()
 

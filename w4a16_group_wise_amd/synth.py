@@ -166,3 +166,21 @@ WORKLOADS: Dict[str, Workload] = {
 def linears_of(name: str) -> List[Tuple[int, Linear]]:
     c = WORKLOADS[name]
     return [(layer, lin) for layer in range(c.layers) for lin in c.linears]
+
+
+def correlated_x(stream: int, layer: int, tensor_id: int, n_tok: int, d: int, rank: int,
+                 eps: float, sigma: float = 1.0) -> np.ndarray:
+    """bf16 bits [n_tok][d] of correlated calibration activations:
+    X = (Z M + eps * N) * c_j, with Z ~ N(0,1) [n_tok][rank], one shared mixing M ~ N(0,1)
+    [rank][d], independent noise N ~ N(0,1) [n_tok][d] and lognormal(0, sigma) channel factors
+    c_j.  Every 32x32 diagonal block of X^T X is then close to rank `rank`, with its smallest
+    eigenvalues about eps^2 of its largest (condition numbers of 1e4 .. 1e8 for eps 1e-2 ..
+    1e-4): errors along the shared directions are weighted far more than the others."""
+    g = rng(stream, layer, tensor_id)
+    c = np.exp(sigma * g.standard_normal(d)).astype(np.float32)
+    m = g.standard_normal((rank, d), dtype=np.float32)
+    z = g.standard_normal((n_tok, rank), dtype=np.float32)
+    x = z @ m
+    x += np.float32(eps) * g.standard_normal((n_tok, d), dtype=np.float32)
+    x *= c[None, :]
+    return f32_to_bf16_bits(x)

@@ -215,6 +215,21 @@ int w4a16_gemm_dq(const uint16_t* x, int64_t m, const uint8_t* packed, const uin
 int w4a16_gemm_dq_workspace_size(int64_t m, int64_t d_out, int64_t d_in, size_t* bytes);
 
 /*
+ * w4a16_gemm_dq_noalloc -- w4a16_gemm_dq for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * product, kernels and arguments, without the workspace arguments.  Its scratch is a static
+ * device array of 128 MB inside the library (the most any w4a16_gemm_dq schedule uses), which
+ * every GPU the library runs on holds until the process ends; its address is looked up once per
+ * device (the stream's device) and nothing is allocated.  Sizes whose fastest schedule would
+ * need more than the array are refused with W4Q_EUNSUPPORTED.  All calls on one GPU share the
+ * array: calls that overlap on one GPU (different streams, a graph replay beside a direct
+ * call) race on it and give undefined results; calls in stream order on one stream are safe.
+ */
+int w4a16_gemm_dq_noalloc(const uint16_t* x, int64_t m, const uint8_t* packed,
+                          const uint16_t* scale_f16, int64_t d_out, int64_t d_in, void* y,
+                          int y_dtype, hipStream_t stream);
+
+/*
  * w4a16_gemv_grouped -- many independent one-row W4A16 products (decode: one token through
  * several linears, e.g. the q/k/v or gate/up projections that share an input, or a whole
  * decoder's linears) in as few launches as possible: one launch per 64 problems.  Each problem

@@ -25,7 +25,8 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == {"w4q_status_string", "w4q_version", "quant_hessian",
                           "quant_hessian_workspace_size", "quant_scale_search", "quant_pack",
                           "lsq_fwd", "lsq_bwd", "w4a16_gemm", "w4a16_gemm_workspace_size",
-                          "w4a16_gemm_dq", "w4a16_gemm_dq_workspace_size", "w4a16_gemv_grouped",
+                          "w4a16_gemm_dq", "w4a16_gemm_dq_workspace_size", "w4a16_gemm_dq_noalloc",
+                          "w4a16_gemv_grouped",
                           "w4q_probe_read", "w4q_probe_mfma_bf16"}
     l = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:

@@ -1,18 +1,28 @@
-"""Benchmark of the W4A16 group-wise hot path on one MI355X.
+"""Benchmark of the W4A16 group-wise hot path on one MI355X, on the 36-layer decoder stack.
 
-One step = one pass of the whole path over one synthetic layer, inputs resident in HBM:
-  quant_hessian (X^T X) -> quant_scale_search (K candidates/group) -> quant_pack ->
-  lsq_fwd -> lsq_bwd (fused forward) -> w4a16_gemm at M = 1, 4, 16 (decode GEMV) and at
-  M = n_tok (prefill GEMM on the matrix cores).
+Workload (the largest configuration; it fits one GPU): 36 decoder layers at hidden 4096, 32
+query / 8 KV heads of dim 128, intermediate 12288 -> 252 linears (q, o 4096x4096; k, v
+1024x4096; gate, up 12288x4096; down 4096x12288), 6.95e9 weights; 8192 calibration tokens per
+layer input (bf16, lognormal(0,1) channel scales); K = 40 candidates over alpha in [0.4, 1.0];
+LSQ on the gate and up weights; prefill at M = 2048 and decode at M = 1 on every linear.  Inputs
+are drawn once on the GPU (seeded; synth.device_*) and stay resident in HBM.
 
-Default workload: the 2048x2048 attention-projection layer (X 2048 tokens x 2048 bf16,
-K = 40 candidates over alpha in [0.4, 1.0]).  Every kernel is timed with HIP events on the
-stream it runs on; the JSON line reports the M=1 GEMV bandwidth as `value`, each kernel's
-rate against its roofline, and the CPU oracle timed on a bounded sample of the same work.
+One step = one pass of the whole hot path over the stack, in a decoder's order:
+  for each layer: quant_hessian of its 4 inputs -> quant_scale_search, quant_pack of its 7
+  linears -> lsq_fwd + lsq_bwd (fused forward) on gate and up -> w4a16_gemm at M = 2048 (prefill)
+  on its 7 linears;
+  then the decode pass: w4a16_gemm at M = 1 over all 252 linears as grouped launches per decoder
+  phase (q|k|v, o, gate|up, down: the order a decoder issues them in), replayed from a HIP graph.
+`value` is the decode pass's HBM bandwidth (bytes of codes, scales, x and y per pass / its
+time in the timed region).  Every launch is bracketed by HIP events on its stream; `kernels`
+reports each family's algorithmic rate (sum of the work of its launches / sum of their
+durations) against its roofline, and `roofline` repeats it for the family with the largest share
+of the step.  `components` adds measurements outside the step: the dequantizing prefill product
+(w4a16_gemm_dq), the decode pass in other launch orders, and single-launch rates.
 
-    python bench.py [--steps K] [--warmup W]
-                    [--workload proj_2048x2048|mlp_gate_8192x2048|decoder36_gate_12288x4096] [--no-cpu]
-    python bench.py --pmc-summary FETCH_DIR WRITE_DIR   (writes profiles/traffic_<workload>.json)
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--no-cpu] [--no-components]
+    python bench.py --pmc-copy                       (copy kernel that calibrates the counters)
+    python bench.py --pmc-summary FETCH_DIR WRITE_DIR [MFMA_DIR]   (-> profiles/traffic_*.json)
 """
 from __future__ import annotations
 
@@ -31,17 +41,37 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "W4A16 GEMV GB/s (% HBM peak); scale-search groups/s; Hessian+GEMM MFMA util"
+WORKLOAD = "decoder36_h4096"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
-PEAK_FP32_VALU_TFLOPS = 157.3  # fp32 vector (published; counts packed FP32)
+PEAK_FP32_VALU_TFLOPS = 157.3  # fp32 vector (published)
 GS = 1.0 / np.sqrt(32 * 7)
-FLUSH_BYTES = 1 << 30
+PREFILL_M = 2048
+CSRC = os.path.join(ROOT, "w4a16_group_wise_amd", "csrc")
+
+# kernel family -> (source file, kernel symbol substrings as they appear in a kernel trace)
+KERNELS = {
+    "hessian": ("hessian.hip", ["hessian_kernel", "hessian_fixup_kernel"]),
+    "scale_search": ("scale_search.hip", ["search_split_kernel", "search_split16_kernel"]),
+    "pack": ("pack_lsq.hip", ["pack_kernel"]),
+    "lsq_fwd": ("pack_lsq.hip", ["lsq_fwd_kernel"]),
+    "lsq_bwd": ("pack_lsq.hip", ["lsq_bwd_kernel"]),
+    "prefill_gemm": ("gemm.hip", ["gemm_group_kernel", "gemm_dq_kernel", "gemm_fixup_kernel"]),
+    "decode_gemv": ("gemv.hip", ["gemv_stream_kernel"]),
+}
+
+
+def src_hash(fname: str) -> str:
+    h = hashlib.sha256()
+    for f in (fname, "common.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def measured_peaks(dev):
     """Measured peaks in the same job: a plain streaming read of 2 GiB and a loop of independent
-    bf16 matrix-core products (the library's probe calls), best of 5, timed with HIP events.
-    Returns {"hbm": bytes/s, "mfma": flop/s}."""
+    bf16 matrix-core products (the library's probe calls), best of 5, timed with HIP events."""
     import torch
     import w4a16_group_wise_amd as w4q
 
@@ -64,185 +94,316 @@ def measured_peaks(dev):
     del buf
     torch.cuda.empty_cache()
     return {"hbm": best_r, "mfma": best_m}
-CSRC = os.path.join(ROOT, "w4a16_group_wise_amd", "csrc")
-
-# kernel family -> (source file, symbol substrings as they appear in a kernel trace)
-KERNELS = {
-    "hessian": ("hessian.hip", ["hessian_kernel", "hessian_fixup_kernel"]),
-    "scale_search": ("scale_search.hip", ["search_split_kernel", "search_split16_kernel"]),
-    "pack": ("pack_lsq.hip", ["pack_kernel"]),
-    "lsq_fwd": ("pack_lsq.hip", ["lsq_fwd_kernel"]),
-    "lsq_bwd": ("pack_lsq.hip", ["lsq_bwd_kernel"]),
-    "gemv_m1": ("gemv.hip", ["gemv_stream_kernel"]),
-    "gemv_m4": ("gemv.hip", []),   # the matrix-core kernel also runs M=16: not separable by name
-    "gemv_m16": ("gemv.hip", []),
-    "gemm": ("gemm.hip", ["gemm_group_kernel"]),
-    "gemm_dq": ("gemm.hip", ["gemm_dq_kernel", "gemm_fixup_kernel"]),
-}
 
 
-def src_hash(fname: str) -> str:
-    h = hashlib.sha256()
-    for f in (fname, "common.hpp"):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+def gemv_bytes(d_out, d_in, m=1):
+    return d_out * d_in * 9 // 16 + 2 * m * d_in + 4 * m * d_out
 
 
-WORKLOADS = {
-    "proj_2048x2048": dict(synth="proj_2048x2048", lin=0, desc="2048x2048 attention-projection layer; X 2048 tok x 2048 bf16 "
-                 "(lognormal(0,1) channel scales); K=40, alpha in [0.4,1.0]; GEMV M=1,4,16; "
-                 "GEMM M=2048", gemm_m=2048),
-    "mlp_gate_8192x2048": dict(synth="mlp_8192x2048", lin=0, desc="MLP gate 8192x2048; X 4096 tok x 2048 bf16 (lognormal(0,1.5)); "
-                 "K=40; GEMV M=1,4,16; GEMM M=256", gemm_m=256),
-    "decoder36_gate_12288x4096": dict(synth="decoder36_h4096", lin=4, desc="36-layer stack's gate projection 12288x4096; X 8192 tok x 4096 "
-                 "bf16; K=40; GEMV M=1,4,16; GEMM M=2048", gemm_m=2048),
-}
+class Stack:
+    """The 36-layer stack's inputs and outputs, resident in HBM, and the launches of one step."""
 
-
-class Step:
-    """Preallocated inputs/outputs and the ordered launches of one step."""
-
-    def __init__(self, wl, dev):
+    def __init__(self, dev, layers):
         import torch
+        import w4a16_group_wise_amd as w4q
         from w4a16_group_wise_amd import synth
 
-        c = synth.WORKLOADS[wl["synth"]]
-        lin = c.linears[wl["lin"]]
-        self.c, self.lin = c, lin
-        w = c.weight(0, lin)
-        x = c.x(0, lin.inp)
-        g = c.grad(0, lin)
-        self.host = dict(w=w, x=x, g=g, alpha=c.alpha())
+        self.c = c = synth.WORKLOADS[WORKLOAD]
         self.dev = dev
-        self.w = torch.from_numpy(w).to(dev)
-        self.x = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
-        self.g = torch.from_numpy(g).to(dev)
-        self.alpha = torch.from_numpy(self.host["alpha"]).to(dev)
-        d_out, d_in = w.shape
-        G, K = d_in // 32, c.n_cand
-        self.d_out, self.d_in, self.G, self.K, self.n_tok = d_out, d_in, G, K, x.shape[0]
+        self.layers = layers
+        g = synth.device_generator(dev, 5)
         f32 = torch.float32
-        self.h = torch.empty((d_in, d_in), dtype=f32, device=dev)
-        self.scale = torch.empty((d_out, G), dtype=f32, device=dev)
-        self.idx = torch.empty((d_out, G), dtype=torch.uint8, device=dev)
-        self.obj = torch.empty((d_out, G), dtype=f32, device=dev)
-        self.packed = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=dev)
-        self.s16 = torch.empty((d_out, G), dtype=torch.float16, device=dev)
-        self.w_hat = torch.empty_like(self.w)
-        self.gw = torch.empty_like(self.w)
-        self.gsc = torch.empty((d_out, G), dtype=f32, device=dev)
-        self.w_hat2 = torch.empty_like(self.w)
-        self.gemm_m = min(wl["gemm_m"], self.n_tok)
-        self.y = {m: torch.empty((m, d_out), dtype=f32, device=dev) for m in (1, 4, 16, self.gemm_m)}
-        self.y_dq = torch.empty((self.gemm_m, d_out), dtype=f32, device=dev)
-        self.names = ["hessian", "scale_search", "pack", "lsq_fwd", "lsq_bwd", "gemv_m1", "gemv_m4",
-                      "gemv_m16", "gemm", "gemm_dq"]
+        self.alpha = torch.from_numpy(c.alpha()).to(dev)
+        self.K = c.n_cand
+        dims = c.inputs()
+        self.x = [{inp: synth.device_calib_x(g, c.n_tok, d, c.sigma, dev) for inp, d in dims.items()}
+                  for _ in range(layers)]
+        self.lin = []
+        for layer in range(layers):
+            per = {}
+            for lin in c.linears:
+                G = lin.d_in // 32
+                e = dict(lin=lin, w=synth.device_weights(g, lin.d_out, lin.d_in, c.outlier_frac, dev),
+                         scale=torch.empty((lin.d_out, G), dtype=f32, device=dev),
+                         idx=torch.empty((lin.d_out, G), dtype=torch.uint8, device=dev),
+                         obj=torch.empty((lin.d_out, G), dtype=f32, device=dev),
+                         packed=torch.empty((lin.d_out, lin.d_in // 2), dtype=torch.uint8, device=dev),
+                         s16=torch.empty((lin.d_out, G), dtype=torch.float16, device=dev),
+                         y1=torch.empty((1, lin.d_out), dtype=f32, device=dev))
+                if lin.name in c.lsq:
+                    e["g"] = synth.device_grad(g, lin.d_out, lin.d_in, dev)
+                per[lin.name] = e
+            self.lin.append(per)
+        # per-step scratch reused by every layer: Hessians, LSQ outputs, prefill outputs
+        self.h = {inp: torch.empty((d, d), dtype=f32, device=dev) for inp, d in dims.items()}
+        big = max(lin.d_out * lin.d_in for lin in c.linears)
+        self.w_hat = torch.empty(big, dtype=f32, device=dev)
+        self.gw = torch.empty(big, dtype=f32, device=dev)
+        self.w_hat2 = torch.empty(big, dtype=f32, device=dev)
+        self.gsc = torch.empty(big // 32, dtype=f32, device=dev)
+        self.y_pre = torch.empty(PREFILL_M * max(lin.d_out for lin in c.linears), dtype=f32, device=dev)
+        ws = max([w4q.workspace_size("quant_hessian", c.n_tok, d) for d in dims.values()] +
+                 [w4q.workspace_size("w4a16_gemm", PREFILL_M, lin.d_out, lin.d_in) for lin in c.linears] +
+                 [w4q.workspace_size("w4a16_gemm_dq", PREFILL_M, lin.d_out, lin.d_in) for lin in c.linears])
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.decode_bytes = sum(gemv_bytes(lin.d_out, lin.d_in) for lin in c.linears) * layers
+        self._decode_graph = None
 
-    def launches(self):
+    def view(self, buf, *shape):
+        n = int(np.prod(shape))
+        return buf[:n].view(*shape)
+
+    def layer_launches(self, layer):
+        """(family, work, fn) of one layer's launches, in order."""
         import w4a16_group_wise_amd as w4q
 
-        yield "hessian", lambda: w4q.quant_hessian(self.x, h=self.h)
-        yield "scale_search", lambda: w4q.quant_scale_search(
-            self.w, self.h, self.alpha, out=(self.scale, self.idx, self.obj, None))
-        yield "pack", lambda: w4q.quant_pack(self.w, self.scale, out=(self.packed, self.s16))
-        yield "lsq_fwd", lambda: w4q.lsq_fwd(self.w, self.scale, out=self.w_hat)
-        yield "lsq_bwd", lambda: w4q.lsq_bwd(self.w, self.scale, self.g, GS,
-                                             out=(self.gw, self.gsc, self.w_hat2))
-        for m, name in ((1, "gemv_m1"), (4, "gemv_m4"), (16, "gemv_m16"), (self.gemm_m, "gemm")):
-            yield name, (lambda m=m: w4q.w4a16_gemm(self.x[:m], self.packed, self.s16, out=self.y[m]))
-        yield "gemm_dq", lambda: w4q.w4a16_gemm_dq(self.x[:self.gemm_m], self.packed, self.s16, out=self.y_dq)
+        c = self.c
+        out = []
+        xs = self.x[layer]
+        for inp, xt in xs.items():
+            n, d = xt.shape
+            out.append(("hessian", n * d * (d + 1),
+                        lambda xt=xt, inp=inp: w4q.quant_hessian(xt, h=self.h[inp], workspace=self.ws)))
+        for name, e in self.lin[layer].items():
+            lin = e["lin"]
+            ng = lin.d_out * lin.d_in // 32
+            out.append(("scale_search", ng * self.K * 1056,
+                        lambda e=e, lin=lin: w4q.quant_scale_search(e["w"], self.h[lin.inp], self.alpha,
+                                                                    out=(e["scale"], e["idx"], e["obj"], None))))
+            out.append(("pack", lin.d_out * lin.d_in * 4.5 + ng * 6,
+                        lambda e=e: w4q.quant_pack(e["w"], e["scale"], out=(e["packed"], e["s16"]))))
+            if name in c.lsq:
+                nw = lin.d_out * lin.d_in
+                shp = (lin.d_out, lin.d_in)
+                out.append(("lsq_fwd", nw * 8 + ng * 4,
+                            lambda e=e, shp=shp: w4q.lsq_fwd(e["w"], e["scale"], out=self.view(self.w_hat, *shp))))
+                out.append(("lsq_bwd", nw * 16 + ng * 8,
+                            lambda e=e, shp=shp, ng=ng: w4q.lsq_bwd(
+                                e["w"], e["scale"], e["g"], GS,
+                                out=(self.view(self.gw, *shp), self.view(self.gsc, shp[0], shp[1] // 32),
+                                     self.view(self.w_hat2, *shp)))))
+        for name, e in self.lin[layer].items():
+            lin = e["lin"]
+            xt = xs[lin.inp][:PREFILL_M]
+            out.append(("prefill_gemm", 2 * PREFILL_M * lin.d_out * lin.d_in,
+                        lambda e=e, xt=xt, lin=lin: w4q.w4a16_gemm(
+                            xt, e["packed"], e["s16"], out=self.view(self.y_pre, PREFILL_M, lin.d_out),
+                            workspace=self.ws)))
+        return out
 
-    def work(self):
-        """Algorithmic work per launch: (amount, unit, bound, peak)."""
-        d_out, d_in, G, K, N = self.d_out, self.d_in, self.G, self.K, self.n_tok
-        nw = d_out * d_in
-        ng = d_out * G
+    def decode_plans(self):
+        """Grouped M = 1 launches per decoder phase, in dependency order: q|k|v share the
+        attention input, o follows them, gate|up share the MLP input, down follows them."""
+        import w4a16_group_wise_amd as w4q
 
-        def gemv_bytes(m):
-            return nw * 9 / 16 + 2 * m * d_in + 4 * m * d_out
+        plans = []
+        for layer in range(self.layers):
+            per = self.lin[layer]
+            xs = self.x[layer]
+            for names in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+                es = [per[n] for n in names]
+                plans.append(w4q.GemvGroupPlan([xs[e["lin"].inp][:1] for e in es], [e["packed"] for e in es],
+                                               [e["s16"] for e in es], outs=[e["y1"] for e in es]))
+        return plans
 
-        return {
-            "hessian": (N * d_in * (d_in + 1), "flop", "mfma", PEAK_BF16_TFLOPS * 1e12),
-            # pass 1 scores with fp32 accuracy from fp16-split products on the matrix cores; its
-            # time goes mostly to vector instructions (codes, splits, dots), so it is priced
-            # against the fp32 vector peak.  The algorithmic count is the symmetric form
-            # (K * 1056 flop per group), half the full 32x32 form the matrix cores evaluate
-            "scale_search": (ng * K * 1056, "flop", "alu", PEAK_FP32_VALU_TFLOPS * 1e12),
-            "pack": (nw * 4.5 + ng * 6, "byte", "hbm", PEAK_HBM_GBS * 1e9),
-            "lsq_fwd": (nw * 8 + ng * 4, "byte", "hbm", PEAK_HBM_GBS * 1e9),
-            "lsq_bwd": (nw * 16 + ng * 8, "byte", "hbm", PEAK_HBM_GBS * 1e9),
-            "gemv_m1": (gemv_bytes(1), "byte", "hbm", PEAK_HBM_GBS * 1e9),
-            "gemv_m4": (gemv_bytes(4), "byte", "hbm", PEAK_HBM_GBS * 1e9),
-            "gemv_m16": (gemv_bytes(16), "byte", "hbm", PEAK_HBM_GBS * 1e9),
-            "gemm": (2 * self.gemm_m * d_out * d_in, "flop", "mfma", PEAK_BF16_TFLOPS * 1e12),
-            "gemm_dq": (2 * self.gemm_m * d_out * d_in, "flop", "mfma", PEAK_BF16_TFLOPS * 1e12),
-        }
+    def decode_graph(self):
+        """The per-phase decode pass captured once in a HIP graph (a decoder replays it per token)."""
+        import torch
+
+        if self._decode_graph is None:
+            plans = self.decode_plans()
+            for p in plans:
+                p()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for p in plans:
+                    p()
+            self._decode_graph = (graph, plans)
+        return self._decode_graph[0]
 
 
-def cpu_baseline(step, budget_s=15.0):
-    """The oracle (as it is) on a bounded sample of the same workload, on the host cores."""
+def run_step(stack, events):
+    """One step; when `events` is a dict, each launch is bracketed by two HIP events."""
+    import torch
+
+    def timed(fam, work, fn):
+        if events is None:
+            fn()
+            return
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        events.setdefault(fam, []).append((e0, e1, work))
+
+    for layer in range(stack.layers):
+        for fam, work, fn in stack.layer_launches(layer):
+            timed(fam, work, fn)
+    graph = stack.decode_graph()
+    timed("decode_pass", stack.decode_bytes, graph.replay)
+
+
+def components(stack, dev, reps=5):
+    """Measurements outside the step: the dequantizing prefill product, the decode pass in other
+    launch orders, single launches of the largest shapes."""
+    import torch
+    import w4a16_group_wise_amd as w4q
+
+    def median_us(fn, n=reps):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    out = {}
+    # prefill with bf16-dequantized weights (w4a16_gemm_dq) on each distinct shape of layer 0
+    per = stack.lin[0]
+    xs = stack.x[0]
+    dq = {}
+    for name in ("q", "k", "gate", "down"):
+        e = per[name]
+        lin = e["lin"]
+        xt = xs[lin.inp][:PREFILL_M]
+        y = stack.view(stack.y_pre, PREFILL_M, lin.d_out)
+        fl = 2 * PREFILL_M * lin.d_out * lin.d_in
+        t_dq = median_us(lambda: w4q.w4a16_gemm_dq(xt, e["packed"], e["s16"], out=y, workspace=stack.ws))
+        t_ex = median_us(lambda: w4q.w4a16_gemm(xt, e["packed"], e["s16"], out=y, workspace=stack.ws))
+        dq[f"{lin.d_out}x{lin.d_in}"] = {"gemm_dq_us": round(t_dq, 1),
+                                          "gemm_dq_frac_bf16": round(fl / (t_dq * 1e-6) / (PEAK_BF16_TFLOPS * 1e12), 4),
+                                          "gemm_exact_us": round(t_ex, 1),
+                                          "gemm_exact_frac_bf16": round(fl / (t_ex * 1e-6) / (PEAK_BF16_TFLOPS * 1e12), 4)}
+    out["prefill_m2048_per_shape"] = dq
+    # the decode pass in other orders (all 252 linears, weights far beyond the Infinity Cache)
+    plans = stack.decode_plans()
+    flat = [(e, stack.x[layer][e["lin"].inp][:1]) for layer in range(stack.layers) for e in stack.lin[layer].values()]
+    whole = w4q.GemvGroupPlan([x for _, x in flat], [e["packed"] for e, _ in flat], [e["s16"] for e, _ in flat],
+                              outs=[e["y1"] for e, _ in flat])
+
+    def singles():
+        for e, x in flat:
+            w4q.w4a16_gemm(x, e["packed"], e["s16"], out=e["y1"])
+
+    def per_phase():
+        for p in plans:
+            p()
+
+    B = stack.decode_bytes
+    for name, fn in (("one_call_per_linear", singles), ("grouped_per_phase_host", per_phase),
+                     ("grouped_per_phase_graph", stack.decode_graph().replay), ("grouped_whole_pass", whole)):
+        us = median_us(fn)
+        out.setdefault("decode_pass", {})[name] = {"us": round(us, 1), "GBps": round(B / (us * 1e-6) / 1e9, 1),
+                                                   "frac_hbm": round(B / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    out["decode_pass"]["bytes"] = B
+    out["decode_pass"]["linears"] = len(flat)
+    # one M = 1 launch of the largest weight (gate 12288x4096, 28 MB)
+    e = per["gate"]
+    us = median_us(lambda: w4q.w4a16_gemm(xs["mlp"][:1], e["packed"], e["s16"], out=e["y1"]), n=20)
+    gb = gemv_bytes(12288, 4096)
+    out["gemv_single_12288x4096"] = {"us": round(us, 2), "frac_hbm": round(gb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(budget_s=20.0):
+    """The oracle (as it is, untuned) on a bounded sample of the same workload, on the host cores:
+    the decode product of one gate linear (12288x4096) repeated for about a quarter of the
+    budget, the search on 65536 groups of it, a 256-column slab of an 8192x4096 Hessian, pack and
+    LSQ on 4M weights, and the prefill product on 16 output columns.  The inputs are the host
+    (numpy) draws of the same recipe."""
     import oracle
+    from w4a16_group_wise_amd import synth
 
-    h = step.host
-    w, x, alpha = h["w"], h["x"], h["alpha"]
-    d_out, d_in, G = step.d_out, step.d_in, step.G
-    hh = step.h.cpu().numpy()
-    sc = step.scale.cpu().numpy()
-    packed = step.packed.cpu().numpy()
-    s16 = step.s16.cpu().view(__import__("torch").int16).numpy().view(np.uint16)
-    rates = {}
-    t_total = 0.0
+    c = synth.WORKLOADS[WORKLOAD]
+    lin = [l for l in c.linears if l.name == "gate"][0]
+    w = c.weight(0, lin)
+    x = c.x(0, lin.inp)
+    alpha = c.alpha()
+    G = lin.d_in // 32
+    rates, t_step = {}, 0.0
 
     def timed(fn):
         t0 = time.perf_counter()
-        fn()
-        return time.perf_counter() - t0
+        r = fn()
+        return time.perf_counter() - t0, r
 
-    # GEMV M=1 over every output row (bytes as on the GPU)
-    reps = 0
-    t = 0.0
-    while t < budget_s * 0.25 or reps < 1:
-        t += timed(lambda: oracle.gemm_cols(x[:1], packed, s16))
-        reps += 1
-    gemv_bytes = d_out * d_in * 9 / 16 + 2 * d_in + 4 * d_out
-    rates["gemv_m1_GBps"] = gemv_bytes * reps / t / 1e9
-    t_total += t / reps
-    # scale search on the first rows (groups/s)
-    rows = max(1, min(d_out, int(4096 / G)))
-    ts = timed(lambda: oracle.scale_search(w[:rows], hh, alpha))
-    rates["search_groups_per_s"] = rows * G / ts
-    t_total += ts * d_out / rows
-    # Hessian: a 256-column slab of X^T X (entries/s -> flop/s)
-    cols = min(256, d_in)
-    ij = np.stack(np.meshgrid(np.arange(cols), np.arange(cols), indexing="ij"), -1).reshape(-1, 2)
+    # Hessian: 256-column slab (unique entries) -> flop/s
+    ij = np.stack(np.meshgrid(np.arange(256), np.arange(256), indexing="ij"), -1).reshape(-1, 2)
     ij = ij[ij[:, 0] <= ij[:, 1]]
-    th = timed(lambda: oracle.hessian_entries(x, ij))
+    th, _ = timed(lambda: oracle.hessian_entries(x, ij))
     rates["hessian_GFLOPs"] = ij.shape[0] * 2 * x.shape[0] / th / 1e9
-    t_total += th * (d_in * (d_in + 1) / 2) / ij.shape[0]
-    # pack + LSQ on the first 1M weights
-    r1 = max(1, min(d_out, (1 << 20) // d_in))
-    tp = timed(lambda: oracle.pack(w[:r1], sc[:r1]))
-    tl = timed(lambda: oracle.lsq_bwd(w[:r1], sc[:r1], h["g"][:r1], GS))
-    rates["pack_GBps"] = r1 * d_in * 4.5 / tp / 1e9
-    rates["lsq_bwd_GBps"] = r1 * d_in * 16 / tl / 1e9
-    t_total += (tp + 2 * tl) * d_out / r1
-    # prefill GEMM on 16 output columns
-    cols_g = np.arange(min(16, d_out))
-    tg = timed(lambda: oracle.gemm_cols(x[:step.gemm_m], packed, s16, cols_g))
-    rates["gemm_GFLOPs"] = 2 * step.gemm_m * cols_g.shape[0] * d_in / tg / 1e9
-    t_total += tg * d_out / cols_g.shape[0] + t / reps * (4 + 16)  # GEMV M=4, M=16 ~ linear in M
-    return dict(
-        value=rates["gemv_m1_GBps"], unit="GB/s", cores=oracle.threads(), kind="oracle",
-        sample=(f"GEMV M=1 over all {d_out} rows x{reps}; search on {rows * G} groups; Hessian "
-                f"{ij.shape[0]} entries of a {cols}-col slab; pack/LSQ on {r1 * d_in} weights; "
-                f"GEMM M={step.gemm_m} on {cols_g.shape[0]} cols"),
-        rates=rates, step_ms_extrapolated=t_total * 1e3)
+    # search on the first 65536 groups (needs the H blocks of those groups: the slab covers the
+    # first 8 group columns; the rest of H is computed on the GPU's shapes only for its blocks)
+    rows = 65536 // G
+    h = np.zeros((lin.d_in, lin.d_in), np.float32)
+    for g0 in range(G):
+        blk = np.stack(np.meshgrid(np.arange(32 * g0, 32 * g0 + 32), np.arange(32 * g0, 32 * g0 + 32),
+                                   indexing="ij"), -1).reshape(-1, 2)
+        h[blk[:, 0], blk[:, 1]] = oracle.hessian_entries(x, blk)
+    ts, (sc, _, _, _) = timed(lambda: oracle.scale_search(w[:rows], h, alpha))
+    rates["search_groups_per_s"] = rows * G / ts
+    # pack and LSQ on the first 4M weights
+    r4 = (4 << 20) // lin.d_in
+    scale = np.abs(w[:r4].reshape(r4, G, 32)).max(axis=2).astype(np.float32) / 7
+    tp, (packed, s16) = timed(lambda: oracle.pack(w[:r4], scale))
+    gr = c.grad(0, lin)[:r4]
+    tl, _ = timed(lambda: oracle.lsq_bwd(w[:r4], scale, gr, GS))
+    rates["pack_GBps"] = r4 * lin.d_in * 4.5 / tp / 1e9
+    rates["lsq_bwd_GBps"] = r4 * lin.d_in * 16 / tl / 1e9
+    # decode product over all rows of the packed gate weight, repeated
+    scale_all = np.abs(w.reshape(lin.d_out, G, 32)).max(axis=2).astype(np.float32) / 7
+    packed_all, s16_all = oracle.pack(w, scale_all)
+    reps, t = 0, 0.0
+    while t < budget_s * 0.25 or reps < 1:
+        dt, _ = timed(lambda: oracle.gemm_cols(x[:1], packed_all, s16_all))
+        t += dt
+        reps += 1
+    decode_gbps = gemv_bytes(lin.d_out, lin.d_in) * reps / t / 1e9
+    rates["decode_GBps"] = decode_gbps
+    # prefill on 16 output columns
+    tg, _ = timed(lambda: oracle.gemm_cols(x[:PREFILL_M], packed_all, s16_all, np.arange(16)))
+    rates["prefill_GFLOPs"] = 2 * PREFILL_M * 16 * lin.d_in / tg / 1e9
+    # the whole step extrapolated from these rates over the stack's work
+    wl = synth.WORKLOADS[WORKLOAD]
+    n_w = sum(l.d_out * l.d_in for l in wl.linears) * wl.layers
+    hess = sum(wl.n_tok * d * (d + 1) for d in wl.inputs().values()) * wl.layers
+    t_step = (hess / (rates["hessian_GFLOPs"] * 1e9) + n_w / 32 / rates["search_groups_per_s"]
+              + n_w * 4.5 / (rates["pack_GBps"] * 1e9)
+              + 2 * 12288 * 4096 * wl.layers * 24 / (rates["lsq_bwd_GBps"] * 1e9)
+              + 2 * PREFILL_M * n_w / (rates["prefill_GFLOPs"] * 1e9)
+              + sum(gemv_bytes(l.d_out, l.d_in) for l in wl.linears) * wl.layers / (decode_gbps * 1e9))
+    return dict(value=round(decode_gbps, 3), unit="GB/s", cores=oracle.threads(), kind="oracle",
+                cpu_model=cpu_model(),
+                sample=(f"decode product of one 12288x4096 gate linear x{reps}; search on {rows * G} groups; "
+                        f"Hessian {ij.shape[0]} entries of a 256-col slab (8192 tokens); pack/LSQ on {r4 * lin.d_in} "
+                        f"weights; prefill M={PREFILL_M} on 16 cols"),
+                rates={k: round(v, 3) for k, v in rates.items()},
+                step_s_extrapolated=round(t_step, 1))
 
 
-def traffic_for(workload, kernel):
-    """HBM bytes/launch from committed PMC counters, if the kernel source is unchanged."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def traffic_for(kernel):
+    """HBM bytes per launch (mean over the family's launches in a step) from the committed
+    counters, if the kernel source is unchanged since they were taken."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{WORKLOAD}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -253,206 +414,109 @@ def traffic_for(workload, kernel):
     return k.get("bytes_per_launch")
 
 
-def decode_pass(dev, reps=3):
-    """The 36-layer decoder's decode pass: one M=1 W4A16 product per linear over all 252
-    linears (hidden 4096, intermediate 12288; 3.9 GB of packed codes and scales, far beyond the
-    256 MB Infinity Cache, so every pass streams the weights from HBM), on one stream and timed
-    as a whole with HIP events, three ways: one w4a16_gemm call per linear; w4a16_gemv_grouped
-    per decoder phase (q|k|v, o, gate|up, down: the order a decoder can issue them in), issued
-    from the host and replayed from a HIP graph; and w4a16_gemv_grouped over all 252 linears
-    (the grouped forms as prepared plans).  Codes and
-    scales are random: this measures bandwidth only (parity of the same calls is tested
-    separately)."""
-    import torch
-    import w4a16_group_wise_amd as w4q
-    from w4a16_group_wise_amd import synth
-
-    c = synth.WORKLOADS["decoder36_h4096"]
-    g = torch.Generator(device=dev)
-    g.manual_seed(5)
-    mats, total = [], 0
-    for _layer in range(c.layers):
-        for lin in c.linears:
-            p = torch.randint(0, 256, (lin.d_out, lin.d_in // 2), dtype=torch.uint8, device=dev, generator=g)
-            sc = (torch.rand((lin.d_out, lin.d_in // 32), device=dev, generator=g) * 0.01 + 1e-3).half()
-            y = torch.empty((1, lin.d_out), dtype=torch.float32, device=dev)
-            mats.append((p, sc, lin.d_in, y))
-            total += lin.d_out * lin.d_in * 9 // 16 + 2 * lin.d_in + 4 * lin.d_out
-    xs = {d: torch.randn((1, d), device=dev, generator=g).to(torch.bfloat16) for d in {m[2] for m in mats}}
-
-    def single():
-        for p, sc, d, y in mats:
-            w4q.w4a16_gemm(xs[d], p, sc, out=y)
-
-    # the calls a decoder makes in dependency order: q|k|v and gate|up share an input, o and down
-    # follow their producers -> 4 grouped launches per layer.  A decoder reuses its weight, input
-    # and output buffers every step, so each grouped call is a plan marshalled once, here.
-    plans = []
-    per_layer = len(c.linears)
-    for l0 in range(0, len(mats), per_layer):
-        layer = mats[l0:l0 + per_layer]
-        for idx in ((0, 1, 2), (3,), (4, 5), (6,)):
-            sel = [layer[i] for i in idx]
-            plans.append(w4q.GemvGroupPlan([xs[m[2]] for m in sel], [m[0] for m in sel], [m[1] for m in sel],
-                                           outs=[m[3] for m in sel]))
-
-    def grouped_layers():
-        for pl in plans:
-            pl()
-
-    whole = w4q.GemvGroupPlan([xs[m[2]] for m in mats], [m[0] for m in mats], [m[1] for m in mats],
-                              outs=[m[3] for m in mats])
-
-    def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
-        return {"us_per_pass": round(us, 1), "GBps": round(total / (us * 1e-6) / 1e9, 1),
-                "frac_hbm": round(total / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-
-    # the per-phase sequence captured once in a HIP graph and replayed (no host launch cost)
-    grouped_layers()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        grouped_layers()
-
-    res = {"linears": len(mats), "bytes": total,
-           "one_call_per_linear": timed(single),
-           "grouped_per_layer_phase": timed(grouped_layers),
-           "grouped_per_layer_phase_graph": timed(graph.replay),
-           "grouped_whole_pass": timed(whole)}
-    del mats, plans, whole, graph
-    torch.cuda.empty_cache()
-    return res
-
-
 def run(args):
     import torch
     import w4a16_group_wise_amd as w4q
 
     if args.gpus != 1:
-        print(json.dumps({"error": "runs on one GPU only; --gpus must be 1 "
-                          "(sharding over several GPUs is not implemented)"}))
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (how the path "
+                          "would shard over several GPUs is described, not built)"}))
         sys.exit(2)
     dev = torch.device("cuda:0")
-    wl = WORKLOADS[args.workload]
-    step = Step(wl, dev)
+    print(f"[bench] drawing the {args.layers}-layer stack on the GPU", file=sys.stderr, flush=True)
+    stack = Stack(dev, args.layers)
     torch.cuda.synchronize()
-    work = step.work()
-    launches = list(step.launches())
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        for _, fn in launches:
-            fn()
+        run_step(stack, None)
     torch.cuda.synchronize()
-    # (1) the timed region: exactly `steps` passes of every launch, host clock, synchronised on
-    #     both sides, each launch between two HIP events on its stream (the roofline kernel's
-    #     average launch duration comes from these)
-    ev_t = {n: [] for n, _ in launches}
+    # the timed region: exactly `steps` passes, host clock, synchronised on both sides; every
+    # launch between two HIP events on the current stream (the library's launch stream)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    events = {}
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        for name, fn in launches:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            ev_t[name].append((e0, e1))
+        run_step(stack, events)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    # (2) per launch: each repetition first reads 1 GiB of other data with ordinary loads (the
-    #     inputs leave the 256 MB Infinity Cache without leaving dirty lines behind, and the host
-    #     has time to enqueue the launch behind the read, so the two events bracket GPU work
-    #     only), then times the launch between two HIP events on the current stream; the median
-    #     over repetitions is reported
-    flush_buf = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device=dev)
-    flush_sink = torch.empty(65536, dtype=torch.int32, device=dev)
-    # the floor of this protocol: a kernel that reads 4 KB, timed the same way
-    tiny_buf = torch.ones(4096, dtype=torch.uint8, device=dev)
-    floor = [("_floor", lambda: w4q.probe_read(tiny_buf, nontemporal=False, sink=flush_sink))]
-    reps = max(args.steps, 20)
-    ev = {n: [] for n, _ in launches + floor}
-    for _ in range(reps):
-        for name, fn in launches + floor:
-            w4q.probe_read(flush_buf, nontemporal=False, sink=flush_sink)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            ev[name].append((e0, e1))
-    torch.cuda.synchronize()
-    del flush_buf, flush_sink, tiny_buf
-    floor_us = float(np.median([a.elapsed_time(b) for a, b in ev.pop("_floor")])) * 1e3
+    fam_info = {
+        "hessian": ("flop", "mfma", PEAK_BF16_TFLOPS * 1e12),
+        "scale_search": ("flop", "alu", PEAK_FP32_VALU_TFLOPS * 1e12),
+        "pack": ("byte", "hbm", PEAK_HBM_GBS * 1e9),
+        "lsq_fwd": ("byte", "hbm", PEAK_HBM_GBS * 1e9),
+        "lsq_bwd": ("byte", "hbm", PEAK_HBM_GBS * 1e9),
+        "prefill_gemm": ("flop", "mfma", PEAK_BF16_TFLOPS * 1e12),
+        "decode_pass": ("byte", "hbm", PEAK_HBM_GBS * 1e9),
+    }
+    print("[bench] measured peaks", file=sys.stderr, flush=True)
     peaks = measured_peaks(dev)
-    comps = {}
-    for name, pairs in ev.items():
-        us = float(np.median([a.elapsed_time(b) for a, b in pairs])) * 1e3
-        amt, unit, bound, peak = work[name]
-        rate = amt / (us * 1e-6)
-        comps[name] = dict(us=round(us, 3), work=amt, work_unit=unit, bound=bound,
-                           peak=round(peak / (1e9 if unit == "byte" else 1e12), 1),
-                           achieved=round(rate / (1e9 if unit == "byte" else 1e12), 3),
-                           rate_unit="GB/s" if unit == "byte" else "TFLOP/s",
-                           frac=round(rate / peak, 4))
-        # measured peaks exist for HBM streaming and bf16 matrix cores only
-        mp = peaks.get(bound) if (bound == "hbm" or peak == PEAK_BF16_TFLOPS * 1e12) else None
+    kernels = {}
+    total_us = 0.0
+    for fam, lst in events.items():
+        durs = np.array([a.elapsed_time(b) * 1e3 for a, b, _ in lst])
+        work = float(sum(w for _, _, w in lst))
+        unit, bound, peak = fam_info[fam]
+        rate = work / (durs.sum() * 1e-6)
+        scale = 1e9 if unit == "byte" else 1e12
+        kernels[fam] = dict(launches_per_step=len(lst) // args.steps, us_per_step=round(durs.sum() / args.steps, 1),
+                            mean_launch_us=round(float(durs.mean()), 3),
+                            work_per_launch=work / len(lst), work_unit=unit, bound=bound,
+                            achieved=round(rate / scale, 3), peak=round(peak / scale, 1),
+                            rate_unit="GB/s" if unit == "byte" else "TFLOP/s", frac=round(rate / peak, 4))
+        mp = peaks["hbm"] if bound == "hbm" else (peaks["mfma"] if bound == "mfma" else None)
         if mp:
-            comps[name]["frac_of_measured_peak"] = round(rate / mp, 4)
-        ut = float(np.mean([a.elapsed_time(b) for a, b in ev_t[name]])) * 1e3
-        comps[name]["us_timed_region"] = round(ut, 3)
-        comps[name]["achieved_timed_region"] = round(amt / (ut * 1e-6) / (1e9 if unit == "byte" else 1e12), 3)
-    dom = max(comps, key=lambda n: comps[n]["us_timed_region"])
-    d = comps[dom]
-    pk = d["peak"]
-    roof = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved_timed_region"], "peak": pk,
-            "unit": d["rate_unit"], "frac": round(d["achieved_timed_region"] / pk, 4),
-            "traffic": traffic_for(args.workload, dom),
-            "launch_us": d["us_timed_region"]}
-    gv = comps["gemv_m1"]
+            kernels[fam]["frac_of_measured_peak"] = round(rate / mp, 4)
+        total_us += durs.sum() / args.steps
+    for k in kernels.values():
+        k["share_of_step"] = round(k["us_per_step"] / total_us, 4)
+    dom = max((f for f in kernels if f != "decode_pass"), key=lambda f: kernels[f]["us_per_step"])
+    d = kernels[dom]
+    roof = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"],
+            "unit": d["rate_unit"], "frac": d["frac"], "traffic": traffic_for(dom),
+            "launch_us": d["mean_launch_us"], "algorithmic_per_launch": d["work_per_launch"],
+            "algorithmic_unit": d["work_unit"]}
+    dp = kernels["decode_pass"]
+    c = stack.c
     out = {
-        "metric": METRIC, "value": gv["achieved"], "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "metric": METRIC, "value": dp["achieved"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16+fp32",
-        "data": "synthetic (seeded; see w4a16_group_wise_amd/synth.py)",
-        "config": {"workload": f"{args.workload}: {wl['desc']}", "d_out": step.d_out,
-                   "d_in": step.d_in, "n_tok": step.n_tok, "n_cand": step.K,
-                   "gemm_m": step.gemm_m, "parallelism": "single GPU"},
+        "data": "synthetic (seeded, drawn on the GPU; see w4a16_group_wise_amd/synth.py)",
+        "config": {"workload": f"{WORKLOAD}: 36-layer decoder stack at hidden 4096 (q, o 4096x4096; k, v "
+                               f"1024x4096; gate, up 12288x4096; down 4096x12288; 252 linears); X 8192 tok "
+                               f"bf16 per layer input; K=40, alpha in [0.4,1.0]; LSQ on gate/up; prefill "
+                               f"M={PREFILL_M}; decode M=1 per-phase grouped, graph-replayed",
+                   "layers": args.layers, "linears": args.layers * len(c.linears), "n_tok": c.n_tok,
+                   "n_cand": c.n_cand, "prefill_m": PREFILL_M, "parallelism": "single GPU"},
         "roofline": roof,
+        "value_detail": {"decode_pass_us": round(dp["mean_launch_us"], 1), "bytes": stack.decode_bytes,
+                         "frac_hbm": dp["frac"]},
         "measured_peaks": {"hbm_read_GBps": round(peaks["hbm"] / 1e9, 1),
                            "mfma_bf16_TFLOPs": round(peaks["mfma"] / 1e12, 1),
                            "how": "w4q_probe_read (non-temporal) over 2 GiB and w4q_probe_mfma_bf16, "
                                   "best of 5, HIP events"},
-        "timing": f"per launch: median of {reps} repetitions, each after a 1 GiB read of other data "
-                  "(cold Infinity Cache), HIP events on the launch stream",
-        "launch_floor_us": round(floor_us, 3),  # a 4 KB read kernel timed the same way
-        "components": {
-            "gemv_m1_frac_hbm": gv["frac"],
-            "search_groups_per_s": round(step.d_out * step.G / (comps["scale_search"]["us"] * 1e-6), 1),
-            "hessian_mfma_frac": comps["hessian"]["frac"],
-            "gemm_mfma_frac": comps["gemm"]["frac"],
-            "gemm_dq_mfma_frac": comps["gemm_dq"]["frac"],
-        },
-        "kernels": comps,
+        "timing": "timed region: HIP events around every launch on its stream; per family, sum of "
+                  "algorithmic work / sum of launch durations",
+        "kernels": kernels,
+        "components": {"search_groups_per_s": round(
+            sum(l.d_out * l.d_in // 32 for l in c.linears) * args.layers / (kernels["scale_search"]["us_per_step"] * 1e-6), 1)},
     }
-    if not args.no_decode:
-        out["components"]["decode_pass_36_layer"] = decode_pass(dev)
+    if not args.no_components:
+        print("[bench] components", file=sys.stderr, flush=True)
+        out["components"].update(components(stack, dev))
+    del stack
+    torch.cuda.empty_cache()
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(step)
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))
 
 
 def pmc_summary(args):
-    """Per-kernel FETCH_SIZE / WRITE_SIZE (KiB per dispatch) -> bytes per launch, scaled by the
-    counter reading of torch's plain copy of a known size that bench.py --pmc-copy runs."""
+    """Per-kernel FETCH_SIZE / WRITE_SIZE (KiB per dispatch) -> bytes per launch (mean over the
+    family's dispatches), scaled by the reading of torch's plain copy of a known size that
+    bench.py --pmc-copy runs; with a third directory, the matrix-core busy counters."""
     import csv
     import glob
 
@@ -466,27 +530,26 @@ def pmc_summary(args):
                     rows.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return rows
 
-    fetch = read(args.pmc_summary[0], "FETCH_SIZE")
-    write = read(args.pmc_summary[1], "WRITE_SIZE")
-    copy_bytes = float(args.copy_bytes)
-
     def mean_of(rows, keys):
         """Sum over the launch's kernels of each kernel's mean per dispatch."""
         tot, found = 0.0, False
         for key in keys:
-            pat = re.compile(r"\b" + re.escape(key) + (r"" if key.endswith(",") else r"\b"))
+            pat = re.compile(r"\b" + re.escape(key) + r"\b")
             vals = [v for k, vs in rows.items() if pat.search(k) for v in vs]
             if vals:
                 tot += float(np.mean(vals))
                 found = True
         return tot if found else None
 
+    fetch = read(args.pmc_summary[0], "FETCH_SIZE")
+    write = read(args.pmc_summary[1], "WRITE_SIZE")
+    copy_bytes = float(args.copy_bytes)
     cf = mean_of(fetch, ["neg_kernel_cuda"])
     cw = mean_of(write, ["neg_kernel_cuda"])
     f_scale = copy_bytes / (cf * 1024) if cf else 1.0
     w_scale = copy_bytes / (cw * 1024) if cw else 1.0
-    res = {"workload": args.workload, "copy_bytes": copy_bytes, "fetch_scale": f_scale,
-           "write_scale": w_scale, "kernels": {}}
+    res = {"workload": WORKLOAD, "copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
+           "kernels": {}}
     for name, (src, keys) in KERNELS.items():
         fk = mean_of(fetch, keys)
         wk = mean_of(write, keys)
@@ -496,7 +559,7 @@ def pmc_summary(args):
                                 "bytes_per_launch": fk * 1024 * f_scale + wk * 1024 * w_scale,
                                 "src_hash": src_hash(src)}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    p = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    p = os.path.join(ROOT, "profiles", f"traffic_{WORKLOAD}.json")
     with open(p, "w") as f:
         json.dump(res, f, indent=1)
     print(p)
@@ -519,13 +582,13 @@ def pmc_copy(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="proj_2048x2048", choices=sorted(WORKLOADS))
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=36, help="layers of the stack (36; fewer for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="DIR")
     ap.add_argument("--pmc-copy", action="store_true")
-    ap.add_argument("--no-decode", action="store_true", help="skip the 36-layer decode-pass measurement")
     ap.add_argument("--copy-bytes", type=float, default=float(1 << 30))
     args = ap.parse_args()
     if args.pmc_summary:

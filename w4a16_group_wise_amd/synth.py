@@ -184,3 +184,45 @@ def correlated_x(stream: int, layer: int, tensor_id: int, n_tok: int, d: int, ra
     x += np.float32(eps) * g.standard_normal((n_tok, d), dtype=np.float32)
     x *= c[None, :]
     return f32_to_bf16_bits(x)
+
+
+# ------------------------------------------------------------------ drawn on the device
+# The benchmark's 36-layer stack holds 7e9 weights; drawing them with numpy on the host would
+# take minutes, so the same distributions are drawn with torch's seeded device generator.  The
+# values differ from the host streams above (different generator), the recipe does not.
+
+def device_generator(device, seed: int):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def device_weights(gen, d_out: int, d_in: int, outlier_frac: float, device):
+    """fp32 [d_out][d_in] = 0.02 * N(0,1) with round(p * numel) distinct entries scaled by 10."""
+    import torch
+
+    w = torch.randn((d_out, d_in), generator=gen, device=device, dtype=torch.float32)
+    w *= 0.02
+    n_out = int(round(outlier_frac * w.numel()))
+    if n_out:
+        flat = torch.randperm(w.numel(), generator=gen, device=device)[:n_out]
+        w.view(-1)[flat] *= 10.0
+    return w
+
+
+def device_calib_x(gen, n_tok: int, d: int, sigma: float, device):
+    """bf16 [n_tok][d]: N(0,1) times a lognormal(0, sigma) factor per input channel (RNE)."""
+    import torch
+
+    c = torch.exp(sigma * torch.randn(d, generator=gen, device=device, dtype=torch.float32))
+    z = torch.randn((n_tok, d), generator=gen, device=device, dtype=torch.float32)
+    z *= c[None, :]
+    return z.to(torch.bfloat16)
+
+
+def device_grad(gen, d_out: int, d_in: int, device):
+    import torch
+
+    return torch.randn((d_out, d_in), generator=gen, device=device, dtype=torch.float32)

@@ -558,6 +558,33 @@ def pmc_summary(args):
         res["kernels"][name] = {"fetch_kib": fk, "write_kib": wk,
                                 "bytes_per_launch": fk * 1024 * f_scale + wk * 1024 * w_scale,
                                 "src_hash": src_hash(src)}
+    # a family's launches differ in shape: these are means per dispatch over one step's launches,
+    # comparable with the mean algorithmic work per launch the bench reports
+    if len(args.pmc_summary) > 2:
+        # matrix cores: SQ_INSTS_VALU_MFMA_MOPS_* count matrix operations in units of 512 flop;
+        # SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE is normalised by the same ratio read for the
+        # probe kernel of the same job, which issues independent products back to back on every
+        # SIMD (busy fraction 1 by construction)
+        mdir = args.pmc_summary[2]
+        mops_bf16 = read(mdir, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        mops_f16 = read(mdir, "SQ_INSTS_VALU_MFMA_MOPS_F16")
+        busy = read(mdir, "SQ_VALU_MFMA_BUSY_CYCLES")
+        gui = read(mdir, "GRBM_GUI_ACTIVE")
+        pb, pg = mean_of(busy, ["mfma_kernel"]), mean_of(gui, ["mfma_kernel"])
+        norm = pb / pg if pb and pg else None
+        res["mfma_probe"] = {"busy_cycles": pb, "gui_active": pg,
+                             "mops_bf16_flop": (mean_of(mops_bf16, ["mfma_kernel"]) or 0) * 512}
+        for name, (src, keys) in KERNELS.items():
+            b, gact = mean_of(busy, keys), mean_of(gui, keys)
+            if b is None or gact is None:
+                continue
+            ent = res["kernels"].setdefault(name, {"src_hash": src_hash(src)})
+            ent["mfma_busy_cycles"] = b
+            ent["gui_active"] = gact
+            ent["mfma_bf16_flop_issued"] = (mean_of(mops_bf16, keys) or 0) * 512
+            ent["mfma_f16_flop_issued"] = (mean_of(mops_f16, keys) or 0) * 512
+            if norm:
+                ent["mfma_busy_frac"] = b / gact / norm
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     p = os.path.join(ROOT, "profiles", f"traffic_{WORKLOAD}.json")
     with open(p, "w") as f:

@@ -168,6 +168,44 @@ int lsq_bwd(const float* w, const float* scale, const float* grad_w_hat, int64_t
             hipStream_t stream);
 
 /*
+ * lsq_adam_step -- one fused QAT optimisation step for one linear.
+ * [blog] section 3: the weights and the step sizes are optimised jointly (the gradient reaches
+ * the step through the LSQ estimator); [card] "QAT Highlights": the forward emulates the
+ * deployment grid.  In one pass over W: the gradients of lsq_bwd (G = dL/dw_hat, D = the group's
+ * fp32 step), then, in fp32 in this order, with hp's bias corrections c1 = 1 - beta1^t and
+ * c2 = 1 - beta2^t of step t:
+ *   g_w = G * m (STE mask)          m_w = beta1 m_w + (1 - beta1) g_w
+ *                                    v_w = beta2 v_w + (1 - beta2) g_w^2
+ *   w   = w - lr_w ((m_w / c1) / (sqrt(v_w / c2) + eps) + weight_decay w)
+ *   ds  = grad_scale * sum_group G f  (as lsq_bwd)
+ *   m_s = beta1 m_s + (1 - beta1) ds,  v_s = beta2 v_s + (1 - beta2) ds^2
+ *   D   = max(D - lr_s (m_s / c1) / (sqrt(v_s / c2) + eps), scale_min)
+ * Division and square root are correctly rounded.  The mask and the codes use the step and
+ * weights before the update.
+ *   w, m_w, v_w          fp32 [d_out][d_in] in/out (updated in place), 16-B aligned.
+ *   scale, m_s, v_s      fp32 [d_out][G] in/out (updated in place).
+ *   grad_w_hat           fp32 [d_out][d_in], 16-B aligned.
+ *   hp                   HOST pointer: 0 <= beta < 1, eps > 0, 0 < c <= 1, lr >= 0,
+ *                        weight_decay >= 0, scale_min > 0, all finite (else W4Q_EINVAL).
+ *   grad_scale_out       fp32 [d_out][G] out or NULL: ds.
+ *   w_hat_next           fp32 [d_out][d_in] out or NULL (16-B aligned): D_new * code(w_new,
+ *                        D_new), the next step's forward.
+ * Outputs must not overlap the inputs except the in/out pairs named above.
+ */
+typedef struct w4q_adam_params {
+  float lr_w, lr_s;       /* learning rates of the weights and of the steps */
+  float beta1, beta2, eps;
+  float weight_decay;     /* decoupled, on the weights only */
+  float bias_c1, bias_c2; /* 1 - beta1^t, 1 - beta2^t for step t >= 1 */
+  float scale_min;        /* lower bound kept on every step */
+} w4q_adam_params;
+
+int lsq_adam_step(float* w, float* scale, const float* grad_w_hat, int64_t d_out, int64_t d_in,
+                  float grad_scale, float* m_w, float* v_w, float* m_s, float* v_s,
+                  const w4q_adam_params* hp, float* grad_scale_out, float* w_hat_next,
+                  hipStream_t stream);
+
+/*
  * w4a16_gemm -- deployment W4A16 product on packed codes.
  * [card] intro and configuration: INT4 weights with 16-bit activations; speed is set by
  * weight memory, bandwidth and the kernels of the accelerator.

@@ -70,6 +70,7 @@ def _L():
         lib.orc_lsq_fwd.argtypes = [P, P, I, I, P]
         lib.orc_lsq_bwd.argtypes = [P, P, P, I, I, ctypes.c_double, P, P, P]
         lib.orc_gemm_cols_mode.argtypes = [P, I, P, P, I, P, I, ctypes.c_int, P, P]
+        lib.orc_lsq_adam_step.argtypes = [P, P, P, I, I, ctypes.c_double, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.orc_round_bf16.restype = ctypes.c_double
         lib.orc_round_bf16.argtypes = [ctypes.c_double]
         _lib = lib
@@ -216,3 +217,32 @@ def gemm_cols(x_bf16: np.ndarray, packed: np.ndarray, s16: np.ndarray,
     _L().orc_gemm_cols_mode(_p(x), m, _p(packed), _p(s16), d_in, _p(cols), cols.shape[0],
                             1 if dequant_bf16 else 0, _p(y), _p(ya))
     return y, ya
+
+
+ADAM_KEYS = ("lr_w", "lr_s", "beta1", "beta2", "eps", "weight_decay", "step", "scale_min")
+
+
+def adam_hparams(lr_w, lr_s, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, step=1, scale_min=1e-12):
+    """The step's hyperparameters as the array the C oracle takes (bias corrections for step t),
+    each rounded to fp32 as the library receives them (0.9 is not an fp32 value: the update is
+    defined on the parameters actually passed)."""
+    v = [lr_w, lr_s, beta1, beta2, eps, weight_decay, 1.0 - beta1 ** step, 1.0 - beta2 ** step, scale_min]
+    return np.array(v, dtype=np.float32).astype(np.float64)
+
+
+def lsq_adam_step(w, scale, g, gs, m_w, v_w, m_s, v_s, hp, ext_ds=None, with_w_hat=True):
+    """-> dict of w, scale, m_w, v_w, m_s, v_s (fp32), ds (f64 step-size gradient), w_hat (fp32)."""
+    w, scale, g = _c(w, np.float32), _c(scale, np.float32), _c(g, np.float32)
+    m_w, v_w, m_s, v_s = (_c(a, np.float32) for a in (m_w, v_w, m_s, v_s))
+    hp = _c(hp, np.float64)
+    d_out, d_in = w.shape
+    G = d_in // 32
+    out = {k: np.empty_like(a) for k, a in (("w", w), ("m_w", m_w), ("v_w", v_w))}
+    out.update({k: np.empty((d_out, G), np.float32) for k in ("scale", "m_s", "v_s")})
+    out["ds"] = np.empty((d_out, G), np.float64)
+    out["w_hat"] = np.empty_like(w) if with_w_hat else None
+    ext = None if ext_ds is None else _c(ext_ds, np.float64)
+    _L().orc_lsq_adam_step(_p(w), _p(scale), _p(g), d_out, d_in, float(gs), _p(m_w), _p(v_w), _p(m_s), _p(v_s),
+                           _p(hp), _p(ext), _p(out["w"]), _p(out["scale"]), _p(out["m_w"]), _p(out["v_w"]),
+                           _p(out["m_s"]), _p(out["v_s"]), _p(out["ds"]), _p(out["w_hat"]))
+    return out

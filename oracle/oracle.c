@@ -337,3 +337,67 @@ void orc_gemm_cols_mode(const uint16_t* x, int64_t m, const uint8_t* packed, con
     }
   }
 }
+
+/* ------------------------------------------------------------ fused QAT update (Adam) */
+
+/*
+ * One optimisation step of QAT with LSQ ([blog] section 3: weights and step sizes are learned
+ * jointly; [card] "QAT Highlights": the forward emulates the deployment grid), for one linear:
+ * the LSQ / straight-through gradients of orc_lsq_bwd, then Adam on both (decoupled weight decay
+ * on W only; the step is kept at or above scale_min), and optionally the fake-quantised updated
+ * weights for the next forward.  hp = {lr_w, lr_s, beta1, beta2, eps, weight_decay, c1, c2,
+ * scale_min} with c1 = 1 - beta1^t, c2 = 1 - beta2^t.  Per element, in fp64:
+ *   m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) g^2
+ *   w = w - lr_w ((m / c1) / (sqrt(v / c2) + eps) + weight_decay w)
+ *   D = max(D - lr_s (m_s / c1) / (sqrt(v_s / c2) + eps), scale_min)
+ * ext_ds (nullable) replaces the computed step-size gradients (to check the update alone on
+ * given gradients).  Outputs are rounded to fp32 once.
+ */
+void orc_lsq_adam_step(const float* w, const float* scale, const float* gup, int64_t d_out,
+                       int64_t d_in, double gs, const float* m_w, const float* v_w,
+                       const float* m_s, const float* v_s, const double* hp, const double* ext_ds,
+                       float* w_out, float* scale_out, float* m_w_out, float* v_w_out,
+                       float* m_s_out, float* v_s_out, double* ds_out, float* w_hat_next) {
+  const double lr_w = hp[0], lr_s = hp[1], b1 = hp[2], b2 = hp[3], eps = hp[4], wd = hp[5];
+  const double c1 = hp[6], c2 = hp[7], smin = hp[8];
+  int64_t G = d_in / GROUP;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < d_out; ++r)
+    for (int64_t g = 0; g < G; ++g) {
+      int64_t gi = r * G + g;
+      double d = (double)scale[gi];
+      double acc = 0.0;
+      for (int64_t i = 0; i < GROUP; ++i) {
+        int64_t k = r * d_in + g * GROUP + i;
+        double wv = (double)w[k];
+        int q = orc_code(wv, d);
+        int in_range = (wv >= QMIN * d) && (wv <= QMAX * d);
+        double gw = in_range ? (double)gup[k] : 0.0;
+        double f = in_range ? (double)q - wv / d : (double)q;
+        acc += (double)gup[k] * f;
+        double m = b1 * (double)m_w[k] + (1.0 - b1) * gw;
+        double v = b2 * (double)v_w[k] + (1.0 - b2) * gw * gw;
+        double wn = wv - lr_w * ((m / c1) / (sqrt(v / c2) + eps) + wd * wv);
+        m_w_out[k] = (float)m;
+        v_w_out[k] = (float)v;
+        w_out[k] = (float)wn;
+      }
+      double ds = ext_ds ? ext_ds[gi] : gs * acc;
+      if (ds_out) ds_out[gi] = ds;
+      double ms = b1 * (double)m_s[gi] + (1.0 - b1) * ds;
+      double vs = b2 * (double)v_s[gi] + (1.0 - b2) * ds * ds;
+      double dn = d - lr_s * (ms / c1) / (sqrt(vs / c2) + eps);
+      if (dn < smin) dn = smin;
+      m_s_out[gi] = (float)ms;
+      v_s_out[gi] = (float)vs;
+      scale_out[gi] = (float)dn;
+      if (w_hat_next) {
+        double dd = (double)scale_out[gi]; /* the fp32 step the next forward uses */
+        for (int64_t i = 0; i < GROUP; ++i) {
+          int64_t k = r * d_in + g * GROUP + i;
+          int q = orc_code((double)w_out[k], dd);
+          w_hat_next[k] = (float)(dd * q);
+        }
+      }
+    }
+}

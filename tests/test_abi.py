@@ -24,7 +24,7 @@ def test_library_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"w4q_status_string", "w4q_version", "quant_hessian",
                           "quant_hessian_workspace_size", "quant_scale_search", "quant_pack",
-                          "lsq_fwd", "lsq_bwd", "w4a16_gemm", "w4a16_gemm_workspace_size",
+                          "lsq_fwd", "lsq_bwd", "lsq_adam_step", "w4a16_gemm", "w4a16_gemm_workspace_size",
                           "w4a16_gemm_dq", "w4a16_gemm_dq_workspace_size", "w4a16_gemm_dq_noalloc",
                           "w4a16_gemv_grouped",
                           "w4q_probe_read", "w4q_probe_mfma_bf16"}
@@ -168,3 +168,25 @@ def test_python_front_end_rejects_host_tensors():
     w = torch.zeros(4, 64)
     with pytest.raises(ValueError):
         w4q.lsq_fwd(w, torch.zeros(4, 2))
+
+
+def test_adam_step_argument_errors():
+    from w4a16_group_wise_amd._lib import AdamParams
+    L = w4q.lib()
+    ok = AdamParams(1e-3, 1e-4, 0.9, 0.999, 1e-8, 0.0, 0.1, 0.001, 1e-12)
+
+    def call(hp=ok, **kw):
+        a = dict(w=A, scale=A, g=A, d_out=4, d_in=64, m_w=A, v_w=A, m_s=A, v_s=A, ds=None, wh=None)
+        a.update(kw)
+        return L.lsq_adam_step(a["w"], a["scale"], a["g"], a["d_out"], a["d_in"], 0.5, a["m_w"], a["v_w"],
+                               a["m_s"], a["v_s"], ctypes.byref(hp) if hp is not None else None, a["ds"],
+                               a["wh"], None)
+    assert call(hp=None) == w4q.W4Q_EINVAL
+    assert call(m_w=None) == w4q.W4Q_EINVAL
+    for bad in (dict(beta1=1.0), dict(eps=0.0), dict(bias_c1=0.0), dict(bias_c2=1.5), dict(lr_w=-1.0),
+                dict(scale_min=0.0), dict(lr_s=float("nan"))):
+        hp = AdamParams(*[bad.get(f, getattr(ok, f)) for f, _ in AdamParams._fields_])
+        assert call(hp=hp) == w4q.W4Q_EINVAL, bad
+    assert call(d_in=48) == w4q.W4Q_ESHAPE
+    assert call(v_w=A + 4) == w4q.W4Q_EALIGN
+    assert call(wh=A + 8) == w4q.W4Q_EALIGN

@@ -455,3 +455,101 @@ def test_gemv_plan_graph_replays(dev):
         torch.cuda.synchronize()
         for y, e in zip(plan.outs, eager):
             assert torch.equal(y, e), f"replay {rep}"
+
+
+# Rows whose codes are zero except on a few of the channels where |x| is smallest, with widely
+# spread channel scales (lognormal sigma 2.5): the product is tiny next to sum |x|, so an error that
+# scales with sum |x| instead of sum |x * w_hat| would break the bound.  One-row (vector) and
+# 2..16-row (matrix-core) paths, single and grouped calls.
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_gemv_sparse_codes_on_small_activations(dev, m):
+    d_out, d_in = 256, 4096
+    x = synth.calib_x(38, 0, m, m, d_in, 2.5)
+    order = np.argsort(np.abs(bf16_bits_to_np(x[0])))          # smallest |x| first
+    rng = np.random.default_rng(38 + m)
+    q = np.zeros((d_out, d_in), np.int64)
+    for r in range(d_out):
+        nz = 1 + r % 4
+        pos = order[rng.choice(16, nz, replace=False)]          # among the 16 smallest channels
+        q[r, pos] = rng.choice([-8, -5, -1, 1, 3, 7], nz)
+    s = (rng.uniform(1e-3, 1e-2, (d_out, d_in // 32))).astype(np.float16).astype(np.float32)
+    w = (q * np.repeat(s, 32, axis=1)).astype(np.float32)      # exactly s * q
+    packed, s16 = oracle.pack(w, s)
+    pt = torch.from_numpy(packed).to(dev)
+    st = torch.from_numpy(s16.view(np.float16)).to(dev)
+    say("gemv sparse codes, m", m)
+    y = w4q.w4a16_gemm(dev_bf16(x, dev), pt, st).cpu().numpy()
+    yr, ya = oracle.gemm_cols(x, packed, s16)
+    check_gemm(y, yr, ya)
+    if m == 1:
+        yg = w4q.w4a16_gemv_grouped([dev_bf16(x, dev)] * 3, [pt] * 3, [st] * 3)
+        for t in yg:
+            check_gemm(t.cpu().numpy(), yr, ya)
+
+
+# ------------------------------------------------------- fused QAT update (LSQ + Adam, in place)
+def _adam_check(w0, s0, g, st, dev, step, rows=None, lr_w=1e-3, lr_s=1e-4, wd=0.01):
+    """One GPU step from state st (host arrays); checks it against the oracle fed the same inputs
+    and returns the GPU's new state."""
+    wt, sct, gt = dev_f32(w0, dev), dev_f32(s0, dev), dev_f32(g, dev)
+    mw, vw, ms, vs = (dev_f32(a, dev) for a in st)
+    wh, ds = w4q.lsq_adam_step(wt, sct, gt, GS, mw, vw, ms, vs, lr_w=lr_w, lr_s=lr_s, step=step,
+                               weight_decay=wd, scale_min=1e-8, with_w_hat_next=True, with_grad_scale=True)
+    torch.cuda.synchronize()
+    out = {k: t.cpu().numpy() for k, t in (("w", wt), ("scale", sct), ("m_w", mw), ("v_w", vw), ("m_s", ms),
+                                           ("v_s", vs), ("w_hat", wh), ("ds", ds))}
+    sel = slice(None) if rows is None else rows
+    hp = oracle.adam_hparams(lr_w, lr_s, weight_decay=wd, step=step, scale_min=1e-8)
+    o = oracle.lsq_adam_step(w0[sel], s0[sel], g[sel], GS, *(a[sel] for a in st), hp, with_w_hat=False)
+    # step-size gradient: the LSQ backward's bound
+    d = np.repeat(s0[sel].astype(np.float64), 32, axis=1)
+    wr = w0[sel].astype(np.float64)
+    q = np.array([[oracle.code(a, b) for a, b in zip(ra, rb)] for ra, rb in zip(wr, d)], np.float64)
+    m = (wr >= -8 * d) & (wr <= 7 * d)
+    f = np.where(m, q - wr / d, q)
+    G = w0.shape[1] // 32
+    gf = np.abs(g[sel] * f).reshape(-1, G, 32).sum(axis=2)
+    ga = np.abs(g[sel]).reshape(-1, G, 32).sum(axis=2)
+    assert np.all(np.abs(out["ds"][sel] - o["ds"]) <= LSQ_REL * GS * gf + GS * 2.0 ** -20 * ga)
+    # weights and their moments: a few fp32 roundings of each update
+    u = 2.0 ** -22
+    gw = np.where(m, g[sel], 0.0)
+    # the first moment can cancel (b1 m0 against (1 - b1) g): its rounding error scales with
+    # b1 |m0| + (1 - b1) |g|, not with |m|, and so does the update's
+    b1, b2, c1, c2 = hp[2], hp[3], hp[6], hp[7]
+    a_w = b1 * np.abs(st[0][sel]) + (1 - b1) * np.abs(gw)
+    assert np.all(np.abs(out["m_w"][sel] - o["m_w"]) <= u * a_w + 1e-37)
+    assert np.all(np.abs(out["v_w"][sel] - o["v_w"]) <= u * (b2 * st[1][sel] + (1 - b2) * gw * gw) + 1e-37)
+    upd = (a_w / c1) / (np.sqrt(o["v_w"].astype(np.float64) / c2) + 1e-8)
+    tol_w = 2.0 ** -22 * np.abs(o["w"]) + lr_w * 8 * 2.0 ** -24 * (upd + wd * np.abs(w0[sel]))
+    assert np.all(np.abs(out["w"][sel] - o["w"]) <= tol_w + 1e-37)
+    # the steps' update from the GPU's own gradient (stage-isolated), then the next forward on the
+    # GPU's updated weights and steps
+    o2 = oracle.lsq_adam_step(w0[sel], s0[sel], g[sel], GS, *(a[sel] for a in st), hp,
+                              ext_ds=out["ds"][sel].astype(np.float64), with_w_hat=False)
+    a_s = b1 * np.abs(st[2][sel]) + (1 - b1) * np.abs(out["ds"][sel].astype(np.float64))
+    us = (a_s / c1) / (np.sqrt(o2["v_s"].astype(np.float64) / c2) + 1e-8)
+    assert np.all(np.abs(out["m_s"][sel] - o2["m_s"]) <= u * a_s + 1e-37)
+    assert np.all(np.abs(out["v_s"][sel] - o2["v_s"]) <= u * np.abs(o2["v_s"]) + 1e-37)
+    assert np.all(np.abs(out["scale"][sel] - o2["scale"]) <= 2.0 ** -22 * np.abs(o2["scale"]) + lr_s * 8 * 2.0 ** -24 * us)
+    assert np.array_equal(out["w_hat"][sel], oracle.lsq_fwd(out["w"][sel], out["scale"][sel]))
+    return out
+
+
+@pytest.mark.parametrize("wl,rows", [("linear_256x512", None), ("mlp_8192x2048", 40)])
+def test_lsq_adam_steps(dev, wl, rows):
+    c = synth.WORKLOADS[wl]
+    lin = c.linears[0]
+    w = c.weight(0, lin)
+    g = c.grad(0, lin)
+    G = w.shape[1] // 32
+    rng = np.random.default_rng(8)
+    s = (np.abs(w.reshape(-1, G, 32)).max(axis=2) / 7 * rng.uniform(0.5, 1.1, (w.shape[0], G))).astype(np.float32)
+    st = (np.zeros_like(w), np.zeros_like(w), np.zeros_like(s), np.zeros_like(s))
+    sel = None if rows is None else np.sort(rng.choice(w.shape[0], rows, replace=False))
+    for step in (1, 2, 3):
+        say("lsq adam", wl, "step", step)
+        out = _adam_check(w, s, g, st, dev, step, rows=sel)
+        w, s = out["w"], out["scale"]
+        st = (out["m_w"], out["v_w"], out["m_s"], out["v_s"])
+        g = (g * np.float32(0.9) + np.float32(0.1)).astype(np.float32)     # a different upstream gradient

@@ -96,7 +96,7 @@ def _lsq_rows(w, sc, g, dev, rows):
 
 
 # ------------------------------------------------------------- MLP block (8192x2048 gate/up)
-@pytest.mark.parametrize("name", ["gate", "down"])
+@pytest.mark.parametrize("name", ["gate", "up", "down"])
 def test_mlp_block(dev, name):
     c = synth.WORKLOADS["mlp_8192x2048"]
     lin = {l.name: l for l in c.linears}[name]

@@ -7,16 +7,17 @@ computation runs in the library's kernels.  There is no CPU fallback: if the lib
 missing the calls raise.
 
 Entry points (same names as the C ABI):
-  quant_hessian, quant_scale_search, quant_pack, lsq_fwd, lsq_bwd, w4a16_gemm, w4a16_gemm_dq,
+  quant_hessian, quant_scale_search, quant_pack, lsq_fwd, lsq_bwd, lsq_adam_step, w4a16_gemm, w4a16_gemm_dq,
   w4a16_gemv_grouped (and GemvGroupPlan, the same call with its problem table marshalled once)
 """
 from ._lib import (LIB_PATH, W4Q_EALIGN, W4Q_EHIP, W4Q_EINVAL, W4Q_ESHAPE, W4Q_EUNSUPPORTED,
                    W4Q_GROUP, W4Q_OK, W4QError, lib, status_string, version)
-from .ops import (GemvGroupPlan, lsq_bwd, probe_mfma_bf16, probe_read, lsq_fwd, quant_hessian, quant_pack, quant_scale_search, w4a16_gemm,
+from .ops import (GemvGroupPlan, lsq_adam_step, lsq_bwd, probe_mfma_bf16, probe_read, lsq_fwd, quant_hessian, quant_pack, quant_scale_search, w4a16_gemm,
                   w4a16_gemm_dq, w4a16_gemv_grouped, workspace_size)
 
 __all__ = [
-    "quant_hessian", "quant_scale_search", "quant_pack", "lsq_fwd", "lsq_bwd", "w4a16_gemm", "w4a16_gemm_dq",
+    "quant_hessian", "quant_scale_search", "quant_pack", "lsq_fwd", "lsq_bwd", "lsq_adam_step", "w4a16_gemm",
+    "w4a16_gemm_dq",
     "w4a16_gemv_grouped", "GemvGroupPlan", "workspace_size", "probe_read", "probe_mfma_bf16",
     "W4QError", "lib", "LIB_PATH", "status_string", "version", "W4Q_GROUP", "W4Q_OK",
     "W4Q_EINVAL", "W4Q_ESHAPE", "W4Q_EALIGN", "W4Q_EUNSUPPORTED", "W4Q_EHIP",

@@ -27,6 +27,12 @@ class GemvProblem(ctypes.Structure):
                 ("y", ctypes.c_void_p), ("d_out", ctypes.c_int64), ("d_in", ctypes.c_int64)]
 
 
+class AdamParams(ctypes.Structure):
+    """w4q_adam_params of w4a16q.h"""
+    _fields_ = [(n, ctypes.c_float) for n in ("lr_w", "lr_s", "beta1", "beta2", "eps", "weight_decay",
+                                              "bias_c1", "bias_c2", "scale_min")]
+
+
 SIGNATURES = {
     "w4q_status_string": (ctypes.c_char_p, [_INT]),
     "w4q_version": (_INT, []),
@@ -36,6 +42,7 @@ SIGNATURES = {
     "quant_pack": (_INT, [_P, _P, _I64, _I64, _P, _P, _P]),
     "lsq_fwd": (_INT, [_P, _P, _I64, _I64, _P, _P]),
     "lsq_bwd": (_INT, [_P, _P, _P, _I64, _I64, _F, _P, _P, _P, _P]),
+    "lsq_adam_step": (_INT, [_P, _P, _P, _I64, _I64, _F, _P, _P, _P, _P, _P, _P, _P, _P]),
     "w4a16_gemm": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _INT, _P, _SZ, _P]),
     "w4a16_gemm_workspace_size": (_INT, [_I64, _I64, _I64, _P]),
     "w4a16_gemm_dq": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _INT, _P, _SZ, _P]),

@@ -112,6 +112,33 @@ int lsq_bwd(const float* w, const float* scale, const float* grad_w_hat, int64_t
                             w_hat, stream);
 }
 
+static bool finite_in(float v, float lo, float hi, bool lo_open) {
+  if (!(v == v) || v > hi) return false;  // NaN or above
+  return lo_open ? v > lo : v >= lo;
+}
+
+int lsq_adam_step(float* w, float* scale, const float* grad_w_hat, int64_t d_out, int64_t d_in,
+                  float grad_scale, float* m_w, float* v_w, float* m_s, float* v_s,
+                  const w4q_adam_params* hp, float* grad_scale_out, float* w_hat_next,
+                  hipStream_t stream) {
+  if (!w || !scale || !grad_w_hat || !m_w || !v_w || !m_s || !v_s || !hp) return W4Q_EINVAL;
+  const float big = 3.0e38f;
+  if (!finite_in(hp->lr_w, 0.0f, big, false) || !finite_in(hp->lr_s, 0.0f, big, false) ||
+      !finite_in(hp->beta1, 0.0f, 0.99999994f, false) || !finite_in(hp->beta2, 0.0f, 0.99999994f, false) ||
+      !finite_in(hp->eps, 0.0f, big, true) || !finite_in(hp->weight_decay, 0.0f, big, false) ||
+      !finite_in(hp->bias_c1, 0.0f, 1.0f, true) || !finite_in(hp->bias_c2, 0.0f, 1.0f, true) ||
+      !finite_in(hp->scale_min, 0.0f, big, true) || !(grad_scale == grad_scale))
+    return W4Q_EINVAL;
+  const int rc = check_wshape(d_out, d_in);
+  if (rc != W4Q_OK) return rc;
+  if (!aligned(w, 16) || !aligned(grad_w_hat, 16) || !aligned(m_w, 16) || !aligned(v_w, 16) ||
+      (w_hat_next && !aligned(w_hat_next, 16)) || !aligned(scale, 4) || !aligned(m_s, 4) ||
+      !aligned(v_s, 4) || (grad_scale_out && !aligned(grad_scale_out, 4)))
+    return W4Q_EALIGN;
+  return w4q_launch_lsq_adam(w, scale, grad_w_hat, d_out, d_in, grad_scale, m_w, v_w, m_s, v_s, *hp,
+                             grad_scale_out, w_hat_next, stream);
+}
+
 static int gemm_shape(int64_t m, int64_t d_out, int64_t d_in);
 
 static int gemm_args(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,

@@ -185,6 +185,9 @@ int w4q_launch_lsq_fwd(const float* w, const float* scale, int64_t d_out, int64_
 int w4q_launch_lsq_bwd(const float* w, const float* scale, const float* g, int64_t d_out,
                        int64_t d_in, float gs, float* grad_w, float* grad_scale, float* w_hat,
                        hipStream_t s);
+int w4q_launch_lsq_adam(float* w, float* scale, const float* g, int64_t d_out, int64_t d_in, float gs,
+                        float* m_w, float* v_w, float* m_s, float* v_s, const w4q_adam_params& hp,
+                        float* ds_out, float* w_hat, hipStream_t s);
 int w4q_launch_gemv(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
                     int64_t d_out, int64_t d_in, void* y, int y_dtype, hipStream_t s);
 bool w4q_gemv_group_fits(const w4q_gemv_problem* probs, int n);

@@ -14,13 +14,15 @@
 // contiguous (LPR * 16 bytes).  The lane keeps its group's activations as bf16 pairs in
 // registers, reused for all the rows of the wavefront.
 //
-// Dequantisation in registers: the nibble n = q + 8 goes into the top four mantissa bits of a
-// bf16 with exponent 2^7, giving the exact value 8 * (24 + q); v_dot2 multiplies two such codes
-// with two activations into an fp32 sum.  The constant part is removed per group by the same
-// dot2 chain run on the code q = 0 (bitwise the same sum when every code of the group is 0),
-// and the factor 8 is removed (exactly) after the row reduction.  The bias is 24/|q| times the
-// signal, so the fp32 sum error stays near 2^-24 * 31 * sum|x| per group.  The next chunk's
-// codes, scales and activations are loaded while the current chunk is being reduced.
+// Codes: every product x * q is formed exactly from the unbiased code.  The vector kernels
+// extract each two's-complement nibble sign-extended (v_bfe_i32), convert it to fp32 and
+// accumulate x * q with fused multiply-adds; the matrix-core kernel converts the codes to bf16
+// (exact small integers) for the products.  The group's scale multiplies the group's sum, in
+// fp32.  So the rounding error of a product is a few 2^-24 of sum |x * w_hat|, whatever the
+// codes and the spread of x (an offset encoding of the codes, x * (q + c) - x * c, would carry
+// an error of order 2^-24 c sum |x|, far above the product when the codes are mostly zero where
+// |x| is large).  The next chunk's codes, scales and activations are loaded while the current
+// chunk is being reduced.
 #include <atomic>
 
 #include "common.hpp"
@@ -29,33 +31,37 @@ namespace w4q {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr uint32_t kMask = 0x00780078u;  // mantissa bits 3..6 of each bf16 half
-constexpr uint32_t kC0 = 0x43404340u;    // bf16 pair 2^7 with the nibble bias folded in
-constexpr uint32_t kZero = 0x43404340u;  // code q = 0 (n = 8) in both halves
 
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
-                                         false);
+// code i (0..7) of a dword of 8 two's-complement nibbles (nibble i at bits 4i..4i+3), exactly
+__device__ __forceinline__ float code_f32(uint32_t v, int i) {
+  // the builtin's result type is unsigned: the sign-extended field is taken back as int
+  return static_cast<float>(static_cast<int>(__builtin_amdgcn_sbfe(v, 4 * i, 4)));
 }
 
-// 8 activations x[8b .. 8b+7] as 4 dwords (x0,x1)(x2,x3)(x4,x5)(x6,x7) -> the pairs
-// (x0,x4)(x1,x5)(x2,x6)(x3,x7) that match the nibble pairs extracted below.
-__device__ __forceinline__ void pair_x(const u32x4 d, uint32_t* p) {
-  p[0] = __builtin_amdgcn_perm(d.z, d.x, 0x05040100u);
-  p[1] = __builtin_amdgcn_perm(d.z, d.x, 0x07060302u);
-  p[2] = __builtin_amdgcn_perm(d.w, d.y, 0x05040100u);
-  p[3] = __builtin_amdgcn_perm(d.w, d.y, 0x07060302u);
+// the 8 codes of a dword as four bf16 pairs (codes 2j, 2j + 1), exact
+__device__ __forceinline__ u32x4 codes_bf16x8(uint32_t v) {
+  uint32_t p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    p[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{code_f32(v, 2 * j), code_f32(v, 2 * j + 1)}, bf16x2));
+  return u32x4{p[0], p[1], p[2], p[3]};
 }
 
-// 8 two's-complement nibbles (one dword) -> 4 bf16 pairs (nibble i with i+4) holding
-// 8 * (24 + q).  ((v >> s) & mask) ^ c0 moves a nibble to mantissa bits 3..6 and flips its top
-// bit (two's complement -> offset binary n = q + 8) while inserting the exponent; the
-// compiler emits one v_bitop3 per pair with mask in an SGPR and c0 in a VGPR.
-__device__ __forceinline__ void codes_bf16(uint32_t v, uint32_t mask, uint32_t c0, uint32_t* c) {
-  c[0] = ((v << 3) & mask) ^ c0;
-  c[1] = ((v >> 1) & mask) ^ c0;
-  c[2] = ((v >> 5) & mask) ^ c0;
-  c[3] = ((v >> 9) & mask) ^ c0;
+// 8 activations (4 dwords of bf16 pairs) as fp32, in order
+__device__ __forceinline__ void x_f32(const u32x4 d, float* o) {
+  const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    o[2 * j] = bf16_lo(w[j]);
+    o[2 * j + 1] = bf16_hi(w[j]);
+  }
+}
+
+// sum_{i < 8} x[i] * code i of v, added to a (fused multiply-adds, exact products)
+__device__ __forceinline__ float dot8(const float* x, uint32_t v, float a) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = __builtin_fmaf(x[i], code_f32(v, i), a);
+  return a;
 }
 
 template <int MT, int RS>
@@ -70,7 +76,7 @@ template <int MT, int LPR, int RS>
 __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, int m_rows,
                                           const uint8_t* __restrict__ packed,
                                           const uint16_t* __restrict__ s16, int64_t d_out, int64_t d_in,
-                                          void* __restrict__ y, int y_dtype, uint32_t mask, int64_t block) {
+                                          void* __restrict__ y, int y_dtype, int64_t block) {
   constexpr int RPS = 64 / LPR;  // rows per row-step
   const int lane = threadIdx.x & 63;
   const int sub = lane / LPR;
@@ -80,8 +86,6 @@ __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, int m_
   if (row0 >= d_out) return;  // uniform per wavefront
   const int G = static_cast<int>(d_in / kGroup);
   const int nchunk = G / LPR;
-  uint32_t c0 = kC0;
-  asm volatile("" : "+v"(c0));  // keep the constant in a VGPR so v_bitop3 can take it
 
   // per row-step base pointers (64-bit once), then 32-bit offsets per chunk
   const uint8_t* prow[RS];
@@ -118,32 +122,27 @@ __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, int m_
     for (int m = 0; m < MT; ++m) acc[rs][m] = 0.0f;
 
   auto compute = [&](const Chunk<MT, RS>& cur) {
-    // activations of this group, paired, plus the zero-code sum (same dot2 order as below)
-    uint32_t xp[MT][16];
-    float corr[MT];
+    float sums[RS][MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
+    for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) pair_x(m < m_rows ? cur.xv[m][b] : u32x4{0u, 0u, 0u, 0u}, &xp[m][4 * b]);
-      float a = 0.0f;
+      for (int m = 0; m < MT; ++m) sums[rs][m] = 0.0f;
+    // 8 activations at a time (as fp32), against dword b of every row's codes
 #pragma unroll
-      for (int i = 0; i < 16; ++i) a = dot2(xp[m][i], kZero, a);
-      corr[m] = a;
+    for (int b = 0; b < 4; ++b) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        float xf[8];
+        x_f32(m < m_rows ? cur.xv[m][b] : u32x4{0u, 0u, 0u, 0u}, xf);
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs) sums[rs][m] = dot8(xf, cur.code[rs][b], sums[rs][m]);
+      }
     }
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs) {
-      uint32_t cb[16];
-      const uint32_t words[4] = {cur.code[rs].x, cur.code[rs].y, cur.code[rs].z, cur.code[rs].w};
-#pragma unroll
-      for (int b = 0; b < 4; ++b) codes_bf16(words[b], mask, c0, &cb[4 * b]);
       const float sc = f16_bits_to_f32(static_cast<uint16_t>(cur.sc[rs]));
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        float a = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) a = dot2(xp[m][i], cb[i], a);
-        acc[rs][m] = __builtin_fmaf(sc, a - corr[m], acc[rs][m]);
-      }
+      for (int m = 0; m < MT; ++m) acc[rs][m] = __builtin_fmaf(sc, sums[rs][m], acc[rs][m]);
     }
   };
 
@@ -161,7 +160,7 @@ __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, int m_
     compute(cb);
   }
   if (c < nchunk) compute(ca);
-  // reduce the LPR lane partials of each row (fixed butterfly order); undo the factor 8
+  // reduce the LPR lane partials of each row (fixed butterfly order)
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs) {
     const int64_t n = row0 + rs * RPS + sub;
@@ -170,7 +169,6 @@ __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, int m_
       float v = acc[rs][m];
 #pragma unroll
       for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-      v *= 0.125f;
       if (j == 0 && rok[rs] && m < m_rows) {
         if (y_dtype == 0)
           reinterpret_cast<float*>(y)[m * d_out + n] = v;
@@ -186,22 +184,18 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint16_t* __restri
                                                         const uint8_t* __restrict__ packed,
                                                         const uint16_t* __restrict__ s16,
                                                         int64_t d_out, int64_t d_in,
-                                                        void* __restrict__ y, int y_dtype,
-                                                        uint32_t mask) {
-  gemv_body<MT, LPR, RS>(x, m_rows, packed, s16, d_out, d_in, y, y_dtype, mask, blockIdx.x);
+                                                        void* __restrict__ y, int y_dtype) {
+  gemv_body<MT, LPR, RS>(x, m_rows, packed, s16, d_out, d_in, y, y_dtype, blockIdx.x);
 }
 
 // ---- 2..16 activation rows on the matrix cores ------------------------------------------
 //
 // One v_mfma_f32_16x16x32_bf16 per (group, 16 rows of W) forms the 16 x 16 block of per-group
-// sums sum_{k in g} x[m][k] * 8 (24 + q[n][k]) for all activation rows at once (rows past
-// m_rows repeat the last one and are never stored); the code-0 product of the same activations
-// (one more product per group, shared by the tiles) is subtracted and the group's scale applied
-// in fp32, exactly as in the vector kernels above.  A operand: lane (q, m) = (lane / 16,
-// lane % 16) holds x[m][32 g + 8 q + e]; B operand: lane (q, n) holds the 8 codes of W row n
-// at the same offsets, as the nibble pairs of codes_bf16 (the activations are paired to match,
-// so the order of the 8 products inside the group is the same on both sides).  The result:
-// lane (q, n) holds rows m = 4 q + r of column n.
+// sums sum_{k in g} x[m][k] * q[n][k] for all activation rows at once (rows past m_rows repeat
+// the last one and are never stored), from the codes as exact bf16 integers; the group's scale
+// is applied in fp32.  A operand: lane (q, m) = (lane / 16, lane % 16) holds x[m][32 g + 8 q + e]
+// (e = 0..7); B operand: lane (q, n) holds the 8 codes of W row n at the same offsets.  The
+// result: lane (q, n) holds rows m = 4 q + r of column n.
 //
 // A workgroup owns 32 rows of W (two tiles; 16 rows, one tile, when d_out < 8192, where two
 // would leave too few workgroups); its wavefronts take d_in's 8-group batches
@@ -261,8 +255,6 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_mma_kernel(const uint16_t* _
   const int G = static_cast<int>(d_in / kGroup);
   const int nbat = (G + kMmaBatch - 1) / kMmaBatch;
   const int64_t nbase = (int64_t)blockIdx.x * (16 * kMmaTiles);
-  uint32_t c0 = kC0;
-  asm volatile("" : "+v"(c0));  // keep the constant in a VGPR so v_bitop3 can take it
 
   // rows of W past d_out read the last row (their columns are never stored)
   const uint8_t* prow[kMmaTiles];
@@ -276,7 +268,6 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_mma_kernel(const uint16_t* _
   }
   const int mr = nl < m_rows ? nl : m_rows - 1;
   const uint16_t* xrow = x + (int64_t)mr * d_in + 8 * q;
-  const u32x4 zero_codes = {kZero, kZero, kZero, kZero};
   const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
   // the loads of batch b, all issued at once; groups past G repeat the last one.  Every loaded
@@ -341,16 +332,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_mma_kernel(const uint16_t* _
 #pragma unroll
     for (int i = 0; i < kMmaBatch; ++i) {
       if (i >= nb) break;  // wavefront-uniform
-      uint32_t xp[4];
-      pair_x(xv[i], xp);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{xp[0], xp[1], xp[2], xp[3]});
-      const f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, zero_codes), zero4, 0, 0, 0);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, xv[i]);
 #pragma unroll
       for (int t = 0; t < kMmaTiles; ++t) {
-        uint32_t cb[4];
-        codes_bf16(B.cv[i / 4][t][i % 4], kMask, c0, cb);
         const f32x4 dv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            a, __builtin_bit_cast(bf16x8, u32x4{cb[0], cb[1], cb[2], cb[3]}), zero4, 0, 0, 0);
+            a, __builtin_bit_cast(bf16x8, codes_bf16x8(B.cv[i / 4][t][i % 4])), zero4, 0, 0, 0);
         uint32_t sbits;
         if constexpr (kVecScales)
           sbits = B.sc[t][i / 2] >> (16 * (i % 2));
@@ -358,7 +344,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_mma_kernel(const uint16_t* _
           sbits = B.s1[i][t];
         const float sc = f16_bits_to_f32(static_cast<uint16_t>(sbits));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[t][r] = __builtin_fmaf(sc, dv[r] - d0[r], acc[t][r]);
+        for (int r = 0; r < 4; ++r) acc[t][r] = __builtin_fmaf(sc, dv[r], acc[t][r]);
       }
     }
   };
@@ -387,15 +373,13 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_mma_kernel(const uint16_t* _
 #pragma unroll
     for (int r = 0; r < 4; ++r) part[wid][t][r][lane] = acc[t][r];
   __syncthreads();
-  // outputs: tile t, activation row m, column c; wavefront partials in order, then the factor
-  // 8 removed (exactly)
+  // outputs: tile t, activation row m, column c; wavefront partials in order
   for (int o = threadIdx.x; o < kMmaTiles * 256; o += kWaves * 64) {
     const int t = o >> 8, m = (o >> 4) & 15, c = o & 15;
     const int src = 16 * (m >> 2) + c;
     float v = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) v += part[w][t][m & 3][src];
-    v *= 0.125f;
     const int64_t n = nbase + 16 * t + c;
     if (m < m_rows && n < d_out) {
       if (y_dtype == 0)
@@ -498,9 +482,6 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(const GroupArgs a
   const int64_t W = static_cast<int64_t>(uniform_int(static_cast<int>(gridDim.x))) * (kThreads / 64);
   const int64_t w0 = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + uniform_int(threadIdx.x / 64);
   if (w0 >= nitems) return;  // uniform per wavefront; no barrier follows
-  uint32_t c0 = kC0;
-  asm volatile("" : "+v"(c0));  // keep the constant in a VGPR so v_bitop3 can take it
-  const uint32_t mask = kMask;
   const uint32_t xoff = static_cast<uint32_t>(j * kGroup);
 
   auto problem_of = [&](int64_t item) { return __builtin_popcountll(__ballot(fq <= item)); };
@@ -552,24 +533,19 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(const GroupArgs a
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs) acc[rs] = 0.0f;
   auto compute = [&](const Chunk<1, RS>& cur) {
-    uint32_t xp[16];
+    float sums[RS];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) pair_x(cur.xv[0][b], &xp[4 * b]);
-    float corr = 0.0f;
+    for (int rs = 0; rs < RS; ++rs) sums[rs] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) corr = dot2(xp[i], kZero, corr);
+    for (int b = 0; b < 4; ++b) {
+      float xf[8];
+      x_f32(cur.xv[0][b], xf);
 #pragma unroll
-    for (int rs = 0; rs < RS; ++rs) {
-      uint32_t cb[16];
-      const uint32_t words[4] = {cur.code[rs].x, cur.code[rs].y, cur.code[rs].z, cur.code[rs].w};
-#pragma unroll
-      for (int b = 0; b < 4; ++b) codes_bf16(words[b], mask, c0, &cb[4 * b]);
-      const float sc = f16_bits_to_f32(static_cast<uint16_t>(cur.sc[rs]));
-      float v = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v = dot2(xp[i], cb[i], v);
-      acc[rs] = __builtin_fmaf(sc, v - corr, acc[rs]);
+      for (int rs = 0; rs < RS; ++rs) sums[rs] = dot8(xf, cur.code[rs][b], sums[rs]);
     }
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs)
+      acc[rs] = __builtin_fmaf(f16_bits_to_f32(static_cast<uint16_t>(cur.sc[rs])), sums[rs], acc[rs]);
   };
   auto store = [&](void* y, int64_t row, float v) {
     if (ydt == 0)
@@ -577,8 +553,8 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(const GroupArgs a
     else
       global_ptr(reinterpret_cast<uint16_t*>(y))[row] = f32_to_bf16_bits(v);
   };
-  // reduce the lane partials of each row of `item` (fixed order), undo the factor 8, store, and
-  // restart the accumulators
+  // reduce the lane partials of each row of `item` (fixed order), store, and restart the
+  // accumulators
   auto finish = [&](int64_t item) {
     const int p = problem_of(item);
     const int64_t d_out = uniform_int(t.d_out[p]);
@@ -599,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(const GroupArgs a
       v += dpp<0x122>(v);   // row_ror:2
       v += dpp<0x121>(v);   // row_ror:1
       const int64_t row = r0 + (lane >> 4);
-      if ((lane & 15) == 0 && row < d_out) store(y, row, v * 0.125f);
+      if ((lane & 15) == 0 && row < d_out) store(y, row, v);
 #pragma unroll
       for (int rs = 0; rs < RS; ++rs) acc[rs] = 0.0f;
     } else {
@@ -610,7 +586,7 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(const GroupArgs a
         for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
         acc[rs] = 0.0f;
         const int64_t row = r0 + rs * RPS + sub;
-        if (j == 0 && row < d_out) store(y, row, v * 0.125f);
+        if (j == 0 && row < d_out) store(y, row, v);
       }
     }
   };
@@ -669,14 +645,14 @@ int launch_lpr(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16
   if (waves1 >= 4 * 1024) {
     const int64_t waves = (d_out + 4 * RPS - 1) / (4 * RPS);
     hipLaunchKernelGGL((gemv_kernel<MT, LPR, 4>), dim3(static_cast<unsigned>((waves + 3) / 4)),
-                       dim3(kThreads), 0, s, x, static_cast<int>(m), packed, s16, d_out, d_in, y, ydt, kMask);
+                       dim3(kThreads), 0, s, x, static_cast<int>(m), packed, s16, d_out, d_in, y, ydt);
   } else if (waves1 >= 2 * 1024) {
     const int64_t waves = (d_out + 2 * RPS - 1) / (2 * RPS);
     hipLaunchKernelGGL((gemv_kernel<MT, LPR, 2>), dim3(static_cast<unsigned>((waves + 3) / 4)),
-                       dim3(kThreads), 0, s, x, static_cast<int>(m), packed, s16, d_out, d_in, y, ydt, kMask);
+                       dim3(kThreads), 0, s, x, static_cast<int>(m), packed, s16, d_out, d_in, y, ydt);
   } else {
     hipLaunchKernelGGL((gemv_kernel<MT, LPR, 1>), dim3(static_cast<unsigned>((waves1 + 3) / 4)),
-                       dim3(kThreads), 0, s, x, static_cast<int>(m), packed, s16, d_out, d_in, y, ydt, kMask);
+                       dim3(kThreads), 0, s, x, static_cast<int>(m), packed, s16, d_out, d_in, y, ydt);
   }
   return w4q_launch_status();
 }

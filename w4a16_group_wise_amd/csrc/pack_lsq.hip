@@ -1,5 +1,6 @@
 // pack_lsq.hip -- the elementwise, HBM-bound steps: export onto the INT4 grid (quant_pack),
-// the LSQ fake-quant forward (lsq_fwd) and the straight-through / step-size backward (lsq_bwd).
+// the LSQ fake-quant forward (lsq_fwd), the straight-through / step-size backward (lsq_bwd), and
+// the fused QAT update (lsq_adam_step: backward + Adam on weights and steps + next forward).
 //
 // Each thread owns 8 consecutive weights of one row (a quarter of a 32-weight group), so a
 // wavefront reads and writes fully coalesced 32-byte pieces and 4 lanes share one group; the
@@ -157,6 +158,80 @@ __global__ __launch_bounds__(kThreads) void lsq_bwd_kernel(const float* __restri
   if ((t & 3) == 0) grad_scale[e0 / kGroup] = gs * acc;
 }
 
+// One QAT optimisation step ([blog] section 3: weights and step sizes learned jointly; [card]
+// "QAT Highlights"): the gradients of lsq_bwd_kernel, then AdamW on the weights and Adam on the
+// group's step (clamped at scale_min), in place; optionally the step-size gradient and the
+// fake-quantised updated weights (the next forward's w_hat).  Every lane of a group computes
+// the group's new step from the same reduced gradient (same bits), then the codes of its
+// updated weights at that step.
+template <bool kFwd>
+__global__ __launch_bounds__(kThreads) void lsq_adam_kernel(float* __restrict__ w, float* __restrict__ scale,
+                                                            const float* __restrict__ g, int64_t n8, float gs,
+                                                            float* __restrict__ m_w, float* __restrict__ v_w,
+                                                            float* __restrict__ m_s, float* __restrict__ v_s,
+                                                            w4q_adam_params hp, float* __restrict__ ds_out,
+                                                            float* __restrict__ w_hat) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const bool live = t < n8;
+  const int64_t e0 = (live ? t : 0) * kPer;
+  const int64_t grp = e0 / kGroup;
+  const float d = scale[grp];
+  float wv[8], gv[8], mv[8], vv[8];
+  auto ld8 = [&](const float* p, float (&o)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p + e0);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + e0 + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  };
+  auto st8 = [&](float* p, const float (&o)[8]) {
+    *reinterpret_cast<f32x4*>(p + e0) = f32x4{o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<f32x4*>(p + e0 + 4) = f32x4{o[4], o[5], o[6], o[7]};
+  };
+  ld8(w, wv);
+  ld8(g, gv);
+  ld8(m_w, mv);
+  ld8(v_w, vv);
+  const float b1 = hp.beta1, b2 = hp.beta2;
+  float acc = 0.0f;
+  const Coder code(d);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float q = code(wv[i]);
+    const bool in = (__builtin_fmaf(8.0f, d, wv[i]) >= 0.0f) && (__builtin_fmaf(-7.0f, d, wv[i]) <= 0.0f);
+    const float gw = in ? gv[i] : 0.0f;
+    const float f = in ? q - wv[i] / d : q;
+    acc = __builtin_fmaf(gv[i], f, acc);
+    mv[i] = b1 * mv[i] + (1.0f - b1) * gw;
+    vv[i] = b2 * vv[i] + (1.0f - b2) * (gw * gw);
+    const float upd = (mv[i] / hp.bias_c1) / (__builtin_sqrtf(vv[i] / hp.bias_c2) + hp.eps);
+    wv[i] = wv[i] - hp.lr_w * (upd + hp.weight_decay * wv[i]);
+  }
+  // 4 lanes (32 weights) per group: butterfly over lane bits 0 and 1 (same sum in all four)
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  const float ds = gs * acc;
+  const float ms = b1 * m_s[grp] + (1.0f - b1) * ds;
+  const float vs = b2 * v_s[grp] + (1.0f - b2) * (ds * ds);
+  const float dn = __builtin_fmaxf(d - hp.lr_s * ((ms / hp.bias_c1) / (__builtin_sqrtf(vs / hp.bias_c2) + hp.eps)),
+                                   hp.scale_min);
+  if (!live) return;
+  st8(w, wv);
+  st8(m_w, mv);
+  st8(v_w, vv);
+  if ((t & 3) == 0) {
+    scale[grp] = dn;
+    m_s[grp] = ms;
+    v_s[grp] = vs;
+    if (ds_out != nullptr) ds_out[grp] = ds;
+  }
+  if (kFwd) {
+    const Coder next(dn);
+    float wh[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wh[i] = dn * next(wv[i]);
+    st8(w_hat, wh);
+  }
+}
+
 inline unsigned blocks_for(int64_t n8) { return static_cast<unsigned>((n8 + kThreads - 1) / kThreads); }
 
 }  // namespace
@@ -190,5 +265,18 @@ int w4q_launch_lsq_bwd(const float* w, const float* scale, const float* g, int64
   else
     hipLaunchKernelGGL(lsq_bwd_kernel<false>, dim3(blocks_for(n8)), dim3(kThreads), 0, s, w,
                        scale, g, n8, gs, grad_w, grad_scale, w_hat);
+  return w4q_launch_status();
+}
+
+int w4q_launch_lsq_adam(float* w, float* scale, const float* g, int64_t d_out, int64_t d_in, float gs,
+                        float* m_w, float* v_w, float* m_s, float* v_s, const w4q_adam_params& hp,
+                        float* ds_out, float* w_hat, hipStream_t s) {
+  const int64_t n8 = d_out * d_in / kPer;
+  if (w_hat)
+    hipLaunchKernelGGL(lsq_adam_kernel<true>, dim3(blocks_for(n8)), dim3(kThreads), 0, s, w, scale, g, n8, gs,
+                       m_w, v_w, m_s, v_s, hp, ds_out, w_hat);
+  else
+    hipLaunchKernelGGL(lsq_adam_kernel<false>, dim3(blocks_for(n8)), dim3(kThreads), 0, s, w, scale, g, n8, gs,
+                       m_w, v_w, m_s, v_s, hp, ds_out, w_hat);
   return w4q_launch_status();
 }

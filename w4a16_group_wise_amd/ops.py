@@ -153,6 +153,34 @@ def lsq_bwd(w: torch.Tensor, scale: torch.Tensor, grad_w_hat: torch.Tensor, grad
     return gw, gsc, wh
 
 
+def lsq_adam_step(w: torch.Tensor, scale: torch.Tensor, grad_w_hat: torch.Tensor, grad_scale: float,
+                  m_w: torch.Tensor, v_w: torch.Tensor, m_s: torch.Tensor, v_s: torch.Tensor, *,
+                  lr_w: float, lr_s: float, step: int, beta1: float = 0.9, beta2: float = 0.999,
+                  eps: float = 1e-8, weight_decay: float = 0.0, scale_min: float = 1e-12,
+                  with_w_hat_next: bool = False, with_grad_scale: bool = False):
+    """One fused QAT step: updates w, scale and the four Adam moments in place; returns
+    (w_hat_next | None, grad_scale_out | None)."""
+    from ._lib import AdamParams
+    _need(w, "w", torch.float32)
+    d_out, d_in = w.shape
+    G = d_in // W4Q_GROUP
+    for t, n in ((grad_w_hat, "grad_w_hat"), (m_w, "m_w"), (v_w, "v_w")):
+        _need(t, n, torch.float32, (d_out, d_in), w.device)
+    for t, n in ((scale, "scale"), (m_s, "m_s"), (v_s, "v_s")):
+        _need(t, n, torch.float32, (d_out, G), w.device)
+    if step < 1:
+        raise ValueError("step counts from 1")
+    hp = AdamParams(lr_w, lr_s, beta1, beta2, eps, weight_decay, 1.0 - beta1 ** step, 1.0 - beta2 ** step,
+                    scale_min)
+    wh = torch.empty_like(w) if with_w_hat_next else None
+    ds = torch.empty((d_out, G), dtype=torch.float32, device=w.device) if with_grad_scale else None
+    check("lsq_adam_step", lib().lsq_adam_step(
+        w.data_ptr(), scale.data_ptr(), grad_w_hat.data_ptr(), d_out, d_in, float(grad_scale), m_w.data_ptr(),
+        v_w.data_ptr(), m_s.data_ptr(), v_s.data_ptr(), ctypes.byref(hp),
+        ds.data_ptr() if ds is not None else None, wh.data_ptr() if wh is not None else None, _stream(w)))
+    return wh, ds
+
+
 def _gemm(name: str, x: torch.Tensor, packed: torch.Tensor, scale_f16: torch.Tensor,
           out_dtype: torch.dtype, out: Optional[torch.Tensor], workspace: Optional[torch.Tensor] = None):
     _need(x, "x", torch.bfloat16)

@@ -14,11 +14,13 @@
 // contiguous (LPR * 16 bytes).  The lane keeps its group's activations as bf16 pairs in
 // registers, reused for all the rows of the wavefront.
 //
-// Codes: every product x * q is formed exactly from the unbiased code.  The vector kernels
-// extract each two's-complement nibble sign-extended (v_bfe_i32), convert it to fp32 and
-// accumulate x * q with fused multiply-adds; the matrix-core kernel converts the codes to bf16
-// (exact small integers) for the products.  The group's scale multiplies the group's sum, in
-// fp32.  So the rounding error of a product is a few 2^-24 of sum |x * w_hat|, whatever the
+// Codes: every product x * q is formed exactly from the unbiased code.  A dword of 8
+// two's-complement nibbles is spread into two dwords of signed bytes, each nibble in the high
+// half of its byte (one shift and two masks), so that every byte holds 16 q; one conversion per
+// byte (byte select with sign extension) gives 16 q in fp32.  The vector kernels accumulate
+// x * 16q with fused multiply-adds; the matrix-core kernel packs 16 q as bf16 (small integers,
+// exact) for the products.  The group's scale, times 1/16 (exact for every fp16 scale),
+// multiplies the group's sum, in fp32.  So the rounding error of a product is a few 2^-24 of sum |x * w_hat|, whatever the
 // codes and the spread of x (an offset encoding of the codes, x * (q + c) - x * c, would carry
 // an error of order 2^-24 c sum |x|, far above the product when the codes are mostly zero where
 // |x| is large).  The next chunk's codes, scales and activations are loaded while the current
@@ -32,19 +34,33 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// code i (0..7) of a dword of 8 two's-complement nibbles (nibble i at bits 4i..4i+3), exactly
-__device__ __forceinline__ float code_f32(uint32_t v, int i) {
-  // the builtin's result type is unsigned: the sign-extended field is taken back as int
-  return static_cast<float>(static_cast<int>(__builtin_amdgcn_sbfe(v, 4 * i, 4)));
+// the 8 codes of a dword of two's-complement nibbles (nibble i at bits 4i..4i+3), times 16, in
+// order: nibble i goes to the high half of byte i / 2 of one of two dwords, whose signed bytes
+// convert exactly (one byte-select conversion each)
+__device__ __forceinline__ void codes16_f32(uint32_t v, float* c) {
+  const uint32_t ev = (v << 4) & 0xF0F0F0F0u;  // nibbles 0, 2, 4, 6
+  const uint32_t od = v & 0xF0F0F0F0u;         // nibbles 1, 3, 5, 7
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c[2 * j] = static_cast<float>(static_cast<int8_t>(ev >> (8 * j)));
+    c[2 * j + 1] = static_cast<float>(static_cast<int8_t>(od >> (8 * j)));
+  }
 }
 
-// the 8 codes of a dword as four bf16 pairs (codes 2j, 2j + 1), exact
-__device__ __forceinline__ u32x4 codes_bf16x8(uint32_t v) {
+// the same 8 values (16 q) as four bf16 pairs (codes 2j, 2j + 1), exact
+__device__ __forceinline__ u32x4 codes16_bf16x8(uint32_t v) {
+  float c[8];
+  codes16_f32(v, c);
   uint32_t p[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    p[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{code_f32(v, 2 * j), code_f32(v, 2 * j + 1)}, bf16x2));
+    p[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{c[2 * j], c[2 * j + 1]}, bf16x2));
   return u32x4{p[0], p[1], p[2], p[3]};
+}
+
+// a group's fp16 scale times 1/16, the factor the codes above carry
+__device__ __forceinline__ float scale16(uint32_t bits) {
+  return f16_bits_to_f32(static_cast<uint16_t>(bits)) * 0.0625f;
 }
 
 // 8 activations (4 dwords of bf16 pairs) as fp32, in order
@@ -57,10 +73,12 @@ __device__ __forceinline__ void x_f32(const u32x4 d, float* o) {
   }
 }
 
-// sum_{i < 8} x[i] * code i of v, added to a (fused multiply-adds, exact products)
+// sum_{i < 8} x[i] * 16 * code i of v, added to a (fused multiply-adds, exact products)
 __device__ __forceinline__ float dot8(const float* x, uint32_t v, float a) {
+  float c[8];
+  codes16_f32(v, c);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a = __builtin_fmaf(x[i], code_f32(v, i), a);
+  for (int i = 0; i < 8; ++i) a = __builtin_fmaf(x[i], c[i], a);
   return a;
 }
 
@@ -140,7 +158,7 @@ __device__ __forceinline__ void gemv_body(const uint16_t* __restrict__ x, int m_
     }
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs) {
-      const float sc = f16_bits_to_f32(static_cast<uint16_t>(cur.sc[rs]));
+      const float sc = scale16(cur.sc[rs]);
 #pragma unroll
       for (int m = 0; m < MT; ++m) acc[rs][m] = __builtin_fmaf(sc, sums[rs][m], acc[rs][m]);
     }
@@ -336,13 +354,13 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_mma_kernel(const uint16_t* _
 #pragma unroll
       for (int t = 0; t < kMmaTiles; ++t) {
         const f32x4 dv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            a, __builtin_bit_cast(bf16x8, codes_bf16x8(B.cv[i / 4][t][i % 4])), zero4, 0, 0, 0);
+            a, __builtin_bit_cast(bf16x8, codes16_bf16x8(B.cv[i / 4][t][i % 4])), zero4, 0, 0, 0);
         uint32_t sbits;
         if constexpr (kVecScales)
           sbits = B.sc[t][i / 2] >> (16 * (i % 2));
         else
           sbits = B.s1[i][t];
-        const float sc = f16_bits_to_f32(static_cast<uint16_t>(sbits));
+        const float sc = scale16(sbits);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[t][r] = __builtin_fmaf(sc, dv[r], acc[t][r]);
       }
@@ -545,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(const GroupArgs a
     }
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs)
-      acc[rs] = __builtin_fmaf(f16_bits_to_f32(static_cast<uint16_t>(cur.sc[rs])), sums[rs], acc[rs]);
+      acc[rs] = __builtin_fmaf(scale16(cur.sc[rs]), sums[rs], acc[rs]);
   };
   auto store = [&](void* y, int64_t row, float v) {
     if (ydt == 0)

@@ -15,6 +15,14 @@ Functions and the passages they follow (page titles and sections):
   pack                      -- model card "QAT Highlights" / "Quickstart"; blog "Conclusion".
   lsq_fwd, lsq_bwd          -- blog section 3 (LSQ forward, STE, normalised scale gradient).
   gemm_cols                 -- model card intro (W4A16: INT4 weights, 16-bit activations).
+  group=d_in in pack / lsq_* / gemm_cols, scale_search_pc
+                            -- model card intro and "Quickstart" (per-channel symmetric INT4:
+                               one scale per output row, the whole row as the group).
+  joint_objective, joint_refine
+                            -- model card "Quantization Configuration" objective over a whole
+                               row with the full H, and coordinate descent over the row's groups.
+  lsq_adam_step             -- blog section 3 / model card "QAT Highlights" (weights and steps
+                               learned together), with Adam as the optimiser.
 """
 from __future__ import annotations
 
@@ -70,6 +78,13 @@ def _L():
         lib.orc_lsq_fwd.argtypes = [P, P, I, I, P]
         lib.orc_lsq_bwd.argtypes = [P, P, P, I, I, ctypes.c_double, P, P, P]
         lib.orc_gemm_cols_mode.argtypes = [P, I, P, P, I, P, I, ctypes.c_int, P, P]
+        lib.orc_scale_search_pc.argtypes = [P, I, P, I, P, ctypes.c_int, P, I, P, P, P, P]
+        lib.orc_pack_g.argtypes = [P, P, I, I, I, P, P]
+        lib.orc_lsq_fwd_g.argtypes = [P, P, I, I, I, P]
+        lib.orc_lsq_bwd_g.argtypes = [P, P, P, I, I, I, ctypes.c_double, P, P, P]
+        lib.orc_gemm_cols_g.argtypes = [P, I, P, P, I, I, P, I, ctypes.c_int, P, P]
+        lib.orc_joint_objective.argtypes = [P, P, I, P, I, P, I, P]
+        lib.orc_joint_refine.argtypes = [P, I, P, I, P, ctypes.c_int, P, I, ctypes.c_int, P, P, P, P, P]
         lib.orc_lsq_adam_step.argtypes = [P, P, P, I, I, ctypes.c_double, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.orc_round_bf16.restype = ctypes.c_double
         lib.orc_round_bf16.argtypes = [ctypes.c_double]
@@ -170,41 +185,43 @@ def scale_search_groups(w: np.ndarray, h: np.ndarray, alpha: np.ndarray, rows: n
     return scale, idx, obj, obj_all
 
 
-def pack(w: np.ndarray, scale: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+def pack(w: np.ndarray, scale: np.ndarray, group: int = 32) -> Tuple[np.ndarray, np.ndarray]:
+    """group = 32 ([blog] grid) or d_in (one scale per row)."""
     w = _c(w, np.float32)
     scale = _c(scale, np.float32)
     d_out, d_in = w.shape
     packed = np.empty((d_out, d_in // 2), np.uint8)
-    s16 = np.empty((d_out, d_in // 32), np.uint16)
-    _L().orc_pack(_p(w), _p(scale), d_out, d_in, _p(packed), _p(s16))
+    s16 = np.empty((d_out, d_in // group), np.uint16)
+    _L().orc_pack_g(_p(w), _p(scale), d_out, d_in, group, _p(packed), _p(s16))
     return packed, s16
 
 
-def lsq_fwd(w: np.ndarray, scale: np.ndarray) -> np.ndarray:
+def lsq_fwd(w: np.ndarray, scale: np.ndarray, group: int = 32) -> np.ndarray:
     w = _c(w, np.float32)
     scale = _c(scale, np.float32)
     out = np.empty_like(w)
-    _L().orc_lsq_fwd(_p(w), _p(scale), w.shape[0], w.shape[1], _p(out))
+    _L().orc_lsq_fwd_g(_p(w), _p(scale), w.shape[0], w.shape[1], group, _p(out))
     return out
 
 
-def lsq_bwd(w: np.ndarray, scale: np.ndarray, g: np.ndarray, gs: float):
-    """-> (grad_w f32, grad_scale f64 [d_out][G], w_hat f32)."""
+def lsq_bwd(w: np.ndarray, scale: np.ndarray, g: np.ndarray, gs: float, group: int = 32):
+    """-> (grad_w f32, grad_scale f64 [d_out][d_in / group], w_hat f32)."""
     w = _c(w, np.float32)
     scale = _c(scale, np.float32)
     g = _c(g, np.float32)
     gw = np.empty_like(w)
-    gsc = np.empty((w.shape[0], w.shape[1] // 32), np.float64)
+    gsc = np.empty((w.shape[0], w.shape[1] // group), np.float64)
     wh = np.empty_like(w)
-    _L().orc_lsq_bwd(_p(w), _p(scale), _p(g), w.shape[0], w.shape[1], float(gs), _p(gw),
-                     _p(gsc), _p(wh))
+    _L().orc_lsq_bwd_g(_p(w), _p(scale), _p(g), w.shape[0], w.shape[1], group, float(gs), _p(gw),
+                       _p(gsc), _p(wh))
     return gw, gsc, wh
 
 
 def gemm_cols(x_bf16: np.ndarray, packed: np.ndarray, s16: np.ndarray,
-              cols: Optional[np.ndarray] = None, dequant_bf16: bool = False):
+              cols: Optional[np.ndarray] = None, dequant_bf16: bool = False, group: int = 32):
     """-> (y f64 [m][len(cols)], yabs f64 [m][len(cols)]) with yabs = sum |x * w_hat|.
-    w_hat = s16 * q exactly, or bf16_RNE(s16 * q) with dequant_bf16."""
+    w_hat = s16 * q exactly, or bf16_RNE(s16 * q) with dequant_bf16; s16 holds d_in / group
+    scales per row."""
     x = _c(x_bf16, np.uint16)
     packed = _c(packed, np.uint8)
     s16 = _c(s16, np.uint16)
@@ -214,9 +231,56 @@ def gemm_cols(x_bf16: np.ndarray, packed: np.ndarray, s16: np.ndarray,
     cols = _c(cols, np.int64)
     y = np.empty((m, cols.shape[0]), np.float64)
     ya = np.empty_like(y)
-    _L().orc_gemm_cols_mode(_p(x), m, _p(packed), _p(s16), d_in, _p(cols), cols.shape[0],
-                            1 if dequant_bf16 else 0, _p(y), _p(ya))
+    _L().orc_gemm_cols_g(_p(x), m, _p(packed), _p(s16), d_in, group, _p(cols), cols.shape[0],
+                         1 if dequant_bf16 else 0, _p(y), _p(ya))
     return y, ya
+
+
+def scale_search_pc(w: np.ndarray, h: np.ndarray, alpha: np.ndarray, rows: Optional[np.ndarray] = None,
+                    with_all: bool = False):
+    """Per-channel search (whole row, full H) on rows (all by default).
+    -> (scale f32 [cnt], idx u8 [cnt], obj f64 [cnt], obj_all f64 [cnt][K] | None)."""
+    w = _c(w, np.float32)
+    h = _c(h, np.float32)
+    alpha = _c(alpha, np.float32)
+    rows = _c(np.arange(w.shape[0]) if rows is None else rows, np.int64)
+    cnt, K = rows.shape[0], alpha.shape[0]
+    scale = np.empty(cnt, np.float32)
+    idx = np.empty(cnt, np.uint8)
+    obj = np.empty(cnt, np.float64)
+    obj_all = np.empty((cnt, K), np.float64) if with_all else None
+    _L().orc_scale_search_pc(_p(w), w.shape[1], _p(h), h.shape[1], _p(alpha), K, _p(rows), cnt,
+                             _p(scale), _p(idx), _p(obj), _p(obj_all))
+    return scale, idx, obj, obj_all
+
+
+def joint_objective(w: np.ndarray, scale: np.ndarray, h: np.ndarray, rows: Optional[np.ndarray] = None):
+    """e^T H e per selected row with the full H, e = w - w_hat on the given group-32 steps."""
+    w = _c(w, np.float32)
+    scale = _c(scale, np.float32)
+    h = _c(h, np.float32)
+    rows = _c(np.arange(w.shape[0]) if rows is None else rows, np.int64)
+    obj = np.empty(rows.shape[0], np.float64)
+    _L().orc_joint_objective(_p(w), _p(scale), w.shape[1], _p(h), h.shape[1], _p(rows), rows.shape[0], _p(obj))
+    return obj
+
+
+def joint_refine(w: np.ndarray, h: np.ndarray, alpha: np.ndarray, idx: np.ndarray,
+                 rows: Optional[np.ndarray] = None, n_sweeps: int = 2):
+    """Coordinate descent over the groups of each selected row on the joint objective, from the
+    start idx [cnt][G].  -> dict idx, scale, obj, margin, sweeps."""
+    w = _c(w, np.float32)
+    h = _c(h, np.float32)
+    alpha = _c(alpha, np.float32)
+    rows = _c(np.arange(w.shape[0]) if rows is None else rows, np.int64)
+    cnt, G = rows.shape[0], w.shape[1] // 32
+    out = {"idx": np.array(idx, dtype=np.uint8, copy=True).reshape(cnt, G),
+           "scale": np.empty((cnt, G), np.float32), "obj": np.empty(cnt, np.float64),
+           "margin": np.empty(cnt, np.float64), "sweeps": np.empty(cnt, np.int32)}
+    _L().orc_joint_refine(_p(w), w.shape[1], _p(h), h.shape[1], _p(alpha), alpha.shape[0], _p(rows), cnt,
+                          int(n_sweeps), _p(out["idx"]), _p(out["scale"]), _p(out["obj"]), _p(out["margin"]),
+                          _p(out["sweeps"]))
+    return out
 
 
 ADAM_KEYS = ("lr_w", "lr_s", "beta1", "beta2", "eps", "weight_decay", "step", "scale_min")

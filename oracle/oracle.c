@@ -157,26 +157,29 @@ void orc_hessian_entries(const uint16_t* x, int64_t n, int64_t d, const int64_t*
 /* ------------------------------------------------------------------ scale search */
 
 /*
- * One group ([card] "Quantization Configuration" objective, read per group of 32 with the
- * group's diagonal block of H): returns the chosen index, its scale and objective, and
- * optionally every candidate's objective.  hg points at H[32g][32g] with row stride ldh.
+ * One group of n consecutive weights ([card] "Quantization Configuration" objective, read per
+ * group with the group's diagonal block of H): returns the chosen index, its scale and
+ * objective, and optionally every candidate's objective.  hg points at the block's first entry
+ * with row stride ldh.  n = 32 is the [blog] group; n = d_in is one scale per output row (the
+ * [card] per-channel checkpoint), where the block is the whole H.
  */
-static void search_group(const float* wg, const float* hg, int64_t ldh, const float* alpha, int K,
-                         float* scale, uint8_t* idx, double* obj, double* obj_all) {
+static void search_span(const float* wg, int64_t n, const float* hg, int64_t ldh,
+                        const float* alpha, int K, float* scale, uint8_t* idx, double* obj,
+                        double* obj_all) {
   float amax = 0.0f;
-  for (int i = 0; i < GROUP; ++i)
+  for (int64_t i = 0; i < n; ++i)
     if (fabsf(wg[i]) > amax) amax = fabsf(wg[i]);
+  double* e = (double*)malloc((size_t)n * sizeof(double));
   double best = INFINITY;
   int kbest = 0;
   float dbest = 0.0f;
   for (int k = 0; k < K; ++k) {
     float dk = orc_candidate(amax, alpha[k]);
     double d = (double)dk;
-    double e[GROUP];
-    for (int i = 0; i < GROUP; ++i) e[i] = (double)wg[i] - d * (double)orc_code((double)wg[i], d);
+    for (int64_t i = 0; i < n; ++i) e[i] = (double)wg[i] - d * (double)orc_code((double)wg[i], d);
     double o = 0.0;
-    for (int i = 0; i < GROUP; ++i)
-      for (int j = 0; j < GROUP; ++j) o += e[i] * (double)hg[i * ldh + j] * e[j];
+    for (int64_t i = 0; i < n; ++i)
+      for (int64_t j = 0; j < n; ++j) o += e[i] * (double)hg[i * ldh + j] * e[j];
     if (obj_all) obj_all[k] = o;
     if (o < best) { /* strict: the first minimum wins */
       best = o;
@@ -184,9 +187,15 @@ static void search_group(const float* wg, const float* hg, int64_t ldh, const fl
       dbest = dk;
     }
   }
+  free(e);
   *scale = dbest;
   *idx = (uint8_t)kbest;
   *obj = best;
+}
+
+static void search_group(const float* wg, const float* hg, int64_t ldh, const float* alpha, int K,
+                         float* scale, uint8_t* idx, double* obj, double* obj_all) {
+  search_span(wg, GROUP, hg, ldh, alpha, K, scale, idx, obj, obj_all);
 }
 
 /* Every group of W [d_out][d_in].  obj [d_out][G]; obj_all [d_out][G][K] or NULL. */
@@ -215,6 +224,17 @@ void orc_scale_search_groups(const float* w, int64_t d_in, const float* h, int64
   }
 }
 
+/* Per-channel search on selected rows: the whole row is one group and H is used in full.
+ * Outputs indexed by c: scale, idx, obj [cnt]; obj_all [cnt][K] or NULL. */
+void orc_scale_search_pc(const float* w, int64_t d_in, const float* h, int64_t ldh,
+                         const float* alpha, int K, const int64_t* rows, int64_t cnt, float* scale,
+                         uint8_t* idx, double* obj, double* obj_all) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t c = 0; c < cnt; ++c)
+    search_span(w + rows[c] * d_in, d_in, h, ldh, alpha, K, scale + c, idx + c, obj + c,
+                obj_all ? obj_all + c * K : 0);
+}
+
 /* ------------------------------------------------------------------------- export */
 
 /*
@@ -222,23 +242,28 @@ void orc_scale_search_groups(const float* w, int64_t d_in, const float* h, int64
  * "Conclusion"): fp16 scale, codes on that scale, two's-complement nibbles, low nibble
  * first.
  */
-void orc_pack(const float* w, const float* scale, int64_t d_out, int64_t d_in, uint8_t* packed,
-              uint16_t* s16) {
-  int64_t G = d_in / GROUP;
+void orc_pack_g(const float* w, const float* scale, int64_t d_out, int64_t d_in, int64_t gsz,
+                uint8_t* packed, uint16_t* s16) {
+  int64_t G = d_in / gsz;
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < d_out; ++r) {
     for (int64_t g = 0; g < G; ++g) {
       uint16_t hs = orc_f32_to_f16(scale[r * G + g]);
       s16[r * G + g] = hs;
       double d = orc_f16_to_f64(hs);
-      for (int64_t i = 0; i < GROUP; i += 2) {
-        int64_t k = g * GROUP + i;
+      for (int64_t i = 0; i < gsz; i += 2) {
+        int64_t k = g * gsz + i;
         int q0 = orc_code((double)w[r * d_in + k], d);
         int q1 = orc_code((double)w[r * d_in + k + 1], d);
         packed[r * (d_in / 2) + k / 2] = (uint8_t)((q0 & 0xF) | ((q1 & 0xF) << 4));
       }
     }
   }
+}
+
+void orc_pack(const float* w, const float* scale, int64_t d_out, int64_t d_in, uint8_t* packed,
+              uint16_t* s16) {
+  orc_pack_g(w, scale, d_out, d_in, GROUP, packed, s16);
 }
 
 /* Decode one packed code (two's-complement nibble). */
@@ -250,15 +275,20 @@ int orc_unpack(const uint8_t* packed_row, int64_t k) {
 /* ----------------------------------------------------------------------------- LSQ */
 
 /* [blog] section 3 forward: w_hat = Delta * code(w, Delta) with the fp32 learnable Delta. */
-void orc_lsq_fwd(const float* w, const float* scale, int64_t d_out, int64_t d_in, float* w_hat) {
-  int64_t G = d_in / GROUP;
+void orc_lsq_fwd_g(const float* w, const float* scale, int64_t d_out, int64_t d_in, int64_t gsz,
+                   float* w_hat) {
+  int64_t G = d_in / gsz;
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < d_out; ++r)
     for (int64_t k = 0; k < d_in; ++k) {
-      double d = (double)scale[r * G + k / GROUP];
+      double d = (double)scale[r * G + k / gsz];
       int q = orc_code((double)w[r * d_in + k], d);
       w_hat[r * d_in + k] = (float)(d * q); /* exact product, one rounding to fp32 */
     }
+}
+
+void orc_lsq_fwd(const float* w, const float* scale, int64_t d_out, int64_t d_in, float* w_hat) {
+  orc_lsq_fwd_g(w, scale, d_out, d_in, GROUP, w_hat);
 }
 
 /*
@@ -267,16 +297,17 @@ void orc_lsq_fwd(const float* w, const float* scale, int64_t d_out, int64_t d_in
  * d w_hat / d Delta = q - w/Delta inside, the clamp level outside, summed over the group and
  * multiplied by the normalisation factor gs.  Range test -8*D <= w <= 7*D is exact in fp64.
  */
-void orc_lsq_bwd(const float* w, const float* scale, const float* gup, int64_t d_out, int64_t d_in,
-                 double gs, float* grad_w, double* grad_scale, float* w_hat) {
-  int64_t G = d_in / GROUP;
+void orc_lsq_bwd_g(const float* w, const float* scale, const float* gup, int64_t d_out,
+                   int64_t d_in, int64_t gsz, double gs, float* grad_w, double* grad_scale,
+                   float* w_hat) {
+  int64_t G = d_in / gsz;
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < d_out; ++r)
     for (int64_t g = 0; g < G; ++g) {
       double d = (double)scale[r * G + g];
       double acc = 0.0;
-      for (int64_t i = 0; i < GROUP; ++i) {
-        int64_t k = r * d_in + g * GROUP + i;
+      for (int64_t i = 0; i < gsz; ++i) {
+        int64_t k = r * d_in + g * gsz + i;
         double wv = (double)w[k];
         int q = orc_code(wv, d);
         int in_range = (wv >= QMIN * d) && (wv <= QMAX * d);
@@ -287,6 +318,11 @@ void orc_lsq_bwd(const float* w, const float* scale, const float* gup, int64_t d
       }
       grad_scale[r * G + g] = gs * acc;
     }
+}
+
+void orc_lsq_bwd(const float* w, const float* scale, const float* gup, int64_t d_out, int64_t d_in,
+                 double gs, float* grad_w, double* grad_scale, float* w_hat) {
+  orc_lsq_bwd_g(w, scale, gup, d_out, d_in, GROUP, gs, grad_w, grad_scale, w_hat);
 }
 
 /* ------------------------------------------------------------------------ W4A16 GEMM */
@@ -316,9 +352,10 @@ double orc_round_bf16(double v) {
  *   dq = 0: w_hat = s16 * q exactly ([card] W4A16 deployment with the [blog] group grid);
  *   dq = 1: w_hat = bf16_RNE(s16 * q), the weight as a bf16 operand of the matrix product
  *           (dequantization to the 16-bit activation format before the product). */
-void orc_gemm_cols_mode(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
-                        int64_t d_in, const int64_t* cols, int64_t ncols, int dq, double* y, double* yabs) {
-  int64_t G = d_in / GROUP;
+void orc_gemm_cols_g(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
+                     int64_t d_in, int64_t gsz, const int64_t* cols, int64_t ncols, int dq, double* y,
+                     double* yabs) {
+  int64_t G = d_in / gsz;
 #pragma omp parallel for schedule(static)
   for (int64_t c = 0; c < ncols; ++c) {
     int64_t n = cols[c];
@@ -326,7 +363,7 @@ void orc_gemm_cols_mode(const uint16_t* x, int64_t m, const uint8_t* packed, con
     for (int64_t mi = 0; mi < m; ++mi) {
       double s = 0.0, sa = 0.0;
       for (int64_t k = 0; k < d_in; ++k) {
-        double wh = orc_f16_to_f64(s16[n * G + k / GROUP]) * (double)orc_unpack(prow, k);
+        double wh = orc_f16_to_f64(s16[n * G + k / gsz]) * (double)orc_unpack(prow, k);
         if (dq) wh = orc_round_bf16(wh);
         double p = orc_bf16_to_f64(x[mi * d_in + k]) * wh;
         s += p;
@@ -336,6 +373,11 @@ void orc_gemm_cols_mode(const uint16_t* x, int64_t m, const uint8_t* packed, con
       if (yabs) yabs[mi * ncols + c] = sa;
     }
   }
+}
+
+void orc_gemm_cols_mode(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
+                        int64_t d_in, const int64_t* cols, int64_t ncols, int dq, double* y, double* yabs) {
+  orc_gemm_cols_g(x, m, packed, s16, d_in, GROUP, cols, ncols, dq, y, yabs);
 }
 
 /* ------------------------------------------------------------ fused QAT update (Adam) */
@@ -400,4 +442,113 @@ void orc_lsq_adam_step(const float* w, const float* scale, const float* gup, int
         }
       }
     }
+}
+
+/* ---------------------------------------------------- joint objective across groups */
+
+/* e = w - Delta_g * code(w, Delta_g) for one row, Delta_g = step[g] (fp32 as given), exact. */
+static void row_error(const float* wr, const double* step, int64_t d_in, double* e) {
+  for (int64_t k = 0; k < d_in; ++k) {
+    double d = step[k / GROUP];
+    e[k] = (double)wr[k] - d * (double)orc_code((double)wr[k], d);
+  }
+}
+
+/* e^T H e over the whole row, full H, plain index order. */
+static double row_form(const double* e, int64_t d_in, const float* h, int64_t ldh) {
+  double o = 0.0;
+  for (int64_t i = 0; i < d_in; ++i)
+    for (int64_t j = 0; j < d_in; ++j) o += e[i] * (double)h[i * ldh + j] * e[j];
+  return o;
+}
+
+/*
+ * The [card] "Quantization Configuration" objective read literally for one output row:
+ * ||(w - w_hat) X||^2 = e^T H e with the full H, which couples the groups of the row through the
+ * off-diagonal blocks of H.  w_hat is the group-32 grid on the given fp32 steps scale[r][g].
+ * Selected rows; obj [cnt].
+ */
+void orc_joint_objective(const float* w, const float* scale, int64_t d_in, const float* h,
+                         int64_t ldh, const int64_t* rows, int64_t cnt, double* obj) {
+  int64_t G = d_in / GROUP;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t c = 0; c < cnt; ++c) {
+    int64_t r = rows[c];
+    double* step = (double*)malloc((size_t)G * sizeof(double));
+    double* e = (double*)malloc((size_t)d_in * sizeof(double));
+    for (int64_t g = 0; g < G; ++g) step[g] = (double)scale[r * G + g];
+    row_error(w + r * d_in, step, d_in, e);
+    obj[c] = row_form(e, d_in, h, ldh);
+    free(step);
+    free(e);
+  }
+}
+
+/*
+ * Coordinate descent over the groups of a row on that joint objective.  The start is one
+ * candidate index per group (idx, e.g. the per-group choice).  A sweep visits the groups in
+ * order; at group g each candidate step Delta_k = candidate(amax_g, alpha_k) is tried with the
+ * other groups held, its joint objective evaluated in full, and the first k with the smallest
+ * objective is kept.  The current index is one of the candidates, so the objective never rises.
+ * Sweeps repeat up to n_sweeps times and stop after one that changes nothing.
+ * Outputs per selected row c: idx [cnt][G] (in: start, out: result), scale [cnt][G] (the steps
+ * of the result), obj [cnt] (its joint objective), sweeps [cnt] (sweeps run), and margin [cnt]:
+ * over all decisions, the smallest (o_k - o_kept) / o_kept among candidates whose step differs
+ * from the kept one (+inf if none); a small margin marks a near-tie.
+ */
+void orc_joint_refine(const float* w, int64_t d_in, const float* h, int64_t ldh,
+                      const float* alpha, int K, const int64_t* rows, int64_t cnt, int n_sweeps,
+                      uint8_t* idx, float* scale, double* obj, double* margin, int* sweeps) {
+  int64_t G = d_in / GROUP;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t c = 0; c < cnt; ++c) {
+    const float* wr = w + rows[c] * d_in;
+    uint8_t* ir = idx + c * G;
+    float* cand = (float*)malloc((size_t)(G * K) * sizeof(float));
+    double* step = (double*)malloc((size_t)G * sizeof(double));
+    double* e = (double*)malloc((size_t)d_in * sizeof(double));
+    double* o = (double*)malloc((size_t)K * sizeof(double));
+    for (int64_t g = 0; g < G; ++g) {
+      float amax = 0.0f;
+      for (int i = 0; i < GROUP; ++i)
+        if (fabsf(wr[g * GROUP + i]) > amax) amax = fabsf(wr[g * GROUP + i]);
+      for (int k = 0; k < K; ++k) cand[g * K + k] = orc_candidate(amax, alpha[k]);
+      step[g] = (double)cand[g * K + ir[g]];
+    }
+    double mg = INFINITY;
+    int s = 0;
+    while (s < n_sweeps) {
+      ++s;
+      int changed = 0;
+      for (int64_t g = 0; g < G; ++g) {
+        int kb = 0;
+        for (int k = 0; k < K; ++k) {
+          step[g] = (double)cand[g * K + k];
+          row_error(wr, step, d_in, e);
+          o[k] = row_form(e, d_in, h, ldh);
+          if (o[k] < o[kb]) kb = k; /* strict: the first minimum wins */
+        }
+        for (int k = 0; k < K; ++k)
+          if (cand[g * K + k] != cand[g * K + kb] && o[kb] > 0.0) {
+            double gap = (o[k] - o[kb]) / o[kb];
+            if (gap < mg) mg = gap;
+          }
+        if (kb != ir[g]) {
+          ir[g] = (uint8_t)kb;
+          changed = 1;
+        }
+        step[g] = (double)cand[g * K + kb];
+      }
+      if (!changed) break;
+    }
+    for (int64_t g = 0; g < G; ++g) scale[c * G + g] = (float)step[g];
+    row_error(wr, step, d_in, e);
+    obj[c] = row_form(e, d_in, h, ldh);
+    margin[c] = mg;
+    sweeps[c] = s;
+    free(cand);
+    free(step);
+    free(e);
+    free(o);
+  }
 }

@@ -296,6 +296,82 @@ typedef struct w4q_gemv_problem {
 int w4a16_gemv_grouped(const w4q_gemv_problem* problems, int n_problems, int y_dtype,
                        hipStream_t stream);
 
+/* ------------------------------------------------------------------ per-channel variant
+ * One scale per output row, the whole row being the group ([card] intro and "Quickstart":
+ * the per-channel symmetric INT4 checkpoint).  Codes, nibble layout and the exact-quotient
+ * code rule are those above; scales are fp32 [d_out] (search, LSQ) or fp16 bits [d_out]
+ * (export, product).
+ *
+ * quant_scale_search_pc -- for row r with w = W[r][:] and the full H:
+ *   amax = max_i |w_i|;  Delta_k = fp16_RNE(fl32(fl32(alpha[k] * amax) / 7));
+ *   e = w - Delta_k * code(w, Delta_k);  obj_k = e^T H e;  idx = the first k with the smallest obj_k.
+ *   Every e and every product and sum is fp64 (fp64 matrix cores), so the index is the exact
+ *   first minimum up to fp64 rounding.  h: fp32 [d_in][ldh], all d_in x d_in entries read
+ *   (16-B aligned, ldh >= d_in, ldh % 4 == 0).  scale fp32 [d_out] out, idx uint8 [d_out] out,
+ *   obj fp32 [d_out] out or NULL, obj_all fp32 [d_out][n_cand] out or NULL.  No scratch.
+ *   Precondition (not checked on the device): amax * alpha / 7 <= 65504.
+ *
+ * per_channel_workspace_size -- bytes of the workspace the four calls below take for an
+ *   m x d_in activation (m = 1 for the calls without one): d_out x G steps, d_out x G partial
+ *   sums, and the group product's workspace.  The calls broadcast the row's scale to the row's
+ *   groups in the workspace and run the group-32 kernels: the codes, w_hat and dW are the same
+ *   operations, the product differs only in summation order.  workspace: 256-B aligned, at least
+ *   that size (W4Q_EINVAL if smaller or NULL, W4Q_EALIGN if misaligned).
+ * quant_pack_pc   -- packed as quant_pack; scale_f16 [d_out] out = fp16_RNE(scale).
+ * lsq_fwd_pc      -- w_hat = fl32(scale[r] * code(w, scale[r])).
+ * lsq_bwd_pc      -- dW as lsq_bwd; grad_scale_out[r] = grad_scale * sum over the row of
+ *                    G * (q - (w / Delta) m) (the group partial sums added in group order in fp64);
+ *                    pass grad_scale = 1 / sqrt(d_in * 7) for the LSQ normalisation of a row.
+ * w4a16_gemm_pc   -- y = x W_hat^T with W_hat[n][k] = fp16(scale_f16[n]) * q[n][k]; w_mode 0 as
+ *                    w4a16_gemm (exact weights), 1 as w4a16_gemm_dq (bf16-dequantized weights).
+ */
+int quant_scale_search_pc(const float* w, int64_t d_out, int64_t d_in, const float* h, int64_t ldh,
+                          const float* alpha, int n_cand, float* scale, uint8_t* idx, float* obj,
+                          float* obj_all, hipStream_t stream);
+int per_channel_workspace_size(int64_t m, int64_t d_out, int64_t d_in, size_t* bytes);
+int quant_pack_pc(const float* w, const float* scale, int64_t d_out, int64_t d_in, uint8_t* packed,
+                  uint16_t* scale_f16, void* workspace, size_t workspace_bytes, hipStream_t stream);
+int lsq_fwd_pc(const float* w, const float* scale, int64_t d_out, int64_t d_in, float* w_hat,
+               void* workspace, size_t workspace_bytes, hipStream_t stream);
+int lsq_bwd_pc(const float* w, const float* scale, const float* grad_w_hat, int64_t d_out, int64_t d_in,
+               float grad_scale, float* grad_w, float* grad_scale_out, float* w_hat, void* workspace,
+               size_t workspace_bytes, hipStream_t stream);
+int w4a16_gemm_pc(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
+                  int64_t d_out, int64_t d_in, void* y, int y_dtype, int w_mode, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------- joint objective across the groups
+ * [card] "Quantization Configuration" read over a whole output row: ||(w - w_hat) X||^2 =
+ * e^T H e with the full H couples the groups of the row through the off-diagonal blocks of H
+ * (quant_scale_search reads it per group, with the diagonal blocks only).
+ *
+ * quant_joint_objective -- obj[r] = e^T H e over row r, e = w - Delta_g * code(w, Delta_g) with the
+ *   fp32 steps scale[r][g] (0, or fp32-normal and finite), full H (as in quant_scale_search_pc).
+ *   obj fp64 [d_out] out.
+ * quant_joint_refine -- coordinate descent over the groups of each row on that objective.  Start:
+ *   idx [d_out][G] (in; e.g. quant_scale_search's choice; an index >= n_cand is read as
+ *   n_cand - 1), steps Delta_k = candidate of the group
+ *   as in quant_scale_search.  A sweep visits the groups in order; at group g every candidate is
+ *   tried with the other groups held, and the first k with the smallest joint objective is kept
+ *   (the current one is among them: the objective never rises).  Up to n_sweeps sweeps (>= 1),
+ *   stopping after one that changes nothing.  Trials are scored exactly in fp64 as the change
+ *   2 d^T u_g + d^T H_gg d of the objective (d = the group's error change, u = H e kept current
+ *   through every accepted change).  Outputs: idx (out: the result), scale fp32 [d_out][G] out
+ *   (its steps), obj_before / obj_after fp64 [d_out] or NULL, sweeps int32 [d_out] or NULL
+ *   (sweeps run per row).
+ * joint_workspace_size -- bytes of the workspace both calls use to run all rows of up to 2048 at a
+ *   time (u = H e for those rows in fp64 and partial objectives); any workspace of at least 64
+ *   rows' share works, in more launches (W4Q_EINVAL below that, W4Q_EALIGN if misaligned).
+ */
+int joint_workspace_size(int64_t d_out, int64_t d_in, size_t* bytes);
+int quant_joint_objective(const float* w, const float* scale, int64_t d_out, int64_t d_in,
+                          const float* h, int64_t ldh, double* obj, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+int quant_joint_refine(const float* w, int64_t d_out, int64_t d_in, const float* h, int64_t ldh,
+                       const float* alpha, int n_cand, uint8_t* idx, float* scale, int n_sweeps,
+                       double* obj_before, double* obj_after, int32_t* sweeps, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
 /*
  * Diagnostics (not part of the quantization path): measured peaks that rooflines are quoted
  * against besides the chip's nominal ones.

@@ -27,6 +27,9 @@ def test_library_exports_every_declared_symbol():
                           "lsq_fwd", "lsq_bwd", "lsq_adam_step", "w4a16_gemm", "w4a16_gemm_workspace_size",
                           "w4a16_gemm_dq", "w4a16_gemm_dq_workspace_size", "w4a16_gemm_dq_noalloc",
                           "w4a16_gemv_grouped",
+                          "quant_scale_search_pc", "per_channel_workspace_size", "quant_pack_pc", "lsq_fwd_pc",
+                          "lsq_bwd_pc", "w4a16_gemm_pc", "joint_workspace_size", "quant_joint_objective",
+                          "quant_joint_refine",
                           "w4q_probe_read", "w4q_probe_mfma_bf16"}
     l = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
@@ -190,3 +193,32 @@ def test_adam_step_argument_errors():
     assert call(d_in=48) == w4q.W4Q_ESHAPE
     assert call(v_w=A + 4) == w4q.W4Q_EALIGN
     assert call(wh=A + 8) == w4q.W4Q_EALIGN
+
+
+def test_per_channel_and_joint_argument_errors():
+    L = w4q.lib()
+    sz = ctypes.c_size_t(0)
+    # per-channel search: as the group search (same shape and H rules)
+    assert L.quant_scale_search_pc(None, 4, 64, A, 64, A, 3, A, A, None, None, None) == w4q.W4Q_EINVAL
+    assert L.quant_scale_search_pc(A, 4, 64, A, 64, A, 0, A, A, None, None, None) == w4q.W4Q_EINVAL
+    assert L.quant_scale_search_pc(A, 4, 48, A, 64, A, 3, A, A, None, None, None) == w4q.W4Q_ESHAPE
+    assert L.quant_scale_search_pc(A, 4, 64, A, 66, A, 3, A, A, None, None, None) == w4q.W4Q_ESHAPE
+    assert L.quant_scale_search_pc(A, 4, 64, A + 4, 64, A, 3, A, A, None, None, None) == w4q.W4Q_EALIGN
+    # per-channel workspace: query, then too small / missing / misaligned
+    assert L.per_channel_workspace_size(1, 8, 64, ctypes.byref(sz)) == w4q.W4Q_OK and sz.value > 0
+    need = sz.value
+    assert L.quant_pack_pc(A, A, 8, 64, A, A, None, 0, None) == w4q.W4Q_EINVAL
+    assert L.quant_pack_pc(A, A, 8, 64, A, A, A, need - 1, None) == w4q.W4Q_EINVAL
+    assert L.quant_pack_pc(A, A, 8, 64, A, A, A + 16, need, None) == w4q.W4Q_EALIGN
+    assert L.lsq_fwd_pc(A, A, 8, 40, A, A, need, None) == w4q.W4Q_ESHAPE
+    assert L.lsq_bwd_pc(A, A, None, 8, 64, ctypes.c_float(1.0), A, A, None, A, need, None) == w4q.W4Q_EINVAL
+    assert L.w4a16_gemm_pc(A, 1, A, A, 8, 64, A, 0, 2, A, need, None) == w4q.W4Q_EINVAL   # w_mode
+    assert L.w4a16_gemm_pc(A, 1, A, A, 8, 64, A, 0, 0, A, need - 1, None) == w4q.W4Q_EINVAL
+    # joint: workspace must hold at least 64 rows' share (or all rows)
+    assert L.joint_workspace_size(8, 64, ctypes.byref(sz)) == w4q.W4Q_OK and sz.value > 0
+    need = sz.value
+    assert L.quant_joint_refine(A, 8, 64, A, 64, A, 3, A, A, 0, None, None, None, A, need, None) == w4q.W4Q_EINVAL
+    assert L.quant_joint_refine(A, 8, 64, A, 64, A, 3, A, A, 1, None, None, None, None, 0, None) == w4q.W4Q_EINVAL
+    assert L.quant_joint_refine(A, 8, 64, A, 64, A, 3, A, A, 1, None, None, None, A + 16, need, None) == w4q.W4Q_EALIGN
+    assert L.quant_joint_objective(A, A, 8, 64, A, 60, A, A, need, None) == w4q.W4Q_ESHAPE
+    assert L.quant_joint_objective(A, A, 8, 64, A, 64, None, A, need, None) == w4q.W4Q_EINVAL

@@ -49,6 +49,15 @@ SIGNATURES = {
     "w4a16_gemm_dq_workspace_size": (_INT, [_I64, _I64, _I64, _P]),
     "w4a16_gemm_dq_noalloc": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _INT, _P]),
     "w4a16_gemv_grouped": (_INT, [_P, _INT, _INT, _P]),
+    "quant_scale_search_pc": (_INT, [_P, _I64, _I64, _P, _I64, _P, _INT, _P, _P, _P, _P, _P]),
+    "per_channel_workspace_size": (_INT, [_I64, _I64, _I64, _P]),
+    "quant_pack_pc": (_INT, [_P, _P, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "lsq_fwd_pc": (_INT, [_P, _P, _I64, _I64, _P, _P, _SZ, _P]),
+    "lsq_bwd_pc": (_INT, [_P, _P, _P, _I64, _I64, _F, _P, _P, _P, _P, _SZ, _P]),
+    "w4a16_gemm_pc": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _INT, _INT, _P, _SZ, _P]),
+    "joint_workspace_size": (_INT, [_I64, _I64, _P]),
+    "quant_joint_objective": (_INT, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P]),
+    "quant_joint_refine": (_INT, [_P, _I64, _I64, _P, _I64, _P, _INT, _P, _P, _INT, _P, _P, _P, _P, _SZ, _P]),
     "w4q_probe_read": (_INT, [_P, _I64, _INT, _P, _P]),
     "w4q_probe_mfma_bf16": (_INT, [_P, _I64, _P, _P]),
 }

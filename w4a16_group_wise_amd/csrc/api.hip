@@ -198,6 +198,130 @@ int w4a16_gemm_dq(const uint16_t* x, int64_t m, const uint8_t* packed, const uin
 }
 
 
+// ---------------------------------------------------------------- per-channel variant
+static int h_args(const float* h, int64_t ldh, int64_t d_in) {
+  if (ldh < d_in || ldh % 4 != 0) return W4Q_ESHAPE;
+  if (!aligned(h, 16)) return W4Q_EALIGN;
+  return W4Q_OK;
+}
+
+int quant_scale_search_pc(const float* w, int64_t d_out, int64_t d_in, const float* h, int64_t ldh,
+                          const float* alpha, int n_cand, float* scale, uint8_t* idx, float* obj,
+                          float* obj_all, hipStream_t stream) {
+  if (!w || !h || !alpha || !scale || !idx) return W4Q_EINVAL;
+  if (n_cand < 1 || n_cand > W4Q_MAX_CAND) return W4Q_EINVAL;
+  int rc = check_wshape(d_out, d_in);
+  if (rc != W4Q_OK) return rc;
+  if (d_out > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;  // one workgroup per row
+  if ((rc = h_args(h, ldh, d_in)) != W4Q_OK) return rc;
+  if (!aligned(w, 16) || !aligned(alpha, 4) || !aligned(scale, 4) || (obj && !aligned(obj, 4)) ||
+      (obj_all && !aligned(obj_all, 4)))
+    return W4Q_EALIGN;
+  return w4q_launch_pc_search(w, d_out, d_in, h, ldh, alpha, n_cand, scale, idx, obj, obj_all, stream);
+}
+
+int per_channel_workspace_size(int64_t m, int64_t d_out, int64_t d_in, size_t* bytes) {
+  if (!bytes) return W4Q_EINVAL;
+  const int rc = gemm_shape(m, d_out, d_in);
+  if (rc != W4Q_OK) return rc;
+  *bytes = w4q_pc_workspace(m, d_out, d_in);
+  return W4Q_OK;
+}
+
+// the per-channel workspace: present, aligned and of the size the query gives for (m, d_out, d_in)
+static int pc_ws(int64_t m, int64_t d_out, int64_t d_in, const void* ws, size_t ws_bytes) {
+  if (ws == nullptr) return W4Q_EINVAL;
+  if (!aligned(ws, 256)) return W4Q_EALIGN;
+  if (ws_bytes < w4q_pc_workspace(m, d_out, d_in)) return W4Q_EINVAL;
+  return W4Q_OK;
+}
+
+int quant_pack_pc(const float* w, const float* scale, int64_t d_out, int64_t d_in, uint8_t* packed,
+                  uint16_t* scale_f16, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!w || !scale || !packed || !scale_f16) return W4Q_EINVAL;
+  int rc = check_wshape(d_out, d_in);
+  if (rc != W4Q_OK) return rc;
+  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scale, 4) || !aligned(scale_f16, 2))
+    return W4Q_EALIGN;
+  if ((rc = pc_ws(1, d_out, d_in, workspace, workspace_bytes)) != W4Q_OK) return rc;
+  return w4q_launch_pc(0, w, scale, nullptr, d_out, d_in, 0.0f, nullptr, nullptr, nullptr, packed, scale_f16,
+                       workspace, stream);
+}
+
+int lsq_fwd_pc(const float* w, const float* scale, int64_t d_out, int64_t d_in, float* w_hat,
+               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!w || !scale || !w_hat) return W4Q_EINVAL;
+  int rc = check_wshape(d_out, d_in);
+  if (rc != W4Q_OK) return rc;
+  if (!aligned(w, 16) || !aligned(w_hat, 16) || !aligned(scale, 4)) return W4Q_EALIGN;
+  if ((rc = pc_ws(1, d_out, d_in, workspace, workspace_bytes)) != W4Q_OK) return rc;
+  return w4q_launch_pc(1, w, scale, nullptr, d_out, d_in, 0.0f, nullptr, nullptr, w_hat, nullptr, nullptr,
+                       workspace, stream);
+}
+
+int lsq_bwd_pc(const float* w, const float* scale, const float* grad_w_hat, int64_t d_out, int64_t d_in,
+               float grad_scale, float* grad_w, float* grad_scale_out, float* w_hat, void* workspace,
+               size_t workspace_bytes, hipStream_t stream) {
+  if (!w || !scale || !grad_w_hat || !grad_w || !grad_scale_out) return W4Q_EINVAL;
+  int rc = check_wshape(d_out, d_in);
+  if (rc != W4Q_OK) return rc;
+  if (!aligned(w, 16) || !aligned(grad_w_hat, 16) || !aligned(grad_w, 16) || (w_hat && !aligned(w_hat, 16)) ||
+      !aligned(scale, 4) || !aligned(grad_scale_out, 4))
+    return W4Q_EALIGN;
+  if ((rc = pc_ws(1, d_out, d_in, workspace, workspace_bytes)) != W4Q_OK) return rc;
+  return w4q_launch_pc(2, w, scale, grad_w_hat, d_out, d_in, grad_scale, grad_w, grad_scale_out, w_hat, nullptr,
+                       nullptr, workspace, stream);
+}
+
+int w4a16_gemm_pc(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* scale_f16,
+                  int64_t d_out, int64_t d_in, void* y, int y_dtype, int w_mode, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  if (w_mode != 0 && w_mode != 1) return W4Q_EINVAL;
+  int rc = gemm_args(x, m, packed, scale_f16, d_out, d_in, y, y_dtype);
+  if (rc != W4Q_OK) return rc;
+  if ((rc = pc_ws(m, d_out, d_in, workspace, workspace_bytes)) != W4Q_OK) return rc;
+  return w4q_launch_gemm_pc(x, m, packed, scale_f16, d_out, d_in, y, y_dtype, w_mode, workspace, workspace_bytes,
+                            stream);
+}
+
+// ------------------------------------------------------------------- joint objective
+int joint_workspace_size(int64_t d_out, int64_t d_in, size_t* bytes) {
+  if (!bytes) return W4Q_EINVAL;
+  const int rc = check_wshape(d_out, d_in);
+  if (rc != W4Q_OK) return rc;
+  *bytes = w4q_joint_workspace(d_out, d_in);
+  return W4Q_OK;
+}
+
+int quant_joint_objective(const float* w, const float* scale, int64_t d_out, int64_t d_in,
+                          const float* h, int64_t ldh, double* obj, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  if (!w || !scale || !h || !obj || !workspace) return W4Q_EINVAL;
+  int rc = check_wshape(d_out, d_in);
+  if (rc != W4Q_OK) return rc;
+  if ((rc = h_args(h, ldh, d_in)) != W4Q_OK) return rc;
+  if (!aligned(w, 16) || !aligned(scale, 4) || !aligned(obj, 8) || !aligned(workspace, 256)) return W4Q_EALIGN;
+  return w4q_launch_joint(w, d_out, d_in, h, ldh, nullptr, 0, nullptr, const_cast<float*>(scale), 0, nullptr,
+                          obj, nullptr, workspace, workspace_bytes, stream);
+}
+
+int quant_joint_refine(const float* w, int64_t d_out, int64_t d_in, const float* h, int64_t ldh,
+                       const float* alpha, int n_cand, uint8_t* idx, float* scale, int n_sweeps,
+                       double* obj_before, double* obj_after, int32_t* sweeps, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  if (!w || !h || !alpha || !idx || !scale || !workspace) return W4Q_EINVAL;
+  if (n_cand < 1 || n_cand > W4Q_MAX_CAND || n_sweeps < 1) return W4Q_EINVAL;
+  int rc = check_wshape(d_out, d_in);
+  if (rc != W4Q_OK) return rc;
+  if (d_out > 0x7FFFFFFF) return W4Q_EUNSUPPORTED;
+  if ((rc = h_args(h, ldh, d_in)) != W4Q_OK) return rc;
+  if (!aligned(w, 16) || !aligned(alpha, 4) || !aligned(scale, 4) || (obj_before && !aligned(obj_before, 8)) ||
+      (obj_after && !aligned(obj_after, 8)) || (sweeps && !aligned(sweeps, 4)) || !aligned(workspace, 256))
+    return W4Q_EALIGN;
+  return w4q_launch_joint(w, d_out, d_in, h, ldh, alpha, n_cand, idx, scale, n_sweeps, obj_before, obj_after,
+                          sweeps, workspace, workspace_bytes, stream);
+}
+
 int w4a16_gemv_grouped(const w4q_gemv_problem* problems, int n_problems, int y_dtype,
                        hipStream_t stream) {
   if (n_problems < 0 || (y_dtype != 0 && y_dtype != 1)) return W4Q_EINVAL;

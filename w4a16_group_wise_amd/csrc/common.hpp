@@ -193,6 +193,20 @@ int w4q_launch_gemv(const uint16_t* x, int64_t m, const uint8_t* packed, const u
 bool w4q_gemv_group_fits(const w4q_gemv_problem* probs, int n);
 int w4q_launch_gemv_group(const w4q_gemv_problem* probs, int n, int y_dtype, hipStream_t s);
 // w_mode: 0 = exact weights (s16 * q), 1 = weights dequantized to bf16 (RNE of s16 * q)
+int w4q_launch_pc_search(const float* w, int64_t d_out, int64_t d_in, const float* h, int64_t ldh,
+                         const float* alpha, int n_cand, float* scale, uint8_t* idx, float* obj,
+                         float* obj_all, hipStream_t s);
+size_t w4q_joint_workspace(int64_t d_out, int64_t d_in);
+int w4q_launch_joint(const float* w, int64_t d_out, int64_t d_in, const float* h, int64_t ldh,
+                     const float* alpha, int n_cand, uint8_t* idx, float* steps, int n_sweeps,
+                     double* obj_before, double* obj_after, int32_t* sweeps, void* ws, size_t ws_bytes,
+                     hipStream_t s);
+size_t w4q_pc_workspace(int64_t m, int64_t d_out, int64_t d_in);
+int w4q_launch_pc(int op, const float* w, const float* scale, const float* grad, int64_t d_out, int64_t d_in,
+                  float gs, float* out_w, float* out_s, float* w_hat, uint8_t* packed, uint16_t* s16_out,
+                  void* ws, hipStream_t s);
+int w4q_launch_gemm_pc(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16, int64_t d_out,
+                       int64_t d_in, void* y, int y_dtype, int w_mode, void* ws, size_t ws_bytes, hipStream_t s);
 int w4q_launch_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
                     int64_t d_out, int64_t d_in, void* y, int y_dtype, int w_mode, void* ws,
                     size_t ws_bytes, hipStream_t s);

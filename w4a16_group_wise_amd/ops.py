@@ -216,6 +216,140 @@ def w4a16_gemm_dq(x: torch.Tensor, packed: torch.Tensor, scale_f16: torch.Tensor
     return _gemm("w4a16_gemm_dq", x, packed, scale_f16, out_dtype, out, workspace)
 
 
+# ------------------------------------------------------------------ per-channel variant
+def _h_check(h: torch.Tensor, d_in: int, device) -> None:
+    if h.dim() != 2 or h.shape[0] != d_in or h.shape[1] < d_in:
+        raise ValueError(f"h must be [{d_in}][ldh >= {d_in}], got {tuple(h.shape)}")
+    _need(h, "h", torch.float32, device=device)
+
+
+def quant_scale_search_pc(w: torch.Tensor, h: torch.Tensor, alpha: torch.Tensor,
+                          with_obj: bool = True, with_obj_all: bool = False):
+    """One scale per output row, scored with the full H in fp64.
+    -> (scale f32 [d_out], idx u8 [d_out], obj f32 [d_out] | None, obj_all f32 [d_out][K] | None)."""
+    _need(w, "w", torch.float32)
+    d_out, d_in = w.shape
+    _h_check(h, d_in, w.device)
+    _need(alpha, "alpha", torch.float32, device=w.device)
+    K, dev = alpha.numel(), w.device
+    scale = torch.empty(d_out, dtype=torch.float32, device=dev)
+    idx = torch.empty(d_out, dtype=torch.uint8, device=dev)
+    obj = torch.empty(d_out, dtype=torch.float32, device=dev) if with_obj else None
+    obj_all = torch.empty((d_out, K), dtype=torch.float32, device=dev) if with_obj_all else None
+    check("quant_scale_search_pc", lib().quant_scale_search_pc(
+        w.data_ptr(), d_out, d_in, h.data_ptr(), h.shape[1], alpha.data_ptr(), K, scale.data_ptr(),
+        idx.data_ptr(), obj.data_ptr() if obj is not None else None,
+        obj_all.data_ptr() if obj_all is not None else None, _stream(w)))
+    return scale, idx, obj, obj_all
+
+
+def _pc_ws(m, d_out, d_in, device, workspace):
+    return _workspace("per_channel_workspace_size", (m, d_out, d_in), device, workspace)
+
+
+def quant_pack_pc(w: torch.Tensor, scale: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+    """-> (packed u8 [d_out][d_in/2], scale_f16 fp16 [d_out]) on one scale per row."""
+    _need(w, "w", torch.float32)
+    d_out, d_in = w.shape
+    _need(scale, "scale", torch.float32, (d_out,), w.device)
+    packed = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=w.device)
+    s16 = torch.empty(d_out, dtype=torch.float16, device=w.device)
+    wp, wb, _keep = _pc_ws(1, d_out, d_in, w.device, workspace)
+    check("quant_pack_pc", lib().quant_pack_pc(w.data_ptr(), scale.data_ptr(), d_out, d_in, packed.data_ptr(),
+                                               s16.data_ptr(), wp, wb, _stream(w)))
+    return packed, s16
+
+
+def lsq_fwd_pc(w: torch.Tensor, scale: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+    _need(w, "w", torch.float32)
+    d_out, d_in = w.shape
+    _need(scale, "scale", torch.float32, (d_out,), w.device)
+    w_hat = torch.empty_like(w)
+    wp, wb, _keep = _pc_ws(1, d_out, d_in, w.device, workspace)
+    check("lsq_fwd_pc", lib().lsq_fwd_pc(w.data_ptr(), scale.data_ptr(), d_out, d_in, w_hat.data_ptr(), wp, wb,
+                                         _stream(w)))
+    return w_hat
+
+
+def lsq_bwd_pc(w: torch.Tensor, scale: torch.Tensor, grad_w_hat: torch.Tensor, grad_scale: float,
+               with_w_hat: bool = False, workspace: Optional[torch.Tensor] = None):
+    """-> (grad_w f32, grad_scale_out f32 [d_out], w_hat f32 | None) on one scale per row."""
+    _need(w, "w", torch.float32)
+    d_out, d_in = w.shape
+    _need(scale, "scale", torch.float32, (d_out,), w.device)
+    _need(grad_w_hat, "grad_w_hat", torch.float32, (d_out, d_in), w.device)
+    gw = torch.empty_like(w)
+    gs = torch.empty(d_out, dtype=torch.float32, device=w.device)
+    wh = torch.empty_like(w) if with_w_hat else None
+    wp, wb, _keep = _pc_ws(1, d_out, d_in, w.device, workspace)
+    check("lsq_bwd_pc", lib().lsq_bwd_pc(w.data_ptr(), scale.data_ptr(), grad_w_hat.data_ptr(), d_out, d_in,
+                                         float(grad_scale), gw.data_ptr(), gs.data_ptr(),
+                                         wh.data_ptr() if wh is not None else None, wp, wb, _stream(w)))
+    return gw, gs, wh
+
+
+def w4a16_gemm_pc(x: torch.Tensor, packed: torch.Tensor, scale_f16: torch.Tensor,
+                  out_dtype: torch.dtype = torch.float32, dequant_bf16: bool = False,
+                  workspace: Optional[torch.Tensor] = None):
+    """y [m][d_out] = x W_hat^T with one fp16 scale per row (scale_f16 [d_out]); dequant_bf16 as
+    w4a16_gemm_dq."""
+    _need(x, "x", torch.bfloat16)
+    m, d_in = x.shape
+    _need(packed, "packed", torch.uint8, device=x.device)
+    d_out = packed.shape[0]
+    if packed.dim() != 2 or packed.shape[1] * 2 != d_in:
+        raise ValueError(f"packed must be [d_out][{d_in // 2}], got {tuple(packed.shape)}")
+    _need(scale_f16, "scale_f16", torch.float16, (d_out,), x.device)
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    y = torch.empty((m, d_out), dtype=out_dtype, device=x.device)
+    wp, wb, _keep = _pc_ws(m, d_out, d_in, x.device, workspace)
+    check("w4a16_gemm_pc", lib().w4a16_gemm_pc(x.data_ptr(), m, packed.data_ptr(), scale_f16.data_ptr(), d_out,
+                                               d_in, y.data_ptr(), 0 if out_dtype == torch.float32 else 1,
+                                               1 if dequant_bf16 else 0, wp, wb, _stream(x)))
+    return y
+
+
+# ------------------------------------------------------------------- joint objective
+def quant_joint_objective(w: torch.Tensor, scale: torch.Tensor, h: torch.Tensor,
+                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """e^T H e per row with the full H on the group-32 steps scale [d_out][G] -> fp64 [d_out]."""
+    _need(w, "w", torch.float32)
+    d_out, d_in = w.shape
+    _need(scale, "scale", torch.float32, (d_out, d_in // W4Q_GROUP), w.device)
+    _h_check(h, d_in, w.device)
+    obj = torch.empty(d_out, dtype=torch.float64, device=w.device)
+    wp, wb, _keep = _workspace("joint_workspace_size", (d_out, d_in), w.device, workspace)
+    check("quant_joint_objective", lib().quant_joint_objective(
+        w.data_ptr(), scale.data_ptr(), d_out, d_in, h.data_ptr(), h.shape[1], obj.data_ptr(), wp, wb,
+        _stream(w)))
+    return obj
+
+
+def quant_joint_refine(w: torch.Tensor, h: torch.Tensor, alpha: torch.Tensor, idx: torch.Tensor,
+                       n_sweeps: int = 2, inplace: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Coordinate descent over the groups of each row on the joint objective, from idx [d_out][G]
+    (u8).  -> (idx, scale f32 [d_out][G], obj_before f64, obj_after f64, sweeps i32) per row."""
+    _need(w, "w", torch.float32)
+    d_out, d_in = w.shape
+    G = d_in // W4Q_GROUP
+    _h_check(h, d_in, w.device)
+    _need(alpha, "alpha", torch.float32, device=w.device)
+    _need(idx, "idx", torch.uint8, (d_out, G), w.device)
+    if not inplace:
+        idx = idx.clone()
+    dev = w.device
+    scale = torch.empty((d_out, G), dtype=torch.float32, device=dev)
+    ob = torch.empty(d_out, dtype=torch.float64, device=dev)
+    oa = torch.empty(d_out, dtype=torch.float64, device=dev)
+    sw = torch.empty(d_out, dtype=torch.int32, device=dev)
+    wp, wb, _keep = _workspace("joint_workspace_size", (d_out, d_in), dev, workspace)
+    check("quant_joint_refine", lib().quant_joint_refine(
+        w.data_ptr(), d_out, d_in, h.data_ptr(), h.shape[1], alpha.data_ptr(), alpha.numel(), idx.data_ptr(),
+        scale.data_ptr(), int(n_sweeps), ob.data_ptr(), oa.data_ptr(), sw.data_ptr(), wp, wb, _stream(w)))
+    return idx, scale, ob, oa, sw
+
+
 class GemvGroupPlan:
     """A prepared w4a16_gemv_grouped call: the problem table is checked and marshalled once, and
     each call of the plan is a single library call (a decode step reuses the same weight, input

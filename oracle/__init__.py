@@ -21,6 +21,8 @@ Functions and the passages they follow (page titles and sections):
   joint_objective, joint_refine
                             -- model card "Quantization Configuration" objective over a whole
                                row with the full H, and coordinate descent over the row's groups.
+  gptq                      -- the published GPTQ algorithm (static groups on the group-32
+                               grid), which the blog's section 2 names as its starting point.
   lsq_adam_step             -- blog section 3 / model card "QAT Highlights" (weights and steps
                                learned together), with Adam as the optimiser.
 """
@@ -85,6 +87,8 @@ def _L():
         lib.orc_gemm_cols_g.argtypes = [P, I, P, P, I, I, P, I, ctypes.c_int, P, P]
         lib.orc_joint_objective.argtypes = [P, P, I, P, I, P, I, P]
         lib.orc_joint_refine.argtypes = [P, I, P, I, P, ctypes.c_int, P, I, ctypes.c_int, P, P, P, P, P]
+        lib.orc_gptq.restype = ctypes.c_int
+        lib.orc_gptq.argtypes = [P, I, P, I, P, ctypes.c_double, P, I, P, P, P]
         lib.orc_lsq_adam_step.argtypes = [P, P, P, I, I, ctypes.c_double, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.orc_round_bf16.restype = ctypes.c_double
         lib.orc_round_bf16.argtypes = [ctypes.c_double]
@@ -280,6 +284,25 @@ def joint_refine(w: np.ndarray, h: np.ndarray, alpha: np.ndarray, idx: np.ndarra
     _L().orc_joint_refine(_p(w), w.shape[1], _p(h), h.shape[1], _p(alpha), alpha.shape[0], _p(rows), cnt,
                           int(n_sweeps), _p(out["idx"]), _p(out["scale"]), _p(out["obj"]), _p(out["margin"]),
                           _p(out["sweeps"]))
+    return out
+
+
+def gptq(w: np.ndarray, h: np.ndarray, scale: np.ndarray, damp: float = 0.01,
+         rows: Optional[np.ndarray] = None):
+    """GPTQ error feedback with fixed group-32 steps on selected rows.
+    -> dict w_hat f32 [cnt][d_in], w_upd f64 [cnt][d_in], margin f64 [cnt]; raises if H' is not
+    positive definite."""
+    w = _c(w, np.float32)
+    h = _c(h, np.float32)
+    scale = _c(scale, np.float32)
+    rows = _c(np.arange(w.shape[0]) if rows is None else rows, np.int64)
+    cnt, d_in = rows.shape[0], w.shape[1]
+    out = {"w_hat": np.empty((cnt, d_in), np.float32), "w_upd": np.empty((cnt, d_in), np.float64),
+           "margin": np.empty(cnt, np.float64)}
+    rc = _L().orc_gptq(_p(w), d_in, _p(h), h.shape[1], _p(scale), float(damp), _p(rows), cnt,
+                       _p(out["w_hat"]), _p(out["w_upd"]), _p(out["margin"]))
+    if rc != 0:
+        raise ValueError("H + damping is not positive definite")
     return out
 
 

@@ -552,3 +552,107 @@ void orc_joint_refine(const float* w, int64_t d_in, const float* h, int64_t ldh,
     free(o);
   }
 }
+
+/* ------------------------------------------------ GPTQ-style error feedback (prior art) */
+
+/* In-place Cholesky a = L L^T of an n x n symmetric matrix (row-major, lower triangle used);
+ * L left in the lower triangle.  Returns 0, or 1 if a pivot is not positive. */
+static int chol_lower(double* a, int64_t n) {
+  for (int64_t j = 0; j < n; ++j) {
+    double s = a[j * n + j];
+    for (int64_t p = 0; p < j; ++p) s -= a[j * n + p] * a[j * n + p];
+    if (!(s > 0.0)) return 1;
+    double d = sqrt(s);
+    a[j * n + j] = d;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = j + 1; i < n; ++i) {
+      double t = a[i * n + j];
+      for (int64_t p = 0; p < j; ++p) t -= a[i * n + p] * a[j * n + p];
+      a[i * n + j] = t / d;
+    }
+  }
+  return 0;
+}
+
+/*
+ * GPTQ (Frantar et al., "GPTQ: Accurate Post-Training Quantization for Generative Pre-trained
+ * Transformers", the published algorithm; [blog] section 2 names it as the second-order output
+ * reconstruction method the Hessian initialization starts from) on the group-32 grid with the
+ * caller's fixed steps scale[r][g] (static groups), columns in natural order:
+ *   dead columns (H_ii == 0): H_ii = 1 and w_i = 0;  H' = H + damp * mean(diag H) I;
+ *   U = the upper Cholesky factor of H'^-1 (H'^-1 = U^T U);
+ *   per row, for i = 0 .. d_in-1:  q = code(w_i, Delta_g(i));  w_hat_i = Delta q;
+ *     err = (w_i - w_hat_i) / U_ii;  w_j -= err * U_ij for every j > i.
+ * Selected rows; w_hat [cnt][d_in] (fp32 of the exact product), w_upd [cnt][d_in] or NULL (the
+ * updated weight each column was quantized from), margin [cnt] or NULL: the smallest distance,
+ * in steps, of an updated weight w_i / Delta from a decision midpoint c + 1/2 (c = -8 .. 6).
+ * Returns 0, or 1 if H' is not positive definite.
+ */
+int orc_gptq(const float* w, int64_t d_in, const float* h, int64_t ldh, const float* scale,
+             double damp, const int64_t* rows, int64_t cnt, float* w_hat, double* w_upd,
+             double* margin) {
+  int64_t n = d_in, G = d_in / GROUP;
+  double* hd = (double*)malloc((size_t)(n * n) * sizeof(double));
+  double* inv = (double*)malloc((size_t)(n * n) * sizeof(double));
+  unsigned char* dead = (unsigned char*)malloc((size_t)n);
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t j = 0; j < n; ++j) hd[i * n + j] = (double)h[i * ldh + j];
+  double mean = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    dead[i] = hd[i * n + i] == 0.0;
+    if (dead[i]) hd[i * n + i] = 1.0;
+    mean += hd[i * n + i];
+  }
+  mean /= (double)n;
+  for (int64_t i = 0; i < n; ++i) hd[i * n + i] += damp * mean;
+  /* H'^-1 from H' = L L^T: column c of the inverse solves L L^T x = e_c */
+  int bad = chol_lower(hd, n);
+  if (!bad) {
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t c = 0; c < n; ++c) {
+      double* x = (double*)malloc((size_t)n * sizeof(double));
+      for (int64_t i = 0; i < n; ++i) { /* L y = e_c */
+        double t = (i == c) ? 1.0 : 0.0;
+        for (int64_t p = 0; p < i; ++p) t -= hd[i * n + p] * x[p];
+        x[i] = t / hd[i * n + i];
+      }
+      for (int64_t i = n - 1; i >= 0; --i) { /* L^T x = y */
+        double t = x[i];
+        for (int64_t p = i + 1; p < n; ++p) t -= hd[p * n + i] * x[p];
+        x[i] = t / hd[i * n + i];
+      }
+      for (int64_t i = 0; i < n; ++i) inv[i * n + c] = x[i];
+      free(x);
+    }
+    bad = chol_lower(inv, n); /* inv = L2 L2^T, U = L2^T: U_ij = inv[j][i] for j >= i */
+  }
+  if (!bad) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < cnt; ++c) {
+      int64_t r = rows[c];
+      double* wr = (double*)malloc((size_t)n * sizeof(double));
+      double mg = INFINITY;
+      for (int64_t i = 0; i < n; ++i) wr[i] = dead[i] ? 0.0 : (double)w[r * d_in + i];
+      for (int64_t i = 0; i < n; ++i) {
+        double d = (double)scale[r * G + i / GROUP];
+        int q = orc_code(wr[i], d);
+        double wh = d * (double)q;
+        if (d > 0.0)
+          for (int k = QMIN; k < QMAX; ++k) {
+            double dist = fabs(wr[i] / d - ((double)k + 0.5));
+            if (dist < mg) mg = dist;
+          }
+        if (w_upd) w_upd[c * n + i] = wr[i];
+        w_hat[c * n + i] = (float)wh;
+        double err = (wr[i] - wh) / inv[i * n + i];
+        for (int64_t j = i + 1; j < n; ++j) wr[j] -= err * inv[j * n + i];
+      }
+      if (margin) margin[c] = mg;
+      free(wr);
+    }
+  }
+  free(hd);
+  free(inv);
+  free(dead);
+  return bad;
+}

@@ -372,6 +372,33 @@ int quant_joint_refine(const float* w, int64_t d_out, int64_t d_in, const float*
                        double* obj_before, double* obj_after, int32_t* sweeps, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------- GPTQ error feedback
+ * quant_gptq -- GPTQ (the published algorithm of Frantar et al.; [blog] section 2 names it as the
+ *   second-order reconstruction method the Hessian initialization starts from) on the group-32
+ *   grid with fixed steps scale[r][g] (e.g. quant_scale_search's; static groups), columns in
+ *   natural order.  H' = H with every dead column (H_ii == 0) given a unit diagonal and a zero
+ *   weight, plus damp * mean(diag) on the diagonal.  Per row, column i is quantized from
+ *   w'_i = w_i + (1 / R_ii) sum_{p < i} R_pi (w_p - w_hat_p),  H' = R R^T with R upper triangular,
+ *   which is the least-squares update of the remaining weights given the columns already
+ *   quantized (the published form's err / U_ii feedback through U = chol(H'^-1)^T = R^-1):
+ *   w_hat_i = Delta * code(w'_i, Delta) with the exact nearest-code rule on the fp64 value.
+ *   Everything in fp64 (fp64 matrix cores for the Cholesky update and the feedback sums).
+ *   w      fp32 [d_out][d_in], 16-B aligned;  h fp32 [d_in][ldh] (all entries read; 16-B aligned,
+ *          ldh >= d_in, ldh % 4 == 0);  scale fp32 [d_out][G] (0 or fp32-normal, finite);
+ *   damp   >= 0 and finite (0.01 is the published default);
+ *   w_hat  fp32 [d_out][d_in] out: Delta * q (exact for steps on the fp16 grid; quant_pack(w_hat,
+ *          scale) then gives exactly these codes);
+ *   info   int32 device scalar, or NULL: set to 1 if a Cholesky pivot of H' is not positive
+ *          (w_hat is then unspecified); never cleared by the call.
+ *   workspace: gptq_workspace_size bytes, 256-B aligned (W4Q_EINVAL if smaller or NULL,
+ *          W4Q_EALIGN if misaligned): H' factor (d_in rounded up to 64, squared, fp64) and the
+ *          rows' fp64 quantization errors.
+ */
+int gptq_workspace_size(int64_t d_out, int64_t d_in, size_t* bytes);
+int quant_gptq(const float* w, int64_t d_out, int64_t d_in, const float* h, int64_t ldh,
+               const float* scale, float damp, float* w_hat, int32_t* info, void* workspace,
+               size_t workspace_bytes, hipStream_t stream);
+
 /*
  * Diagnostics (not part of the quantization path): measured peaks that rooflines are quoted
  * against besides the chip's nominal ones.

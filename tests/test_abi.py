@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
                           "w4a16_gemv_grouped",
                           "quant_scale_search_pc", "per_channel_workspace_size", "quant_pack_pc", "lsq_fwd_pc",
                           "lsq_bwd_pc", "w4a16_gemm_pc", "joint_workspace_size", "quant_joint_objective",
-                          "quant_joint_refine",
+                          "quant_joint_refine", "gptq_workspace_size", "quant_gptq",
                           "w4q_probe_read", "w4q_probe_mfma_bf16"}
     l = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
@@ -222,3 +222,19 @@ def test_per_channel_and_joint_argument_errors():
     assert L.quant_joint_refine(A, 8, 64, A, 64, A, 3, A, A, 1, None, None, None, A + 16, need, None) == w4q.W4Q_EALIGN
     assert L.quant_joint_objective(A, A, 8, 64, A, 60, A, A, need, None) == w4q.W4Q_ESHAPE
     assert L.quant_joint_objective(A, A, 8, 64, A, 64, None, A, need, None) == w4q.W4Q_EINVAL
+
+
+def test_gptq_argument_errors():
+    L = w4q.lib()
+    sz = ctypes.c_size_t(0)
+    assert L.gptq_workspace_size(8, 64, ctypes.byref(sz)) == w4q.W4Q_OK and sz.value >= 64 * 64 * 8 + 8 * 64 * 8
+    need = sz.value
+    f = ctypes.c_float
+    assert L.quant_gptq(A, 8, 64, A, 64, A, f(0.01), A, None, None, 0, None) == w4q.W4Q_EINVAL
+    assert L.quant_gptq(A, 8, 64, A, 64, A, f(0.01), A, None, A, need - 1, None) == w4q.W4Q_EINVAL
+    assert L.quant_gptq(A, 8, 64, A, 64, A, f(-1.0), A, None, A, need, None) == w4q.W4Q_EINVAL
+    assert L.quant_gptq(A, 8, 64, A, 64, A, f(float("nan")), A, None, A, need, None) == w4q.W4Q_EINVAL
+    assert L.quant_gptq(A, 8, 40, A, 64, A, f(0.01), A, None, A, need, None) == w4q.W4Q_ESHAPE
+    assert L.quant_gptq(A, 8, 64, A, 62, A, f(0.01), A, None, A, need, None) == w4q.W4Q_ESHAPE
+    assert L.quant_gptq(A, 8, 64, A + 4, 64, A, f(0.01), A, None, A, need, None) == w4q.W4Q_EALIGN
+    assert L.quant_gptq(A, 8, 64, A, 64, A, f(0.01), A, None, A + 16, need, None) == w4q.W4Q_EALIGN

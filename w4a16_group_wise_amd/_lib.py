@@ -58,6 +58,8 @@ SIGNATURES = {
     "joint_workspace_size": (_INT, [_I64, _I64, _P]),
     "quant_joint_objective": (_INT, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _SZ, _P]),
     "quant_joint_refine": (_INT, [_P, _I64, _I64, _P, _I64, _P, _INT, _P, _P, _INT, _P, _P, _P, _P, _SZ, _P]),
+    "gptq_workspace_size": (_INT, [_I64, _I64, _P]),
+    "quant_gptq": (_INT, [_P, _I64, _I64, _P, _I64, _P, _F, _P, _P, _P, _SZ, _P]),
     "w4q_probe_read": (_INT, [_P, _I64, _INT, _P, _P]),
     "w4q_probe_mfma_bf16": (_INT, [_P, _I64, _P, _P]),
 }

@@ -322,6 +322,32 @@ int quant_joint_refine(const float* w, int64_t d_out, int64_t d_in, const float*
                           sweeps, workspace, workspace_bytes, stream);
 }
 
+// ------------------------------------------------------------------ GPTQ feedback
+int gptq_workspace_size(int64_t d_out, int64_t d_in, size_t* bytes) {
+  if (!bytes) return W4Q_EINVAL;
+  const int rc = check_wshape(d_out, d_in);
+  if (rc != W4Q_OK) return rc;
+  if (d_in > 65536) return W4Q_EUNSUPPORTED;
+  *bytes = w4q_gptq_workspace(d_out, d_in);
+  return W4Q_OK;
+}
+
+int quant_gptq(const float* w, int64_t d_out, int64_t d_in, const float* h, int64_t ldh,
+               const float* scale, float damp, float* w_hat, int32_t* info, void* workspace,
+               size_t workspace_bytes, hipStream_t stream) {
+  if (!w || !h || !scale || !w_hat || !workspace) return W4Q_EINVAL;
+  if (!(damp >= 0.0f) || damp > 3.0e38f) return W4Q_EINVAL;
+  int rc = check_wshape(d_out, d_in);
+  if (rc != W4Q_OK) return rc;
+  if (d_in > 65536) return W4Q_EUNSUPPORTED;
+  if ((rc = h_args(h, ldh, d_in)) != W4Q_OK) return rc;
+  if (!aligned(w, 16) || !aligned(scale, 4) || !aligned(w_hat, 4) || (info && !aligned(info, 4)) ||
+      !aligned(workspace, 256))
+    return W4Q_EALIGN;
+  if (workspace_bytes < w4q_gptq_workspace(d_out, d_in)) return W4Q_EINVAL;
+  return w4q_launch_gptq(w, d_out, d_in, h, ldh, scale, damp, w_hat, info, workspace, stream);
+}
+
 int w4a16_gemv_grouped(const w4q_gemv_problem* problems, int n_problems, int y_dtype,
                        hipStream_t stream) {
   if (n_problems < 0 || (y_dtype != 0 && y_dtype != 1)) return W4Q_EINVAL;

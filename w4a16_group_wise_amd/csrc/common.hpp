@@ -207,6 +207,9 @@ int w4q_launch_pc(int op, const float* w, const float* scale, const float* grad,
                   void* ws, hipStream_t s);
 int w4q_launch_gemm_pc(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16, int64_t d_out,
                        int64_t d_in, void* y, int y_dtype, int w_mode, void* ws, size_t ws_bytes, hipStream_t s);
+size_t w4q_gptq_workspace(int64_t d_out, int64_t d_in);
+int w4q_launch_gptq(const float* w, int64_t d_out, int64_t d_in, const float* h, int64_t ldh, const float* scale,
+                    float damp, float* w_hat, int* info, void* ws, hipStream_t s);
 int w4q_launch_gemm(const uint16_t* x, int64_t m, const uint8_t* packed, const uint16_t* s16,
                     int64_t d_out, int64_t d_in, void* y, int y_dtype, int w_mode, void* ws,
                     size_t ws_bytes, hipStream_t s);

@@ -1,0 +1,323 @@
+// gptq.hip -- GPTQ error feedback on the group-32 grid with fixed steps (static groups).
+//
+// GPTQ (Frantar et al., "GPTQ: Accurate Post-Training Quantization for Generative Pre-trained
+// Transformers", the published algorithm) is the second-order output reconstruction method the
+// blog "Opt.Gear-QAT: Preserving On-Device Performance with QAT", section 2, starts from.  With
+// H' = H (dead columns: unit diagonal, zero weight) + damp * mean(diag) I, the columns of a row are
+// quantized in order, each from the least-squares update of the not-yet-quantized weights given
+// the ones already quantized.  The published form feeds err_i = (w'_i - w_hat_i) / U_ii through
+// U = chol(H'^-1)^T.  Here the same updated weights come from the Cholesky factor of H' itself,
+// without the inverse: with H' = R R^T, R upper (R = J L J for J H' J = L L^T, J the reversal),
+//   w'_i = w_i + (1 / R_ii) sum_{p < i} R_pi (w_p - w_hat_p),
+// (U = R^-1 gives U^T U = H'^-1, and (w - w_hat) = U^T err unrolls to the sum above).  So:
+//   1. A = J H' J in fp64, dp x dp (dp = d_in rounded up to 64, identity beyond d_in);
+//   2. blocked Cholesky A = L L^T (panels of 64: a one-workgroup diagonal factor, a wavefront per
+//      row for the panel below it, and the trailing update on the fp64 matrix cores);
+//   3. per block of 64 columns: the sums over earlier columns on the matrix cores
+//      (delta [rows][c0] times R [c0][block]), then the block's columns in order inside the
+//      workgroup, delta_i = w_i - w_hat_i kept in fp64 for the later blocks.
+// Everything runs in fp64; codes follow the exact nearest-code rule on the fp64 updated weight.
+#include "common.hpp"
+
+namespace w4q {
+namespace {
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kNb = 64;  // panel and column-block width
+
+__device__ __forceinline__ int64_t rup64(int64_t v) { return (v + 63) & ~int64_t(63); }
+
+// nearest code of the fp64 value v at step d (fp32, >= 0): ties to the even code, clamped.
+// (c +- 1/2) d is exact in fp64 and v - (c +- 1/2) d has the sign of the exact difference.
+__device__ __forceinline__ double code64(double v, double d) {
+  if (!(d > 0.0)) return 0.0;
+  double c = __builtin_rint(v / d);
+  c = __builtin_fmin(__builtin_fmax(c, -8.0), 7.0);
+  const double rh = v - (c + 0.5) * d;
+  const double rl = v - (c - 0.5) * d;
+  const bool odd = __builtin_fmod(c, 2.0) != 0.0;
+  const bool up = (rh > 0.0 || (rh == 0.0 && odd)) && c < 7.0;
+  const bool dn = (rl < 0.0 || (rl == 0.0 && odd)) && c > -8.0;
+  return c + (up ? 1.0 : 0.0) - (dn ? 1.0 : 0.0);
+}
+
+// ------------------------------------------------------------------------------ prep
+// mean of the diagonal with dead entries read as 1 (one workgroup, fixed summation order)
+__global__ __launch_bounds__(256) void diag_mean_kernel(const float* __restrict__ h, int64_t ldh, int64_t d,
+                                                        double* __restrict__ mean) {
+  __shared__ double part[256];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < d; i += 256) {
+    const double v = static_cast<double>(h[i * ldh + i]);
+    s += v == 0.0 ? 1.0 : v;
+  }
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int k = 128; k >= 1; k >>= 1) {
+    if (static_cast<int>(threadIdx.x) < k) part[threadIdx.x] += part[threadIdx.x + k];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *mean = part[0] / static_cast<double>(d);
+}
+
+// A[i][j] = H'[d-1-i][d-1-j] inside d x d, identity beyond; dead[k] = (H_kk == 0)
+__global__ __launch_bounds__(256) void build_kernel(const float* __restrict__ h, int64_t ldh, int64_t d, int64_t dp,
+                                                    const double* __restrict__ mean, float damp,
+                                                    double* __restrict__ a, uint8_t* __restrict__ dead) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= dp * dp) return;
+  const int64_t i = e / dp, j = e % dp;
+  double v;
+  if (i < d && j < d) {
+    const int64_t hi = d - 1 - i, hj = d - 1 - j;
+    v = static_cast<double>(h[hi * ldh + hj]);
+    if (i == j) {
+      if (v == 0.0) v = 1.0;
+      v += static_cast<double>(damp) * *mean;
+    }
+  } else {
+    v = i == j ? 1.0 : 0.0;
+  }
+  a[e] = v;
+  if (i == j && i < d) dead[d - 1 - i] = h[(d - 1 - i) * ldh + (d - 1 - i)] == 0.0f ? 1 : 0;
+}
+
+// --------------------------------------------------------------------- blocked Cholesky
+// diagonal block [k0, k0 + 64): factor in LDS (right-looking), lower triangle written back;
+// a pivot that is not positive sets *info
+__global__ __launch_bounds__(256) void chol_diag_kernel(double* __restrict__ a, int64_t dp, int64_t k0,
+                                                        int* __restrict__ info) {
+  __shared__ double t[kNb][kNb + 1];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < kNb * kNb; e += 256) t[e / kNb][e % kNb] = a[(k0 + e / kNb) * dp + k0 + e % kNb];
+  __syncthreads();
+  for (int j = 0; j < kNb; ++j) {
+    const double p = t[j][j];
+    if (tid == 0 && !(p > 0.0) && info != nullptr) *info = 1;
+    const double dj = __builtin_sqrt(p);
+    __syncthreads();
+    if (tid == 0) t[j][j] = dj;
+    for (int i = j + 1 + tid; i < kNb; i += 256) t[i][j] /= dj;
+    __syncthreads();
+    const int m = kNb - 1 - j;  // trailing rows/cols j+1 .. 63: lower triangle incl. diagonal
+    for (int e = tid; e < m * m; e += 256) {
+      const int i = j + 1 + e / m, k = j + 1 + e % m;
+      if (k <= i) t[i][k] -= t[i][j] * t[k][j];
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < kNb * kNb; e += 256) {
+    const int i = e / kNb, k = e % kNb;
+    if (k <= i) a[(k0 + i) * dp + k0 + k] = t[i][k];
+  }
+}
+
+// panel below the diagonal block: row i solves x L11^T = a_i (one wavefront per row, lane j
+// holds x_j; the columns are settled in order)
+__global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ a, int64_t dp, int64_t k0) {
+  __shared__ double l[kNb][kNb + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int e = tid; e < kNb * kNb; e += 256) l[e / kNb][e % kNb] = a[(k0 + e / kNb) * dp + k0 + e % kNb];
+  __syncthreads();
+  const int64_t row = k0 + kNb + static_cast<int64_t>(blockIdx.x) * 4 + (tid >> 6);
+  if (row >= dp) return;  // uniform per wavefront; no barrier follows
+  double s = a[row * dp + k0 + lane];
+  double x = 0.0;
+  for (int j = 0; j < kNb; ++j) {
+    const double xj = __shfl(s / l[j][j], j);
+    if (lane == j) x = xj;
+    if (lane > j) s -= xj * l[lane][j];
+  }
+  a[row * dp + k0 + lane] = x;
+}
+
+// trailing update of the lower tile pairs: A[ti][tj] -= L21[ti] L21[tj]^T (K = 64), tiles of 64
+// rows past k0 + 64, ti >= tj; 16 rows x 64 columns per wavefront
+__global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ a, int64_t dp, int64_t k0) {
+  // tile pair of this workgroup: b = ti (ti + 1) / 2 + tj
+  const int64_t b = blockIdx.x;
+  int64_t ti = static_cast<int64_t>((__builtin_sqrt(8.0 * static_cast<double>(b) + 1.0) - 1.0) * 0.5);
+  while ((ti + 1) * (ti + 2) / 2 <= b) ++ti;
+  while (ti * (ti + 1) / 2 > b) --ti;
+  const int64_t tj = b - ti * (ti + 1) / 2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, j = lane & 15;
+  const int64_t base = k0 + kNb;
+  const int64_t ra = base + ti * kNb + 16 * wave + j;  // A-side row
+  const double* arow = a + ra * dp + k0;
+  f64x4 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int kk0 = 0; kk0 < kNb; kk0 += 16) {
+    const f64x2 a01 = *reinterpret_cast<const f64x2*>(arow + kk0 + 4 * q);
+    const f64x2 a23 = *reinterpret_cast<const f64x2*>(arow + kk0 + 4 * q + 2);
+    const double av[4] = {a01.x, a01.y, a23.x, a23.y};
+    double bv[4][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const double* brow = a + (base + tj * kNb + 16 * c + j) * dp + k0 + kk0 + 4 * q;
+      const f64x2 b01 = *reinterpret_cast<const f64x2*>(brow);
+      const f64x2 b23 = *reinterpret_cast<const f64x2*>(brow + 2);
+      bv[c][0] = b01.x; bv[c][1] = b01.y; bv[c][2] = b23.x; bv[c][3] = b23.y;
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[s], bv[c][s], acc[c], 0, 0, 0);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = base + ti * kNb + 16 * wave + 4 * r + q;
+      const int64_t col = base + tj * kNb + 16 * c + j;
+      a[row * dp + col] -= acc[c][r];
+    }
+}
+
+// ------------------------------------------------------------------------------ sweep
+// R[p][i] = L[d-1-p][d-1-i] (p <= i): the upper factor of H' read through the reversal
+__device__ __forceinline__ double rfac(const double* __restrict__ l, int64_t dp, int64_t d, int64_t p, int64_t i) {
+  return l[(d - 1 - p) * dp + (d - 1 - i)];
+}
+
+// Block of columns [c0, c0 + nb) for 16 rows per workgroup.  Wavefront w first sums over the
+// earlier columns for block columns 16w .. 16w+15 on the matrix cores; then each wavefront takes
+// 4 of the 16 rows, 16 lanes a row, each lane 4 of the block's columns, and the block's columns
+// are quantized in order with the correction of every later column of the block kept current.
+__global__ __launch_bounds__(256) void gptq_block_kernel(const float* __restrict__ w, int64_t d_out, int64_t d_in,
+                                                         const float* __restrict__ scale,
+                                                         const double* __restrict__ l, int64_t dp,
+                                                         const uint8_t* __restrict__ dead,
+                                                         double* __restrict__ delta, float* __restrict__ w_hat,
+                                                         int64_t c0) {
+  __shared__ double cs[16][kNb + 1];
+  __shared__ double rd[kNb][kNb + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, j = lane & 15;
+  const int64_t G = d_in / kGroup;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int nb = d_in - c0 < kNb ? static_cast<int>(d_in - c0) : kNb;
+  // 1. C[row][c0 + 16 wave + j] = sum_{p < c0} delta[row][p] R[p][c0 + 16 wave + j]
+  {
+    const int64_t ra = r0 + j;
+    const bool va = ra < d_out;
+    const double* drow = delta + (va ? ra : 0) * d_in;
+    const int64_t col = c0 + 16 * wave + j;
+    const bool vc = col < d_in;
+    f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int64_t kk0 = 0; kk0 < c0; kk0 += 16) {
+      const f64x2 a01 = *reinterpret_cast<const f64x2*>(drow + kk0 + 4 * q);
+      const f64x2 a23 = *reinterpret_cast<const f64x2*>(drow + kk0 + 4 * q + 2);
+      double av[4] = {a01.x, a01.y, a23.x, a23.y};
+      double bv[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bv[s] = vc ? rfac(l, dp, d_in, kk0 + 4 * q + s, col) : 0.0;
+        if (!va) av[s] = 0.0;
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av[s], bv[s], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cs[4 * r + q][16 * wave + j] = acc[r];
+  }
+  // 2. the block's diagonal part of R
+  for (int e = tid; e < kNb * kNb; e += 256) {
+    const int i = e / kNb, k = e % kNb;
+    rd[i][k] = (i <= k && i < nb && k < nb) ? rfac(l, dp, d_in, c0 + i, c0 + k) : 0.0;
+  }
+  __syncthreads();
+  // 3. the block's columns in order: row 4 wave + lane / 16 of the workgroup's 16, lane % 16 owns
+  //    block columns 4 (lane % 16) .. + 3
+  const int rr = lane >> 4, part = lane & 15;
+  const int64_t row = r0 + 4 * wave + rr;
+  const bool vr = row < d_out;
+  double cl[4], wl[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int k = 4 * part + t;
+    cl[t] = cs[4 * wave + rr][k];
+    const bool in = vr && k < nb;
+    wl[t] = (in && dead[c0 + k] == 0) ? static_cast<double>(w[row * d_in + c0 + k]) : 0.0;
+  }
+  for (int i = 0; i < nb; ++i) {
+    const int owner = i >> 2, ti = i & 3;
+    double di = 0.0;
+    if (part == owner) {
+      double wi = wl[0], ci = cl[0];
+#pragma unroll
+      for (int t = 1; t < 4; ++t)
+        if (ti == t) {
+          wi = wl[t];
+          ci = cl[t];
+        }
+      const double v = wi + ci / rd[i][i];
+      const double d = vr ? static_cast<double>(scale[row * G + (c0 + i) / kGroup]) : 0.0;
+      const double wh = d * code64(v, d);
+      di = wi - wh;
+      if (vr) {
+        w_hat[row * d_in + c0 + i] = static_cast<float>(wh);
+        delta[row * d_in + c0 + i] = di;
+      }
+    }
+    di = __shfl(di, (lane & ~15) | owner);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int k = 4 * part + t;
+      if (k > i && k < nb) cl[t] += rd[i][k] * di;
+    }
+  }
+}
+
+inline unsigned cdiv(int64_t a, int64_t b) { return static_cast<unsigned>((a + b - 1) / b); }
+inline size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
+
+}  // namespace
+}  // namespace w4q
+
+using namespace w4q;
+
+size_t w4q_gptq_workspace(int64_t d_out, int64_t d_in) {
+  const int64_t dp = (d_in + 63) & ~int64_t(63);
+  return up256(static_cast<size_t>(dp * dp) * 8) + up256(static_cast<size_t>(d_out * d_in) * 8) +
+         up256(static_cast<size_t>(d_in)) + 256;
+}
+
+int w4q_launch_gptq(const float* w, int64_t d_out, int64_t d_in, const float* h, int64_t ldh, const float* scale,
+                    float damp, float* w_hat, int* info, void* ws, hipStream_t s) {
+  const int64_t dp = (d_in + 63) & ~int64_t(63);
+  char* p = static_cast<char*>(ws);
+  double* a = reinterpret_cast<double*>(p);
+  p += up256(static_cast<size_t>(dp * dp) * 8);
+  double* delta = reinterpret_cast<double*>(p);
+  p += up256(static_cast<size_t>(d_out * d_in) * 8);
+  uint8_t* dead = reinterpret_cast<uint8_t*>(p);
+  p += up256(static_cast<size_t>(d_in));
+  double* mean = reinterpret_cast<double*>(p);
+  int rc;
+#define W4Q_GO(...)                                  \
+  do {                                               \
+    hipLaunchKernelGGL(__VA_ARGS__);                 \
+    if ((rc = w4q_launch_status()) != W4Q_OK) return rc; \
+  } while (0)
+  W4Q_GO(diag_mean_kernel, dim3(1), dim3(256), 0, s, h, ldh, d_in, mean);
+  W4Q_GO(build_kernel, dim3(cdiv(dp * dp, 256)), dim3(256), 0, s, h, ldh, d_in, dp, mean, damp, a, dead);
+  for (int64_t k0 = 0; k0 < dp; k0 += kNb) {
+    W4Q_GO(chol_diag_kernel, dim3(1), dim3(256), 0, s, a, dp, k0, info);
+    const int64_t rest = dp - k0 - kNb;
+    if (rest > 0) {
+      W4Q_GO(chol_panel_kernel, dim3(cdiv(rest, 4)), dim3(256), 0, s, a, dp, k0);
+      const int64_t T = rest / kNb;
+      W4Q_GO(chol_update_kernel, dim3(static_cast<unsigned>(T * (T + 1) / 2)), dim3(256), 0, s, a, dp, k0);
+    }
+  }
+  for (int64_t c0 = 0; c0 < d_in; c0 += kNb)
+    W4Q_GO(gptq_block_kernel, dim3(cdiv(d_out, 16)), dim3(256), 0, s, w, d_out, d_in, scale, a, dp, dead, delta,
+           w_hat, c0);
+#undef W4Q_GO
+  return W4Q_OK;
+}

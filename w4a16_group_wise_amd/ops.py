@@ -350,6 +350,24 @@ def quant_joint_refine(w: torch.Tensor, h: torch.Tensor, alpha: torch.Tensor, id
     return idx, scale, ob, oa, sw
 
 
+# -------------------------------------------------------------------- GPTQ feedback
+def quant_gptq(w: torch.Tensor, h: torch.Tensor, scale: torch.Tensor, damp: float = 0.01,
+               workspace: Optional[torch.Tensor] = None):
+    """GPTQ error feedback with the fixed group-32 steps scale [d_out][G].
+    -> (w_hat f32 [d_out][d_in] = Delta * q, info int32 [1]: 1 if H + damping was not positive
+    definite)."""
+    _need(w, "w", torch.float32)
+    d_out, d_in = w.shape
+    _h_check(h, d_in, w.device)
+    _need(scale, "scale", torch.float32, (d_out, d_in // W4Q_GROUP), w.device)
+    w_hat = torch.empty_like(w)
+    info = torch.zeros(1, dtype=torch.int32, device=w.device)
+    wp, wb, _keep = _workspace("gptq_workspace_size", (d_out, d_in), w.device, workspace)
+    check("quant_gptq", lib().quant_gptq(w.data_ptr(), d_out, d_in, h.data_ptr(), h.shape[1], scale.data_ptr(),
+                                         float(damp), w_hat.data_ptr(), info.data_ptr(), wp, wb, _stream(w)))
+    return w_hat, info
+
+
 class GemvGroupPlan:
     """A prepared w4a16_gemv_grouped call: the problem table is checked and marshalled once, and
     each call of the plan is a single library call (a decode step reuses the same weight, input

@@ -45,6 +45,7 @@ WORKLOAD = "decoder36_h4096"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 PEAK_FP32_VALU_TFLOPS = 157.3  # fp32 vector (published)
+PEAK_FP64_TFLOPS = 78.6        # fp64 vector and matrix (published)
 GS = 1.0 / np.sqrt(32 * 7)
 PREFILL_M = 2048
 CSRC = os.path.join(ROOT, "w4a16_group_wise_amd", "csrc")
@@ -310,7 +311,68 @@ def components(stack, dev, reps=5):
     us = median_us(lambda: w4q.w4a16_gemm(xs["mlp"][:1], e["packed"], e["s16"], out=e["y1"]), n=20)
     gb = gemv_bytes(12288, 4096)
     out["gemv_single_12288x4096"] = {"us": round(us, 2), "frac_hbm": round(gb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    out["next_rows"] = next_rows(stack, dev, median_us)
     return out
+
+
+def next_rows(stack, dev, median_us):
+    """The rows beyond the step, each on one full-size shape of layer 0: the per-channel search,
+    the joint objective's coordinate descent and GPTQ on the q projection (4096x4096, its 8192-token
+    H, K = 40), and the fused LSQ + Adam update on the gate weight (12288x4096).  Rates are
+    algorithmic work over the median duration; the fp64 work is priced against the fp64 peak."""
+    import torch
+    import w4a16_group_wise_amd as w4q
+
+    per, xs = stack.lin[0], stack.x[0]
+    e = per["q"]
+    lin = e["lin"]
+    n, k = lin.d_out, lin.d_in
+    K = stack.K
+    h = w4q.quant_hessian(xs[lin.inp], workspace=stack.ws)
+    w4q.quant_scale_search(e["w"], h, stack.alpha, out=(e["scale"], e["idx"], e["obj"], None))
+    fp64 = PEAK_FP64_TFLOPS * 1e12
+    res = {}
+    # per-channel: K candidates x (E H) over the row, 2 K d_in^2 flop per row
+    t = median_us(lambda: w4q.quant_scale_search_pc(e["w"], h, stack.alpha), n=3)
+    fl = 2.0 * n * K * k * k
+    res["scale_search_pc_4096x4096"] = {"us": round(t, 1), "fp64_TFLOPs": round(fl / (t * 1e-6) / 1e12, 3),
+                                        "frac_fp64": round(fl / (t * 1e-6) / fp64, 4)}
+    # joint: U = E H (2 d_out d_in^2 flop) and the descent; the objective ratio it reached
+    ws = torch.empty(w4q.workspace_size("joint", n, k), dtype=torch.uint8, device=dev)
+    t_obj = median_us(lambda: w4q.quant_joint_objective(e["w"], e["scale"], h, workspace=ws), n=3)
+    res_ref = {}
+
+    def refine():
+        res_ref["r"] = w4q.quant_joint_refine(e["w"], h, stack.alpha, e["idx"], n_sweeps=2, workspace=ws)
+
+    t_ref = median_us(refine, n=3)
+    _, _, ob, oa, sw = res_ref["r"]
+    fl = 2.0 * n * k * k
+    res["joint_4096x4096"] = {"objective_us": round(t_obj, 1),
+                              "objective_fp64_TFLOPs": round(fl / (t_obj * 1e-6) / 1e12, 3),
+                              "objective_frac_fp64": round(fl / (t_obj * 1e-6) / fp64, 4),
+                              "refine_2_sweeps_us": round(t_ref, 1),
+                              "objective_after_over_before": round(float((oa / ob).mean().item()), 5),
+                              "rows_converged": int((sw < 2).sum().item())}
+    # GPTQ: Cholesky (d^3 / 3 flop) and the feedback sums (d_out d_in^2 flop)
+    wsg = torch.empty(w4q.workspace_size("gptq", n, k), dtype=torch.uint8, device=dev)
+    t = median_us(lambda: w4q.quant_gptq(e["w"], h, e["scale"], workspace=wsg), n=3)
+    fl = k ** 3 / 3.0 + 1.0 * n * k * k
+    res["gptq_4096x4096"] = {"us": round(t, 1), "fp64_TFLOPs": round(fl / (t * 1e-6) / 1e12, 3),
+                             "frac_fp64": round(fl / (t * 1e-6) / fp64, 4)}
+    del ws, wsg
+    # fused LSQ + Adam on the gate weight (parameters and moments updated in place, next forward)
+    g = per["gate"]
+    gn, gk = g["lin"].d_out, g["lin"].d_in
+    wc, sc = g["w"].clone(), g["scale"].clone()
+    mw, vw = torch.zeros_like(wc), torch.zeros_like(wc)
+    ms, vs = torch.zeros_like(sc), torch.zeros_like(sc)
+    t = median_us(lambda: w4q.lsq_adam_step(wc, sc, g["g"], GS, mw, vw, ms, vs, lr_w=1e-5, lr_s=1e-6, step=1,
+                                            with_w_hat_next=True), n=5)
+    nb = gn * gk * 32 + gn * gk // 32 * 24      # w, m_w, v_w read+written, g read, w_hat written
+    res["lsq_adam_12288x4096"] = {"us": round(t, 1), "GBps": round(nb / (t * 1e-6) / 1e9, 1),
+                                  "frac_hbm": round(nb / (t * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    return res
 
 
 def cpu_model():

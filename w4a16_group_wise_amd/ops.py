@@ -55,8 +55,8 @@ def _workspace(query: str, sizes, device, workspace: Optional[torch.Tensor]):
 
 
 def workspace_size(op: str, *sizes) -> int:
-    """Scratch bytes of the fastest schedule: op in ("quant_hessian", "w4a16_gemm",
-    "w4a16_gemm_dq") with (n_tok, d) or (m, d_out, d_in)."""
+    """Scratch bytes: op in ("quant_hessian", "w4a16_gemm", "w4a16_gemm_dq", "per_channel", "joint",
+    "gptq") with (n_tok, d), (m, d_out, d_in) or (d_out, d_in) as the C query takes them."""
     n = ctypes.c_size_t(0)
     check(op + "_workspace_size", getattr(lib(), op + "_workspace_size")(*sizes, ctypes.byref(n)))
     return n.value

@@ -553,3 +553,39 @@ def test_lsq_adam_steps(dev, wl, rows):
         w, s = out["w"], out["scale"]
         st = (out["m_w"], out["v_w"], out["m_s"], out["v_s"])
         g = (g * np.float32(0.9) + np.float32(0.1)).astype(np.float32)     # a different upstream gradient
+
+
+# The one-row product converts codes through an LDS table on launches of >= 48 MB of codes (and
+# by byte selects below): four 8192 x 4096 problems in one grouped launch take the table path.
+# One problem holds rows whose codes are zero except on a few of the smallest activations
+# (lognormal sigma 2.5), the case an offset encoding of the codes would fail.
+def test_gemv_grouped_table_path(dev):
+    d_out, d_in = 8192, 4096
+    rng = np.random.default_rng(61)
+    probs = []
+    for p in range(4):
+        x = synth.calib_x(61, p, 0, 1, d_in, 2.5 if p == 0 else 1.0)
+        if p == 0:
+            order = np.argsort(np.abs(bf16_bits_to_np(x[0])))
+            q = np.zeros((d_out, d_in), np.int8)
+            for r in range(0, d_out):
+                nz = 1 + r % 4
+                q[r, order[rng.choice(16, nz, replace=False)]] = rng.choice([-8, -5, -1, 1, 3, 7], nz)
+        else:
+            q = rng.integers(-8, 8, (d_out, d_in)).astype(np.int8)
+        nib = (q.astype(np.int16) & 0xF).astype(np.uint8)
+        packed = nib[:, 0::2] | (nib[:, 1::2] << 4)
+        s16 = rng.uniform(1e-3, 1e-2, (d_out, d_in // 32)).astype(np.float16).view(np.uint16)
+        probs.append((x, packed, s16))
+    say("gemv grouped table path, 4 x 8192 x 4096")
+    xs = [dev_bf16(x, dev) for x, _, _ in probs]
+    ps = [torch.from_numpy(pk).to(dev) for _, pk, _ in probs]
+    ss = [torch.from_numpy(s.view(np.float16)).to(dev) for _, _, s in probs]
+    ys = w4q.w4a16_gemv_grouped(xs, ps, ss)
+    for i, (x, packed, s16) in enumerate(probs):
+        cols = np.sort(rng.choice(d_out, 48, replace=False))
+        yr, ya = oracle.gemm_cols(x, packed, s16, cols)
+        check_gemm(ys[i].cpu().numpy()[:, cols], yr, ya)
+        y1 = w4q.w4a16_gemm(xs[i], ps[i], ss[i]).cpu().numpy().astype(np.float64)
+        yg = ys[i].cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(yg - y1) <= 1e-5 * (np.abs(y1).max() + 1e-30))

@@ -477,15 +477,32 @@ __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, false));
 }
 
+// code byte e (codes 2j and 2j + 1 in its low and high nibble) -> the exact bf16 pair of the two
+// codes (small integers), low half = code 2j
+__device__ __forceinline__ uint32_t lut_pair(int e) {
+  const int lo = static_cast<int>(static_cast<uint32_t>(e) << 28) >> 28;  // sign-extended low nibble
+  const int hi = static_cast<int>(static_cast<uint32_t>(e) << 24) >> 28;  // sign-extended high nibble
+  const uint32_t blo = __builtin_bit_cast(uint32_t, static_cast<float>(lo)) >> 16;  // exact in bf16
+  const uint32_t bhi = __builtin_bit_cast(uint32_t, static_cast<float>(hi)) >> 16;
+  return blo | (bhi << 16);
+}
+
+// threads per workgroup of the stream kernel: 512 with the code table (two workgroups of 64 KB of
+// table per compute unit), 256 without
+template <bool kLut>
+constexpr int stream_threads() { return kLut ? 512 : 256; }
+
 // The argument table is copied to LDS once per workgroup: the problem of an item is then one
 // ballot over first[] (the number of problems q >= 1 with first[q] <= item) and a few LDS reads.
-template <int LPR, int RS>
-__global__ __launch_bounds__(kThreads) void gemv_stream_kernel(const GroupArgs a) {
+template <int LPR, int RS, bool kLut>
+__global__ __launch_bounds__(stream_threads<kLut>()) void gemv_stream_kernel(const GroupArgs a) {
+  constexpr int kStreamThreads = stream_threads<kLut>();
+  __shared__ uint32_t lut[kLut ? 256 * 64 : 1];
   __shared__ GroupArgs t;
   {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(&a);
     uint32_t* dst = reinterpret_cast<uint32_t*>(&t);
-    for (int i = threadIdx.x; i < static_cast<int>(sizeof(GroupArgs) / 4); i += kThreads) dst[i] = src[i];
+    for (int i = threadIdx.x; i < static_cast<int>(sizeof(GroupArgs) / 4); i += kStreamThreads) dst[i] = src[i];
   }
   __syncthreads();
   constexpr int RPS = 64 / LPR;
@@ -497,10 +514,11 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(const GroupArgs a
   const int64_t nitems = uniform_int(t.first[n]);
   const int ydt = uniform_int(t.y_dtype);
   const int fq = lane >= 1 && lane < n ? t.first[lane] : 0x7FFFFFFF;
-  const int64_t W = static_cast<int64_t>(uniform_int(static_cast<int>(gridDim.x))) * (kThreads / 64);
-  const int64_t w0 = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + uniform_int(threadIdx.x / 64);
-  if (w0 >= nitems) return;  // uniform per wavefront; no barrier follows
+  const int64_t W = static_cast<int64_t>(uniform_int(static_cast<int>(gridDim.x))) * (kStreamThreads / 64);
+  const int64_t w0 = static_cast<int64_t>(blockIdx.x) * (kStreamThreads / 64) + uniform_int(threadIdx.x / 64);
+  const bool active = w0 < nitems;  // uniform per wavefront
   const uint32_t xoff = static_cast<uint32_t>(j * kGroup);
+  const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
 
   auto problem_of = [&](int64_t item) { return __builtin_popcountll(__ballot(fq <= item)); };
   auto setup = [&](int64_t item, Src<RS>& sr) {
@@ -550,20 +568,43 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(const GroupArgs a
   float acc[RS];
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs) acc[rs] = 0.0f;
+  // code byte k of word cw -> its two codes as an exact bf16 pair, from the lane's copy of the table
+  // (dword e * 64 + lane: bank = lane, no conflict); the address is one byte permute
+  auto pair = [&](uint32_t cw, int k) {
+    const uint32_t addr = __builtin_amdgcn_perm(cw, lane4, 0x0C0C0400u | (static_cast<uint32_t>(4 + k) << 8));
+    return __builtin_bit_cast(bf16x2, *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lut) + addr));
+  };
   auto compute = [&](const Chunk<1, RS>& cur) {
     float sums[RS];
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs) sums[rs] = 0.0f;
+    if constexpr (kLut) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      float xf[8];
-      x_f32(cur.xv[0][b], xf);
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t xw[4] = {cur.xv[0][b].x, cur.xv[0][b].y, cur.xv[0][b].z, cur.xv[0][b].w};
 #pragma unroll
-      for (int rs = 0; rs < RS; ++rs) sums[rs] = dot8(xf, cur.code[rs][b], sums[rs]);
+        for (int rs = 0; rs < RS; ++rs) {
+          const uint32_t cw = cur.code[rs][b];
+#pragma unroll
+          for (int k = 0; k < 4; ++k)  // activations 2k, 2k + 1 of dword b against codes 2k, 2k + 1
+            sums[rs] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xw[k]), pair(cw, k), sums[rs], false);
+        }
+      }
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs)
+        acc[rs] = __builtin_fmaf(f16_bits_to_f32(static_cast<uint16_t>(cur.sc[rs])), sums[rs], acc[rs]);
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        float xf[8];
+        x_f32(cur.xv[0][b], xf);
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs) sums[rs] = dot8(xf, cur.code[rs][b], sums[rs]);
+      }
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs)
+        acc[rs] = __builtin_fmaf(scale16(cur.sc[rs]), sums[rs], acc[rs]);
     }
-#pragma unroll
-    for (int rs = 0; rs < RS; ++rs)
-      acc[rs] = __builtin_fmaf(scale16(cur.sc[rs]), sums[rs], acc[rs]);
   };
   auto store = [&](void* y, int64_t row, float v) {
     if (ydt == 0)
@@ -613,10 +654,10 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(const GroupArgs a
   Src<RS> ls;
   int64_t li = w0;
   int lc = 0;
-  setup(li, ls);
+  if (active) setup(li, ls);
   int64_t ci = w0;
   int cc = 0;
-  int cn = ls.nchunk;
+  int cn = active ? ls.nchunk : 0;
   auto advance_load = [&]() {
     if (++lc == ls.nchunk) {
       lc = 0;
@@ -634,23 +675,54 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(const GroupArgs a
     cn = uniform_int(t.d_in[problem_of(ci)]) / kGroup / LPR;
     return true;
   };
-  // The loads are issued unconditionally: past the wavefront's last unit the cursor still holds
-  // the last item, so a spare (valid, unused) unit is loaded.  Every reduction then has the same
-  // number of loads after it, and the wait before it is a fixed count instead of a full drain.
   Chunk<1, RS> ca, cb;
-  load(ls, lc, ca);
-  advance_load();
-  while (true) {
-    load(ls, lc, cb);
-    if (li < nitems) advance_load();
-    asm volatile("" ::: "memory");
-    compute(ca);
-    if (!advance_compute()) break;
+  if constexpr (kLut) {
+    // The first two units' loads are issued before the code table is written, so that the table's
+    // 64 KB of LDS stores overlap their latency; every wavefront (idle ones too) writes its share
+    // of the table and meets the barrier before any wavefront returns.
+    if (active) {
+      load(ls, lc, ca);
+      advance_load();
+      load(ls, lc, cb);
+      if (li < nitems) advance_load();
+    }
+    for (int i = threadIdx.x; i < 256 * 64 / 4; i += kStreamThreads) {  // 4 copies of entry i / 16 per store
+      const uint32_t v = lut_pair(i >> 4);
+      reinterpret_cast<u32x4*>(lut)[i] = u32x4{v, v, v, v};
+    }
+    __syncthreads();
+    if (!active) return;  // no barrier follows
+    while (true) {
+      asm volatile("" ::: "memory");
+      compute(ca);
+      if (!advance_compute()) break;
+      load(ls, lc, ca);
+      if (li < nitems) advance_load();
+      asm volatile("" ::: "memory");
+      compute(cb);
+      if (!advance_compute()) break;
+      load(ls, lc, cb);
+      if (li < nitems) advance_load();
+    }
+  } else {
+    // The loads are issued unconditionally: past the wavefront's last unit the cursor still holds
+    // the last item, so a spare (valid, unused) unit is loaded.  Every reduction then has the same
+    // number of loads after it, and the wait before it is a fixed count instead of a full drain.
+    if (!active) return;  // no barrier follows
     load(ls, lc, ca);
-    if (li < nitems) advance_load();
-    asm volatile("" ::: "memory");
-    compute(cb);
-    if (!advance_compute()) break;
+    advance_load();
+    while (true) {
+      load(ls, lc, cb);
+      if (li < nitems) advance_load();
+      asm volatile("" ::: "memory");
+      compute(ca);
+      if (!advance_compute()) break;
+      load(ls, lc, ca);
+      if (li < nitems) advance_load();
+      asm volatile("" ::: "memory");
+      compute(cb);
+      if (!advance_compute()) break;
+    }
   }
 }
 
@@ -698,9 +770,9 @@ namespace {
 
 // Workgroups of a kernel that fit on the device at once: compute units x resident workgroups per
 // compute unit, queried once per device and kernel.
-int resident_grid(const void* kernel, int slot) {
+int resident_grid(const void* kernel, int slot, int threads = kThreads) {
   constexpr int kDevices = 64;
-  static std::atomic<int> cache[kDevices][8];
+  static std::atomic<int> cache[kDevices][24];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
   if (dev < kDevices) {
@@ -709,21 +781,36 @@ int resident_grid(const void* kernel, int slot) {
   }
   int cus = 0, per = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kThreads, 0) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess) return 0;
   const int v = cus * (per > 0 ? per : 1);
   if (dev < kDevices) cache[dev][slot].store(v, std::memory_order_relaxed);
   return v;
 }
 
-template <int LPR>
+template <int LPR, int RS, bool kLut>
 int launch_stream(const GroupArgs& a, int64_t items, int slot, hipStream_t s) {
-  auto* k = &gemv_stream_kernel<LPR, 4>;
-  const int res = resident_grid(reinterpret_cast<const void*>(k), slot);
+  constexpr int nt = stream_threads<kLut>();
+  auto* k = &gemv_stream_kernel<LPR, RS, kLut>;
+  const int res = resident_grid(reinterpret_cast<const void*>(k), slot, nt);
   if (res <= 0) return W4Q_EHIP;
-  const int64_t need = (items + kThreads / 64 - 1) / (kThreads / 64);
+  const int64_t need = (items + nt / 64 - 1) / (nt / 64);
   const unsigned grid = static_cast<unsigned>(need < res ? need : res);
-  hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(nt), 0, s, a);
   return w4q_launch_status();
+}
+
+template <bool kLut>
+int launch_stream_lpr(const GroupArgs& a, int64_t items, int lpr, hipStream_t s) {
+  constexpr int base = kLut ? 0 : 7;  // resident-grid cache slots
+  switch (lpr) {
+    case 64: return launch_stream<64, 4, kLut>(a, items, base + 0, s);
+    case 32: return launch_stream<32, 4, kLut>(a, items, base + 1, s);
+    case 16: return launch_stream<16, 4, kLut>(a, items, base + 2, s);
+    case 8: return launch_stream<8, 4, kLut>(a, items, base + 3, s);
+    case 4: return launch_stream<4, 4, kLut>(a, items, base + 4, s);
+    case 2: return launch_stream<2, 4, kLut>(a, items, base + 5, s);
+    default: return launch_stream<1, 4, kLut>(a, items, base + 6, s);
+  }
 }
 
 // lane split of a launch: the largest power of two (<= 64) dividing every group count
@@ -742,12 +829,17 @@ int64_t chunk_items(const w4q_gemv_problem* probs, int cnt, int lpr) {
   return items;
 }
 
-// problems [0, cnt) of `probs` in one launch (sizes checked by w4q_gemv_group_fits)
+// problems [0, cnt) of `probs` in one launch (sizes checked by w4q_gemv_group_fits).  Launches of
+// at least 48 MB of codes whose items fill every wavefront of a resident grid convert codes through
+// the LDS table (its 64 KB per workgroup are written once and amortised over many units); smaller
+// ones take the byte-select conversion, whose workgroups start streaming at once.  (Measured per
+// launch, 4096x4096 repeated: 5.4 us with the table, 4.0 us without; 24576x4096: 12.3 vs 13.9 us;
+// all 252 linears of the 36-layer stack in 64-problem launches: 699 vs 836 us.)
 int launch_group_chunk(const w4q_gemv_problem* probs, int cnt, int y_dtype, hipStream_t s) {
   GroupArgs a = {};
   const int lpr = chunk_lpr(probs, cnt);
   const int rows_per_item = 4 * (64 / lpr);
-  int64_t items = 0;
+  int64_t items = 0, bytes = 0;
   for (int i = 0; i < cnt; ++i) {
     const w4q_gemv_problem& q = probs[i];
     a.x[i] = q.x;
@@ -758,19 +850,13 @@ int launch_group_chunk(const w4q_gemv_problem* probs, int cnt, int y_dtype, hipS
     a.d_in[i] = static_cast<int>(q.d_in);
     a.first[i] = static_cast<int>(items);
     items += (q.d_out + rows_per_item - 1) / rows_per_item;
+    bytes += q.d_out * q.d_in / 2;
   }
   a.first[cnt] = static_cast<int>(items);
   a.n = cnt;
   a.y_dtype = y_dtype;
-  switch (lpr) {
-    case 64: return launch_stream<64>(a, items, 0, s);
-    case 32: return launch_stream<32>(a, items, 1, s);
-    case 16: return launch_stream<16>(a, items, 2, s);
-    case 8: return launch_stream<8>(a, items, 3, s);
-    case 4: return launch_stream<4>(a, items, 4, s);
-    case 2: return launch_stream<2>(a, items, 5, s);
-    default: return launch_stream<1>(a, items, 6, s);
-  }
+  if (bytes >= (int64_t(48) << 20) && items >= 4096) return launch_stream_lpr<true>(a, items, lpr, s);
+  return launch_stream_lpr<false>(a, items, lpr, s);
 }
 
 }  // namespace

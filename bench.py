@@ -9,16 +9,17 @@ are drawn once on the GPU (seeded; synth.device_*) and stay resident in HBM.
 
 One step = one pass of the whole hot path over the stack, in a decoder's order:
   for each layer: quant_hessian of its 4 inputs -> quant_scale_search, quant_pack of its 7
-  linears -> lsq_fwd + lsq_bwd (fused forward) on gate and up -> w4a16_gemm at M = 2048 (prefill)
-  on its 7 linears;
+  linears -> lsq_fwd + lsq_bwd (fused forward) on gate and up -> w4a16_gemm_dq at M = 2048
+  (prefill, weights dequantized to bf16 in registers) on its 7 linears;
   then the decode pass: w4a16_gemm at M = 1 over all 252 linears as grouped launches per decoder
   phase (q|k|v, o, gate|up, down: the order a decoder issues them in), replayed from a HIP graph.
 `value` is the decode pass's HBM bandwidth (bytes of codes, scales, x and y per pass / its
 time in the timed region).  Every launch is bracketed by HIP events on its stream; `kernels`
 reports each family's algorithmic rate (sum of the work of its launches / sum of their
 durations) against its roofline, and `roofline` repeats it for the family with the largest share
-of the step.  `components` adds measurements outside the step: the dequantizing prefill product
-(w4a16_gemm_dq), the decode pass in other launch orders, and single-launch rates.
+of the step.  `components` adds measurements outside the step: the prefill product on exact weights
+(w4a16_gemm) beside the dequantizing one, the decode pass in other launch orders, single-launch
+rates, and the rows beyond the step (per-channel search, joint descent, GPTQ, fused LSQ + Adam).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--no-cpu] [--no-components]
     python bench.py --pmc-copy                       (copy kernel that calibrates the counters)
@@ -57,7 +58,7 @@ KERNELS = {
     "pack": ("pack_lsq.hip", ["pack_kernel"]),
     "lsq_fwd": ("pack_lsq.hip", ["lsq_fwd_kernel"]),
     "lsq_bwd": ("pack_lsq.hip", ["lsq_bwd_kernel"]),
-    "prefill_gemm": ("gemm.hip", ["gemm_group_kernel", "gemm_dq_kernel", "gemm_fixup_kernel"]),
+    "prefill_gemm": ("gemm.hip", ["gemm_dq_kernel", "gemm_fixup_kernel"]),
     "decode_gemv": ("gemv.hip", ["gemv_stream_kernel"]),
 }
 
@@ -186,8 +187,9 @@ class Stack:
         for name, e in self.lin[layer].items():
             lin = e["lin"]
             xt = xs[lin.inp][:PREFILL_M]
+            # prefill: the product with the weights dequantized to bf16 in registers
             out.append(("prefill_gemm", 2 * PREFILL_M * lin.d_out * lin.d_in,
-                        lambda e=e, xt=xt, lin=lin: w4q.w4a16_gemm(
+                        lambda e=e, xt=xt, lin=lin: w4q.w4a16_gemm_dq(
                             xt, e["packed"], e["s16"], out=self.view(self.y_pre, PREFILL_M, lin.d_out),
                             workspace=self.ws)))
         return out
@@ -247,8 +249,9 @@ def run_step(stack, events):
 
 
 def components(stack, dev, reps=5):
-    """Measurements outside the step: the dequantizing prefill product, the decode pass in other
-    launch orders, single launches of the largest shapes."""
+    """Measurements outside the step: the prefill product on exact weights beside the step's
+    dequantizing one, the decode pass in other launch orders, single launches of the largest
+    shapes, and the rows beyond the step."""
     import torch
     import w4a16_group_wise_amd as w4q
 
@@ -267,7 +270,7 @@ def components(stack, dev, reps=5):
         return float(np.median(ts))
 
     out = {}
-    # prefill with bf16-dequantized weights (w4a16_gemm_dq) on each distinct shape of layer 0
+    # prefill on each distinct shape of layer 0: bf16-dequantized weights (the step's) and exact ones
     per = stack.lin[0]
     xs = stack.x[0]
     dq = {}
@@ -442,7 +445,7 @@ def cpu_baseline(budget_s=20.0):
     decode_gbps = gemv_bytes(lin.d_out, lin.d_in) * reps / t / 1e9
     rates["decode_GBps"] = decode_gbps
     # prefill on 16 output columns
-    tg, _ = timed(lambda: oracle.gemm_cols(x[:PREFILL_M], packed_all, s16_all, np.arange(16)))
+    tg, _ = timed(lambda: oracle.gemm_cols(x[:PREFILL_M], packed_all, s16_all, np.arange(16), dequant_bf16=True))
     rates["prefill_GFLOPs"] = 2 * PREFILL_M * 16 * lin.d_in / tg / 1e9
     # the whole step extrapolated from these rates over the stack's work
     wl = synth.WORKLOADS[WORKLOAD]

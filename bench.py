@@ -309,6 +309,35 @@ def components(stack, dev, reps=5):
                                                    "frac_hbm": round(B / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
     out["decode_pass"]["bytes"] = B
     out["decode_pass"]["linears"] = len(flat)
+    # the ceiling of the per-phase launch structure: the same dependent launches (phase sizes, in
+    # a graph) done by a plain streaming read of the library's read probe
+    phase_bytes = []
+    for layer in range(stack.layers):
+        per = stack.lin[layer]
+        for names in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+            nb = sum(per[nm]["packed"].numel() + 2 * per[nm]["s16"].numel() for nm in names)
+            phase_bytes.append((nb + 15) // 16 * 16)
+    buf = torch.empty(sum(phase_bytes), dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(65536, dtype=torch.int32, device=dev)
+    offs = np.cumsum([0] + phase_bytes[:-1])
+    views = [buf[o:o + b] for o, b in zip(offs, phase_bytes)]
+
+    def reads():
+        for v in views:
+            w4q.probe_read(v, nontemporal=True, sink=sink)
+
+    reads()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        reads()
+    us = median_us(gr.replay)
+    out["decode_pass"]["per_phase_read_floor"] = {
+        "us": round(us, 1), "frac_hbm": round(sum(phase_bytes) / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "how": "144 dependent streaming reads (w4q_probe_read, non-temporal) of the phase sizes, graph-replayed"}
+    del buf, views
+    torch.cuda.empty_cache()
     # one M = 1 launch of the largest weight (gate 12288x4096, 28 MB)
     e = per["gate"]
     us = median_us(lambda: w4q.w4a16_gemm(xs["mlp"][:1], e["packed"], e["s16"], out=e["y1"]), n=20)

@@ -492,19 +492,15 @@ __device__ __forceinline__ uint32_t lut_pair(int e) {
 template <bool kLut>
 constexpr int stream_threads() { return kLut ? 512 : 256; }
 
-// The argument table is copied to LDS once per workgroup: the problem of an item is then one
-// ballot over first[] (the number of problems q >= 1 with first[q] <= item) and a few LDS reads.
+// The argument table is read where it is passed (the kernel arguments): the problem of an item
+// is one ballot over first[] (the number of problems q >= 1 with first[q] <= item), then scalar
+// reads of that problem's entries.  (Staging the table through LDS first put a barrier and an LDS
+// round trip before the first code load: per-phase decode pass of the 36-layer stack 1262 ->
+// 1205 us without it.)
 template <int LPR, int RS, bool kLut>
-__global__ __launch_bounds__(stream_threads<kLut>()) void gemv_stream_kernel(const GroupArgs a) {
+__global__ __launch_bounds__(stream_threads<kLut>()) void gemv_stream_kernel(const GroupArgs t) {
   constexpr int kStreamThreads = stream_threads<kLut>();
   __shared__ uint32_t lut[kLut ? 256 * 64 : 1];
-  __shared__ GroupArgs t;
-  {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(&a);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(&t);
-    for (int i = threadIdx.x; i < static_cast<int>(sizeof(GroupArgs) / 4); i += kStreamThreads) dst[i] = src[i];
-  }
-  __syncthreads();
   constexpr int RPS = 64 / LPR;
   constexpr int ROWS = RPS * RS;
   const int lane = threadIdx.x & 63;

@@ -85,37 +85,51 @@ __global__ __launch_bounds__(256) void build_kernel(const float* __restrict__ h,
 }
 
 // --------------------------------------------------------------------- blocked Cholesky
-// diagonal block [k0, k0 + 64): factor in LDS (right-looking), lower triangle written back;
-// a pivot that is not positive sets *info
+// diagonal block [k0, k0 + 64), right-looking: thread (i, m) = (tid / 4, tid % 4) keeps entries
+// (i, 16 m .. 16 m + 15) of the block in registers; for column j its owners (m = j / 16) publish
+// column j through LDS (two buffers, so one barrier per column), every thread then forms its own
+// L_ij and updates its entries k in (j, i].  A pivot that is not positive sets *info.
 __global__ __launch_bounds__(256) void chol_diag_kernel(double* __restrict__ a, int64_t dp, int64_t k0,
                                                         int* __restrict__ info) {
-  __shared__ double t[kNb][kNb + 1];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < kNb * kNb; e += 256) t[e / kNb][e % kNb] = a[(k0 + e / kNb) * dp + k0 + e % kNb];
-  __syncthreads();
-  for (int j = 0; j < kNb; ++j) {
-    const double p = t[j][j];
-    if (tid == 0 && !(p > 0.0) && info != nullptr) *info = 1;
-    const double dj = __builtin_sqrt(p);
-    __syncthreads();
-    if (tid == 0) t[j][j] = dj;
-    for (int i = j + 1 + tid; i < kNb; i += 256) t[i][j] /= dj;
-    __syncthreads();
-    const int m = kNb - 1 - j;  // trailing rows/cols j+1 .. 63: lower triangle incl. diagonal
-    for (int e = tid; e < m * m; e += 256) {
-      const int i = j + 1 + e / m, k = j + 1 + e % m;
-      if (k <= i) t[i][k] -= t[i][j] * t[k][j];
-    }
-    __syncthreads();
+  __shared__ double colbuf[2][kNb];
+  __shared__ double lo[kNb][kNb + 1];
+  const int tid = threadIdx.x, i = tid >> 2, m = tid & 3;
+  double t[16];
+  const double* arow = a + (k0 + i) * dp + k0 + 16 * m;
+#pragma unroll
+  for (int c = 0; c < 16; c += 2) {
+    const f64x2 v = *reinterpret_cast<const f64x2*>(arow + c);
+    t[c] = v.x;
+    t[c + 1] = v.y;
   }
+  for (int jb = 0; jb < 4; ++jb) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int j = 16 * jb + c, b = c & 1;
+      if (m == jb) colbuf[b][i] = t[c];
+      __syncthreads();
+      const double p = colbuf[b][j];
+      if (tid == 0 && !(p > 0.0) && info != nullptr) *info = 1;
+      const double dj = __builtin_sqrt(p);
+      const double lij = i == j ? dj : colbuf[b][i] / dj;
+      if (m == jb && i >= j) lo[i][j] = lij;
+      const double f = lij / dj;
+#pragma unroll
+      for (int c2 = 0; c2 < 16; ++c2) {
+        const int k = 16 * m + c2;
+        if (k > j && k <= i) t[c2] -= f * colbuf[b][k];
+      }
+    }
+  }
+  __syncthreads();
   for (int e = tid; e < kNb * kNb; e += 256) {
-    const int i = e / kNb, k = e % kNb;
-    if (k <= i) a[(k0 + i) * dp + k0 + k] = t[i][k];
+    const int r = e / kNb, k = e % kNb;
+    if (k <= r) a[(k0 + r) * dp + k0 + k] = lo[r][k];
   }
 }
 
 // panel below the diagonal block: row i solves x L11^T = a_i (one wavefront per row, lane j
-// holds x_j; the columns are settled in order)
+// holds x_j; the columns are settled in order, x_j = s_j / L_jj taken from lane j by readlane)
 __global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ a, int64_t dp, int64_t k0) {
   __shared__ double l[kNb][kNb + 1];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -124,9 +138,14 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ a,
   const int64_t row = k0 + kNb + static_cast<int64_t>(blockIdx.x) * 4 + (tid >> 6);
   if (row >= dp) return;  // uniform per wavefront; no barrier follows
   double s = a[row * dp + k0 + lane];
+  const double ldiag = l[lane][lane];
   double x = 0.0;
   for (int j = 0; j < kNb; ++j) {
-    const double xj = __shfl(s / l[j][j], j);
+    const double q = s / ldiag;  // lane j's value is x_j
+    const uint64_t qb = __builtin_bit_cast(uint64_t, q);
+    const uint32_t lo32 = __builtin_amdgcn_readlane(static_cast<uint32_t>(qb), j);
+    const uint32_t hi32 = __builtin_amdgcn_readlane(static_cast<uint32_t>(qb >> 32), j);
+    const double xj = __builtin_bit_cast(double, (static_cast<uint64_t>(hi32) << 32) | lo32);
     if (lane == j) x = xj;
     if (lane > j) s -= xj * l[lane][j];
   }
@@ -184,70 +203,91 @@ __device__ __forceinline__ double rfac(const double* __restrict__ l, int64_t dp,
   return l[(d - 1 - p) * dp + (d - 1 - i)];
 }
 
-// Block of columns [c0, c0 + nb) for 16 rows per workgroup.  Wavefront w first sums over the
-// earlier columns for block columns 16w .. 16w+15 on the matrix cores; then each wavefront takes
-// 4 of the 16 rows, 16 lanes a row, each lane 4 of the block's columns, and the block's columns
-// are quantized in order with the correction of every later column of the block kept current.
-__global__ __launch_bounds__(256) void gptq_block_kernel(const float* __restrict__ w, int64_t d_out, int64_t d_in,
-                                                         const float* __restrict__ scale,
-                                                         const double* __restrict__ l, int64_t dp,
-                                                         const uint8_t* __restrict__ dead,
-                                                         double* __restrict__ delta, float* __restrict__ w_hat,
-                                                         int64_t c0) {
-  __shared__ double cs[16][kNb + 1];
+// Block of columns [c0, c0 + nb) for 16 rows per workgroup (16 wavefronts).  First the sums over
+// the earlier columns on the matrix cores: wavefront w takes block columns 16 (w % 4) .. + 15 and
+// every fourth 16-column step of the earlier columns from step w / 4 on (loads of the next step
+// issued before the products of the current one); the four partial sums of an entry are added in
+// LDS in a fixed order.  Then wavefronts 0..3 take 4 of the 16 rows each, 16 lanes a row, each
+// lane 4 of the block's columns, and the block's columns are quantized in order with the
+// correction of every later column of the block kept current.
+constexpr int kBlockThreads = 1024;
+
+__global__ __launch_bounds__(kBlockThreads) void gptq_block_kernel(const float* __restrict__ w, int64_t d_out,
+                                                                   int64_t d_in, const float* __restrict__ scale,
+                                                                   const double* __restrict__ l, int64_t dp,
+                                                                   const uint8_t* __restrict__ dead,
+                                                                   double* __restrict__ delta,
+                                                                   float* __restrict__ w_hat, int64_t c0) {
+  __shared__ double part[4][16][kNb + 1];
   __shared__ double rd[kNb][kNb + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, j = lane & 15;
+  const int cg = wave & 3, kq = wave >> 2;
   const int64_t G = d_in / kGroup;
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int nb = d_in - c0 < kNb ? static_cast<int>(d_in - c0) : kNb;
-  // 1. C[row][c0 + 16 wave + j] = sum_{p < c0} delta[row][p] R[p][c0 + 16 wave + j]
+  // 1. partial C[row][c0 + 16 cg + j] over the steps kk0 = 16 (kq + 4 n) < c0
   {
     const int64_t ra = r0 + j;
     const bool va = ra < d_out;
-    const double* drow = delta + (va ? ra : 0) * d_in;
-    const int64_t col = c0 + 16 * wave + j;
+    const double* drow = delta + (va ? ra : 0) * d_in + 4 * q;
+    const int64_t col = c0 + 16 * cg + j;
     const bool vc = col < d_in;
+    // R[p][col] = L[d-1-p][d-1-col]: rows p = kk0 + 4 q + s
+    const double* rcol = l + (d_in - 1 - 4 * q) * dp + (vc ? d_in - 1 - col : 0);
     f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
-    for (int64_t kk0 = 0; kk0 < c0; kk0 += 16) {
-      const f64x2 a01 = *reinterpret_cast<const f64x2*>(drow + kk0 + 4 * q);
-      const f64x2 a23 = *reinterpret_cast<const f64x2*>(drow + kk0 + 4 * q + 2);
-      double av[4] = {a01.x, a01.y, a23.x, a23.y};
-      double bv[4];
+    double av[4], bv[4], an[4], bn[4];
+    auto fetch = [&](int64_t kk0, double* ao, double* bo) {
+      const f64x2 a01 = *reinterpret_cast<const f64x2*>(drow + kk0);
+      const f64x2 a23 = *reinterpret_cast<const f64x2*>(drow + kk0 + 2);
+      ao[0] = va ? a01.x : 0.0;
+      ao[1] = va ? a01.y : 0.0;
+      ao[2] = va ? a23.x : 0.0;
+      ao[3] = va ? a23.y : 0.0;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bv[s] = vc ? rfac(l, dp, d_in, kk0 + 4 * q + s, col) : 0.0;
-        if (!va) av[s] = 0.0;
-      }
+      for (int s = 0; s < 4; ++s) bo[s] = vc ? rcol[-(kk0 + s) * dp] : 0.0;
+    };
+    int64_t kk0 = 16 * kq;
+    if (kk0 < c0) fetch(kk0, av, bv);
+    while (kk0 < c0) {
+      const int64_t kn = kk0 + 64;
+      if (kn < c0) fetch(kn, an, bn);
 #pragma unroll
       for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av[s], bv[s], acc, 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        av[s] = an[s];
+        bv[s] = bn[s];
+      }
+      kk0 = kn;
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) cs[4 * r + q][16 * wave + j] = acc[r];
+    for (int r = 0; r < 4; ++r) part[kq][4 * r + q][16 * cg + j] = acc[r];
   }
   // 2. the block's diagonal part of R
-  for (int e = tid; e < kNb * kNb; e += 256) {
+  for (int e = tid; e < kNb * kNb; e += kBlockThreads) {
     const int i = e / kNb, k = e % kNb;
     rd[i][k] = (i <= k && i < nb && k < nb) ? rfac(l, dp, d_in, c0 + i, c0 + k) : 0.0;
   }
   __syncthreads();
+  if (wave >= 4) return;  // no barrier follows
   // 3. the block's columns in order: row 4 wave + lane / 16 of the workgroup's 16, lane % 16 owns
   //    block columns 4 (lane % 16) .. + 3
-  const int rr = lane >> 4, part = lane & 15;
+  const int rr = lane >> 4, pt = lane & 15;
   const int64_t row = r0 + 4 * wave + rr;
   const bool vr = row < d_out;
   double cl[4], wl[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int k = 4 * part + t;
-    cl[t] = cs[4 * wave + rr][k];
+    const int k = 4 * pt + t, lr = 4 * wave + rr;
+    cl[t] = ((part[0][lr][k] + part[1][lr][k]) + part[2][lr][k]) + part[3][lr][k];
     const bool in = vr && k < nb;
     wl[t] = (in && dead[c0 + k] == 0) ? static_cast<double>(w[row * d_in + c0 + k]) : 0.0;
   }
   for (int i = 0; i < nb; ++i) {
     const int owner = i >> 2, ti = i & 3;
     double di = 0.0;
-    if (part == owner) {
+    if (pt == owner) {
       double wi = wl[0], ci = cl[0];
 #pragma unroll
       for (int t = 1; t < 4; ++t)
@@ -267,7 +307,7 @@ __global__ __launch_bounds__(256) void gptq_block_kernel(const float* __restrict
     di = __shfl(di, (lane & ~15) | owner);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int k = 4 * part + t;
+      const int k = 4 * pt + t;
       if (k > i && k < nb) cl[t] += rd[i][k] * di;
     }
   }
@@ -316,8 +356,8 @@ int w4q_launch_gptq(const float* w, int64_t d_out, int64_t d_in, const float* h,
     }
   }
   for (int64_t c0 = 0; c0 < d_in; c0 += kNb)
-    W4Q_GO(gptq_block_kernel, dim3(cdiv(d_out, 16)), dim3(256), 0, s, w, d_out, d_in, scale, a, dp, dead, delta,
-           w_hat, c0);
+    W4Q_GO(gptq_block_kernel, dim3(cdiv(d_out, 16)), dim3(kBlockThreads), 0, s, w, d_out, d_in, scale, a, dp, dead,
+           delta, w_hat, c0);
 #undef W4Q_GO
   return W4Q_OK;
 }

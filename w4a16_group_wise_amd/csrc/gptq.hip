@@ -29,15 +29,16 @@ constexpr int kNb = 64;  // panel and column-block width
 
 __device__ __forceinline__ int64_t rup64(int64_t v) { return (v + 63) & ~int64_t(63); }
 
-// nearest code of the fp64 value v at step d (fp32, >= 0): ties to the even code, clamped.
-// (c +- 1/2) d is exact in fp64 and v - (c +- 1/2) d has the sign of the exact difference.
-__device__ __forceinline__ double code64(double v, double d) {
+// nearest code of the fp64 value v at step d (fp32, >= 0; inv_d ~ 1 / d): ties to the even code,
+// clamped.  The first guess rint(v inv_d) is within one code of the answer; (c +- 1/2) d is exact in
+// fp64 and v - (c +- 1/2) d has the sign of the exact difference, which settles it.
+__device__ __forceinline__ double code64(double v, double d, double inv_d) {
   if (!(d > 0.0)) return 0.0;
-  double c = __builtin_rint(v / d);
+  double c = __builtin_rint(v * inv_d);
   c = __builtin_fmin(__builtin_fmax(c, -8.0), 7.0);
   const double rh = v - (c + 0.5) * d;
   const double rl = v - (c - 0.5) * d;
-  const bool odd = __builtin_fmod(c, 2.0) != 0.0;
+  const bool odd = (static_cast<int>(c) & 1) != 0;
   const bool up = (rh > 0.0 || (rh == 0.0 && odd)) && c < 7.0;
   const bool dn = (rl < 0.0 || (rl == 0.0 && odd)) && c > -8.0;
   return c + (up ? 1.0 : 0.0) - (dn ? 1.0 : 0.0);
@@ -87,8 +88,8 @@ __global__ __launch_bounds__(256) void build_kernel(const float* __restrict__ h,
 // --------------------------------------------------------------------- blocked Cholesky
 // diagonal block [k0, k0 + 64), right-looking: thread (i, m) = (tid / 4, tid % 4) keeps entries
 // (i, 16 m .. 16 m + 15) of the block in registers; for column j its owners (m = j / 16) publish
-// column j through LDS (two buffers, so one barrier per column), every thread then forms its own
-// L_ij and updates its entries k in (j, i].  A pivot that is not positive sets *info.
+// column j through LDS (two buffers, so one barrier per column), every thread then updates its
+// entries by L_ij L_kj and the owners record L_ij.  A pivot that is not positive sets *info.
 __global__ __launch_bounds__(256) void chol_diag_kernel(double* __restrict__ a, int64_t dp, int64_t k0,
                                                         int* __restrict__ info) {
   __shared__ double colbuf[2][kNb];
@@ -109,15 +110,17 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(double* __restrict__ a, 
       if (m == jb) colbuf[b][i] = t[c];
       __syncthreads();
       const double p = colbuf[b][j];
+      const double aij = colbuf[b][i];
       if (tid == 0 && !(p > 0.0) && info != nullptr) *info = 1;
-      const double dj = __builtin_sqrt(p);
-      const double lij = i == j ? dj : colbuf[b][i] / dj;
-      if (m == jb && i >= j) lo[i][j] = lij;
-      const double f = lij / dj;
+      // L_ij L_kj = a_ij a_kj / p: one division on the path from column to column.  All 16 entries
+      // are updated: only those in (j, i] are read again (published columns are j + 1 .. 63, and
+      // rows i <= j only ever feed their own unused entries), so no masks are needed.
+      const double f = aij / p;
 #pragma unroll
-      for (int c2 = 0; c2 < 16; ++c2) {
-        const int k = 16 * m + c2;
-        if (k > j && k <= i) t[c2] -= f * colbuf[b][k];
+      for (int c2 = 0; c2 < 16; ++c2) t[c2] = __builtin_fma(-f, colbuf[b][16 * m + c2], t[c2]);
+      if (m == jb && i >= j) {  // the factor's entry, off that path
+        const double dj = __builtin_sqrt(p);
+        lo[i][j] = i == j ? dj : aij / dj;
       }
     }
   }
@@ -129,7 +132,8 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(double* __restrict__ a, 
 }
 
 // panel below the diagonal block: row i solves x L11^T = a_i (one wavefront per row, lane j
-// holds x_j; the columns are settled in order, x_j = s_j / L_jj taken from lane j by readlane)
+// holds x_j; the columns are settled in order, x_j = s_j / L_jj (by the lane's reciprocal of its
+// pivot) taken from lane j by readlane)
 __global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ a, int64_t dp, int64_t k0) {
   __shared__ double l[kNb][kNb + 1];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -138,10 +142,10 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ a,
   const int64_t row = k0 + kNb + static_cast<int64_t>(blockIdx.x) * 4 + (tid >> 6);
   if (row >= dp) return;  // uniform per wavefront; no barrier follows
   double s = a[row * dp + k0 + lane];
-  const double ldiag = l[lane][lane];
+  const double rdiag = 1.0 / l[lane][lane];
   double x = 0.0;
   for (int j = 0; j < kNb; ++j) {
-    const double q = s / ldiag;  // lane j's value is x_j
+    const double q = s * rdiag;  // lane j's value is x_j
     const uint64_t qb = __builtin_bit_cast(uint64_t, q);
     const uint32_t lo32 = __builtin_amdgcn_readlane(static_cast<uint32_t>(qb), j);
     const uint32_t hi32 = __builtin_amdgcn_readlane(static_cast<uint32_t>(qb >> 32), j);
@@ -153,7 +157,8 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ a,
 }
 
 // trailing update of the lower tile pairs: A[ti][tj] -= L21[ti] L21[tj]^T (K = 64), tiles of 64
-// rows past k0 + 64, ti >= tj; 16 rows x 64 columns per wavefront
+// rows past k0 + 64, ti >= tj; 16 rows x 64 columns per wavefront.  Every operand and the 16
+// target entries of a lane are loaded before the first product (one round trip per launch).
 __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ a, int64_t dp, int64_t k0) {
   // tile pair of this workgroup: b = ti (ti + 1) / 2 + tj
   const int64_t b = blockIdx.x;
@@ -166,26 +171,25 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ a
   const int64_t base = k0 + kNb;
   const int64_t ra = base + ti * kNb + 16 * wave + j;  // A-side row
   const double* arow = a + ra * dp + k0;
-  f64x4 acc[4];
+  double av[16], bv[4][16], tv[4][4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) acc[c] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-  for (int kk0 = 0; kk0 < kNb; kk0 += 16) {
-    const f64x2 a01 = *reinterpret_cast<const f64x2*>(arow + kk0 + 4 * q);
-    const f64x2 a23 = *reinterpret_cast<const f64x2*>(arow + kk0 + 4 * q + 2);
-    const double av[4] = {a01.x, a01.y, a23.x, a23.y};
-    double bv[4][4];
+  for (int st = 0; st < 4; ++st) {
+    const f64x2 a01 = *reinterpret_cast<const f64x2*>(arow + 16 * st + 4 * q);
+    const f64x2 a23 = *reinterpret_cast<const f64x2*>(arow + 16 * st + 4 * q + 2);
+    av[4 * st] = a01.x;
+    av[4 * st + 1] = a01.y;
+    av[4 * st + 2] = a23.x;
+    av[4 * st + 3] = a23.y;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const double* brow = a + (base + tj * kNb + 16 * c + j) * dp + k0 + kk0 + 4 * q;
+      const double* brow = a + (base + tj * kNb + 16 * c + j) * dp + k0 + 16 * st + 4 * q;
       const f64x2 b01 = *reinterpret_cast<const f64x2*>(brow);
       const f64x2 b23 = *reinterpret_cast<const f64x2*>(brow + 2);
-      bv[c][0] = b01.x; bv[c][1] = b01.y; bv[c][2] = b23.x; bv[c][3] = b23.y;
+      bv[c][4 * st] = b01.x;
+      bv[c][4 * st + 1] = b01.y;
+      bv[c][4 * st + 2] = b23.x;
+      bv[c][4 * st + 3] = b23.y;
     }
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[s], bv[c][s], acc[c], 0, 0, 0);
   }
 #pragma unroll
   for (int c = 0; c < 4; ++c)
@@ -193,7 +197,23 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ a
     for (int r = 0; r < 4; ++r) {
       const int64_t row = base + ti * kNb + 16 * wave + 4 * r + q;
       const int64_t col = base + tj * kNb + 16 * c + j;
-      a[row * dp + col] -= acc[c][r];
+      tv[c][r] = a[row * dp + col];
+    }
+  asm volatile("" ::: "memory");
+  f64x4 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int s = 0; s < 16; ++s)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[s], bv[c][s], acc[c], 0, 0, 0);
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = base + ti * kNb + 16 * wave + 4 * r + q;
+      const int64_t col = base + tj * kNb + 16 * c + j;
+      a[row * dp + col] = tv[c][r] - acc[c][r];
     }
 }
 
@@ -207,9 +227,9 @@ __device__ __forceinline__ double rfac(const double* __restrict__ l, int64_t dp,
 // the earlier columns on the matrix cores: wavefront w takes block columns 16 (w % 4) .. + 15 and
 // every fourth 16-column step of the earlier columns from step w / 4 on (loads of the next step
 // issued before the products of the current one); the four partial sums of an entry are added in
-// LDS in a fixed order.  Then wavefronts 0..3 take 4 of the 16 rows each, 16 lanes a row, each
-// lane 4 of the block's columns, and the block's columns are quantized in order with the
-// correction of every later column of the block kept current.
+// LDS in a fixed order.  Then each wavefront takes one of the 16 rows, a lane per block column,
+// and the block's columns are quantized in order with the correction of every later column of
+// the block kept current.
 constexpr int kBlockThreads = 1024;
 
 __global__ __launch_bounds__(kBlockThreads) void gptq_block_kernel(const float* __restrict__ w, int64_t d_out,
@@ -226,40 +246,47 @@ __global__ __launch_bounds__(kBlockThreads) void gptq_block_kernel(const float* 
   const int64_t G = d_in / kGroup;
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int nb = d_in - c0 < kNb ? static_cast<int>(d_in - c0) : kNb;
-  // 1. partial C[row][c0 + 16 cg + j] over the steps kk0 = 16 (kq + 4 n) < c0
+  // 1. partial C[row][c0 + 16 cg + j] over the steps kk0 = 16 (kq + 4 n) < c0.  Rows past d_out and
+  //    columns past d_in read the last valid ones (their sums are never used), so every load is
+  //    unconditional and the next step's loads stay in flight across the current products.
   {
-    const int64_t ra = r0 + j;
-    const bool va = ra < d_out;
-    const double* drow = delta + (va ? ra : 0) * d_in + 4 * q;
-    const int64_t col = c0 + 16 * cg + j;
-    const bool vc = col < d_in;
+    const int64_t ra = r0 + j < d_out ? r0 + j : d_out - 1;
+    const double* drow = delta + ra * d_in + 4 * q;
+    const int64_t col = c0 + 16 * cg + j < d_in ? c0 + 16 * cg + j : d_in - 1;
     // R[p][col] = L[d-1-p][d-1-col]: rows p = kk0 + 4 q + s
-    const double* rcol = l + (d_in - 1 - 4 * q) * dp + (vc ? d_in - 1 - col : 0);
+    const double* rcol = l + (d_in - 1 - 4 * q) * dp + (d_in - 1 - col);
     f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
     double av[4], bv[4], an[4], bn[4];
     auto fetch = [&](int64_t kk0, double* ao, double* bo) {
       const f64x2 a01 = *reinterpret_cast<const f64x2*>(drow + kk0);
       const f64x2 a23 = *reinterpret_cast<const f64x2*>(drow + kk0 + 2);
-      ao[0] = va ? a01.x : 0.0;
-      ao[1] = va ? a01.y : 0.0;
-      ao[2] = va ? a23.x : 0.0;
-      ao[3] = va ? a23.y : 0.0;
+      ao[0] = a01.x;
+      ao[1] = a01.y;
+      ao[2] = a23.x;
+      ao[3] = a23.y;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) bo[s] = vc ? rcol[-(kk0 + s) * dp] : 0.0;
+      for (int s = 0; s < 4; ++s) bo[s] = rcol[-(kk0 + s) * dp];
     };
-    int64_t kk0 = 16 * kq;
-    if (kk0 < c0) fetch(kk0, av, bv);
-    while (kk0 < c0) {
-      const int64_t kn = kk0 + 64;
-      if (kn < c0) fetch(kn, an, bn);
+    // this wavefront's steps kk0 = 16 kq + 64 n, n < ns; the fetch of step n + 1 (clamped to the
+    // last step) is issued before the products of step n, the compiler fences keep it there.
+    // (Three steps in flight measured no faster: 4096 x 4096 8.47 vs 8.38 ms.)
+    const int64_t ns = 16 * kq < c0 ? (c0 - 16 * kq + 63) / 64 : 0;
+    auto kstep = [&](int64_t n) { return 16 * kq + 64 * (n < ns - 1 ? n : ns - 1); };
+    auto mma = [&](const double* ao, const double* bo) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av[s], bv[s], acc, 0, 0, 0);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        av[s] = an[s];
-        bv[s] = bn[s];
+      for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(ao[s], bo[s], acc, 0, 0, 0);
+    };
+    if (ns > 0) {  // uniform per wavefront
+      fetch(kstep(0), av, bv);
+      for (int64_t n = 0; n < ns; n += 2) {
+        fetch(kstep(n + 1), an, bn);
+        asm volatile("" ::: "memory");
+        mma(av, bv);
+        if (n + 1 >= ns) break;
+        fetch(kstep(n + 2), av, bv);
+        asm volatile("" ::: "memory");
+        mma(an, bn);
       }
-      kk0 = kn;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) part[kq][4 * r + q][16 * cg + j] = acc[r];
@@ -270,46 +297,37 @@ __global__ __launch_bounds__(kBlockThreads) void gptq_block_kernel(const float* 
     rd[i][k] = (i <= k && i < nb && k < nb) ? rfac(l, dp, d_in, c0 + i, c0 + k) : 0.0;
   }
   __syncthreads();
-  if (wave >= 4) return;  // no barrier follows
-  // 3. the block's columns in order: row 4 wave + lane / 16 of the workgroup's 16, lane % 16 owns
-  //    block columns 4 (lane % 16) .. + 3
-  const int rr = lane >> 4, pt = lane & 15;
-  const int64_t row = r0 + 4 * wave + rr;
-  const bool vr = row < d_out;
-  double cl[4], wl[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int k = 4 * pt + t, lr = 4 * wave + rr;
-    cl[t] = ((part[0][lr][k] + part[1][lr][k]) + part[2][lr][k]) + part[3][lr][k];
-    const bool in = vr && k < nb;
-    wl[t] = (in && dead[c0 + k] == 0) ? static_cast<double>(w[row * d_in + c0 + k]) : 0.0;
-  }
+  // 3. the block's columns in order: wavefront w takes row r0 + w, lane k block column k.  Column
+  //    i is quantized by lane i; its delta reaches every lane by readlane and corrects the later
+  //    columns.  Each lane keeps its own column's results and stores them at the end.
+  const int64_t row = r0 + wave;
+  if (row >= d_out) return;  // uniform per wavefront; no barrier follows
+  const int k = lane;
+  const bool in = k < nb;
+  double cl = ((part[0][wave][k] + part[1][wave][k]) + part[2][wave][k]) + part[3][wave][k];
+  const double wl = (in && dead[c0 + k] == 0) ? static_cast<double>(w[row * d_in + c0 + k]) : 0.0;
+  const double d = in ? static_cast<double>(scale[row * G + (c0 + k) / kGroup]) : 0.0;
+  const double inv_d = d > 0.0 ? 1.0 / d : 0.0;
+  const double inv_r = in ? 1.0 / rd[k][k] : 0.0;
+  double wh_k = 0.0, di_k = 0.0;
   for (int i = 0; i < nb; ++i) {
-    const int owner = i >> 2, ti = i & 3;
-    double di = 0.0;
-    if (pt == owner) {
-      double wi = wl[0], ci = cl[0];
-#pragma unroll
-      for (int t = 1; t < 4; ++t)
-        if (ti == t) {
-          wi = wl[t];
-          ci = cl[t];
-        }
-      const double v = wi + ci / rd[i][i];
-      const double d = vr ? static_cast<double>(scale[row * G + (c0 + i) / kGroup]) : 0.0;
-      const double wh = d * code64(v, d);
-      di = wi - wh;
-      if (vr) {
-        w_hat[row * d_in + c0 + i] = static_cast<float>(wh);
-        delta[row * d_in + c0 + i] = di;
-      }
+    // every lane evaluates its own column; lane i's is the one taken
+    const double v = wl + cl * inv_r;
+    const double wh = d * code64(v, d, inv_d);
+    const double di = wl - wh;
+    if (k == i) {
+      wh_k = wh;
+      di_k = di;
     }
-    di = __shfl(di, (lane & ~15) | owner);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int k = 4 * pt + t;
-      if (k > i && k < nb) cl[t] += rd[i][k] * di;
-    }
+    const uint64_t bits = __builtin_bit_cast(uint64_t, di);
+    const uint32_t lo32 = __builtin_amdgcn_readlane(static_cast<uint32_t>(bits), i);
+    const uint32_t hi32 = __builtin_amdgcn_readlane(static_cast<uint32_t>(bits >> 32), i);
+    const double dii = __builtin_bit_cast(double, (static_cast<uint64_t>(hi32) << 32) | lo32);
+    if (k > i) cl = __builtin_fma(rd[i][k], dii, cl);
+  }
+  if (in) {
+    w_hat[row * d_in + c0 + k] = static_cast<float>(wh_k);
+    delta[row * d_in + c0 + k] = di_k;
   }
 }
 

@@ -356,9 +356,10 @@ int w4a16_gemm_pc(const uint16_t* x, int64_t m, const uint8_t* packed, const uin
  *   (the current one is among them: the objective never rises).  Up to n_sweeps sweeps (>= 1),
  *   stopping after one that changes nothing.  Trials are scored exactly in fp64 as the change
  *   2 d^T u_g + d^T H_gg d of the objective (d = the group's error change, u = H e kept current
- *   through every accepted change).  Outputs: idx (out: the result), scale fp32 [d_out][G] out
- *   (its steps), obj_before / obj_after fp64 [d_out] or NULL, sweeps int32 [d_out] or NULL
- *   (sweeps run per row).
+ *   through every accepted change; H must be symmetric, as quant_hessian writes it, since the
+ *   change and the update of u read it by rows).  Outputs: idx (out: the result), scale fp32
+ *   [d_out][G] out (its steps), obj_before / obj_after fp64 [d_out] or NULL, sweeps int32
+ *   [d_out] or NULL (sweeps run per row).
  * joint_workspace_size -- bytes of the workspace both calls use to run all rows of up to 2048 at a
  *   time (u = H e for those rows in fp64 and partial objectives); any workspace of at least 64
  *   rows' share works, in more launches (W4Q_EINVAL below that, W4Q_EALIGN if misaligned).

@@ -278,130 +278,214 @@ __global__ __launch_bounds__(256) void part_sum_kernel(const double* __restrict_
   obj[r] = s;
 }
 
-// Coordinate descent, one workgroup per row, u = H e of the row in global memory (from
-// joint_u_kernel).  Per group: stage w_g, u_g and H_gg, try every candidate (4 threads per
-// candidate, each a quarter of the 32 x 32 form), keep the first minimum of dO (the current
-// candidate has dO = 0 exactly), and on a change apply u += H[:, g] d over the whole row.
-__global__ __launch_bounds__(256) void joint_cd_kernel(const float* __restrict__ w, int64_t d_in,
-                                                       const float* __restrict__ h, int64_t ldh,
-                                                       const float* __restrict__ alpha, int n_cand,
-                                                       uint8_t* __restrict__ idx, float* __restrict__ steps,
-                                                       double* __restrict__ u, const double* __restrict__ part,
-                                                       int n_split, int n_sweeps, double* __restrict__ obj_before,
-                                                       double* __restrict__ obj_after, int32_t* __restrict__ sweeps) {
+// Coordinate descent, kCdRows rows per workgroup (a wavefront per row), u = H e of each row in
+// global memory (from joint_u_kernel).  The rows visit their groups in lockstep, so H_gg is staged
+// once for all of them and the change u += H[:, g] d of every row that changed reads the 32 rows of
+// H once (H symmetric: row g0 + i of H is column g0 + i).  Per group, each wavefront tries its
+// row's candidates (on the fp64 matrix cores: H_gg times the changes of 16 candidates per
+// product) and keeps the first minimum of dO (the current candidate has dO = 0 exactly).  Rows
+// whose last sweep changed nothing stop sweeping (their trials would change nothing either); the
+// workgroup runs until all have.
+constexpr int kCdRows = 8;
+
+__global__ __launch_bounds__(64 * kCdRows) void joint_cd_kernel(const float* __restrict__ w, int64_t d_in,
+                                                                const float* __restrict__ h, int64_t ldh,
+                                                                const float* __restrict__ alpha, int n_cand,
+                                                                uint8_t* __restrict__ idx, float* __restrict__ steps,
+                                                                double* __restrict__ u,
+                                                                const double* __restrict__ part, int n_split,
+                                                                int n_sweeps, double* __restrict__ obj_before,
+                                                                double* __restrict__ obj_after,
+                                                                int32_t* __restrict__ sweeps, int64_t rows) {
+  constexpr int kThreads = 64 * kCdRows;
   __shared__ double hgg[kGroup][kGroup + 1];
-  __shared__ double ug[kGroup], ecur[kGroup], dl[kGroup];
-  __shared__ float wg[kGroup];
-  __shared__ float cand[256];
-  __shared__ double dobj[256];
-  __shared__ double red[256];
-  __shared__ int sel, changed;
-  const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
+  __shared__ double ug[kCdRows][kGroup], ecur[kCdRows][kGroup], dl[kCdRows][kGroup];
+  __shared__ float wg[kCdRows][kGroup];
+  __shared__ float cand[kCdRows][256];
+  __shared__ double dobj[kCdRows][256];
+  __shared__ int s_live, s_change;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kCdRows + wv;
+  const bool have = row < rows;  // uniform per wavefront; rows past the end follow along unseen
+  const int64_t rowc = have ? row : rows - 1;
   const int64_t G = d_in / kGroup;
-  const float* wr = w + row * d_in;
-  double* ur = u + row * d_in;
-  uint8_t* ir = idx + row * G;
-  if (tid == 0) {
+  const float* wr = w + rowc * d_in;
+  double* ur = u + rowc * d_in;
+  uint8_t* ir = idx + rowc * G;
+  if (have && lane == 0 && obj_before != nullptr) {
     double s = 0.0;
     for (int i = 0; i < n_split; ++i) s += part[row * n_split + i];
-    if (obj_before != nullptr) obj_before[row] = s;
+    obj_before[row] = s;
   }
+  bool live = have;  // this row still sweeping (uniform per wavefront)
   int sw = 0;
-  while (sw < n_sweeps) {
-    ++sw;
-    if (tid == 0) changed = 0;
+  for (int sweep = 0; sweep < n_sweeps; ++sweep) {
+    if (tid == 0) s_live = 0;
+    __syncthreads();
+    if (live && lane == 0) atomicOr(&s_live, 1 << wv);
+    __syncthreads();
+    if (s_live == 0) break;  // uniform
+    if (live) ++sw;
+    bool row_changed = false;
     for (int64_t g = 0; g < G; ++g) {
       const int64_t g0 = g * kGroup;
-      if (tid < kGroup) {
-        wg[tid] = wr[g0 + tid];
-        ug[tid] = ur[g0 + tid];
-      }
-      for (int i = tid; i < kGroup * kGroup; i += 256)
+      for (int i = tid; i < kGroup * kGroup; i += kThreads)
         hgg[i / kGroup][i % kGroup] = static_cast<double>(h[(g0 + i / kGroup) * ldh + g0 + i % kGroup]);
+      if (lane < kGroup) {
+        wg[wv][lane] = wr[g0 + lane];
+        ug[wv][lane] = ur[g0 + lane];
+      }
+      if (tid == 0) s_change = 0;
       __syncthreads();
       float amax = 0.0f;
 #pragma unroll
-      for (int i = 0; i < kGroup; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(wg[i]));
-      for (int k = tid; k < n_cand; k += 256) cand[k] = candidate(amax, alpha[k]);
+      for (int i = 0; i < kGroup; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(wg[wv][i]));
+      for (int k = lane; k < n_cand; k += 64) cand[wv][k] = candidate(amax, alpha[k]);
       const int kc = ir[g] < n_cand ? ir[g] : n_cand - 1;  // indices past the list: its last entry
       __syncthreads();
-      if (tid < kGroup) {
-        const float dc = cand[kc];
-        ecur[tid] = err(wg[tid], dc, inv_of(dc));
+      if (lane < kGroup) {
+        const float dc = cand[wv][kc];
+        ecur[wv][lane] = err(wg[wv][lane], dc, inv_of(dc));
       }
       __syncthreads();
-      for (int it = 0; it * 64 < n_cand; ++it) {
-        const int k = it * 64 + (tid >> 2), p4 = tid & 3;
-        const bool valid = k < n_cand;
-        const float dk = valid ? cand[k] : cand[kc];
-        const float ik = inv_of(dk);
-        double dv[kGroup];
+      if (live) {
+        // 16 candidates at a time on the matrix cores: lane (q, j) supplies the change d of
+        // candidate j at columns 16 kt + 4 q + s as the A operand, H_gg the B operand; the result
+        // (H_gg d)[16 ct + j] of candidate 4 r + q (register r of tile ct) is dotted with
+        // 2 u + H d by the same lane and summed over the 16 lanes of the quarter
+        const int q = lane >> 4, j = lane & 15;
+        for (int kb16 = 0; kb16 < n_cand; kb16 += 16) {
+          const int ka = kb16 + j < n_cand ? kb16 + j : kc;
+          const float da = cand[wv][ka], ia = inv_of(da);
+          f64x4 hd[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i) dv[i] = err(wg[i], dk, ik) - ecur[i];
-        double acc = 0.0;
-#pragma unroll 1
-        for (int ii = 0; ii < kGroup / 4; ++ii) {
-          const int i = 8 * p4 + ii;
-          double hd = 0.0;
+          for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int jj = 0; jj < kGroup; ++jj) hd += hgg[i][jj] * dv[jj];
-          // d_i again from LDS operands (a register array indexed by the lane's quarter would
-          // live in scratch memory)
-          const double di = err(wg[i], dk, ik) - ecur[i];
-          acc += di * (2.0 * ug[i] + hd);
+            for (int s = 0; s < 4; ++s) {
+              const int c = 16 * kt + 4 * q + s;
+              const double a = err(wg[wv][c], da, ia) - ecur[wv][c];
+#pragma unroll
+              for (int ct = 0; ct < 2; ++ct)
+                hd[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, hgg[c][16 * ct + j], hd[ct], 0, 0, 0);
+            }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int k = kb16 + 4 * r + q;
+            const float dk = cand[wv][k < n_cand ? k : kc];
+            const float ik = inv_of(dk);
+            double t = 0.0;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+              const int c = 16 * ct + j;
+              const double dc = err(wg[wv][c], dk, ik) - ecur[wv][c];
+              t += dc * (2.0 * ug[wv][c] + hd[ct][r]);
+            }
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+            if (j == 0 && k < n_cand) dobj[wv][k] = t;
+          }
         }
-        acc += __shfl_xor(acc, 1);
-        acc += __shfl_xor(acc, 2);
-        if (valid && p4 == 0) dobj[k] = acc;
       }
       __syncthreads();
-      if (tid == 0) {
-        int kb = 0;
-        for (int k = 1; k < n_cand; ++k)
-          if (dobj[k] < dobj[kb]) kb = k;  // strict: the first minimum wins
-        sel = kb;
-        ir[g] = static_cast<uint8_t>(kb);
-        if (kb != kc) changed = 1;
+      int kb = kc;
+      if (live) {
+        if (lane == 0) {
+          kb = 0;
+          for (int k = 1; k < n_cand; ++k)
+            if (dobj[wv][k] < dobj[wv][kb]) kb = k;  // strict: the first minimum wins
+          ir[g] = static_cast<uint8_t>(kb);
+          if (kb != kc) atomicOr(&s_change, 1 << wv);
+        }
+        kb = __shfl(kb, 0);
+        if (kb != kc) row_changed = true;
+      }
+      if (lane < kGroup) {
+        const float db = cand[wv][kb];
+        dl[wv][lane] = kb != kc ? err(wg[wv][lane], db, inv_of(db)) - ecur[wv][lane] : 0.0;
       }
       __syncthreads();
-      const int kb = sel;
-      if (kb != kc) {
-        if (tid < kGroup) {
-          const float db = cand[kb];
-          dl[tid] = err(wg[tid], db, inv_of(db)) - ecur[tid];
-        }
-        __syncthreads();
-        for (int64_t jc = tid; jc < d_in; jc += 256) {
-          double a = ur[jc];
-#pragma unroll 8
-          for (int i = 0; i < kGroup; ++i) a += static_cast<double>(h[(g0 + i) * ldh + jc]) * dl[i];
-          ur[jc] = a;
+      // u += H[:, g] d for the rows that changed: kCols columns per thread at a time, H read once
+      // for all rows, in two blocks of 16 of its 32 rows (the second block's loads in flight
+      // across the first block's products)
+      const int chg = s_change;  // uniform
+      constexpr int kCols = 2, kIb = 16;
+      if (chg != 0) {
+        // wave-uniform row pointers and 32-bit lane offsets (global loads with a scalar base)
+        double* ublk = u + static_cast<int64_t>(blockIdx.x) * kCdRows * d_in;
+        for (int64_t j0 = 0; j0 < d_in; j0 += kCols * kThreads) {
+          double a[kCols][kCdRows];
+          float hv[2][kIb][kCols];
+          uint32_t off[kCols];
+          bool inb[kCols];
+#pragma unroll
+          for (int m = 0; m < kCols; ++m) {
+            const int64_t jc = j0 + tid + m * kThreads;
+            inb[m] = jc < d_in;
+            off[m] = static_cast<uint32_t>(inb[m] ? jc : 0);
+          }
+          auto fetch = [&](int ib, int sl) {
+#pragma unroll
+            for (int ii = 0; ii < kIb; ++ii) {
+              const float* hrow = h + (g0 + ib + ii) * ldh;
+#pragma unroll
+              for (int m = 0; m < kCols; ++m) hv[sl][ii][m] = hrow[off[m]];
+            }
+          };
+          auto apply = [&](int ib, int sl) {
+#pragma unroll
+            for (int r = 0; r < kCdRows; ++r) {
+              if ((chg >> r) & 1) {  // uniform
+#pragma unroll
+                for (int ii = 0; ii < kIb; ++ii) {
+                  const double dr = dl[r][ib + ii];
+#pragma unroll
+                  for (int m = 0; m < kCols; ++m)
+                    a[m][r] = __builtin_fma(static_cast<double>(hv[sl][ii][m]), dr, a[m][r]);
+                }
+              }
+              asm volatile("" ::: "memory");  // one row's d at a time (bounds the live registers)
+            }
+          };
+          fetch(0, 0);
+#pragma unroll
+          for (int r = 0; r < kCdRows; ++r) {
+            const double* urow = ublk + r * d_in;
+#pragma unroll
+            for (int m = 0; m < kCols; ++m) a[m][r] = ((chg >> r) & 1) ? urow[off[m]] : 0.0;
+          }
+          fetch(kIb, 1);
+          asm volatile("" ::: "memory");
+          apply(0, 0);
+          apply(kIb, 1);
+#pragma unroll
+          for (int r = 0; r < kCdRows; ++r) {
+            double* urow = ublk + r * d_in;
+#pragma unroll
+            for (int m = 0; m < kCols; ++m)
+              if (((chg >> r) & 1) && inb[m]) urow[off[m]] = a[m][r];
+          }
         }
       }
       __syncthreads();
     }
-    if (changed == 0) break;
-    __syncthreads();
+    if (!row_changed) live = false;
   }
-  // the steps of the result, then its objective e . u (u maintained through every change)
-  for (int64_t g = tid; g < G; g += 256) {
+  // the steps of the result, then its objective e . u (u maintained through every change): a lane
+  // per group, the lane partials summed in a fixed order
+  if (!have) return;  // no barrier follows
+  double s = 0.0;
+  for (int64_t g = lane; g < G; g += 64) {
     float m = 0.0f;
     for (int i = 0; i < kGroup; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(wr[g * kGroup + i]));
-    steps[row * G + g] = candidate(m, alpha[ir[g]]);
+    const float d = candidate(m, alpha[ir[g]]);
+    steps[row * G + g] = d;
+    const float inv = inv_of(d);
+    for (int i = 0; i < kGroup; ++i) s += err(wr[g * kGroup + i], d, inv) * ur[g * kGroup + i];
   }
-  __syncthreads();
-  double s = 0.0;
-  for (int64_t jc = tid; jc < d_in; jc += 256) {
-    const float d = steps[row * G + jc / kGroup];
-    s += err(wr[jc], d, inv_of(d)) * ur[jc];
-  }
-  red[tid] = s;
-  __syncthreads();
-  if (tid == 0) {
-    double t = 0.0;
-    for (int i = 0; i < 256; ++i) t += red[i];
-    if (obj_after != nullptr) obj_after[row] = t;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) {
+    if (obj_after != nullptr) obj_after[row] = s;
     if (sweeps != nullptr) sweeps[row] = sw;
   }
 }
@@ -491,10 +575,10 @@ int w4q_launch_joint(const float* w, int64_t d_out, int64_t d_in, const float* h
                          h, ldh, cbs, u, part, n_split);
       int rc = w4q_launch_status();
       if (rc != W4Q_OK) return rc;
-      hipLaunchKernelGGL(joint_cd_kernel, dim3(static_cast<unsigned>(rows)), dim3(256), 0, s, w + r0 * d_in, d_in,
-                         h, ldh, alpha, n_cand, idx + r0 * G, steps + r0 * G, u, part, n_split, n_sweeps,
+      hipLaunchKernelGGL(joint_cd_kernel, dim3(cdiv(rows, kCdRows)), dim3(64 * kCdRows), 0, s, w + r0 * d_in,
+                         d_in, h, ldh, alpha, n_cand, idx + r0 * G, steps + r0 * G, u, part, n_split, n_sweeps,
                          obj_before ? obj_before + r0 : nullptr, obj_after ? obj_after + r0 : nullptr,
-                         sweeps ? sweeps + r0 : nullptr);
+                         sweeps ? sweeps + r0 : nullptr, rows);
       rc = w4q_launch_status();
       if (rc != W4Q_OK) return rc;
     } else {  // the objective of the given steps only

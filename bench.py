@@ -72,14 +72,15 @@ def src_hash(fname: str) -> str:
 
 
 def measured_peaks(dev):
-    """Measured peaks in the same job: a plain streaming read of 2 GiB and a loop of independent
-    bf16 matrix-core products (the library's probe calls), best of 5, timed with HIP events."""
+    """Measured peaks in the same job: a plain streaming read of 2 GiB and loops of independent
+    bf16 and fp64 matrix-core products (the library's probe calls), best of 5, timed with HIP
+    events."""
     import torch
     import w4a16_group_wise_amd as w4q
 
     buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
     buf.fill_(1)
-    best_r, best_m = 0.0, 0.0
+    best_r, best_m, best_d = 0.0, 0.0, 0.0
     for _ in range(5):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -93,9 +94,14 @@ def measured_peaks(dev):
         e1.record()
         e1.synchronize()
         best_m = max(best_m, flop / (e0.elapsed_time(e1) * 1e-3))
+        e0.record()
+        flop = w4q.probe_mfma_f64(8000, dev)
+        e1.record()
+        e1.synchronize()
+        best_d = max(best_d, flop / (e0.elapsed_time(e1) * 1e-3))
     del buf
     torch.cuda.empty_cache()
-    return {"hbm": best_r, "mfma": best_m}
+    return {"hbm": best_r, "mfma": best_m, "mfma_f64": best_d}
 
 
 def gemv_bytes(d_out, d_in, m=1):
@@ -248,7 +254,7 @@ def run_step(stack, events):
     timed("decode_pass", stack.decode_bytes, graph.replay)
 
 
-def components(stack, dev, reps=5):
+def components(stack, dev, peaks, reps=5):
     """Measurements outside the step: the prefill product on exact weights beside the step's
     dequantizing one, the decode pass in other launch orders, single launches of the largest
     shapes, and the rows beyond the step."""
@@ -343,15 +349,16 @@ def components(stack, dev, reps=5):
     us = median_us(lambda: w4q.w4a16_gemm(xs["mlp"][:1], e["packed"], e["s16"], out=e["y1"]), n=20)
     gb = gemv_bytes(12288, 4096)
     out["gemv_single_12288x4096"] = {"us": round(us, 2), "frac_hbm": round(gb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-    out["next_rows"] = next_rows(stack, dev, median_us)
+    out["next_rows"] = next_rows(stack, dev, median_us, peaks)
     return out
 
 
-def next_rows(stack, dev, median_us):
+def next_rows(stack, dev, median_us, peaks):
     """The rows beyond the step, each on one full-size shape of layer 0: the per-channel search,
     the joint objective's coordinate descent and GPTQ on the q projection (4096x4096, its 8192-token
     H, K = 40), and the fused LSQ + Adam update on the gate weight (12288x4096).  Rates are
-    algorithmic work over the median duration; the fp64 work is priced against the fp64 peak."""
+    algorithmic work over the median duration; the fp64 work is priced against the nominal fp64
+    peak and against the fp64 matrix-core rate measured in the same job."""
     import torch
     import w4a16_group_wise_amd as w4q
 
@@ -363,12 +370,14 @@ def next_rows(stack, dev, median_us):
     h = w4q.quant_hessian(xs[lin.inp], workspace=stack.ws)
     w4q.quant_scale_search(e["w"], h, stack.alpha, out=(e["scale"], e["idx"], e["obj"], None))
     fp64 = PEAK_FP64_TFLOPS * 1e12
+    mf64 = peaks["mfma_f64"]
     res = {}
     # per-channel: K candidates x (E H) over the row, 2 K d_in^2 flop per row
     t = median_us(lambda: w4q.quant_scale_search_pc(e["w"], h, stack.alpha), n=3)
     fl = 2.0 * n * K * k * k
     res["scale_search_pc_4096x4096"] = {"us": round(t, 1), "fp64_TFLOPs": round(fl / (t * 1e-6) / 1e12, 3),
-                                        "frac_fp64": round(fl / (t * 1e-6) / fp64, 4)}
+                                        "frac_fp64": round(fl / (t * 1e-6) / fp64, 4),
+                                        "frac_of_measured_fp64": round(fl / (t * 1e-6) / mf64, 4)}
     # joint: U = E H (2 d_out d_in^2 flop) and the descent; the objective ratio it reached
     ws = torch.empty(w4q.workspace_size("joint", n, k), dtype=torch.uint8, device=dev)
     t_obj = median_us(lambda: w4q.quant_joint_objective(e["w"], e["scale"], h, workspace=ws), n=3)
@@ -383,6 +392,7 @@ def next_rows(stack, dev, median_us):
     res["joint_4096x4096"] = {"objective_us": round(t_obj, 1),
                               "objective_fp64_TFLOPs": round(fl / (t_obj * 1e-6) / 1e12, 3),
                               "objective_frac_fp64": round(fl / (t_obj * 1e-6) / fp64, 4),
+                              "objective_frac_of_measured_fp64": round(fl / (t_obj * 1e-6) / mf64, 4),
                               "refine_2_sweeps_us": round(t_ref, 1),
                               "objective_after_over_before": round(float((oa / ob).mean().item()), 5),
                               "rows_converged": int((sw < 2).sum().item())}
@@ -391,7 +401,8 @@ def next_rows(stack, dev, median_us):
     t = median_us(lambda: w4q.quant_gptq(e["w"], h, e["scale"], workspace=wsg), n=3)
     fl = k ** 3 / 3.0 + 1.0 * n * k * k
     res["gptq_4096x4096"] = {"us": round(t, 1), "fp64_TFLOPs": round(fl / (t * 1e-6) / 1e12, 3),
-                             "frac_fp64": round(fl / (t * 1e-6) / fp64, 4)}
+                             "frac_fp64": round(fl / (t * 1e-6) / fp64, 4),
+                             "frac_of_measured_fp64": round(fl / (t * 1e-6) / mf64, 4)}
     del ws, wsg
     # fused LSQ + Adam on the gate weight (parameters and moments updated in place, next forward)
     g = per["gate"]
@@ -588,8 +599,9 @@ def run(args):
                          "frac_hbm": dp["frac"]},
         "measured_peaks": {"hbm_read_GBps": round(peaks["hbm"] / 1e9, 1),
                            "mfma_bf16_TFLOPs": round(peaks["mfma"] / 1e12, 1),
-                           "how": "w4q_probe_read (non-temporal) over 2 GiB and w4q_probe_mfma_bf16, "
-                                  "best of 5, HIP events"},
+                           "mfma_f64_TFLOPs": round(peaks["mfma_f64"] / 1e12, 1),
+                           "how": "w4q_probe_read (non-temporal) over 2 GiB, w4q_probe_mfma_bf16 and "
+                                  "w4q_probe_mfma_f64, best of 5, HIP events"},
         "timing": "timed region: HIP events around every launch on its stream; per family, sum of "
                   "algorithmic work / sum of launch durations",
         "kernels": kernels,
@@ -598,7 +610,7 @@ def run(args):
     }
     if not args.no_components:
         print("[bench] components", file=sys.stderr, flush=True)
-        out["components"].update(components(stack, dev))
+        out["components"].update(components(stack, dev, peaks))
     del stack
     torch.cuda.empty_cache()
     if not args.no_cpu:

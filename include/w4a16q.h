@@ -411,11 +411,15 @@ int quant_gptq(const float* w, int64_t d_out, int64_t d_in, const float* h, int6
  *                        matrix-core products on every wavefront (one per SIMD); sink is device
  *                        memory of W4Q_PROBE_SINK_WORDS floats; *flop (host, nullable) receives
  *                        the flop count of the launch.
- * Both enqueue one kernel on `stream` and return W4Q_EINVAL for bad arguments.
+ *   w4q_probe_mfma_f64   likewise for 8 independent 16x16x4 fp64 products per wavefront, four
+ *                        wavefronts per SIMD; sink is 8-B aligned device memory of
+ *                        W4Q_PROBE_SINK_WORDS / 2 doubles (W4Q_EALIGN if misaligned).
+ * Each enqueues one kernel on `stream` and returns W4Q_EINVAL for bad arguments.
  */
 #define W4Q_PROBE_SINK_WORDS 65536
 int w4q_probe_read(const void* buf, int64_t bytes, int nontemporal, uint32_t* sink, hipStream_t stream);
 int w4q_probe_mfma_bf16(float* sink, int64_t iters, double* flop, hipStream_t stream);
+int w4q_probe_mfma_f64(double* sink, int64_t iters, double* flop, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
                           "quant_scale_search_pc", "per_channel_workspace_size", "quant_pack_pc", "lsq_fwd_pc",
                           "lsq_bwd_pc", "w4a16_gemm_pc", "joint_workspace_size", "quant_joint_objective",
                           "quant_joint_refine", "gptq_workspace_size", "quant_gptq",
-                          "w4q_probe_read", "w4q_probe_mfma_bf16"}
+                          "w4q_probe_read", "w4q_probe_mfma_bf16", "w4q_probe_mfma_f64"}
     l = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(l, n), n
@@ -163,6 +163,9 @@ def test_probe_argument_errors():
     assert L.w4q_probe_read(A, 16, 1, None, None) == w4q.W4Q_EINVAL
     assert L.w4q_probe_read(A + 8, 16, 1, A, None) == w4q.W4Q_EALIGN
     assert L.w4q_probe_mfma_bf16(None, 10, None, None) == w4q.W4Q_EINVAL
+    assert L.w4q_probe_mfma_f64(None, 10, None, None) == w4q.W4Q_EINVAL
+    assert L.w4q_probe_mfma_f64(A, 0, None, None) == w4q.W4Q_EINVAL
+    assert L.w4q_probe_mfma_f64(A + 4, 10, None, None) == w4q.W4Q_EALIGN
     assert L.w4q_probe_mfma_bf16(A, 0, None, None) == w4q.W4Q_EINVAL
 
 

@@ -16,7 +16,7 @@ Entry points (same names as the C ABI):
 from ._lib import (LIB_PATH, W4Q_EALIGN, W4Q_EHIP, W4Q_EINVAL, W4Q_ESHAPE, W4Q_EUNSUPPORTED,
                    W4Q_GROUP, W4Q_OK, W4QError, lib, status_string, version)
 from .ops import (GemvGroupPlan, lsq_adam_step, lsq_bwd, lsq_bwd_pc, lsq_fwd, lsq_fwd_pc, probe_mfma_bf16,
-                  probe_read, quant_gptq, quant_hessian, quant_joint_objective, quant_joint_refine, quant_pack,
+                  probe_mfma_f64, probe_read, quant_gptq, quant_hessian, quant_joint_objective, quant_joint_refine, quant_pack,
                   quant_pack_pc, quant_scale_search, quant_scale_search_pc, w4a16_gemm, w4a16_gemm_dq,
                   w4a16_gemm_pc, w4a16_gemv_grouped, workspace_size)
 
@@ -25,7 +25,7 @@ __all__ = [
     "w4a16_gemm_dq",
     "w4a16_gemv_grouped", "GemvGroupPlan", "workspace_size",
     "quant_scale_search_pc", "quant_pack_pc", "lsq_fwd_pc", "lsq_bwd_pc", "w4a16_gemm_pc",
-    "quant_joint_objective", "quant_joint_refine", "quant_gptq", "probe_read", "probe_mfma_bf16",
+    "quant_joint_objective", "quant_joint_refine", "quant_gptq", "probe_read", "probe_mfma_bf16", "probe_mfma_f64",
     "W4QError", "lib", "LIB_PATH", "status_string", "version", "W4Q_GROUP", "W4Q_OK",
     "W4Q_EINVAL", "W4Q_ESHAPE", "W4Q_EALIGN", "W4Q_EUNSUPPORTED", "W4Q_EHIP",
 ]

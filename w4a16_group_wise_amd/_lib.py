@@ -62,6 +62,7 @@ SIGNATURES = {
     "quant_gptq": (_INT, [_P, _I64, _I64, _P, _I64, _P, _F, _P, _P, _P, _SZ, _P]),
     "w4q_probe_read": (_INT, [_P, _I64, _INT, _P, _P]),
     "w4q_probe_mfma_bf16": (_INT, [_P, _I64, _P, _P]),
+    "w4q_probe_mfma_f64": (_INT, [_P, _I64, _P, _P]),
 }
 W4Q_PROBE_SINK_WORDS = 65536
 

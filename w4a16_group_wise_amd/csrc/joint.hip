@@ -33,7 +33,6 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int kBK = 16;   // reduction rows of H per staged tile
 constexpr int kBN = 64;   // columns per block: four 16-wide matrix-core tiles
 constexpr int kLdt = 68;  // LDS row stride (floats): the four lane quarters read distinct banks
-constexpr int kTileF4 = kBK * kBN / 4;  // float4 loads per tile
 
 // e = w - d * code(w, d), exact in fp64 (d = 0: code 0)
 __device__ __forceinline__ double err(float w, float d, float inv) {
@@ -43,10 +42,11 @@ __device__ __forceinline__ double err(float w, float d, float inv) {
 
 __device__ __forceinline__ float inv_of(float d) { return d > 0.0f ? 1.0f / d : 0.0f; }
 
-// Stages rows kk0..kk0+15, columns c0..c0+63 of H (zeros past column d) through registers:
+// Stages rows kk0..kk0+BK-1, columns c0..c0+63 of H (zeros past column d) through registers:
 // fetch() issues the loads of this thread's share, put() writes them to an LDS buffer.
-template <int NT>
+template <int NT, int BK = kBK>
 struct Stager {
+  static constexpr int kTileF4 = BK * kBN / 4;  // float4 loads per tile
   static constexpr int kPer = (kTileF4 + NT - 1) / NT;
   f32x4 r[kPer];
   __device__ __forceinline__ void fetch(const float* __restrict__ h, int64_t ldh, int64_t d, int64_t kk0,
@@ -104,7 +104,8 @@ __global__ __launch_bounds__(64 * NW) void pc_search_kernel(const float* __restr
                                                              float* __restrict__ scale, uint8_t* __restrict__ idx,
                                                              float* __restrict__ obj, float* __restrict__ obj_all) {
   constexpr int NT = 64 * NW;
-  __shared__ float tile[2][kBK * kLdt];
+  constexpr int kPcBK = 2 * kBK;  // H rows per staged tile: two matrix-core steps per barrier
+  __shared__ float tile[2][kPcBK * kLdt];
   __shared__ double objs[256];
   __shared__ float wmax[NW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -121,8 +122,8 @@ __global__ __launch_bounds__(64 * NW) void pc_search_kernel(const float* __restr
 #pragma unroll
   for (int i = 1; i < NW; ++i) amax = __builtin_fmaxf(amax, wmax[i]);
 
-  const int nkb = static_cast<int>(d_in / kBK);
-  Stager<NT> st;
+  const int nkb = static_cast<int>(d_in / kPcBK);  // d_in % 32 == 0
+  Stager<NT, kPcBK> st;
   for (int cb = 0; cb < n_cand; cb += 16 * NW) {
     const int ka = cb + 16 * wave + j;  // this lane's A-side candidate
     const float da = ka < n_cand ? candidate(amax, alpha[ka]) : 0.0f;
@@ -143,11 +144,14 @@ __global__ __launch_bounds__(64 * NW) void pc_search_kernel(const float* __restr
       st.put(tile[0], tid);
       __syncthreads();
       for (int t = 0; t < nkb; ++t) {
-        const int64_t kk0 = static_cast<int64_t>(t) * kBK;
-        if (t + 1 < nkb) st.fetch(h, ldh, d_in, kk0 + kBK, c0, tid);
-        const f32x4 wv = *reinterpret_cast<const f32x4*>(wrow + kk0 + 4 * q);
-        const double a[4] = {err(wv.x, da, ia), err(wv.y, da, ia), err(wv.z, da, ia), err(wv.w, da, ia)};
-        tile_mma(tile[t & 1], a, acc, lane);
+        const int64_t kk0 = static_cast<int64_t>(t) * kPcBK;
+        if (t + 1 < nkb) st.fetch(h, ldh, d_in, kk0 + kPcBK, c0, tid);
+#pragma unroll
+        for (int sub = 0; sub < kPcBK / kBK; ++sub) {
+          const f32x4 wv = *reinterpret_cast<const f32x4*>(wrow + kk0 + kBK * sub + 4 * q);
+          const double a[4] = {err(wv.x, da, ia), err(wv.y, da, ia), err(wv.z, da, ia), err(wv.w, da, ia)};
+          tile_mma(tile[t & 1] + kBK * sub * kLdt, a, acc, lane);
+        }
         if (t + 1 < nkb) st.put(tile[(t + 1) & 1], tid);
         __syncthreads();
       }

@@ -1,10 +1,12 @@
 // probe.hip -- measured peaks that the rooflines are quoted against besides the nominal ones: a
-// plain streaming read of a large buffer (HBM) and a loop of independent bf16 matrix-core
-// products (MFMA).  Diagnostics only; no step of the quantization path runs here.
+// plain streaming read of a large buffer (HBM) and loops of independent bf16 and fp64
+// matrix-core products (MFMA).  Diagnostics only; no step of the quantization path runs here.
 #include "common.hpp"
 
 namespace w4q {
 namespace {
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kReadThreads = 256;
 constexpr int kReadUnroll = 4;  // independent 16-byte loads in flight per lane
@@ -60,6 +62,25 @@ __global__ __launch_bounds__(256) void mfma_kernel(float* __restrict__ sink, int
   sink[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+constexpr int kF64Chains = 8;   // independent accumulators per wavefront
+constexpr int kF64PerCu = 4;    // workgroups of 4 wavefronts per compute unit: 4 per SIMD
+
+// The fold is stored only if it equals a value it cannot reach, so the products stay live.
+__global__ __launch_bounds__(256) void mfma_f64_kernel(double* __restrict__ sink, int iters) {
+  f64x4 acc[kF64Chains];
+#pragma unroll
+  for (int c = 0; c < kF64Chains; ++c) acc[c] = f64x4{0.0, 0.0, 0.0, 0.0};
+  const double a = threadIdx.x * 1e-3, b = 0.5;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kF64Chains; ++c) acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[c], 0, 0, 0);
+  }
+  double s = 0.0;
+#pragma unroll
+  for (int c = 0; c < kF64Chains; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  if (s == -1.0) sink[(blockIdx.x * 256 + threadIdx.x) & (W4Q_PROBE_SINK_WORDS / 2 - 1)] = s;
+}
+
 }  // namespace
 }  // namespace w4q
 
@@ -97,6 +118,18 @@ int w4q_probe_mfma_bf16(float* sink, int64_t iters, double* flop, hipStream_t st
   if (static_cast<int64_t>(cus) * 256 > W4Q_PROBE_SINK_WORDS) return W4Q_EUNSUPPORTED;
   hipLaunchKernelGGL(mfma_kernel, dim3(cus), dim3(256), 0, stream, sink, static_cast<int>(iters));
   if (flop) *flop = static_cast<double>(cus) * 4 * iters * kMfmaChains * (2.0 * 32 * 32 * 16);
+  return w4q_launch_status();
+}
+
+int w4q_probe_mfma_f64(double* sink, int64_t iters, double* flop, hipStream_t stream) {
+  if (!sink || iters <= 0 || iters > (1 << 24)) return W4Q_EINVAL;
+  if (reinterpret_cast<uintptr_t>(sink) % 8 != 0) return W4Q_EALIGN;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return W4Q_EHIP;
+  hipLaunchKernelGGL(mfma_f64_kernel, dim3(cus * kF64PerCu), dim3(256), 0, stream, sink, static_cast<int>(iters));
+  if (flop) *flop = static_cast<double>(cus) * kF64PerCu * 4 * iters * kF64Chains * (2.0 * 16 * 16 * 4);
   return w4q_launch_status();
 }
 

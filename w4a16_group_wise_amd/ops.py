@@ -441,3 +441,15 @@ def probe_mfma_bf16(iters: int, device, sink: Optional[torch.Tensor] = None) -> 
     check("w4q_probe_mfma_bf16", lib().w4q_probe_mfma_bf16(sink.data_ptr(), int(iters), ctypes.byref(flop),
                                                            torch.cuda.current_stream(device).cuda_stream))
     return flop.value
+
+
+def probe_mfma_f64(iters: int, device, sink: Optional[torch.Tensor] = None) -> float:
+    """Enqueue one launch of independent fp64 matrix-core products (diagnostic: measured fp64
+    MFMA peak); returns its flop count."""
+    from ._lib import W4Q_PROBE_SINK_WORDS
+    device = torch.device(device)
+    sink = _out(sink, "sink", (W4Q_PROBE_SINK_WORDS // 2,), torch.float64, device)
+    flop = ctypes.c_double(0.0)
+    check("w4q_probe_mfma_f64", lib().w4q_probe_mfma_f64(sink.data_ptr(), int(iters), ctypes.byref(flop),
+                                                         torch.cuda.current_stream(device).cuda_stream))
+    return flop.value

@@ -331,21 +331,41 @@ __global__ __launch_bounds__(64 * kCdRows) void joint_cd_kernel(const float* __r
     if (s_live == 0) break;  // uniform
     if (live) ++sw;
     bool row_changed = false;
+    // H_gg, w_g and the current index of group g + 1 are loaded during group g (they do not
+    // change); u_g is read at the start of its group, after the previous group's update
+    constexpr int kHPer = kGroup * kGroup / kThreads;
+    float hpre[kHPer], wpre = 0.0f;
+    int ipre = 0;
+    auto prefetch = [&](int64_t gn) {
+      const int64_t n0 = gn * kGroup;
+#pragma unroll
+      for (int p = 0; p < kHPer; ++p) {
+        const int i = tid + p * kThreads;
+        hpre[p] = h[(n0 + i / kGroup) * ldh + n0 + i % kGroup];
+      }
+      if (lane < kGroup) wpre = wr[n0 + lane];
+      ipre = ir[gn];
+    };
+    prefetch(0);
     for (int64_t g = 0; g < G; ++g) {
       const int64_t g0 = g * kGroup;
-      for (int i = tid; i < kGroup * kGroup; i += kThreads)
-        hgg[i / kGroup][i % kGroup] = static_cast<double>(h[(g0 + i / kGroup) * ldh + g0 + i % kGroup]);
+#pragma unroll
+      for (int p = 0; p < kHPer; ++p) {
+        const int i = tid + p * kThreads;
+        hgg[i / kGroup][i % kGroup] = static_cast<double>(hpre[p]);
+      }
       if (lane < kGroup) {
-        wg[wv][lane] = wr[g0 + lane];
+        wg[wv][lane] = wpre;
         ug[wv][lane] = ur[g0 + lane];
       }
+      const int kc = ipre < n_cand ? ipre : n_cand - 1;  // indices past the list: its last entry
       if (tid == 0) s_change = 0;
       __syncthreads();
+      if (g + 1 < G) prefetch(g + 1);
       float amax = 0.0f;
 #pragma unroll
       for (int i = 0; i < kGroup; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(wg[wv][i]));
       for (int k = lane; k < n_cand; k += 64) cand[wv][k] = candidate(amax, alpha[k]);
-      const int kc = ir[g] < n_cand ? ir[g] : n_cand - 1;  // indices past the list: its last entry
       __syncthreads();
       if (lane < kGroup) {
         const float dc = cand[wv][kc];
@@ -393,14 +413,31 @@ __global__ __launch_bounds__(64 * kCdRows) void joint_cd_kernel(const float* __r
       __syncthreads();
       int kb = kc;
       if (live) {
+        // first minimum: each lane scans its candidates lane, lane + 64, ... in order, then the
+        // lanes combine, the lower index winning equal values
+        double bv = __builtin_inf();
+        int bi = 0x7FFFFFFF;
+        for (int k = lane; k < n_cand; k += 64) {
+          const double v = dobj[wv][k];
+          if (v < bv || bi == 0x7FFFFFFF) {
+            bv = v;
+            bi = k;
+          }
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const double ov = __shfl_xor(bv, off);
+          const int oi = __shfl_xor(bi, off);
+          if (ov < bv || (!(bv < ov) && oi < bi)) {
+            bv = ov;
+            bi = oi;
+          }
+        }
+        kb = bi;
         if (lane == 0) {
-          kb = 0;
-          for (int k = 1; k < n_cand; ++k)
-            if (dobj[wv][k] < dobj[wv][kb]) kb = k;  // strict: the first minimum wins
           ir[g] = static_cast<uint8_t>(kb);
           if (kb != kc) atomicOr(&s_change, 1 << wv);
         }
-        kb = __shfl(kb, 0);
         if (kb != kc) row_changed = true;
       }
       if (lane < kGroup) {

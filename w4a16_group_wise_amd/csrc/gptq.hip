@@ -27,8 +27,6 @@ typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kNb = 64;  // panel and column-block width
 
-__device__ __forceinline__ int64_t rup64(int64_t v) { return (v + 63) & ~int64_t(63); }
-
 // nearest code of the fp64 value v at step d (fp32, >= 0; inv_d ~ 1 / d): ties to the even code,
 // clamped.  The first guess rint(v inv_d) is within one code of the answer; (c +- 1/2) d is exact in
 // fp64 and v - (c +- 1/2) d has the sign of the exact difference, which settles it.

@@ -329,7 +329,8 @@ def quant_joint_objective(w: torch.Tensor, scale: torch.Tensor, h: torch.Tensor,
 def quant_joint_refine(w: torch.Tensor, h: torch.Tensor, alpha: torch.Tensor, idx: torch.Tensor,
                        n_sweeps: int = 2, inplace: bool = False, workspace: Optional[torch.Tensor] = None):
     """Coordinate descent over the groups of each row on the joint objective, from idx [d_out][G]
-    (u8).  -> (idx, scale f32 [d_out][G], obj_before f64, obj_after f64, sweeps i32) per row."""
+    (u8); h must be symmetric (as quant_hessian writes it).  -> (idx, scale f32 [d_out][G],
+    obj_before f64, obj_after f64, sweeps i32) per row."""
     _need(w, "w", torch.float32)
     d_out, d_in = w.shape
     G = d_in // W4Q_GROUP

@@ -20,11 +20,12 @@
 // byte (byte select with sign extension) gives 16 q in fp32.  The vector kernels accumulate
 // x * 16q with fused multiply-adds; the matrix-core kernel packs 16 q as bf16 (small integers,
 // exact) for the products.  The group's scale, times 1/16 (exact for every fp16 scale),
-// multiplies the group's sum, in fp32.  So the rounding error of a product is a few 2^-24 of sum |x * w_hat|, whatever the
-// codes and the spread of x (an offset encoding of the codes, x * (q + c) - x * c, would carry
-// an error of order 2^-24 c sum |x|, far above the product when the codes are mostly zero where
-// |x| is large).  The next chunk's codes, scales and activations are loaded while the current
-// chunk is being reduced.
+// multiplies the group's sum, in fp32.  So the rounding error of a product is a few 2^-24 of
+// sum |x * w_hat|, whatever the codes and the spread of x (an offset encoding of the codes,
+// x * (q + c) - x * c, would carry an error of order 2^-24 c sum |x|, far above the product when
+// the codes are mostly zero where |x| is large).  Launches of at least 48 MB of codes take the
+// exact bf16 code pairs from a table in LDS instead (see the stream kernel).  The next chunk's
+// codes, scales and activations are loaded while the current chunk is being reduced.
 #include <atomic>
 
 #include "common.hpp"
